@@ -1,0 +1,232 @@
+"""Seeded synthetic inputs for varlen paged attention.
+
+This module only builds inputs: request metadata, block tables, and the Q / K / V
+values.  It holds none of the attention arithmetic, and it is the one module that
+both the HIP path (tests, bench) and the CPU oracle's tests read inputs from.
+
+Shapes follow the worked workloads of the pages:
+
+* the ORCA iteration of one 4096-token prefill plus decodes at 1500 and 1700
+  cached positions ("ORCA 和 chunked prefill", section 2 table);
+* decode-heavy and chunked-prefill mixes ("ORCA 和 chunked prefill", sections 4-5);
+* six requests sharing a 4096-position prefix with 1024 private positions each
+  ("How To Scale Your Model 笔记(7-8)", section 3, "物理存一份，不保证从 HBM 只读一次").
+
+Memory layout (the library's own layout, described in include/varlen_attn.h):
+
+* ``q``      : ``[total_q_rows, num_q_heads, head_dim]``
+* ``k_pool`` : ``[num_pages, num_kv_heads, page_size, head_dim]``
+* ``v_pool`` : ``[num_pages, num_kv_heads, head_dim, page_size]``  (transposed page)
+
+bf16 tensors are carried as ``uint16`` bit patterns (numpy has no bf16); fp32 as
+``float32``.  Draw recipe (deterministic, independent of thread count): every
+stream ``s`` (0 lengths, 1 page permutation, 2 Q, 3 K pool, 4 V pool) draws from
+``numpy.random.default_rng(SeedSequence([seed, s, chunk]))``; values are float32
+N(0,1) drawn in memory order in chunks of ``CHUNK`` elements and rounded to bf16
+with round-to-nearest-even.
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+CHUNK = 1 << 22
+STREAM_LENGTHS, STREAM_PERM, STREAM_Q, STREAM_K, STREAM_V = 0, 1, 2, 3, 4
+BF16_NAN = np.uint16(0x7FC0)
+
+
+def _threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _rng(seed: int, stream: int, chunk: int = 0) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence([seed, stream, chunk]))
+
+
+def f32_to_bf16_bits(x: np.ndarray, out: np.ndarray) -> None:
+    """Round float32 to bf16 (nearest, ties to even) into ``out`` (uint16 bits)."""
+    u = x.view(np.uint32)
+    r = (u >> 16) & 1
+    r += 0x7FFF
+    r += u
+    r >>= 16
+    out[...] = r
+
+
+def _normal_fill(seed: int, stream: int, n: int, bf16: bool) -> np.ndarray:
+    out = np.empty(n, np.uint16 if bf16 else np.float32)
+    nchunks = (n + CHUNK - 1) // CHUNK
+
+    def job(c: int) -> None:
+        lo, hi = c * CHUNK, min(n, (c + 1) * CHUNK)
+        g = _rng(seed, stream, c)
+        x = g.standard_normal(hi - lo, dtype=np.float32)
+        if bf16:
+            f32_to_bf16_bits(x, out[lo:hi])
+        else:
+            out[lo:hi] = x
+
+    if nchunks <= 1:
+        for c in range(nchunks):
+            job(c)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(job, range(nchunks)))
+    return out
+
+
+@dataclass
+class Workload:
+    name: str
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    page_size: int
+    dtype: str                      # "bf16" or "f32"
+    q_start: np.ndarray             # int32 [R]
+    q_end: np.ndarray               # int32 [R]
+    kv_len: np.ndarray              # int32 [R]
+    block_table: np.ndarray         # int32 [R, max_pages]; unused entries are -1
+    num_pages: int
+    q: np.ndarray                   # [T, Hq, D]
+    k_pool: np.ndarray              # [P, Hkv, ps, D]
+    v_pool: np.ndarray              # [P, Hkv, D, ps]
+    softmax_scale: float = 0.0      # <= 0 means 1/sqrt(head_dim)
+    shared_prefix_pages: int = 0    # leading pages shared by every request (0: none)
+    notes: dict = field(default_factory=dict)
+
+    @property
+    def num_reqs(self) -> int:
+        return int(self.kv_len.shape[0])
+
+    @property
+    def total_q_rows(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def max_pages_per_req(self) -> int:
+        return int(self.block_table.shape[1])
+
+    @property
+    def elem_bytes(self) -> int:
+        return 2 if self.dtype == "bf16" else 4
+
+
+def build(name: str, q_rows: Sequence[int], kv_lens: Sequence[int], *, num_q_heads: int,
+          num_kv_heads: int, head_dim: int, page_size: int, dtype: str = "bf16", seed: int = 0,
+          permute_pages: bool = True, shared_prefix_pages: int = 0, poison_tail: bool = False,
+          extra_pages: int = 0, softmax_scale: float = 0.0) -> Workload:
+    """Build a workload from per-request (q_rows, kv_length) pairs.
+
+    Requests' Q rows are laid out back to back in request order.  Each request owns
+    ``ceil(kv_len / page_size)`` logical pages, except that with ``shared_prefix_pages``
+    > 0 the first that many logical pages of every request are one set of pages held
+    once in the pool.  The pool holds exactly the pages in use (+ ``extra_pages``
+    never referenced), permuted by a seeded permutation when ``permute_pages``.
+    With ``poison_tail`` the slots past kv_len in each tail page (and the extra pages)
+    hold NaN, so any read beyond a request's length shows in its output.
+    """
+    q_rows = np.asarray(q_rows, np.int64)
+    kv = np.asarray(kv_lens, np.int64)
+    R = len(kv)
+    assert q_rows.shape == (R,)
+    bf16 = dtype == "bf16"
+    ps = page_size
+    npg = (kv + ps - 1) // ps
+    sp = shared_prefix_pages
+    if sp:
+        assert np.all(npg >= sp), "every request must cover the shared prefix"
+    # logical page ids: the shared prefix first, then each request's own pages
+    owned = npg - sp if sp else npg
+    P = int(sp + owned.sum()) + extra_pages
+    perm = _rng(seed, STREAM_PERM).permutation(P) if permute_pages else np.arange(P)
+    maxp = int(npg.max()) if R else 1
+    bt = np.full((R, max(1, maxp)), -1, np.int32)
+    nxt = sp
+    for r in range(R):
+        logical = list(range(sp)) + list(range(nxt, nxt + int(owned[r])))
+        nxt += int(owned[r])
+        bt[r, : len(logical)] = perm[np.asarray(logical, np.int64)] if logical else []
+    qs = np.concatenate([[0], np.cumsum(q_rows)[:-1]]).astype(np.int32) if R else np.zeros(0, np.int32)
+    qe = (qs + q_rows).astype(np.int32)
+    T = int(q_rows.sum())
+    D = head_dim
+    q = _normal_fill(seed, STREAM_Q, T * num_q_heads * D, bf16).reshape(T, num_q_heads, D)
+    k = _normal_fill(seed, STREAM_K, P * num_kv_heads * ps * D, bf16).reshape(P, num_kv_heads, ps, D)
+    v = _normal_fill(seed, STREAM_V, P * num_kv_heads * D * ps, bf16).reshape(P, num_kv_heads, D, ps)
+    if poison_tail:
+        nanv = BF16_NAN if bf16 else np.float32(np.nan)
+        for r in range(R):
+            valid = int(kv[r]) - (int(npg[r]) - 1) * ps
+            if int(npg[r]) > 0 and valid < ps:
+                p = bt[r, int(npg[r]) - 1]
+                k[p, :, valid:, :] = nanv
+                v[p, :, :, valid:] = nanv
+        for u in range(P - extra_pages, P):
+            k[perm[u]] = nanv
+            v[perm[u]] = nanv
+    return Workload(name=name, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, head_dim=D,
+                    page_size=ps, dtype=dtype, q_start=qs, q_end=qe, kv_len=kv.astype(np.int32),
+                    block_table=bt, num_pages=P, q=q, k_pool=k, v_pool=v, softmax_scale=softmax_scale,
+                    shared_prefix_pages=sp)
+
+
+def uniform_lengths(seed: int, n: int, lo: int, hi: int) -> np.ndarray:
+    """n integers uniform in [lo, hi] inclusive (stream 0 of the seed)."""
+    return _rng(seed, STREAM_LENGTHS).integers(lo, hi, size=n, endpoint=True)
+
+
+CONFIG_NAMES = {
+    1: "tiny-mixed-f32",
+    2: "orca-mixed-llama7b",
+    3: "decode-heavy-gqa",
+    4: "chunked-prefill-mix-gqa8",
+    5: "shared-prefix-6",
+    51: "shared-prefix-64",
+}
+
+
+def config(cid: int, seed: Optional[int] = None, poison_tail: bool = False,
+           scale: int = 1) -> Workload:
+    """The five workloads of the pages (plus 51: the scaled shared-prefix variant).
+
+    ``scale`` > 1 shrinks the lengths (integer division, min 1) and keeps the head
+    layout, for parity runs the oracle finishes quickly.
+    """
+    s = cid if seed is None else seed
+
+    def sh(x):
+        return np.maximum(1, np.asarray(x, np.int64) // scale)
+
+    if cid == 1:
+        # A uncached prefill 64/64, B decode 1/100, C chunk 16 rows on S0=32
+        return build(CONFIG_NAMES[1], [64, 1, 16], [64, 100, 48], num_q_heads=4, num_kv_heads=2,
+                     head_dim=64, page_size=16, dtype="f32", seed=s, permute_pages=False,
+                     poison_tail=poison_tail)
+    if cid == 2:
+        a = int(sh(4096))
+        return build(CONFIG_NAMES[2], [a, 1, 1], [a, int(sh(1500)), int(sh(1700))], num_q_heads=32,
+                     num_kv_heads=32, head_dim=128, page_size=16, seed=s, poison_tail=poison_tail)
+    if cid == 3:
+        n = max(1, 256 // scale)
+        kv = sh(uniform_lengths(s, n, 1024, 8192))
+        return build(CONFIG_NAMES[3], [1] * n, kv, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                     page_size=64, seed=s, poison_tail=poison_tail)
+    if cid == 4:
+        n = max(1, 64 // scale)
+        kv = sh(uniform_lengths(s, n, 512, 16384))
+        chunk, total = int(sh(2048)), int(sh(32768))
+        return build(CONFIG_NAMES[4], [chunk] + [1] * n, [total] + list(kv), num_q_heads=64,
+                     num_kv_heads=8, head_dim=128, page_size=64, seed=s, poison_tail=poison_tail)
+    if cid in (5, 51):
+        nreq, shared = (6, 4096) if cid == 5 else (64, 16384)
+        shared = max(64, (shared // scale) // 64 * 64)
+        priv = int(sh(1024))
+        return build(CONFIG_NAMES[cid], [1] * nreq, [shared + priv] * nreq, num_q_heads=32,
+                     num_kv_heads=8, head_dim=128, page_size=64, seed=s,
+                     shared_prefix_pages=shared // 64, poison_tail=poison_tail)
+    raise ValueError(f"unknown config {cid}")

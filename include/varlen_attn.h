@@ -1,0 +1,167 @@
+/*
+ * varlen_attn.h -- C ABI of the MI355X (gfx950) varlen paged attention library.
+ *
+ * One call computes one attention layer of one serving iteration in which requests at
+ * different stages share a flat Q tensor: uncached prefills, chunked-prefill chunks,
+ * and decode steps.
+ *
+ *   Request r contributes q_rows = q_end[r] - q_start[r] new query rows (rows
+ *   q_start[r] .. q_end[r]-1 of the flat Q tensor) and has kv_len[r] positions of
+ *   context after this iteration's K/V were appended ("ORCA 和 chunked prefill",
+ *   section 2: the (q_start, q_end, kv_length) triple).  With S0 = kv_len - q_rows,
+ *   new row i (0-based within the request) reads the S0 cached positions and the new
+ *   positions up to and including its own, i.e. positions 0 .. S0+i
+ *   ("How To Scale Your Model 笔记(7-8)", section 2: the mask is zero on the first S0
+ *   columns and hides only the strict upper triangle of the last q_rows columns).
+ *
+ *   out[t, h, :] = softmax_j( scale * <q[t, h, :], K_r[j, kvh, :]> ) . V_r[j, kvh, :]
+ *   over the visible j, with kvh = h / g, g = num_q_heads / num_kv_heads (grouped-query
+ *   attention: "How To Scale Your Model 笔记(7-8)", section 3, KV 容量与 GQA) and
+ *   scale = 1/sqrt(head_dim) by default ("一次 forward 怎么塞下很多个 request",
+ *   section 6: softmax(Q K^T / sqrt(d_head)) V, computed request by request).
+ *
+ *   K_r / V_r are reached through request r's block table: logical position j lives in
+ *   physical page block_table[r][j / page_size], slot j % page_size ("How To Scale Your
+ *   Model 笔记(7-8)", section 3, paging).
+ *
+ * Memory layouts (all row-major, element type given by va_params.dtype):
+ *   q, out   [total_q_rows][num_q_heads][head_dim]
+ *   k_pool   [num_pages][num_kv_heads][page_size][head_dim]
+ *   v_pool   [num_pages][num_kv_heads][head_dim][page_size]   (V pages are transposed)
+ *   block table  int32 [num_reqs][max_pages_per_req]; only the first
+ *                ceil(kv_len[r] / page_size) entries of row r are read.
+ *
+ * Ownership: the caller owns every buffer passed in (device memory allocated by e.g.
+ * PyTorch).  A plan owns its host metadata and one device buffer of work lists,
+ * freed by varlen_attn_plan_destroy().  The library never frees or keeps caller memory.
+ *
+ * Errors: every entry point returns a va_status and never aborts; on failure
+ * varlen_attn_last_error() returns a message describing the first problem found (per
+ * calling thread).  varlen_attn_plan() validates all metadata on the host;
+ * varlen_attn_run() checks pointers and the workspace size only and assumes the
+ * device block table holds the same ids as the host one given to the plan.
+ *
+ * Streams: run() and debug_gather() only enqueue work on the given stream (NULL = the
+ * null stream); they do not synchronise, allocate or copy from the host, so they can be
+ * captured into a HIP graph.  A plan is immutable and can be reused by every layer of an
+ * iteration and by concurrent runs on different streams (each with its own workspace).
+ */
+#ifndef VARLEN_ATTN_H
+#define VARLEN_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  VA_OK = 0,
+  VA_ERR_INVALID_ARG = -1,          /* bad metadata, null pointer, bad sizes */
+  VA_ERR_UNSUPPORTED = -2,          /* valid but not built for (head_dim, page_size, dtype) */
+  VA_ERR_OUT_OF_MEMORY = -3,        /* host or device allocation of the plan failed */
+  VA_ERR_HIP = -4,                  /* a HIP runtime call failed (message has hipGetErrorString) */
+  VA_ERR_WORKSPACE_TOO_SMALL = -5   /* workspace_bytes below what the plan reported */
+} va_status;
+
+typedef enum { VA_DTYPE_BF16 = 0, VA_DTYPE_F32 = 1 } va_dtype;
+
+enum {
+  /* Find requests whose block tables start with the same physical pages and read those
+   * pages once per group for all the group's rows ("How To Scale Your Model 笔记(7-8)",
+   * section 3: load one common KV block, let several requests' queries use it, each
+   * request keeping its own running max and sum). */
+  VA_FLAG_SHARED_PREFIX = 1u << 0,
+  /* Route every row through the split-KV kernel (no MFMA prefill tiles). */
+  VA_FLAG_NO_PREFILL_KERNEL = 1u << 1,
+  /* Build the plan on the host only: no device buffer, run() refuses it.  Used to test
+   * planning without a GPU. */
+  VA_FLAG_HOST_ONLY = 1u << 2
+};
+
+typedef struct {
+  int32_t num_q_heads;        /* Hq >= 1 */
+  int32_t num_kv_heads;       /* Hkv >= 1, Hq % Hkv == 0 */
+  int32_t head_dim;           /* 64 or 128 */
+  int32_t page_size;          /* 16, 32, 64, 128 or 256 positions per page */
+  int32_t num_pages;          /* pages in each pool */
+  int32_t max_pages_per_req;  /* row stride of the block table */
+  int32_t dtype;              /* va_dtype of q, k_pool, v_pool, out; accumulation is fp32 */
+  float softmax_scale;        /* <= 0: 1/sqrt(head_dim) */
+  uint32_t flags;             /* VA_FLAG_* */
+  int32_t prefill_min_rows;   /* q_rows from which a request uses prefill tiles; <= 0: 64 */
+  int32_t split_len;          /* kv positions per split-KV item; <= 0: chosen by the planner */
+} va_params;
+
+typedef struct {
+  int64_t num_reqs;
+  int64_t total_q_rows;       /* max(q_end): rows q and out must hold */
+  int64_t prefill_tiles;      /* MFMA prefill work tiles */
+  int64_t split_items;        /* split-KV work items (one wavefront each) */
+  int64_t shared_items;       /* of which read a shared prefix for several requests */
+  int64_t shared_groups;      /* groups of requests found sharing leading pages */
+  int64_t partial_slots;      /* (m, l, acc[head_dim]) partial results in the workspace */
+  int64_t combine_rows;       /* (row, head) outputs merged by the combine pass */
+  int64_t visible_pairs;      /* sum over requests of m*S0 + m(m+1)/2 */
+  double flops;               /* 4 * head_dim * num_q_heads * visible_pairs */
+  int64_t logical_kv_bytes;   /* sum kv_len * Hkv * head_dim * 2 (K and V) * elem */
+  int64_t physical_kv_bytes;  /* distinct (page, slot) positions read, same units */
+  int64_t q_bytes;            /* query rows read */
+  int64_t o_bytes;            /* output rows written */
+  int64_t table_bytes;        /* block-table entries read */
+  int64_t workspace_bytes;    /* device scratch run() needs */
+  double plan_host_us;        /* host time spent in varlen_attn_plan */
+} va_plan_stats;
+
+typedef struct va_plan va_plan;   /* opaque, immutable after creation */
+
+/* Build a plan for one iteration's metadata (all arrays are host memory, read during the
+ * call only).  Validates: q_start <= q_end, q_rows <= kv_len, Q ranges do not overlap,
+ * kv_len <= max_pages_per_req * page_size, the first ceil(kv_len/page_size) block-table ids
+ * of every request in [0, num_pages),
+ * Hq % Hkv == 0, supported head_dim / page_size / dtype.  Requests with q_rows == 0 are
+ * skipped.  Unless VA_FLAG_HOST_ONLY is set, uploads the work lists to a device buffer on
+ * the current HIP device (synchronously).  On success *plan_out is a new plan and
+ * *workspace_bytes_out (if not NULL) the device workspace run() needs. */
+va_status varlen_attn_plan(const va_params* params, int32_t num_reqs, const int32_t* q_start,
+                           const int32_t* q_end, const int32_t* kv_len,
+                           const int32_t* block_table_host, va_plan** plan_out,
+                           size_t* workspace_bytes_out);
+
+/* Enqueue the attention of the planned iteration on `stream` (a hipStream_t, NULL for the
+ * null stream).  q, k_pool, v_pool, out: device buffers in the layouts above;
+ * block_table_dev: device copy of the block table given to the plan; workspace: device
+ * buffer of at least the plan's workspace bytes (contents need not be initialised; may be
+ * NULL when the plan needs none).  Output rows outside every request are not written. */
+va_status varlen_attn_run(const va_plan* plan, const void* q, const void* k_pool, const void* v_pool,
+                          const int32_t* block_table_dev, void* out, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* Counters of the planned work (no device access). */
+va_status varlen_attn_plan_stats(const va_plan* plan, va_plan_stats* out);
+
+/* Copy every request's K and V into logical order through the same page-address code the
+ * attention kernels use: k_out, v_out are device [sum_r kv_len[r]][num_kv_heads][head_dim]
+ * (requests back to back).  Exists to test the page gather bit for bit. */
+va_status varlen_attn_debug_gather(const va_plan* plan, const void* k_pool, const void* v_pool,
+                                   const int32_t* block_table_dev, void* k_out, void* v_out,
+                                   void* stream);
+
+/* Introspection for tests: the plan's host work lists as int32 records.
+ * which = 0: split-KV items {req, kvh, col0, ncols, k0, k1, slot, flags}
+ *         1: query columns {q_row, q_head, limit, pbase}
+ *         2: combine rows {q_row, q_head, pbase, nparts}
+ *         3: prefill tiles {req, kvh, c0, ncols, q0, S0, kv_end, key_diag}
+ * *data stays valid until the plan is destroyed. */
+va_status varlen_attn_plan_export(const va_plan* plan, int32_t which, const int32_t** data,
+                                  int64_t* count, int32_t* ints_per_entry);
+
+void varlen_attn_plan_destroy(va_plan* plan);
+const char* varlen_attn_status_string(va_status status);
+const char* varlen_attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VARLEN_ATTN_H */

@@ -1,0 +1,251 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the same seeded
+inputs.  Tolerances: max |gpu - oracle| <= 2e-2 for bf16 inputs/outputs with fp32
+accumulation, <= 1e-4 for fp32; the page gather is compared bit for bit."""
+import functools
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from varlen_paged_attention_amd import api, workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "f32": 1e-4}
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    torch.cuda.set_device(0)
+    api.lib()
+    yield
+
+
+@functools.lru_cache(maxsize=4)
+def _cfg(cid, scale=1, poison=False):
+    return W.config(cid, scale=scale, poison_tail=poison)
+
+
+def _oracle_full(w):
+    return oracle.varlen_paged_attention(w.q, w.k_pool, w.v_pool, w.block_table, w.q_start, w.q_end, w.kv_len,
+                                         w.page_size, w.softmax_scale or None)
+
+
+def _covered_rows(w):
+    rows = np.zeros(w.total_q_rows, bool)
+    for r in range(w.num_reqs):
+        rows[w.q_start[r]:w.q_end[r]] = True
+    return rows
+
+
+def _check_full(w, out, label):
+    got = out.float().cpu().numpy().astype(np.float64)
+    ref = _oracle_full(w)
+    rows = _covered_rows(w)
+    err = np.abs(got[rows] - ref[rows])
+    e = float(err.max()) if err.size else 0.0
+    _say(f"[parity] {label}: max|gpu-oracle| = {e:.3e} (tol {TOL[w.dtype]})")
+    assert np.isfinite(got[rows]).all(), f"{label}: non-finite output"
+    assert e <= TOL[w.dtype], f"{label}: max error {e}"
+    return e
+
+
+SMALL = [
+    ("tiny-f32", 1, 1, 0),
+    ("orca-mixed/4", 2, 4, 0),
+    ("orca-mixed/4 split-only", 2, 4, api.VA_FLAG_NO_PREFILL_KERNEL),
+    ("decode-heavy/8", 3, 8, 0),
+    ("chunk-mix/8", 4, 8, 0),
+    ("shared-6", 5, 1, api.VA_FLAG_SHARED_PREFIX),
+    ("shared-6 plain", 5, 1, 0),
+    ("shared-64/8", 51, 8, api.VA_FLAG_SHARED_PREFIX),
+]
+
+
+@pytest.mark.parametrize("label,cid,scale,flags", SMALL, ids=[s[0] for s in SMALL])
+def test_parity_small_elementwise(label, cid, scale, flags):
+    """Every output element at reduced lengths (several tiles and splits, ragged tails)."""
+    w = W.config(cid, scale=scale, poison_tail=True)
+    _say(f"[gpu] run {label} rows={w.total_q_rows} kv={list(w.kv_len[:4])}...")
+    out, plan = api.run_workload(w, flags=flags)
+    _check_full(w, out, label)
+
+
+def _sample_rows(w, rng, nreq, nrows):
+    """(request, rows) samples: the first/last requests, the longest, and random ones."""
+    R = w.num_reqs
+    reqs = {0, R - 1, int(np.argmax(w.kv_len)), int(np.argmin(w.kv_len))}
+    reqs |= set(int(x) for x in rng.choice(R, size=min(R, nreq), replace=False))
+    out = []
+    for r in sorted(reqs):
+        m = int(w.q_end[r] - w.q_start[r])
+        rows = {0, m - 1} | set(int(x) for x in rng.choice(m, size=min(m, nrows), replace=False))
+        out.append((r, sorted(rows)))
+    return out
+
+
+FULL = [("orca-mixed", 2, 0), ("decode-heavy", 3, 0), ("chunk-mix", 4, 0), ("shared-6", 5, api.VA_FLAG_SHARED_PREFIX),
+        ("shared-64", 51, api.VA_FLAG_SHARED_PREFIX)]
+
+
+@pytest.mark.parametrize("label,cid,flags", FULL, ids=[f[0] for f in FULL])
+def test_parity_full_size_sampled(label, cid, flags):
+    """Full-size workloads in the launch configuration the bench times; sampled rows (all
+    heads) computed one by one by the oracle."""
+    w = _cfg(cid)
+    _say(f"[gpu] run full {label}: reqs={w.num_reqs} rows={w.total_q_rows} pages={w.num_pages}")
+    out, plan = api.run_workload(w, flags=flags)
+    got = out.float().cpu().numpy()
+    rng = np.random.default_rng(100 + cid)
+    worst = 0.0
+    for r, rows in _sample_rows(w, rng, 10, 12):
+        ref = oracle.attention_rows(w.q, w.k_pool, w.v_pool, w.block_table, w.q_start, w.q_end, w.kv_len,
+                                    w.page_size, r, rows)
+        for h, o in ref.items():
+            g = got[int(w.q_start[r]) + np.asarray(rows), h, :]
+            assert np.isfinite(g).all()
+            worst = max(worst, float(np.abs(g - o).max()))
+    _say(f"[parity] full {label}: sampled max|gpu-oracle| = {worst:.3e}")
+    assert worst <= TOL[w.dtype]
+
+
+def _raw_gather(w):
+    """Logical-order K and V of every request by numpy fancy indexing (raw bits)."""
+    ks, vs = [], []
+    for r in range(w.num_reqs):
+        j = np.arange(int(w.kv_len[r]))
+        pages = w.block_table[r][j // w.page_size]
+        slots = j % w.page_size
+        ks.append(w.k_pool[pages, :, slots, :])                       # [L, Hkv, D]
+        vs.append(w.v_pool[pages, :, :, slots])                      # [L, Hkv, D]
+    return np.concatenate(ks), np.concatenate(vs)
+
+
+@pytest.mark.parametrize("cid,scale", [(1, 1), (2, 1), (3, 8), (5, 1)])
+def test_gather_bit_exact(cid, scale):
+    import torch
+    w = W.config(cid, scale=scale, poison_tail=True)
+    _say(f"[gpu] gather config {cid}/{scale}")
+    plan = api.plan_for(w)
+    q, k, v, bt = api.to_device(w)
+    total = int(w.kv_len.sum())
+    ko = torch.empty(total, w.num_kv_heads, w.head_dim, dtype=k.dtype, device="cuda")
+    vo = torch.empty_like(ko)
+    api.varlen_attn_debug_gather(plan, k, v, bt, ko, vo)
+    torch.cuda.synchronize()
+    kr, vr = _raw_gather(w)
+    view = (lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)) if w.dtype == "bf16" else \
+        (lambda t: t.cpu().numpy())
+    gk, gv = view(ko), view(vo)
+    assert gk.shape == kr.shape and gv.shape == vr.shape
+    assert np.array_equal(gk.view(np.uint8), np.ascontiguousarray(kr).view(np.uint8))
+    assert np.array_equal(gv.view(np.uint8), np.ascontiguousarray(vr).view(np.uint8))
+
+
+def _bits(t):
+    import torch
+    return t.view(torch.int16).cpu().numpy() if t.dtype == torch.bfloat16 else t.cpu().numpy().view(np.int32)
+
+
+def test_page_permutation_bitwise():
+    """Physical page placement changes no output bit (same plan shape, same kernel order)."""
+    w = W.config(2, scale=4)
+    _say("[gpu] page permutation")
+    a, _ = api.run_workload(w)
+    perm = np.random.default_rng(5).permutation(w.num_pages)
+    w2 = W.Workload(**{**w.__dict__})
+    w2.k_pool = np.empty_like(w.k_pool)
+    w2.v_pool = np.empty_like(w.v_pool)
+    w2.k_pool[perm] = w.k_pool
+    w2.v_pool[perm] = w.v_pool
+    bt = w.block_table.copy()
+    bt[bt >= 0] = perm[bt[bt >= 0]]
+    w2.block_table = bt
+    b, _ = api.run_workload(w2)
+    assert np.array_equal(_bits(a), _bits(b))
+
+
+def test_request_isolation_bitwise():
+    w = W.config(3, scale=8)
+    _say("[gpu] isolation")
+    a, _ = api.run_workload(w)
+    w2 = W.Workload(**{**w.__dict__})
+    w2.q = w.q.copy()
+    w2.k_pool = w.k_pool.copy()
+    w2.v_pool = w.v_pool.copy()
+    r = 3
+    w2.q[w.q_start[r]:w.q_end[r]] ^= np.uint16(0x0040)
+    npg = (int(w.kv_len[r]) + w.page_size - 1) // w.page_size
+    pages = w.block_table[r, :npg]
+    w2.k_pool[pages] ^= np.uint16(0x0040)
+    w2.v_pool[pages] ^= np.uint16(0x0040)
+    b, _ = api.run_workload(w2)
+    A, B = _bits(a), _bits(b)
+    others = np.ones(w.total_q_rows, bool)
+    others[w.q_start[r]:w.q_end[r]] = False
+    assert np.array_equal(A[others], B[others])
+    assert not np.array_equal(A[~others], B[~others])
+
+
+def test_deterministic():
+    w = W.config(4, scale=8)
+    _say("[gpu] determinism")
+    a, plan = api.run_workload(w)
+    b, _ = api.run_workload(w, plan=plan)
+    assert np.array_equal(_bits(a), _bits(b))
+
+
+EDGE = [
+    ("gap+zero-row+kv1", dict(q_rows=[3, 0, 1, 1, 5], kv=[3, 9, 1, 2, 40], hq=4, hkv=4, d=64, ps=16)),
+    ("g16-multi-row", dict(q_rows=[3, 1], kv=[700, 257], hq=32, hkv=2, d=128, ps=256)),
+    ("mtp-g8-ps32", dict(q_rows=[5, 4, 1], kv=[300, 64, 31], hq=16, hkv=2, d=128, ps=32)),
+    ("long-decode", dict(q_rows=[1, 1], kv=[40000, 77], hq=8, hkv=1, d=128, ps=64)),
+    ("d64-bf16-prefill", dict(q_rows=[130, 2], kv=[200, 2], hq=6, hkv=3, d=64, ps=16)),
+    ("f32-d128", dict(q_rows=[17, 1], kv=[40, 90], hq=4, hkv=2, d=128, ps=16, dtype="f32")),
+]
+
+
+@pytest.mark.parametrize("label,spec", EDGE, ids=[e[0] for e in EDGE])
+def test_edge_cases(label, spec):
+    import torch
+    w = W.build(label, spec["q_rows"], spec["kv"], num_q_heads=spec["hq"], num_kv_heads=spec["hkv"],
+                head_dim=spec["d"], page_size=spec["ps"], dtype=spec.get("dtype", "bf16"), seed=17,
+                poison_tail=True, extra_pages=2)
+    # leave two untouched rows between requests 0 and 1
+    w.q_start = w.q_start.copy()
+    w.q_end = w.q_end.copy()
+    w.q_start[1:] += 2
+    w.q_end[1:] += 2
+    w.q = np.concatenate([w.q[:w.q_end[0]], np.zeros((2,) + w.q.shape[1:], w.q.dtype), w.q[w.q_end[0]:]])
+    _say(f"[gpu] edge {label}")
+    plan = api.plan_for(w)
+    q, k, v, bt = api.to_device(w)
+    out = torch.full_like(q, 7.0)
+    ws = api.new_workspace(plan)
+    api.varlen_attn_run(plan, q, k, v, bt, out, ws)
+    torch.cuda.synchronize()
+    _check_full(w, out, label)
+    gap = out[w.q_end[0]:w.q_start[1]].float().cpu().numpy()
+    assert (gap == 7.0).all(), "rows outside every request were written"
+
+
+def test_run_errors():
+    import torch
+    w = W.config(1)
+    plan = api.plan_for(w)
+    q, k, v, bt = api.to_device(w)
+    out = torch.zeros_like(q)
+    small = torch.empty(max(1, plan.workspace_bytes - 1), dtype=torch.uint8, device="cuda")
+    with pytest.raises(api.VarlenAttnError) as ei:
+        api.varlen_attn_run(plan, q, k, v, bt, out, small)
+    assert ei.value.status == api.VA_ERR_WORKSPACE_TOO_SMALL
+    L = api.lib()
+    assert L.varlen_attn_run(plan.handle, None, None, None, None, None, None, 0, None) == api.VA_ERR_INVALID_ARG

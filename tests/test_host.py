@@ -1,0 +1,195 @@
+"""CPU tests of the C-ABI library: it loads, exports what the header declares, validates
+metadata, and plans work that covers every visible (row, head, position) exactly once.
+No compute call is made (plans are built with VA_FLAG_HOST_ONLY)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from varlen_paged_attention_amd import api, workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HOST = api.VA_FLAG_HOST_ONLY
+
+
+def _declared_functions():
+    names = []
+    for f in os.listdir(os.path.join(ROOT, "include")):
+        if f.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", f)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(varlen_attn_\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    L = api.lib()
+    declared = _declared_functions()
+    assert len(declared) >= 8
+    for name in declared:
+        assert hasattr(L, name), f"{name} declared in include/ but not exported"
+    assert sorted(api.EXPORTED) == declared
+
+
+def _plan(w, flags=HOST, **kw):
+    return api.plan_for(w, flags=flags | HOST, **kw)
+
+
+def _small():
+    return W.build("s", [5, 1, 3], [9, 40, 3], num_q_heads=4, num_kv_heads=2, head_dim=64, page_size=16, seed=1)
+
+
+def _expect(status, **over):
+    w = _small()
+    args = dict(num_q_heads=4, num_kv_heads=2, head_dim=64, page_size=16, num_pages=w.num_pages,
+                q_start=w.q_start, q_end=w.q_end, kv_len=w.kv_len, block_table=w.block_table, flags=HOST)
+    args.update(over)
+    with pytest.raises(api.VarlenAttnError) as ei:
+        api.varlen_attn_plan(**args)
+    assert ei.value.status == status, str(ei.value)
+    return str(ei.value)
+
+
+def test_plan_validation_errors():
+    w = _small()
+    E, U = api.VA_ERR_INVALID_ARG, api.VA_ERR_UNSUPPORTED
+    assert "q_rows > kv_len" in _expect(E, kv_len=np.array([4, 40, 3]))
+    assert "q_start" in _expect(E, q_end=np.array([4, 10, 13]) - 5)
+    assert "overlap" in _expect(E, q_start=np.array([0, 4, 6]), q_end=np.array([5, 5, 9]))
+    bt = w.block_table.copy()
+    bt[1, 0] = w.num_pages
+    assert "outside" in _expect(E, block_table=bt)
+    bt[1, 0] = -1
+    assert "outside" in _expect(E, block_table=bt)
+    assert "max_pages_per_req" in _expect(E, kv_len=np.array([9, 16 * w.block_table.shape[1] + 1, 3]))
+    assert "multiple" in _expect(E, num_q_heads=3)
+    _expect(U, head_dim=96)
+    _expect(U, page_size=24)
+    _expect(E, num_pages=0)
+
+
+def test_status_strings_and_null_args():
+    L = api.lib()
+    for s in (0, -1, -2, -3, -4, -5):
+        assert L.varlen_attn_status_string(s)
+    h = ctypes.c_void_p()
+    assert L.varlen_attn_plan(None, 0, None, None, None, None, ctypes.byref(h), None) == api.VA_ERR_INVALID_ARG
+    assert L.varlen_attn_run(None, None, None, None, None, None, None, 0, None) == api.VA_ERR_INVALID_ARG
+    p = _plan(_small())
+    # a host-only plan refuses to run
+    assert L.varlen_attn_run(p.handle, None, None, None, None, None, None, 0, None) == api.VA_ERR_INVALID_ARG
+    assert b"HOST_ONLY" in L.varlen_attn_last_error()
+
+
+def test_empty_and_zero_row_requests_plan():
+    w = W.build("z", [0, 3, 0], [5, 7, 0], num_q_heads=2, num_kv_heads=1, head_dim=64, page_size=16, seed=2)
+    st = api.varlen_attn_plan_stats(_plan(w))
+    assert st["combine_rows"] == 3 * 2
+    assert st["visible_pairs"] == 3 * 4 + 6
+
+
+def check_coverage(w, plan):
+    """Every visible (row, head, position) is scored exactly once, by a prefill tile or by
+    one split item, and the items' slots of each output are distinct and in range."""
+    items = api.varlen_attn_plan_export(plan, 0)
+    cols = api.varlen_attn_plan_export(plan, 1)
+    comb = api.varlen_attn_plan_export(plan, 2)
+    tiles = api.varlen_attn_plan_export(plan, 3)
+    Hq, g, ps = w.num_q_heads, w.num_q_heads // w.num_kv_heads, w.page_size
+    req_of_row = np.full(w.total_q_rows, -1)
+    for r in range(w.num_reqs):
+        req_of_row[w.q_start[r]:w.q_end[r]] = r
+    cover = {}                 # (row, head) -> list of (k0, k1) intervals
+    slots = {}
+    comb_map = {(int(c[0]), int(c[1])): (int(c[2]), int(c[3])) for c in comb}
+    for it in items:
+        req, kvh, col0, ncols, k0, k1, slot, flags = (int(x) for x in it)
+        assert 1 <= ncols <= 16 and k0 < k1 and k0 % 8 == 0
+        for c in cols[col0:col0 + ncols]:
+            row, head, limit, pbase = (int(x) for x in c)
+            r = req_of_row[row]
+            assert head // g == kvh
+            m = int(w.q_end[r] - w.q_start[r])
+            assert limit == int(w.kv_len[r]) - m + (row - int(w.q_start[r]))
+            # the table used must hold the column's own pages over [k0, min(k1, limit+1))
+            hi = min(k1, limit + 1)
+            if hi > k0:
+                pages = range(k0 // ps, (hi - 1) // ps + 1)
+                assert all(w.block_table[req, p] == w.block_table[r, p] for p in pages)
+                cover.setdefault((row, head), []).append((k0, hi))
+            pb, npart = comb_map[(row, head)]
+            assert pb == pbase and 0 <= slot < npart
+            slots.setdefault((row, head), []).append(slot)
+            if not (flags & 1):
+                assert k1 - 1 <= limit
+    for t in tiles:
+        req, kvh, c0, ncols, q0, S0, kv_end, key_diag = (int(x) for x in t)
+        for c in range(c0, c0 + ncols):
+            i, hh = divmod(c, g)
+            row, head = q0 + i, kvh * g + hh
+            cover.setdefault((row, head), []).append((0, S0 + i + 1))
+            assert kv_end >= S0 + i + 1
+    for (row, head), s in slots.items():
+        assert len(s) == len(set(s)), f"slot reused for {(row, head)}"
+    for r in range(w.num_reqs):
+        m = int(w.q_end[r] - w.q_start[r])
+        S0 = int(w.kv_len[r]) - m
+        for i in range(m):
+            for h in range(Hq):
+                iv = sorted(cover.get((int(w.q_start[r]) + i, h), []))
+                assert iv, f"row {i} head {h} of request {r} not covered"
+                assert iv[0][0] == 0 and iv[-1][1] == S0 + i + 1
+                for a, b in zip(iv, iv[1:]):
+                    assert a[1] == b[0], f"gap/overlap {a} {b}"
+
+
+CASES = [
+    ("tiny", lambda: W.config(1), 0),
+    ("orca-small", lambda: W.config(2, scale=16), 0),
+    ("orca-small-split-only", lambda: W.config(2, scale=16), api.VA_FLAG_NO_PREFILL_KERNEL),
+    ("decode", lambda: W.config(3, scale=16), 0),
+    ("chunk-mix", lambda: W.config(4, scale=16), 0),
+    ("shared", lambda: W.config(5), api.VA_FLAG_SHARED_PREFIX),
+    ("shared-scaled", lambda: W.config(51, scale=8), api.VA_FLAG_SHARED_PREFIX),
+    ("mtp-g8", lambda: W.build("m", [4, 3, 1], [100, 64, 33], num_q_heads=16, num_kv_heads=2, head_dim=128,
+                               page_size=32, seed=3), 0),
+]
+
+
+@pytest.mark.parametrize("name,make,flags", CASES, ids=[c[0] for c in CASES])
+def test_plan_covers_every_visible_pair_once(name, make, flags):
+    w = make()
+    check_coverage(w, _plan(w, flags))
+
+
+@pytest.mark.parametrize("name,make,flags", CASES, ids=[c[0] for c in CASES])
+def test_plan_counters_match_oracle(name, make, flags):
+    w = make()
+    st = api.varlen_attn_plan_stats(_plan(w, flags))
+    m = w.q_end - w.q_start
+    assert st["visible_pairs"] == oracle.visible_pairs(m, w.kv_len)
+    assert st["flops"] == oracle.attention_flops(m, w.kv_len, w.num_q_heads, w.head_dim)
+    assert st["logical_kv_bytes"] == oracle.logical_kv_bytes(w.kv_len, w.num_kv_heads, w.head_dim, w.elem_bytes)
+    assert st["physical_kv_bytes"] == oracle.physical_kv_bytes(w.block_table, w.kv_len, w.page_size,
+                                                               w.num_kv_heads, w.head_dim, w.elem_bytes)
+
+
+def test_shared_prefix_groups_found():
+    w = W.config(5)
+    st = api.varlen_attn_plan_stats(_plan(w, api.VA_FLAG_SHARED_PREFIX))
+    assert st["shared_groups"] == 1 and st["shared_items"] > 0
+    assert st["physical_kv_bytes"] == 40 * 2 ** 20 and st["logical_kv_bytes"] == 120 * 2 ** 20
+    st0 = api.varlen_attn_plan_stats(_plan(w))
+    assert st0["shared_groups"] == 0
+
+
+def test_config_shapes():
+    """The workloads match the configurations they stand for."""
+    w = W.config(2)
+    assert list(w.q_end - w.q_start) == [4096, 1, 1] and list(w.kv_len) == [4096, 1500, 1700]
+    assert w.num_pages == 256 + 94 + 107
+    w = W.config(5)
+    assert w.num_pages == 64 + 6 * 16 and w.shared_prefix_pages == 64

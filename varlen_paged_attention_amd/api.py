@@ -1,0 +1,232 @@
+"""ctypes binding over the C ABI in include/varlen_attn.h (argument marshalling only).
+
+Every function here has the name of the C entry point it calls.  Tensors are PyTorch
+tensors on the GPU (only their data pointers cross the boundary); metadata arrays are
+host numpy int32 arrays.  There is no fallback: if ``libvarlen_attn.so`` has not been
+built the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+VA_OK, VA_ERR_INVALID_ARG, VA_ERR_UNSUPPORTED, VA_ERR_OUT_OF_MEMORY, VA_ERR_HIP, VA_ERR_WORKSPACE_TOO_SMALL = \
+    0, -1, -2, -3, -4, -5
+VA_DTYPE_BF16, VA_DTYPE_F32 = 0, 1
+VA_FLAG_SHARED_PREFIX, VA_FLAG_NO_PREFILL_KERNEL, VA_FLAG_HOST_ONLY = 1, 2, 4
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvarlen_attn.so")
+EXPORTED = ["varlen_attn_plan", "varlen_attn_run", "varlen_attn_plan_stats", "varlen_attn_plan_export",
+            "varlen_attn_debug_gather", "varlen_attn_plan_destroy", "varlen_attn_status_string",
+            "varlen_attn_last_error"]
+
+
+class VaParams(ctypes.Structure):
+    _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32), ("max_pages_per_req", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float), ("flags", ctypes.c_uint32),
+                ("prefill_min_rows", ctypes.c_int32), ("split_len", ctypes.c_int32)]
+
+
+class VaPlanStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("num_reqs", "total_q_rows", "prefill_tiles", "split_items",
+                                              "shared_items", "shared_groups", "partial_slots",
+                                              "combine_rows", "visible_pairs")] + \
+               [("flops", ctypes.c_double)] + \
+               [(n, ctypes.c_int64) for n in ("logical_kv_bytes", "physical_kv_bytes", "q_bytes", "o_bytes",
+                                              "table_bytes", "workspace_bytes")] + \
+               [("plan_host_us", ctypes.c_double)]
+
+
+class VarlenAttnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"status {status}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load libvarlen_attn.so (after torch, so both use the one HIP runtime in the process)."""
+    global _lib
+    if _lib is None:
+        try:
+            import torch  # noqa: F401  (loads torch's libamdhip64 first; ours binds to it by soname)
+        except ImportError:
+            pass
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
+                               "(python -m varlen_paged_attention_amd.build_lib)")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        i32p = ctypes.POINTER(ctypes.c_int32)
+        L.varlen_attn_plan.argtypes = [ctypes.POINTER(VaParams), ctypes.c_int32, i32p, i32p, i32p, i32p,
+                                       ctypes.POINTER(P), ctypes.POINTER(ctypes.c_size_t)]
+        L.varlen_attn_plan.restype = ctypes.c_int
+        L.varlen_attn_run.argtypes = [P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.varlen_attn_run.restype = ctypes.c_int
+        L.varlen_attn_plan_stats.argtypes = [P, ctypes.POINTER(VaPlanStats)]
+        L.varlen_attn_plan_stats.restype = ctypes.c_int
+        L.varlen_attn_plan_export.argtypes = [P, ctypes.c_int32, ctypes.POINTER(i32p),
+                                              ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int32)]
+        L.varlen_attn_plan_export.restype = ctypes.c_int
+        L.varlen_attn_debug_gather.argtypes = [P, P, P, P, P, P, P]
+        L.varlen_attn_debug_gather.restype = ctypes.c_int
+        L.varlen_attn_plan_destroy.argtypes = [P]
+        L.varlen_attn_plan_destroy.restype = None
+        L.varlen_attn_status_string.argtypes = [ctypes.c_int]
+        L.varlen_attn_status_string.restype = ctypes.c_char_p
+        L.varlen_attn_last_error.argtypes = []
+        L.varlen_attn_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != VA_OK:
+        L = lib()
+        raise VarlenAttnError(status, f"{L.varlen_attn_status_string(status).decode()}: "
+                                      f"{L.varlen_attn_last_error().decode()}")
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _ptr32(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+class Plan:
+    """Owns a va_plan handle (destroyed with the object)."""
+
+    def __init__(self, handle: ctypes.c_void_p, workspace_bytes: int, params: VaParams):
+        self.handle = handle
+        self.workspace_bytes = int(workspace_bytes)
+        self.params = params
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h and _lib is not None:
+            _lib.varlen_attn_plan_destroy(h)
+            self.handle = None
+
+
+def varlen_attn_plan(*, num_q_heads: int, num_kv_heads: int, head_dim: int, page_size: int, num_pages: int,
+                     q_start, q_end, kv_len, block_table, dtype: str = "bf16", softmax_scale: float = 0.0,
+                     flags: int = 0, prefill_min_rows: int = 0, split_len: int = 0) -> Plan:
+    qs, qe, kv = _i32(q_start), _i32(q_end), _i32(kv_len)
+    bt = _i32(block_table)
+    if bt.ndim != 2 or not (len(qs) == len(qe) == len(kv) == bt.shape[0]):
+        raise ValueError("q_start/q_end/kv_len must be [R] and block_table [R, max_pages]")
+    p = VaParams(num_q_heads, num_kv_heads, head_dim, page_size, num_pages, bt.shape[1],
+                 VA_DTYPE_BF16 if dtype == "bf16" else VA_DTYPE_F32, softmax_scale, flags,
+                 prefill_min_rows, split_len)
+    h = ctypes.c_void_p()
+    ws = ctypes.c_size_t()
+    _check(lib().varlen_attn_plan(ctypes.byref(p), len(kv), _ptr32(qs), _ptr32(qe), _ptr32(kv), _ptr32(bt),
+                                  ctypes.byref(h), ctypes.byref(ws)))
+    return Plan(h, ws.value, p)
+
+
+def plan_for(w, flags: int = 0, **kw) -> Plan:
+    """Plan for a ``workloads.Workload``."""
+    return varlen_attn_plan(num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+                            page_size=w.page_size, num_pages=w.num_pages, q_start=w.q_start, q_end=w.q_end,
+                            kv_len=w.kv_len, block_table=w.block_table, dtype=w.dtype,
+                            softmax_scale=w.softmax_scale, flags=flags, **kw)
+
+
+def varlen_attn_plan_stats(plan: Plan) -> dict:
+    st = VaPlanStats()
+    _check(lib().varlen_attn_plan_stats(plan.handle, ctypes.byref(st)))
+    return {n: getattr(st, n) for n, _ in VaPlanStats._fields_}
+
+
+def varlen_attn_plan_export(plan: Plan, which: int) -> np.ndarray:
+    data = ctypes.POINTER(ctypes.c_int32)()
+    count = ctypes.c_int64()
+    width = ctypes.c_int32()
+    _check(lib().varlen_attn_plan_export(plan.handle, which, ctypes.byref(data), ctypes.byref(count),
+                                         ctypes.byref(width)))
+    n = count.value * width.value
+    if n == 0:
+        return np.zeros((0, width.value), np.int32)
+    return np.ctypeslib.as_array(data, shape=(n,)).reshape(count.value, width.value).copy()
+
+
+def _dev_ptr(t, name: str, dtype=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_ptr(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _elem_dtype(plan: Plan):
+    import torch
+    return torch.bfloat16 if plan.params.dtype == VA_DTYPE_BF16 else torch.float32
+
+
+def varlen_attn_run(plan: Plan, q, k_pool, v_pool, block_table_dev, out, workspace=None, stream=None) -> None:
+    import torch
+    dt = _elem_dtype(plan)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().varlen_attn_run(plan.handle, _dev_ptr(q, "q", dt), _dev_ptr(k_pool, "k_pool", dt),
+                                 _dev_ptr(v_pool, "v_pool", dt), _dev_ptr(block_table_dev, "block_table", torch.int32),
+                                 _dev_ptr(out, "out", dt), _dev_ptr(workspace, "workspace"), ws_bytes,
+                                 _stream_ptr(stream)))
+
+
+def varlen_attn_debug_gather(plan: Plan, k_pool, v_pool, block_table_dev, k_out, v_out, stream=None) -> None:
+    import torch
+    dt = _elem_dtype(plan)
+    _check(lib().varlen_attn_debug_gather(plan.handle, _dev_ptr(k_pool, "k_pool", dt), _dev_ptr(v_pool, "v_pool", dt),
+                                          _dev_ptr(block_table_dev, "block_table", torch.int32),
+                                          _dev_ptr(k_out, "k_out", dt), _dev_ptr(v_out, "v_out", dt),
+                                          _stream_ptr(stream)))
+
+
+def new_workspace(plan: Plan, device="cuda"):
+    import torch
+    return torch.empty(max(1, plan.workspace_bytes), dtype=torch.uint8, device=device)
+
+
+def to_device(w, device="cuda"):
+    """Move a workload's arrays to the GPU: (q, k_pool, v_pool, block_table) torch tensors."""
+    import torch
+
+    def conv(a):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        if a.dtype == np.uint16:
+            t = t.view(torch.bfloat16)
+        return t.to(device)
+
+    return conv(w.q), conv(w.k_pool), conv(w.v_pool), torch.from_numpy(_i32(w.block_table)).to(device)
+
+
+def run_workload(w, flags: int = 0, plan: Optional[Plan] = None, device="cuda", **kw):
+    """Plan + run one workload; returns (out tensor, plan)."""
+    import torch
+    plan = plan or plan_for(w, flags, **kw)
+    q, k, v, bt = to_device(w, device)
+    out = torch.zeros_like(q)
+    ws = new_workspace(plan, device)
+    varlen_attn_run(plan, q, k, v, bt, out, ws)
+    torch.cuda.synchronize()
+    return out, plan

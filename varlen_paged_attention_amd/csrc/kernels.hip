@@ -1,0 +1,517 @@
+// HIP kernels for gfx950 (MI355X) and the device half of the C ABI.
+//
+// Kernels
+//   split_kv_*   one wavefront per split-KV item: streams a kv range of one request's
+//                paged K/V for one KV head and scores it against up to 16 query columns
+//                (rows x query heads of the group) with 16x16 MFMA tiles; keeps a running
+//                max and sum per column and writes an unnormalised partial (m, l, acc).
+//   combine      merges the partials of each (row, head) output with the log-sum-exp
+//                rule and writes the output row.
+//   gather       copies K/V into logical order through the same page addressing (for
+//                the bit-exact gather test).
+//
+// The softmax runs in the base-2 domain: scores are multiplied by scale*log2(e) once and
+// exponentiated with v_exp_f32, so the running max m is in those units too.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "va_internal.h"
+
+namespace va {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegBig = -1e30f;   // running-max start: finite, so fully masked steps keep alpha = 1
+
+// ---------------------------------------------------------------- page addressing --
+// Pools: K [page][kv_head][slot][d], V [page][kv_head][d][slot] (transposed page).
+// Logical position j of a request is slot j % page_size of page block_table[j / page_size].
+struct Paged {
+  int Hkv, ps_shift, D;
+  __device__ __forceinline__ int ps() const { return 1 << ps_shift; }
+  __device__ __forceinline__ int page_of(const int32_t* bt_row, int pos) const { return bt_row[pos >> ps_shift]; }
+  __device__ __forceinline__ int slot_of(int pos) const { return pos & ((1 << ps_shift) - 1); }
+  // element offset of K[page, kvh, slot, 0]
+  __device__ __forceinline__ size_t k_row(int page, int kvh, int slot) const {
+    return ((size_t(page) * Hkv + kvh) * (size_t(1) << ps_shift) + slot) * D;
+  }
+  // element offset of V[page, kvh, d, slot]
+  __device__ __forceinline__ size_t v_elem(int page, int kvh, int d, int slot) const {
+    return ((size_t(page) * Hkv + kvh) * D + d) * (size_t(1) << ps_shift) + slot;
+  }
+};
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ f32x4 mfma16_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Write one column's partial result.  acc[db][r] holds d = 16*db + 4*grp + r.
+template <int D>
+__device__ __forceinline__ void store_partial(float* ws_ml, float* ws_acc, int slot, int grp, float m, float l,
+                                              const f32x4* acc) {
+  if (grp == 0) {
+    ws_ml[2 * size_t(slot)] = m;
+    ws_ml[2 * size_t(slot) + 1] = l;
+  }
+  float* wa = ws_acc + size_t(slot) * D + 4 * grp;
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) *reinterpret_cast<f32x4*>(wa + 16 * db) = acc[db];
+}
+
+// ----------------------------------------------------------------- split-KV, bf16 --
+// MFMA v_mfma_f32_16x16x32_bf16 operand layout: lane l holds row/column (l % 16) and
+// k-elements 8*(l/16) .. 8*(l/16)+7; the 16x16 f32 result gives lane l column (l % 16),
+// rows 4*(l/16) .. 4*(l/16)+3.
+//
+// Scores are computed transposed, S^T = K . Q^T (keys on M, query columns on N), so a
+// lane's results all belong to its own query column.  The K rows of the four 16-key
+// blocks of a 64-key step are permuted so that lane group grp ends up holding keys
+// 32u + 8*grp .. +7 of sub-step u -- exactly the k-slice the P^T operand of the
+// O^T += V^T . P^T MFMA needs -- so P never leaves registers.  V^T's 8-key slices are
+// contiguous because V pages are stored transposed.
+template <int D>
+__global__ __launch_bounds__(256) void split_kv_bf16_kernel(
+    const SplitItem* __restrict__ items, int nitems, const Column* __restrict__ cols,
+    const bf16* __restrict__ q, const bf16* __restrict__ kpool, const bf16* __restrict__ vpool,
+    const int32_t* __restrict__ bt, int bt_stride, float* __restrict__ ws_ml, float* __restrict__ ws_acc,
+    int Hq, Paged pg, float scale_log2) {
+  constexpr int KC = D / 32;
+  constexpr int DB = D / 16;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int idx = blockIdx.x * kSplitWaves + wv;
+  if (idx >= nitems) return;
+  const SplitItem it = items[idx];
+  const int n = lane & 15, grp = lane >> 4;
+  const bool cvalid = n < it.ncols;
+  const Column c = cols[it.col0 + (cvalid ? n : 0)];
+  const int limit = cvalid ? c.limit : -1;
+
+  bf16x8 qb[KC];
+  {
+    const bf16* qp = q + (size_t(c.q_row) * Hq + c.q_head) * D + 8 * grp;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      qb[kc] = *reinterpret_cast<const bf16x8*>(qp + 32 * kc);
+      if (!cvalid) qb[kc] = bf16x8{};
+    }
+  }
+  f32x4 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = kNegBig, l_run = 0.f;
+  const int32_t* btr = bt + size_t(it.req) * bt_stride;
+  const int kvh = it.kvh;
+  const int klast = it.k1 - 1;
+  const bool masked_item = (it.flags & kItemMasked) != 0;
+
+  for (int k = it.k0; k < it.k1; k += kStepKeys) {
+    const bool tail = k + kStepKeys > it.k1;
+    // ---- loads: K rows (4 blocks x KC chunks) and V^T slices (2 sub-steps x DB rows)
+    bf16x8 ka[4][KC];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int key = k + 32 * (b >> 1) + 8 * (n >> 2) + 4 * (b & 1) + (n & 3);
+      const int kk = min(key, klast);
+      const bf16* kr = kpool + pg.k_row(pg.page_of(btr, kk), kvh, pg.slot_of(kk)) + 8 * grp;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) ka[b][kc] = *reinterpret_cast<const bf16x8*>(kr + 32 * kc);
+    }
+    bf16x8 va[2][DB];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int vkey = k + 32 * u + 8 * grp;
+      const int vk = min(vkey, klast & ~7);
+      const bf16* vr = vpool + pg.v_elem(pg.page_of(btr, vk), kvh, n, pg.slot_of(vk));
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        va[u][db] = *reinterpret_cast<const bf16x8*>(vr + (size_t(16 * db) << pg.ps_shift));
+      if (tail) {
+        // positions at or past k1 may lie past kv_len (unwritten slots): zero them so
+        // 0 * garbage cannot reach the accumulator
+        const int valid = it.k1 - vkey;
+        if (valid < 8) {
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (e >= valid) va[u][db][e] = bf16(0.f);
+        }
+      }
+    }
+    // ---- scores S^T for 64 keys: lane holds v[4b + r] = key k + 32(b>>1) + 8grp + 4(b&1) + r
+    float v[16];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) s = mfma16_bf16(ka[b][kc], qb[kc], s);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[4 * b + r] = s[r] * scale_log2;
+    }
+    if (masked_item || tail) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = k + 32 * (b >> 1) + 8 * grp + 4 * (b & 1) + r;
+          if (key > klast || key > limit) v[4 * b + r] = -INFINITY;
+        }
+    }
+    // ---- online softmax (max shared by the 4 lane groups of a column)
+    float mx = v[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, v[e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = fast_exp2(m_run - m_new);
+    m_run = m_new;
+    bf16x8 pb[2];
+    float sum = 0.f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const bf16 pe = bf16(fast_exp2(v[4 * (2 * u + (e >> 2)) + (e & 3)] - m_new));
+        pb[u][e] = pe;
+        sum += float(pe);
+      }
+    l_run = l_run * alpha + sum;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+    // ---- O^T += V^T . P^T
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db] = mfma16_bf16(va[u][db], pb[u], acc[db]);
+  }
+  float l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  if (cvalid) store_partial<D>(ws_ml, ws_acc, c.pbase + it.slot, grp, m_run, l_tot, acc);
+}
+
+// ------------------------------------------------------------------ split-KV, fp32 --
+// Same structure with v_mfma_f32_16x16x4_f32 (one k-element per lane: k = l / 16) and
+// 16-key steps: S^T rows are keys k + 4*grp + r, and the r-th PV MFMA contracts the keys
+// {k + 4*grp + r : grp = 0..3}.
+template <int D>
+__global__ __launch_bounds__(256) void split_kv_f32_kernel(
+    const SplitItem* __restrict__ items, int nitems, const Column* __restrict__ cols,
+    const float* __restrict__ q, const float* __restrict__ kpool, const float* __restrict__ vpool,
+    const int32_t* __restrict__ bt, int bt_stride, float* __restrict__ ws_ml, float* __restrict__ ws_acc,
+    int Hq, Paged pg, float scale_log2) {
+  constexpr int KC = D / 4;
+  constexpr int DB = D / 16;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int idx = blockIdx.x * kSplitWaves + wv;
+  if (idx >= nitems) return;
+  const SplitItem it = items[idx];
+  const int n = lane & 15, grp = lane >> 4;
+  const bool cvalid = n < it.ncols;
+  const Column c = cols[it.col0 + (cvalid ? n : 0)];
+  const int limit = cvalid ? c.limit : -1;
+  float qb[KC];
+  {
+    const float* qp = q + (size_t(c.q_row) * Hq + c.q_head) * D + grp;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) qb[kc] = cvalid ? qp[4 * kc] : 0.f;
+  }
+  f32x4 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = kNegBig, l_run = 0.f;
+  const int32_t* btr = bt + size_t(it.req) * bt_stride;
+  const int kvh = it.kvh;
+  const int klast = it.k1 - 1;
+  for (int k = it.k0; k < it.k1; k += 16) {
+    const int kk = min(k + n, klast);
+    const float* kr = kpool + pg.k_row(pg.page_of(btr, kk), kvh, pg.slot_of(kk)) + grp;
+    f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) s = mfma16_f32(kr[4 * kc], qb[kc], s);
+    float v[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int key = k + 4 * grp + r;
+      v[r] = (key > klast || key > limit) ? -INFINITY : s[r] * scale_log2;
+    }
+    float mx = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = fast_exp2(m_run - m_new);
+    m_run = m_new;
+    float p[4], sum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      p[r] = fast_exp2(v[r] - m_new);
+      sum += p[r];
+    }
+    l_run = l_run * alpha + sum;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int vkey = k + 4 * grp + r;
+      const int vk = min(vkey, klast);
+      const int page = pg.page_of(btr, vk), slot = pg.slot_of(vk);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        float x = vpool[pg.v_elem(page, kvh, 16 * db + n, slot)];
+        if (vkey > klast) x = 0.f;
+        acc[db] = mfma16_f32(x, p[r], acc[db]);
+      }
+    }
+  }
+  float l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  if (cvalid) store_partial<D>(ws_ml, ws_acc, c.pbase + it.slot, grp, m_run, l_tot, acc);
+}
+
+// ------------------------------------------------------------------------ combine --
+// out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s with M = max_s m_s.
+template <int D, typename OutT>
+__global__ __launch_bounds__(256) void combine_kernel(const CombineRow* __restrict__ rows, int nrows,
+                                                      const float* __restrict__ ws_ml,
+                                                      const float* __restrict__ ws_acc, OutT* __restrict__ out,
+                                                      int Hq) {
+  const int lane = threadIdx.x & 63;
+  const int idx = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (idx >= nrows) return;
+  const CombineRow r = rows[idx];
+  float M = -INFINITY;
+  for (int s = 0; s < r.nparts; ++s) M = fmaxf(M, ws_ml[2 * size_t(r.pbase + s)]);
+  float L = 0.f;
+  float o[D / 64];
+#pragma unroll
+  for (int j = 0; j < D / 64; ++j) o[j] = 0.f;
+  for (int s = 0; s < r.nparts; ++s) {
+    const size_t slot = size_t(r.pbase + s);
+    const float w = fast_exp2(ws_ml[2 * slot] - M);
+    L += w * ws_ml[2 * slot + 1];
+    const float* a = ws_acc + slot * D + lane;
+#pragma unroll
+    for (int j = 0; j < D / 64; ++j) o[j] += w * a[64 * j];
+  }
+  const float inv = 1.f / L;
+  OutT* op = out + (size_t(r.q_row) * Hq + r.q_head) * D + lane;
+#pragma unroll
+  for (int j = 0; j < D / 64; ++j) op[64 * j] = OutT(o[j] * inv);
+}
+
+// ------------------------------------------------------------------------- gather --
+template <typename T>
+__global__ __launch_bounds__(256) void gather_kernel(const int64_t* __restrict__ kv_offset, int num_reqs,
+                                                     int64_t total_elems, const int32_t* __restrict__ bt,
+                                                     int bt_stride, const T* __restrict__ kpool,
+                                                     const T* __restrict__ vpool, T* __restrict__ kout,
+                                                     T* __restrict__ vout, Paged pg) {
+  const int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (t >= total_elems) return;
+  const int d = int(t % pg.D);
+  const int kvh = int((t / pg.D) % pg.Hkv);
+  const int64_t pos = t / (int64_t(pg.D) * pg.Hkv);
+  int lo = 0, hi = num_reqs - 1;   // last request with kv_offset[r] <= pos
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (kv_offset[mid] <= pos) lo = mid; else hi = mid - 1;
+  }
+  const int j = int(pos - kv_offset[lo]);
+  const int32_t* btr = bt + size_t(lo) * bt_stride;
+  const int page = pg.page_of(btr, j), slot = pg.slot_of(j);
+  kout[t] = kpool[pg.k_row(page, kvh, slot) + d];
+  vout[t] = vpool[pg.v_elem(page, kvh, d, slot)];
+}
+
+// ------------------------------------------------------------------ host helpers --
+static va_status hip_fail(const char* what, hipError_t e) {
+  return fail(VA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+bool prefill_kernel_available(const va_params&) { return false; }
+
+static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+va_status upload_plan(va_plan* plan) {
+  const size_t b_items = align256(plan->items.size() * sizeof(SplitItem));
+  const size_t b_cols = align256(plan->cols.size() * sizeof(Column));
+  const size_t b_comb = align256(plan->combine.size() * sizeof(CombineRow));
+  const size_t b_tiles = align256(plan->tiles.size() * sizeof(PrefillTile));
+  const size_t b_off = align256(plan->kv_offset.size() * sizeof(int64_t));
+  const size_t total = b_items + b_cols + b_comb + b_tiles + b_off;
+  std::vector<char> host(total, 0);
+  size_t o = 0;
+  auto put = [&](const void* src, size_t n, size_t span) {
+    if (n) std::memcpy(host.data() + o, src, n);
+    const size_t at = o;
+    o += span;
+    return at;
+  };
+  const size_t o_items = put(plan->items.data(), plan->items.size() * sizeof(SplitItem), b_items);
+  const size_t o_cols = put(plan->cols.data(), plan->cols.size() * sizeof(Column), b_cols);
+  const size_t o_comb = put(plan->combine.data(), plan->combine.size() * sizeof(CombineRow), b_comb);
+  const size_t o_tiles = put(plan->tiles.data(), plan->tiles.size() * sizeof(PrefillTile), b_tiles);
+  const size_t o_off = put(plan->kv_offset.data(), plan->kv_offset.size() * sizeof(int64_t), b_off);
+  hipError_t e = hipGetDevice(&plan->device);
+  if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+  e = hipMalloc(&plan->dev, total);
+  if (e != hipSuccess) {
+    plan->dev = nullptr;
+    return fail(VA_ERR_OUT_OF_MEMORY, std::string("hipMalloc of the plan buffer: ") + hipGetErrorString(e));
+  }
+  plan->dev_bytes = total;
+  e = hipMemcpy(plan->dev, host.data(), total, hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    hipFree(plan->dev);
+    plan->dev = nullptr;
+    return hip_fail("hipMemcpy of the plan buffer", e);
+  }
+  char* base = static_cast<char*>(plan->dev);
+  plan->d_items = reinterpret_cast<const SplitItem*>(base + o_items);
+  plan->d_cols = reinterpret_cast<const Column*>(base + o_cols);
+  plan->d_combine = reinterpret_cast<const CombineRow*>(base + o_comb);
+  plan->d_tiles = reinterpret_cast<const PrefillTile*>(base + o_tiles);
+  plan->d_kv_offset = reinterpret_cast<const int64_t*>(base + o_off);
+  return VA_OK;
+}
+
+void free_plan_device(va_plan* plan) {
+  if (plan->dev) hipFree(plan->dev);
+  plan->dev = nullptr;
+}
+
+static int log2i(int x) {
+  int s = 0;
+  while ((1 << s) < x) ++s;
+  return s;
+}
+
+}  // namespace va
+
+using namespace va;
+
+extern "C" va_status varlen_attn_run(const va_plan* plan, const void* q, const void* k_pool, const void* v_pool,
+                                     const int32_t* block_table_dev, void* out, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  if (!plan) return fail(VA_ERR_INVALID_ARG, "plan is NULL");
+  if (!plan->dev) return fail(VA_ERR_INVALID_ARG, "plan has no device buffer (built with VA_FLAG_HOST_ONLY)");
+  const bool any = !plan->items.empty() || !plan->tiles.empty();
+  if (!any) return VA_OK;
+  if (!q || !k_pool || !v_pool || !block_table_dev || !out)
+    return fail(VA_ERR_INVALID_ARG, "q, k_pool, v_pool, block_table_dev and out must be non-NULL");
+  if (workspace_bytes < plan->ws_bytes)
+    return fail(VA_ERR_WORKSPACE_TOO_SMALL, "workspace has " + std::to_string(workspace_bytes) + " bytes, plan needs " +
+                                                std::to_string(plan->ws_bytes));
+  if (plan->ws_bytes && !workspace) return fail(VA_ERR_INVALID_ARG, "workspace is NULL");
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+  if (dev != plan->device) return fail(VA_ERR_INVALID_ARG, "current HIP device is not the one the plan was built on");
+
+  const va_params& p = plan->p;
+  const int D = p.head_dim;
+  const float scale = p.softmax_scale > 0.f ? p.softmax_scale : 1.f / std::sqrt(float(D));
+  const float scale_log2 = scale * kLog2e;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Paged pg{p.num_kv_heads, log2i(p.page_size), D};
+  float* ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan->ws_ml_off);
+  float* ws_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan->ws_acc_off);
+  const int nitems = int(plan->items.size());
+  const int ncomb = int(plan->combine.size());
+  const int bt_stride = p.max_pages_per_req;
+  const bool bf = p.dtype == VA_DTYPE_BF16;
+
+  (void)hipGetLastError();   // clear a stale error left by earlier, unrelated calls
+  if (nitems) {
+    const dim3 grid((nitems + kSplitWaves - 1) / kSplitWaves), block(64 * kSplitWaves);
+    if (bf) {
+      auto* qq = static_cast<const bf16*>(q);
+      auto* kk = static_cast<const bf16*>(k_pool);
+      auto* vv = static_cast<const bf16*>(v_pool);
+      if (D == 128)
+        split_kv_bf16_kernel<128><<<grid, block, 0, s>>>(plan->d_items, nitems, plan->d_cols, qq, kk, vv,
+                                                         block_table_dev, bt_stride, ws_ml, ws_acc,
+                                                         p.num_q_heads, pg, scale_log2);
+      else
+        split_kv_bf16_kernel<64><<<grid, block, 0, s>>>(plan->d_items, nitems, plan->d_cols, qq, kk, vv,
+                                                        block_table_dev, bt_stride, ws_ml, ws_acc,
+                                                        p.num_q_heads, pg, scale_log2);
+    } else {
+      auto* qq = static_cast<const float*>(q);
+      auto* kk = static_cast<const float*>(k_pool);
+      auto* vv = static_cast<const float*>(v_pool);
+      if (D == 128)
+        split_kv_f32_kernel<128><<<grid, block, 0, s>>>(plan->d_items, nitems, plan->d_cols, qq, kk, vv,
+                                                        block_table_dev, bt_stride, ws_ml, ws_acc,
+                                                        p.num_q_heads, pg, scale_log2);
+      else
+        split_kv_f32_kernel<64><<<grid, block, 0, s>>>(plan->d_items, nitems, plan->d_cols, qq, kk, vv,
+                                                       block_table_dev, bt_stride, ws_ml, ws_acc,
+                                                       p.num_q_heads, pg, scale_log2);
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail("split-KV kernel launch", e);
+  }
+  if (ncomb) {
+    const dim3 grid((ncomb + 3) / 4), block(256);
+    if (bf) {
+      auto* o = static_cast<bf16*>(out);
+      if (D == 128)
+        combine_kernel<128, bf16><<<grid, block, 0, s>>>(plan->d_combine, ncomb, ws_ml, ws_acc, o, p.num_q_heads);
+      else
+        combine_kernel<64, bf16><<<grid, block, 0, s>>>(plan->d_combine, ncomb, ws_ml, ws_acc, o, p.num_q_heads);
+    } else {
+      auto* o = static_cast<float*>(out);
+      if (D == 128)
+        combine_kernel<128, float><<<grid, block, 0, s>>>(plan->d_combine, ncomb, ws_ml, ws_acc, o, p.num_q_heads);
+      else
+        combine_kernel<64, float><<<grid, block, 0, s>>>(plan->d_combine, ncomb, ws_ml, ws_acc, o, p.num_q_heads);
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail("combine kernel launch", e);
+  }
+  return VA_OK;
+}
+
+extern "C" va_status varlen_attn_debug_gather(const va_plan* plan, const void* k_pool, const void* v_pool,
+                                              const int32_t* block_table_dev, void* k_out, void* v_out,
+                                              void* stream) {
+  if (!plan) return fail(VA_ERR_INVALID_ARG, "plan is NULL");
+  if (!plan->dev) return fail(VA_ERR_INVALID_ARG, "plan has no device buffer (built with VA_FLAG_HOST_ONLY)");
+  const va_params& p = plan->p;
+  const int64_t total = plan->kv_offset.back() * p.num_kv_heads * p.head_dim;
+  if (total == 0 || plan->num_reqs == 0) return VA_OK;
+  if (!k_pool || !v_pool || !block_table_dev || !k_out || !v_out)
+    return fail(VA_ERR_INVALID_ARG, "pointer argument is NULL");
+  Paged pg{p.num_kv_heads, log2i(p.page_size), p.head_dim};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid(unsigned((total + 255) / 256)), block(256);
+  (void)hipGetLastError();
+  if (p.dtype == VA_DTYPE_BF16)
+    gather_kernel<bf16><<<grid, block, 0, s>>>(plan->d_kv_offset, plan->num_reqs, total, block_table_dev,
+                                               p.max_pages_per_req, static_cast<const bf16*>(k_pool),
+                                               static_cast<const bf16*>(v_pool), static_cast<bf16*>(k_out),
+                                               static_cast<bf16*>(v_out), pg);
+  else
+    gather_kernel<float><<<grid, block, 0, s>>>(plan->d_kv_offset, plan->num_reqs, total, block_table_dev,
+                                                p.max_pages_per_req, static_cast<const float*>(k_pool),
+                                                static_cast<const float*>(v_pool), static_cast<float*>(k_out),
+                                                static_cast<float*>(v_out), pg);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail("gather kernel launch", e);
+  return VA_OK;
+}

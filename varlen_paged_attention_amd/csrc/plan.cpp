@@ -1,0 +1,419 @@
+// Host-side planner: validates one iteration's metadata and turns it into work lists
+// for the HIP kernels.  Plain C++17 (no HIP calls here; the device upload lives in
+// kernels.hip), so the planning logic can be exercised without a GPU.
+//
+// What it plans, from the pages:
+//  * Each request is its own diagonal block over the flat Q tensor; no work crosses
+//    requests ("一次 forward 怎么塞下很多个 request", section 6.2).
+//  * Rows of long new blocks (prefills and prefill chunks) become MFMA prefill tiles;
+//    short ones (decode, q_rows = 1, and few-row requests) become split-KV items whose
+//    kv range is cut by kv_length so every wavefront gets a similar amount of KV to
+//    stream ("ORCA 和 chunked prefill", section 2: decode and prefill in one iteration;
+//    section 4: decode is the C = 1 case of a chunk).
+//  * With VA_FLAG_SHARED_PREFIX, requests whose block tables start with the same
+//    physical pages form a group; the shared pages are scored once per group for all of
+//    the group's rows, each row keeping its own running max and sum ("How To Scale Your
+//    Model 笔记(7-8)", section 3, 物理存一份，不保证从 HBM 只读一次).
+#include <algorithm>
+#include <chrono>
+#include <cmath>
+#include <cstring>
+#include <map>
+#include <new>
+#include <numeric>
+#include <string>
+#include <vector>
+
+#include "va_internal.h"
+
+namespace va {
+
+static std::string& err_slot() {
+  static thread_local std::string s;
+  return s;
+}
+void set_error(const std::string& msg) { err_slot() = msg; }
+va_status fail(va_status s, const std::string& msg) {
+  err_slot() = msg;
+  return s;
+}
+
+namespace {
+
+struct Block {          // a set of <= 16 query columns scored against one kv range
+  int32_t req, kvh;
+  int32_t kstart, kend;
+  int32_t max_limit, min_limit;
+  std::vector<int32_t> outs;   // output ids (q_row * Hq + q_head)
+  std::vector<int32_t> limits;
+  bool shared;
+  int32_t nchunks;
+};
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+}  // namespace va
+
+using namespace va;
+
+extern "C" const char* varlen_attn_last_error(void) { return err_slot().c_str(); }
+
+extern "C" const char* varlen_attn_status_string(va_status s) {
+  switch (s) {
+    case VA_OK: return "ok";
+    case VA_ERR_INVALID_ARG: return "invalid argument";
+    case VA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case VA_ERR_OUT_OF_MEMORY: return "out of memory";
+    case VA_ERR_HIP: return "HIP runtime error";
+    case VA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+  }
+  return "unknown status";
+}
+
+extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs, const int32_t* q_start,
+                                      const int32_t* q_end, const int32_t* kv_len,
+                                      const int32_t* block_table_host, va_plan** plan_out,
+                                      size_t* workspace_bytes_out) {
+  auto t0 = std::chrono::steady_clock::now();
+  if (!plan_out) return fail(VA_ERR_INVALID_ARG, "plan_out is NULL");
+  *plan_out = nullptr;
+  if (!params) return fail(VA_ERR_INVALID_ARG, "params is NULL");
+  if (num_reqs < 0) return fail(VA_ERR_INVALID_ARG, "num_reqs < 0");
+  if (num_reqs > 0 && (!q_start || !q_end || !kv_len || !block_table_host))
+    return fail(VA_ERR_INVALID_ARG, "metadata array is NULL");
+  const va_params p = *params;
+  if (p.num_q_heads < 1 || p.num_kv_heads < 1) return fail(VA_ERR_INVALID_ARG, "head counts must be >= 1");
+  if (p.num_q_heads % p.num_kv_heads != 0)
+    return fail(VA_ERR_INVALID_ARG, "num_q_heads must be a multiple of num_kv_heads");
+  if (p.dtype != VA_DTYPE_BF16 && p.dtype != VA_DTYPE_F32) return fail(VA_ERR_INVALID_ARG, "unknown dtype");
+  if (p.head_dim != 64 && p.head_dim != 128) return fail(VA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  const int ps = p.page_size;
+  if (ps != 16 && ps != 32 && ps != 64 && ps != 128 && ps != 256)
+    return fail(VA_ERR_UNSUPPORTED, "page_size must be 16, 32, 64, 128 or 256");
+  if (p.num_pages < 1 || p.max_pages_per_req < 1)
+    return fail(VA_ERR_INVALID_ARG, "num_pages and max_pages_per_req must be >= 1");
+
+  const int Hq = p.num_q_heads, Hkv = p.num_kv_heads, D = p.head_dim;
+  const int g = Hq / Hkv;
+  int64_t total_rows = 0;
+  std::vector<std::pair<int32_t, int32_t>> ranges;
+  for (int r = 0; r < num_reqs; ++r) {
+    const int64_t qs = q_start[r], qe = q_end[r], kv = kv_len[r];
+    const std::string who = "request " + std::to_string(r) + ": ";
+    if (qs < 0 || qe < qs) return fail(VA_ERR_INVALID_ARG, who + "need 0 <= q_start <= q_end");
+    if (kv < 0) return fail(VA_ERR_INVALID_ARG, who + "kv_len < 0");
+    const int64_t m = qe - qs;
+    if (m > kv) return fail(VA_ERR_INVALID_ARG, who + "q_rows > kv_len (new rows must be in the context)");
+    if (kv > int64_t(p.max_pages_per_req) * ps)
+      return fail(VA_ERR_INVALID_ARG, who + "kv_len exceeds max_pages_per_req * page_size");
+    // every request's pages are checked (the gather entry point reads them all)
+    const int64_t npg = ceil_div(kv, ps);
+    const int32_t* row = block_table_host + int64_t(r) * p.max_pages_per_req;
+    for (int64_t j = 0; j < npg; ++j)
+      if (row[j] < 0 || row[j] >= p.num_pages)
+        return fail(VA_ERR_INVALID_ARG, who + "block table entry " + std::to_string(j) + " = " +
+                                            std::to_string(row[j]) + " outside [0, num_pages)");
+    if (m == 0) continue;
+    ranges.push_back({int32_t(qs), int32_t(qe)});
+    total_rows = std::max(total_rows, qe);
+  }
+  std::sort(ranges.begin(), ranges.end());
+  for (size_t i = 1; i < ranges.size(); ++i)
+    if (ranges[i].first < ranges[i - 1].second)
+      return fail(VA_ERR_INVALID_ARG, "Q row ranges of two requests overlap");
+
+  va_plan* plan = new (std::nothrow) va_plan();
+  if (!plan) return fail(VA_ERR_OUT_OF_MEMORY, "host allocation of the plan failed");
+  plan->p = p;
+  plan->num_reqs = num_reqs;
+  plan->g = g;
+  plan->q_start.assign(q_start, q_start + num_reqs);
+  plan->q_end.assign(q_end, q_end + num_reqs);
+  plan->kv_len.assign(kv_len, kv_len + num_reqs);
+  plan->kv_offset.resize(num_reqs + 1, 0);
+  for (int r = 0; r < num_reqs; ++r) plan->kv_offset[r + 1] = plan->kv_offset[r] + kv_len[r];
+
+  auto bt = [&](int r, int64_t j) { return block_table_host[int64_t(r) * p.max_pages_per_req + j]; };
+  const int prefill_min = p.prefill_min_rows > 0 ? p.prefill_min_rows : 64;
+  const bool use_prefill = !(p.flags & VA_FLAG_NO_PREFILL_KERNEL) && prefill_kernel_available(p);
+
+  // ---- classify requests -------------------------------------------------------
+  std::vector<int> split_reqs;
+  for (int r = 0; r < num_reqs; ++r) {
+    const int m = q_end[r] - q_start[r];
+    if (m == 0) continue;
+    const int S0 = kv_len[r] - m;
+    if (use_prefill && m >= prefill_min) {
+      const int ncol = m * g;
+      for (int kvh = 0; kvh < Hkv; ++kvh)
+        for (int c0 = 0; c0 < ncol; c0 += kPrefillCols) {
+          PrefillTile t;
+          t.req = r;
+          t.kvh = kvh;
+          t.c0 = c0;
+          t.ncols = std::min(kPrefillCols, ncol - c0);
+          t.q0 = q_start[r];
+          t.S0 = S0;
+          const int i_first = c0 / g, i_last = (c0 + t.ncols - 1) / g;
+          t.kv_end = S0 + i_last + 1;
+          t.key_diag = S0 + i_first;
+          plan->tiles.push_back(t);
+        }
+    } else {
+      split_reqs.push_back(r);
+    }
+  }
+  // heaviest tiles first so the ragged end of the grid is made of short tiles
+  std::stable_sort(plan->tiles.begin(), plan->tiles.end(),
+                   [](const PrefillTile& a, const PrefillTile& b) { return a.kv_end > b.kv_end; });
+
+  // ---- shared-prefix groups --------------------------------------------------------
+  std::vector<int32_t> shared_pages(num_reqs, 0);   // pages read through the group
+  std::vector<std::vector<int>> groups;
+  if (p.flags & VA_FLAG_SHARED_PREFIX) {
+    std::map<int32_t, std::vector<int>> by_first;
+    for (int r : split_reqs) {
+      const int m = q_end[r] - q_start[r];
+      const int S0 = kv_len[r] - m;
+      // a shared page must be full and entirely visible to every row of the request
+      const int lim = std::min(kv_len[r] / ps, (S0 + 1) / ps);
+      if (lim >= 1) by_first[bt(r, 0)].push_back(r);
+    }
+    for (auto& kvp : by_first) {
+      std::vector<int>& mem = kvp.second;
+      if (mem.size() < 2) continue;
+      int cp = INT32_MAX;
+      for (int r : mem) {
+        const int m = q_end[r] - q_start[r];
+        cp = std::min(cp, std::min(kv_len[r] / ps, (kv_len[r] - m + 1) / ps));
+      }
+      const int lead = mem[0];
+      int common = 0;
+      while (common < cp) {
+        bool same = true;
+        for (int r : mem) same = same && bt(r, common) == bt(lead, common);
+        if (!same) break;
+        ++common;
+      }
+      if (common < 1) continue;
+      for (int r : mem) shared_pages[r] = common;
+      groups.push_back(mem);
+    }
+  }
+
+  // ---- column blocks ------------------------------------------------------------------
+  std::vector<Block> blocks;
+  auto add_blocks = [&](const std::vector<std::pair<int, int>>& rowhead,   // (req, local col)
+                        int kvh, int32_t kstart, bool shared, int32_t req_for_table) {
+    for (size_t b0 = 0; b0 < rowhead.size(); b0 += kSplitCols) {
+      Block B;
+      B.req = req_for_table;
+      B.kvh = kvh;
+      B.kstart = kstart;
+      B.shared = shared;
+      B.max_limit = -1;
+      B.min_limit = INT32_MAX;
+      for (size_t c = b0; c < std::min(rowhead.size(), b0 + kSplitCols); ++c) {
+        const int r = rowhead[c].first, lc = rowhead[c].second;
+        const int m = q_end[r] - q_start[r];
+        const int i = lc / g, hh = lc % g;
+        const int limit = kv_len[r] - m + i;
+        B.outs.push_back((q_start[r] + i) * Hq + kvh * g + hh);
+        B.limits.push_back(limit);
+        B.max_limit = std::max(B.max_limit, limit);
+        B.min_limit = std::min(B.min_limit, limit);
+      }
+      B.kend = B.max_limit + 1;   // group blocks are cut at the shared length by the caller
+      blocks.push_back(std::move(B));
+    }
+  };
+  for (auto& mem : groups) {
+    const int32_t kend = shared_pages[mem[0]] * ps;
+    for (int kvh = 0; kvh < Hkv; ++kvh) {
+      std::vector<std::pair<int, int>> rh;
+      for (int r : mem)
+        for (int lc = 0; lc < (q_end[r] - q_start[r]) * g; ++lc) rh.push_back({r, lc});
+      const size_t first = blocks.size();
+      add_blocks(rh, kvh, 0, true, mem[0]);
+      for (size_t b = first; b < blocks.size(); ++b) blocks[b].kend = kend;
+    }
+  }
+  for (int r : split_reqs) {
+    const int ncol = (q_end[r] - q_start[r]) * g;
+    for (int kvh = 0; kvh < Hkv; ++kvh) {
+      std::vector<std::pair<int, int>> rh;
+      for (int lc = 0; lc < ncol; ++lc) rh.push_back({r, lc});
+      add_blocks(rh, kvh, shared_pages[r] * ps, false, r);
+    }
+  }
+
+  // ---- split length: about 8192 items over the whole iteration ------------------------
+  int64_t work = 0;
+  for (auto& B : blocks) work += std::max(0, B.kend - B.kstart);
+  int64_t L;
+  if (p.split_len > 0) {
+    L = ceil_div(p.split_len, kStepKeys) * kStepKeys;
+  } else {
+    L = ceil_div(std::max<int64_t>(1, ceil_div(work, 8192)), kStepKeys) * kStepKeys;
+    L = std::min<int64_t>(std::max<int64_t>(L, 256), 8192);
+  }
+  plan->split_len = int32_t(L);
+  for (auto& B : blocks) B.nchunks = int32_t(ceil_div(std::max(0, B.kend - B.kstart), L));
+
+  // ---- partial slots: every (row, head) output of the split path ----------------------
+  std::vector<int32_t> nparts(size_t(total_rows) * Hq, 0);
+  for (auto& B : blocks)
+    for (int32_t o : B.outs) nparts[o] += B.nchunks;
+  std::vector<int32_t> pbase(nparts.size(), -1);
+  std::vector<int32_t> shared_n(nparts.size(), 0);   // slots taken by group items
+  int64_t slots = 0;
+  for (size_t o = 0; o < nparts.size(); ++o)
+    if (nparts[o] > 0) {
+      pbase[o] = int32_t(slots);
+      slots += nparts[o];
+      CombineRow cr;
+      cr.q_row = int32_t(o / Hq);
+      cr.q_head = int32_t(o % Hq);
+      cr.pbase = pbase[o];
+      cr.nparts = nparts[o];
+      plan->combine.push_back(cr);
+    }
+  if (slots > INT32_MAX) {
+    delete plan;
+    return fail(VA_ERR_UNSUPPORTED, "too many partial results for one plan");
+  }
+  for (auto& B : blocks)
+    if (B.shared)
+      for (int32_t o : B.outs) shared_n[o] = B.nchunks;
+
+  // ---- emit columns and items ----------------------------------------------------------
+  std::vector<SplitItem> shared_items, own_items;
+  for (auto& B : blocks) {
+    if (B.nchunks == 0) continue;
+    const int32_t col0 = int32_t(plan->cols.size());
+    for (size_t c = 0; c < B.outs.size(); ++c) {
+      Column C;
+      C.q_row = B.outs[c] / Hq;
+      C.q_head = B.outs[c] % Hq;
+      C.limit = B.limits[c];
+      C.pbase = pbase[B.outs[c]];
+      plan->cols.push_back(C);
+    }
+    for (int32_t j = 0; j < B.nchunks; ++j) {
+      SplitItem it;
+      it.req = B.req;
+      it.kvh = B.kvh;
+      it.col0 = col0;
+      it.ncols = int32_t(B.outs.size());
+      it.k0 = int32_t(B.kstart + j * L);
+      it.k1 = int32_t(std::min<int64_t>(B.kend, B.kstart + (j + 1) * L));
+      it.slot = B.shared ? j : shared_n[B.outs[0]] + j;
+      it.flags = (B.min_limit < it.k1 - 1) ? kItemMasked : 0;
+      (B.shared ? shared_items : own_items).push_back(it);
+    }
+  }
+  // group items first (each chunk's blocks adjacent), then longest first
+  plan->items = shared_items;
+  plan->items.insert(plan->items.end(), own_items.begin(), own_items.end());
+  std::stable_sort(plan->items.begin(), plan->items.end(), [](const SplitItem& a, const SplitItem& b) {
+    return (a.k1 - a.k0) > (b.k1 - b.k0);
+  });
+
+  // ---- counters ---------------------------------------------------------------------
+  va_plan_stats& st = plan->stats;
+  const int64_t elem = p.dtype == VA_DTYPE_BF16 ? 2 : 4;
+  st.num_reqs = num_reqs;
+  st.total_q_rows = total_rows;
+  st.prefill_tiles = int64_t(plan->tiles.size());
+  st.split_items = int64_t(plan->items.size());
+  st.shared_items = int64_t(shared_items.size());
+  st.shared_groups = int64_t(groups.size());
+  st.partial_slots = slots;
+  st.combine_rows = int64_t(plan->combine.size());
+  std::vector<int32_t> max_slot(p.num_pages, 0);
+  int64_t pairs = 0, logical_pos = 0, rows = 0, table_entries = 0;
+  for (int r = 0; r < num_reqs; ++r) {
+    const int64_t m = q_end[r] - q_start[r];
+    if (m == 0) continue;
+    const int64_t kv = kv_len[r], S0 = kv - m;
+    pairs += m * S0 + m * (m + 1) / 2;
+    logical_pos += kv;
+    rows += m;
+    const int64_t npg = ceil_div(kv, ps);
+    table_entries += npg;
+    for (int64_t j = 0; j < npg; ++j) {
+      const int32_t used = int32_t(std::min<int64_t>(ps, kv - j * ps));
+      int32_t& ms = max_slot[bt(r, j)];
+      ms = std::max(ms, used);
+    }
+  }
+  int64_t phys_pos = 0;
+  for (int32_t v : max_slot) phys_pos += v;
+  const int64_t pos_bytes = int64_t(Hkv) * D * 2 * elem;
+  st.visible_pairs = pairs;
+  st.flops = 4.0 * D * Hq * double(pairs);
+  st.logical_kv_bytes = logical_pos * pos_bytes;
+  st.physical_kv_bytes = phys_pos * pos_bytes;
+  st.q_bytes = rows * Hq * D * elem;
+  st.o_bytes = st.q_bytes;
+  st.table_bytes = table_entries * 4;
+  plan->ws_ml_off = 0;
+  plan->ws_acc_off = size_t(ceil_div(slots * 2 * 4, 256) * 256);
+  plan->ws_bytes = plan->ws_acc_off + size_t(ceil_div(slots * D * 4, 256) * 256);
+  if (slots == 0) plan->ws_bytes = 0;
+  st.workspace_bytes = int64_t(plan->ws_bytes);
+
+  if (!(p.flags & VA_FLAG_HOST_ONLY)) {
+    va_status s = upload_plan(plan);
+    if (s != VA_OK) {
+      delete plan;
+      return s;
+    }
+  }
+  st.plan_host_us =
+      std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t0).count();
+  *plan_out = plan;
+  if (workspace_bytes_out) *workspace_bytes_out = plan->ws_bytes;
+  return VA_OK;
+}
+
+extern "C" va_status varlen_attn_plan_stats(const va_plan* plan, va_plan_stats* out) {
+  if (!plan || !out) return fail(VA_ERR_INVALID_ARG, "plan or out is NULL");
+  *out = plan->stats;
+  return VA_OK;
+}
+
+extern "C" va_status varlen_attn_plan_export(const va_plan* plan, int32_t which, const int32_t** data,
+                                             int64_t* count, int32_t* ints_per_entry) {
+  if (!plan || !data || !count || !ints_per_entry) return fail(VA_ERR_INVALID_ARG, "NULL argument");
+  switch (which) {
+    case 0:
+      *data = reinterpret_cast<const int32_t*>(plan->items.data());
+      *count = int64_t(plan->items.size());
+      *ints_per_entry = sizeof(SplitItem) / 4;
+      return VA_OK;
+    case 1:
+      *data = reinterpret_cast<const int32_t*>(plan->cols.data());
+      *count = int64_t(plan->cols.size());
+      *ints_per_entry = sizeof(Column) / 4;
+      return VA_OK;
+    case 2:
+      *data = reinterpret_cast<const int32_t*>(plan->combine.data());
+      *count = int64_t(plan->combine.size());
+      *ints_per_entry = sizeof(CombineRow) / 4;
+      return VA_OK;
+    case 3:
+      *data = reinterpret_cast<const int32_t*>(plan->tiles.data());
+      *count = int64_t(plan->tiles.size());
+      *ints_per_entry = sizeof(PrefillTile) / 4;
+      return VA_OK;
+  }
+  return fail(VA_ERR_INVALID_ARG, "which must be 0 (items), 1 (columns), 2 (combine rows) or 3 (tiles)");
+}
+
+extern "C" void varlen_attn_plan_destroy(va_plan* plan) {
+  if (!plan) return;
+  free_plan_device(plan);
+  delete plan;
+}

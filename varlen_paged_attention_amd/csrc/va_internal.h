@@ -1,0 +1,84 @@
+// Work-list records shared by the host planner (plan.cpp) and the HIP kernels
+// (kernels.hip).  Plain int32 records so the planner needs no HIP headers and the
+// kernels read them with scalar loads.
+#pragma once
+#include <stdint.h>
+
+#include "varlen_attn.h"
+
+namespace va {
+
+// One split-KV work item = one wavefront.  It reads kv positions [k0, k1) of request
+// `req`'s block table for KV head `kvh` and scores them against up to 16 query columns
+// cols[col0 .. col0+ncols).  Each column's partial result goes to workspace slot
+// cols[c].pbase + slot.
+struct SplitItem {
+  int32_t req, kvh, col0, ncols;
+  int32_t k0, k1, slot, flags;  // flags: kItemMasked if some column's limit < k1 - 1
+};
+enum { kItemMasked = 1 };
+
+// A query column: flat Q row, query head, last visible kv position (S0 + i), and the
+// first workspace slot of this (row, head) output.
+struct Column {
+  int32_t q_row, q_head, limit, pbase;
+};
+
+// One (row, head) output assembled from nparts partial results.
+struct CombineRow {
+  int32_t q_row, q_head, pbase, nparts;
+};
+
+// One MFMA prefill tile: query columns c0 .. c0+ncols of request `req` under KV head
+// `kvh`, where column c is new row i = c / g with query head kvh*g + c % g.
+struct PrefillTile {
+  int32_t req, kvh, c0, ncols;
+  int32_t q0, S0, kv_end, key_diag;  // q_start of the request; S0; keys read [0, kv_end);
+                                     // keys >= key_diag need the causal check
+};
+
+constexpr int kSplitCols = 16;       // query columns per split-KV item (MFMA N)
+constexpr int kSplitWaves = 4;       // items (wavefronts) per split-KV workgroup
+constexpr int kPrefillCols = 128;    // query columns per prefill tile
+constexpr int kStepKeys = 64;        // kv positions per split-KV loop step
+
+}  // namespace va
+
+// Plan object (host side).  Defined here so kernels.hip can read the device pointers.
+#ifdef __cplusplus
+#include <string>
+#include <vector>
+
+struct va_plan {
+  va_params p;
+  int32_t num_reqs = 0;
+  int32_t g = 1;
+  int32_t split_len = 0;
+  std::vector<int32_t> q_start, q_end, kv_len;
+  std::vector<int64_t> kv_offset;            // prefix sum of kv_len (gather output rows)
+  std::vector<va::SplitItem> items;
+  std::vector<va::Column> cols;
+  std::vector<va::CombineRow> combine;
+  std::vector<va::PrefillTile> tiles;
+  va_plan_stats stats{};
+  // device copies (one allocation)
+  void* dev = nullptr;
+  size_t dev_bytes = 0;
+  const va::SplitItem* d_items = nullptr;
+  const va::Column* d_cols = nullptr;
+  const va::CombineRow* d_combine = nullptr;
+  const va::PrefillTile* d_tiles = nullptr;
+  const int64_t* d_kv_offset = nullptr;
+  int device = -1;
+  size_t ws_ml_off = 0, ws_acc_off = 0, ws_bytes = 0;
+};
+
+namespace va {
+void set_error(const std::string& msg);
+va_status fail(va_status s, const std::string& msg);
+// Device side of plan creation / destruction (kernels.hip).
+va_status upload_plan(va_plan* plan);
+void free_plan_device(va_plan* plan);
+bool prefill_kernel_available(const va_params& p);
+}  // namespace va
+#endif

@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Benchmark of one attention layer's mixed prefill/decode varlen paged attention on one
+MI355X.
+
+A step is one ``varlen_attn_run`` of the whole planned iteration (every kernel of the hot
+path) over inputs already resident in HBM.  The headline workload is the ORCA-style mixed
+iteration: a 4096-token uncached prefill plus decodes at 1500 and 1700 cached positions,
+32 query / 32 KV heads, head_dim 128, 16-token pages in a seeded random permutation, bf16.
+It is MFMA-bound, so ``value`` is TFLOP/s of algorithmic attention work (4·head_dim FLOPs
+per visible (query, key) pair per query head).  Secondary lines time the decode-heavy,
+chunked-prefill-mix and shared-prefix workloads (HBM GB/s of algorithmic bytes, µs/step).
+
+Prints progress on stderr and ONE JSON line on stdout.
+"""
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "varlen paged attn: decode HBM GB/s + prefill TFLOP/s, % of MI355X peak"
+PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E
+PEAK_BF16 = 2.5e15         # FLOP/s, MI355X dense bf16 MFMA
+STAGES = ("prefill", "split_kv", "combine")
+KERNEL_NAMES = {"prefill": "prefill_bf16_kernel", "split_kv": "split_kv_bf16_kernel", "combine": "combine_kernel"}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor()
+
+
+def time_runs(api, plan, tensors, steps, warmup, flush=None):
+    """Run warmup + steps iterations with per-stage HIP events; returns (wall ms/step,
+    per-stage mean ms, per-step total ms list)."""
+    import torch
+    q, k, v, bt, out, ws = tensors
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for _ in range(warmup):
+        api.varlen_attn_run(plan, q, k, v, bt, out, ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if flush is not None:
+            flush()
+        api.varlen_attn_run_events(plan, q, k, v, bt, out, ws, evs[i])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    stage = {s: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, s in enumerate(STAGES)}
+    totals = [e[0].elapsed_time(e[3]) for e in evs]
+    return wall, stage, totals
+
+
+def setup(api, w, flags=0):
+    import torch
+    plan = api.plan_for(w, flags=flags)
+    q, k, v, bt = api.to_device(w)
+    out = torch.zeros_like(q)
+    ws = api.new_workspace(plan)
+    return plan, (q, k, v, bt, out, ws)
+
+
+def dominant(stats, stage_ms):
+    """The stage with the largest time, with its algorithmic work and roofline bound."""
+    name = max(stage_ms, key=stage_ms.get)
+    ms = stage_ms[name]
+    if name == "prefill":
+        work, bound = stats["prefill_flops"], "mfma"
+    elif name == "split_kv":
+        # bandwidth-bound unless it also carries the prefill rows (then it is a contraction)
+        flops, byts = stats["split_flops"], stats["split_kv_bytes"] + stats["split_q_bytes"] + stats["table_bytes"]
+        bound = "mfma" if flops / PEAK_BF16 > byts / PEAK_HBM else "hbm"
+        work = flops if bound == "mfma" else byts
+    else:
+        work, bound = stats["o_bytes"], "hbm"
+    return name, ms, work, bound
+
+
+def roofline(stats, stage_ms, traffic=None):
+    name, ms, work, bound = dominant(stats, stage_ms)
+    sec = ms * 1e-3
+    if bound == "mfma":
+        a, p, unit = work / sec / 1e12, PEAK_BF16 / 1e12, "TFLOP/s"
+    else:
+        a, p, unit = work / sec / 1e9, PEAK_HBM / 1e9, "GB/s"
+    return {"bound": bound, "achieved": round(a, 2), "peak": p, "unit": unit, "frac": round(a / p, 4),
+            "traffic": traffic, "kernel": KERNEL_NAMES[name], "kernel_ms": round(ms, 5),
+            "algorithmic_per_launch": work}
+
+
+def cpu_baseline(w, budget_s=15.0):
+    """The fp64 oracle on a bounded sample of the same iteration: the last n rows of the
+    4096-row prefill (as a chunk whose cached prefix is the first 4096-n positions) plus
+    both decodes.  n is grown until the run takes about budget_s / 2.."""
+    import oracle
+    from varlen_paged_attention_amd import workloads as W
+    threads = max(1, min(16, os.cpu_count() or 1))
+
+    def sample(n):
+        s = W.Workload(**{**w.__dict__})
+        a0, a1 = int(w.q_start[0]), int(w.q_end[0])
+        rows = np.r_[a1 - n:a1, a1:w.total_q_rows]
+        s.q = w.q[rows]
+        s.q_start = np.array([0, n, n + 1], np.int32)
+        s.q_end = np.array([n, n + 1, n + 2], np.int32)
+        return s
+
+    n, spent = 32, 0.0
+    while True:
+        s = sample(n)
+        t0 = time.perf_counter()
+        oracle.varlen_paged_attention(s.q, s.k_pool, s.v_pool, s.block_table, s.q_start, s.q_end, s.kv_len,
+                                      s.page_size, threads=threads)
+        dt = time.perf_counter() - t0
+        spent += dt
+        if dt > budget_s / 2 or n >= 4096 or spent > budget_s:
+            break
+        n = min(4096, n * 4 if dt < budget_s / 16 else n * 2)
+    flops = oracle.attention_flops(s.q_end - s.q_start, s.kv_len, s.num_q_heads, s.head_dim)
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"last {n} rows of the 4096-row prefill (cached prefix {4096 - n}) + both decodes, all 32 heads, "
+                      f"fp64 NumPy, {dt:.2f} s", "cpu": cpu_model(), "seconds": round(dt, 3)}
+
+
+def hbm_copy_gbps():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    return round(2 * n * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+
+
+def secondary(api, W, cid, flags, reps, label, flush):
+    plan, tensors = None, None
+    w = W.config(cid)
+    plan, tensors = setup(api, w, flags)
+    st = api.varlen_attn_plan_stats(plan)
+    _, stage, totals = time_runs(api, plan, tensors, reps, 3, flush)
+    us = float(np.median(totals)) * 1e3
+    byts = st["physical_kv_bytes"] + st["q_bytes"] + st["o_bytes"] + st["table_bytes"]
+    res = {"workload": label, "us_per_step": round(us, 2),
+           "hbm_GBps": round(byts / (us * 1e-6) / 1e9, 1), "hbm_frac": round(byts / (us * 1e-6) / PEAK_HBM, 4),
+           "tflops": round(st["flops"] / (us * 1e-6) / 1e12, 2),
+           "algorithmic_bytes": byts, "logical_kv_bytes": st["logical_kv_bytes"],
+           "physical_kv_bytes": st["physical_kv_bytes"], "flops": st["flops"],
+           "stage_ms": {k: round(v, 5) for k, v in stage.items()},
+           "roofline": roofline(st, stage), "l2_flushed": flush is not None}
+    del tensors
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--traffic", default=None, help="JSON file with measured HBM bytes per launch")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from varlen_paged_attention_amd import api, workloads as W
+    torch.cuda.set_device(0)
+    api.lib()
+
+    log("[bench] building the ORCA mixed iteration (4096 prefill + decodes 1500, 1700)")
+    w = W.config(2)
+    plan, tensors = setup(api, w)
+    st = api.varlen_attn_plan_stats(plan)
+    log(f"[bench] plan: {st['prefill_tiles']} prefill tiles, {st['split_items']} split items, "
+        f"{st['plan_host_us']:.0f} us host")
+    wall, stage, totals = time_runs(api, plan, tensors, args.steps, args.warmup)
+    ms = wall
+    value = st["flops"] / (ms * 1e-3) / 1e12
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        traffic = json.load(open(args.traffic)).get("orca-mixed")
+    roof = roofline(st, stage, traffic)
+    log(f"[bench] {ms:.4f} ms/step  {value:.1f} TFLOP/s  stages {stage}")
+
+    rec = {"metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) Q/K/V cast to bf16)",
+           "config": {"workload": "orca-mixed-llama7b: one layer; prefill q_rows=4096 kv=4096 + decodes (1,1500), "
+                                  "(1,1700); Hq=Hkv=32, head_dim=128, page_size=16, permuted pages, bf16",
+                      "total_q_rows": int(w.total_q_rows), "flops_per_step": st["flops"],
+                      "kv_bytes": st["physical_kv_bytes"]},
+           "stage_ms": {k: round(v, 5) for k, v in stage.items()},
+           "peak_frac": round(value * 1e12 / PEAK_BF16, 4),
+           "roofline": roof}
+    del tensors
+    torch.cuda.empty_cache()
+
+    if not args.no_secondary:
+        flush_buf = torch.empty(1 << 29, dtype=torch.uint8, device="cuda")
+
+        def flush():
+            flush_buf.zero_()     # 512 MiB write evicts the 256 MB last-level cache
+
+        sec = []
+        for cid, flags, label, fl in ((3, 0, "decode-heavy-gqa (256 decodes, kv U[1024,8192], g=4, page 64)", None),
+                                      (4, 0, "chunked-prefill-mix (2048@S0=30720 + 64 decodes, g=8)", None),
+                                      (5, api.VA_FLAG_SHARED_PREFIX, "shared-prefix-6 (4096 shared + 1024 each)", flush),
+                                      (51, api.VA_FLAG_SHARED_PREFIX, "shared-prefix-64 (16384 shared + 1024 each)",
+                                       flush)):
+            log(f"[bench] secondary: {label}")
+            sec.append(secondary(api, W, cid, flags, 20, label, fl))
+            torch.cuda.empty_cache()
+        sec.append({"workload": "torch copy 1 GiB (read+write) for reference", "hbm_GBps": hbm_copy_gbps()})
+        rec["secondary"] = sec
+        del flush_buf
+
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        rec["cpu_baseline"] = cpu_baseline(w)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

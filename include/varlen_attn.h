@@ -112,6 +112,11 @@ typedef struct {
   int64_t table_bytes;        /* block-table entries read */
   int64_t workspace_bytes;    /* device scratch run() needs */
   double plan_host_us;        /* host time spent in varlen_attn_plan */
+  double prefill_flops;       /* part of `flops` done by prefill tiles */
+  double split_flops;         /* part of `flops` done by split-KV items */
+  int64_t prefill_kv_bytes;   /* distinct KV bytes the prefill tiles' requests read */
+  int64_t split_kv_bytes;     /* distinct KV bytes the split-KV requests read */
+  int64_t split_q_bytes;      /* query bytes of the split-KV requests */
 } va_plan_stats;
 
 typedef struct va_plan va_plan;   /* opaque, immutable after creation */
@@ -137,6 +142,18 @@ va_status varlen_attn_plan(const va_params* params, int32_t num_reqs, const int3
 va_status varlen_attn_run(const va_plan* plan, const void* q, const void* k_pool, const void* v_pool,
                           const int32_t* block_table_dev, void* out, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/* Same as varlen_attn_run, and also records the VA_RUN_EVENTS hipEvent_t handles in
+ * `events` on `stream` around its kernel stages, for per-kernel timing:
+ *   events[0] before the MFMA prefill kernel, events[1] after it (before the split-KV
+ *   kernel), events[2] after the split-KV kernel (before combine), events[3] at the end.
+ * A stage with no work leaves two consecutive events adjacent.  The events are created
+ * by the caller (with timing enabled) and are only recorded here. */
+#define VA_RUN_EVENTS 4
+va_status varlen_attn_run_events(const va_plan* plan, const void* q, const void* k_pool,
+                                 const void* v_pool, const int32_t* block_table_dev, void* out,
+                                 void* workspace, size_t workspace_bytes, void* stream,
+                                 void* const* events);
 
 /* Counters of the planned work (no device access). */
 va_status varlen_attn_plan_stats(const va_plan* plan, va_plan_stats* out);

@@ -19,7 +19,7 @@ VA_DTYPE_BF16, VA_DTYPE_F32 = 0, 1
 VA_FLAG_SHARED_PREFIX, VA_FLAG_NO_PREFILL_KERNEL, VA_FLAG_HOST_ONLY = 1, 2, 4
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvarlen_attn.so")
-EXPORTED = ["varlen_attn_plan", "varlen_attn_run", "varlen_attn_plan_stats", "varlen_attn_plan_export",
+EXPORTED = ["varlen_attn_plan", "varlen_attn_run", "varlen_attn_run_events", "varlen_attn_plan_stats", "varlen_attn_plan_export",
             "varlen_attn_debug_gather", "varlen_attn_plan_destroy", "varlen_attn_status_string",
             "varlen_attn_last_error"]
 
@@ -39,7 +39,9 @@ class VaPlanStats(ctypes.Structure):
                [("flops", ctypes.c_double)] + \
                [(n, ctypes.c_int64) for n in ("logical_kv_bytes", "physical_kv_bytes", "q_bytes", "o_bytes",
                                               "table_bytes", "workspace_bytes")] + \
-               [("plan_host_us", ctypes.c_double)]
+               [("plan_host_us", ctypes.c_double), ("prefill_flops", ctypes.c_double),
+                ("split_flops", ctypes.c_double)] + \
+               [(n, ctypes.c_int64) for n in ("prefill_kv_bytes", "split_kv_bytes", "split_q_bytes")]
 
 
 class VarlenAttnError(RuntimeError):
@@ -70,6 +72,8 @@ def lib():
         L.varlen_attn_plan.restype = ctypes.c_int
         L.varlen_attn_run.argtypes = [P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.varlen_attn_run.restype = ctypes.c_int
+        L.varlen_attn_run_events.argtypes = [P, P, P, P, P, P, P, ctypes.c_size_t, P, ctypes.POINTER(P)]
+        L.varlen_attn_run_events.restype = ctypes.c_int
         L.varlen_attn_plan_stats.argtypes = [P, ctypes.POINTER(VaPlanStats)]
         L.varlen_attn_plan_stats.restype = ctypes.c_int
         L.varlen_attn_plan_export.argtypes = [P, ctypes.c_int32, ctypes.POINTER(i32p),
@@ -191,6 +195,31 @@ def varlen_attn_run(plan: Plan, q, k_pool, v_pool, block_table_dev, out, workspa
                                  _dev_ptr(v_pool, "v_pool", dt), _dev_ptr(block_table_dev, "block_table", torch.int32),
                                  _dev_ptr(out, "out", dt), _dev_ptr(workspace, "workspace"), ws_bytes,
                                  _stream_ptr(stream)))
+
+
+VA_RUN_EVENTS = 4
+
+
+def varlen_attn_run_events(plan: Plan, q, k_pool, v_pool, block_table_dev, out, workspace, events,
+                           stream=None) -> None:
+    """``events``: VA_RUN_EVENTS torch.cuda.Event(enable_timing=True) objects."""
+    import torch
+    if len(events) != VA_RUN_EVENTS:
+        raise ValueError(f"need {VA_RUN_EVENTS} events")
+    s = torch.cuda.current_stream() if stream is None else stream
+    handles = []
+    for ev in events:
+        if ev.cuda_event == 0:        # torch creates the event on its first record
+            ev.record(s)
+        handles.append(ev.cuda_event)
+    arr = (ctypes.c_void_p * VA_RUN_EVENTS)(*handles)
+    dt = _elem_dtype(plan)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().varlen_attn_run_events(plan.handle, _dev_ptr(q, "q", dt), _dev_ptr(k_pool, "k_pool", dt),
+                                        _dev_ptr(v_pool, "v_pool", dt),
+                                        _dev_ptr(block_table_dev, "block_table", torch.int32),
+                                        _dev_ptr(out, "out", dt), _dev_ptr(workspace, "workspace"), ws_bytes,
+                                        ctypes.c_void_p(s.cuda_stream), arr))
 
 
 def varlen_attn_debug_gather(plan: Plan, k_pool, v_pool, block_table_dev, k_out, v_out, stream=None) -> None:

@@ -404,14 +404,14 @@ static int log2i(int x) {
 
 using namespace va;
 
-extern "C" va_status varlen_attn_run(const va_plan* plan, const void* q, const void* k_pool, const void* v_pool,
-                                     const int32_t* block_table_dev, void* out, void* workspace,
-                                     size_t workspace_bytes, void* stream) {
+static va_status run_impl(const va_plan* plan, const void* q, const void* k_pool, const void* v_pool,
+                          const int32_t* block_table_dev, void* out, void* workspace, size_t workspace_bytes,
+                          void* stream, void* const* events) {
   if (!plan) return fail(VA_ERR_INVALID_ARG, "plan is NULL");
   if (!plan->dev) return fail(VA_ERR_INVALID_ARG, "plan has no device buffer (built with VA_FLAG_HOST_ONLY)");
   const bool any = !plan->items.empty() || !plan->tiles.empty();
-  if (!any) return VA_OK;
-  if (!q || !k_pool || !v_pool || !block_table_dev || !out)
+  if (!any && !events) return VA_OK;
+  if (any && (!q || !k_pool || !v_pool || !block_table_dev || !out))
     return fail(VA_ERR_INVALID_ARG, "q, k_pool, v_pool, block_table_dev and out must be non-NULL");
   if (workspace_bytes < plan->ws_bytes)
     return fail(VA_ERR_WORKSPACE_TOO_SMALL, "workspace has " + std::to_string(workspace_bytes) + " bytes, plan needs " +
@@ -436,6 +436,12 @@ extern "C" va_status varlen_attn_run(const va_plan* plan, const void* q, const v
   const bool bf = p.dtype == VA_DTYPE_BF16;
 
   (void)hipGetLastError();   // clear a stale error left by earlier, unrelated calls
+  auto mark = [&](int i) -> hipError_t {
+    return events ? hipEventRecord(static_cast<hipEvent_t>(events[i]), s) : hipSuccess;
+  };
+  if ((e = mark(0)) != hipSuccess) return hip_fail("hipEventRecord", e);
+  // (prefill tiles are launched here once the MFMA prefill kernel exists)
+  if ((e = mark(1)) != hipSuccess) return hip_fail("hipEventRecord", e);
   if (nitems) {
     const dim3 grid((nitems + kSplitWaves - 1) / kSplitWaves), block(64 * kSplitWaves);
     if (bf) {
@@ -466,6 +472,7 @@ extern "C" va_status varlen_attn_run(const va_plan* plan, const void* q, const v
     e = hipGetLastError();
     if (e != hipSuccess) return hip_fail("split-KV kernel launch", e);
   }
+  if ((e = mark(2)) != hipSuccess) return hip_fail("hipEventRecord", e);
   if (ncomb) {
     const dim3 grid((ncomb + 3) / 4), block(256);
     if (bf) {
@@ -484,7 +491,24 @@ extern "C" va_status varlen_attn_run(const va_plan* plan, const void* q, const v
     e = hipGetLastError();
     if (e != hipSuccess) return hip_fail("combine kernel launch", e);
   }
+  if ((e = mark(3)) != hipSuccess) return hip_fail("hipEventRecord", e);
   return VA_OK;
+}
+
+extern "C" va_status varlen_attn_run(const va_plan* plan, const void* q, const void* k_pool, const void* v_pool,
+                                     const int32_t* block_table_dev, void* out, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  return run_impl(plan, q, k_pool, v_pool, block_table_dev, out, workspace, workspace_bytes, stream, nullptr);
+}
+
+extern "C" va_status varlen_attn_run_events(const va_plan* plan, const void* q, const void* k_pool,
+                                            const void* v_pool, const int32_t* block_table_dev, void* out,
+                                            void* workspace, size_t workspace_bytes, void* stream,
+                                            void* const* events) {
+  if (!events) return fail(VA_ERR_INVALID_ARG, "events is NULL");
+  for (int i = 0; i < VA_RUN_EVENTS; ++i)
+    if (!events[i]) return fail(VA_ERR_INVALID_ARG, "events[" + std::to_string(i) + "] is NULL");
+  return run_impl(plan, q, k_pool, v_pool, block_table_dev, out, workspace, workspace_bytes, stream, events);
 }
 
 extern "C" va_status varlen_attn_debug_gather(const va_plan* plan, const void* k_pool, const void* v_pool,

@@ -331,26 +331,40 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
   st.shared_groups = int64_t(groups.size());
   st.partial_slots = slots;
   st.combine_rows = int64_t(plan->combine.size());
-  std::vector<int32_t> max_slot(p.num_pages, 0);
-  int64_t pairs = 0, logical_pos = 0, rows = 0, table_entries = 0;
+  // distinct positions read: all requests, and each class (prefill tiles / split items)
+  std::vector<int32_t> max_slot(p.num_pages, 0), max_slot_pf(p.num_pages, 0), max_slot_sp(p.num_pages, 0);
+  std::vector<char> is_split(num_reqs, 0);
+  for (int r : split_reqs) is_split[r] = 1;
+  int64_t pairs = 0, logical_pos = 0, rows = 0, table_entries = 0, pairs_pf = 0, rows_sp = 0;
   for (int r = 0; r < num_reqs; ++r) {
     const int64_t m = q_end[r] - q_start[r];
     if (m == 0) continue;
     const int64_t kv = kv_len[r], S0 = kv - m;
-    pairs += m * S0 + m * (m + 1) / 2;
+    const int64_t pr = m * S0 + m * (m + 1) / 2;
+    pairs += pr;
+    if (!is_split[r]) pairs_pf += pr; else rows_sp += m;
     logical_pos += kv;
     rows += m;
     const int64_t npg = ceil_div(kv, ps);
     table_entries += npg;
     for (int64_t j = 0; j < npg; ++j) {
       const int32_t used = int32_t(std::min<int64_t>(ps, kv - j * ps));
-      int32_t& ms = max_slot[bt(r, j)];
-      ms = std::max(ms, used);
+      for (auto* v : {&max_slot, is_split[r] ? &max_slot_sp : &max_slot_pf}) {
+        int32_t& ms = (*v)[bt(r, j)];
+        ms = std::max(ms, used);
+      }
     }
   }
-  int64_t phys_pos = 0;
+  int64_t phys_pos = 0, phys_pf = 0, phys_sp = 0;
   for (int32_t v : max_slot) phys_pos += v;
+  for (int32_t v : max_slot_pf) phys_pf += v;
+  for (int32_t v : max_slot_sp) phys_sp += v;
   const int64_t pos_bytes = int64_t(Hkv) * D * 2 * elem;
+  st.prefill_flops = 4.0 * D * Hq * double(pairs_pf);
+  st.split_flops = 4.0 * D * Hq * double(pairs - pairs_pf);
+  st.prefill_kv_bytes = phys_pf * pos_bytes;
+  st.split_kv_bytes = phys_sp * pos_bytes;
+  st.split_q_bytes = rows_sp * Hq * D * elem;
   st.visible_pairs = pairs;
   st.flops = 4.0 * D * Hq * double(pairs);
   st.logical_kv_bytes = logical_pos * pos_bytes;

@@ -90,7 +90,8 @@ typedef struct {
   int32_t dtype;              /* va_dtype of q, k_pool, v_pool, out; accumulation is fp32 */
   float softmax_scale;        /* <= 0: 1/sqrt(head_dim) */
   uint32_t flags;             /* VA_FLAG_* */
-  int32_t prefill_min_rows;   /* q_rows from which a request uses prefill tiles; <= 0: 64 */
+  int32_t prefill_min_rows;   /* q_rows from which a request uses prefill tiles;
+                                 <= 0: when q_rows * (Hq / Hkv) >= 64 */
   int32_t split_len;          /* kv positions per split-KV item; <= 0: chosen by the planner */
 } va_params;
 

@@ -282,6 +282,220 @@ __global__ __launch_bounds__(256) void split_kv_f32_kernel(
   if (cvalid) store_partial<D>(ws_ml, ws_acc, c.pbase + it.slot, grp, m_run, l_tot, acc);
 }
 
+// ------------------------------------------------------------ MFMA prefill, bf16 --
+// One workgroup = one PrefillTile of up to 32*NW query columns (new rows x query heads of
+// one KV head, row-major), NW wavefronts of 32 columns each.  KV tiles of 64 positions are
+// gathered through the block table into double-buffered LDS (K as [key][d], V^T as
+// [d][key], 16-byte chunks XOR-swizzled by row against bank conflicts) and shared by all
+// waves.  Per wave, v_mfma_f32_32x32x16_bf16 computes S^T = K . Q^T for two 32-key blocks
+// (keys on M, the wave's 32 columns on N) and O^T += V^T . P^T.
+//
+// 32x32x16 layouts: A/B operands give lane l row/column (l % 32) and k-elements
+// 8*(l/32) .. +7; the 32x32 f32 result gives lane l column (l % 32) and rows
+// 8*i + 4*(l/32) + j at element 4*i + j.  A-operand row rho of an S^T block holds key
+// kappa(rho) = rho with bits 2 and 3 swapped, which puts keys 16*t + 8*(l/32) .. +7 of the
+// block in elements 8*t .. 8*t+7 of lane l: the k-slice the P^T operand of the t-th PV
+// MFMA needs.  So P stays in registers.
+//
+// Online softmax in base 2 with lazy rescaling: the reference max of a column only moves
+// when a tile's max exceeds it by more than 8 (p <= 2^8 otherwise); the final division
+// by the running sum makes the result independent of the reference.
+constexpr int kPTileKeys = 64;
+constexpr float kRescaleSlack = 8.f;
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x16 mfma32_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float sum8_bf16(bf16x8 p) {
+  const bf16x2 one = {bf16(1.f), bf16(1.f)};
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) s = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p[e], p[e + 1]}, one, s, false);
+  return s;
+}
+
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_bf16_kernel(
+    const PrefillTile* __restrict__ tiles, const bf16* __restrict__ q, const bf16* __restrict__ kpool,
+    const bf16* __restrict__ vpool, const int32_t* __restrict__ bt, int bt_stride, bf16* __restrict__ out, int Hq,
+    int g, Paged pg, float scale_log2) {
+  constexpr int KCH = D / 8;                          // 16-byte chunks per K row
+  constexpr int TCH = kPTileKeys * D / 8;             // chunks per K (or V) tile
+  constexpr int PER = TCH / (64 * NW);                // chunks per thread per tile
+  static_assert(PER * 64 * NW == TCH, "tile must split evenly over the threads");
+  __shared__ bf16x8 sK[2][TCH];
+  __shared__ bf16x8 sV[2][TCH];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const PrefillTile T = tiles[blockIdx.x];
+  const int h = lane >> 5;
+  const int col = wv * 32 + (lane & 31);
+  const bool cvalid = col < T.ncols;
+  const int c = T.c0 + (cvalid ? col : 0);
+  const int i = c / g;
+  const int row = T.q0 + i, head = T.kvh * g + c % g;
+  const int limit = cvalid ? T.S0 + i : -1;
+  // the wave's first and last visible positions bound its causal work
+  const int wcol_last = min(wv * 32 + 31, T.ncols - 1);
+  const int w_min_limit = T.S0 + (T.c0 + wv * 32) / g;
+  const int w_max_limit = (wv * 32 < T.ncols) ? T.S0 + (T.c0 + wcol_last) / g : -1;
+
+  bf16x8 qb[D / 16];
+  {
+    const bf16* qp = q + (size_t(row) * Hq + head) * D + 8 * h;
+#pragma unroll
+    for (int kc = 0; kc < D / 16; ++kc) {
+      qb[kc] = *reinterpret_cast<const bf16x8*>(qp + 16 * kc);
+      if (!cvalid) qb[kc] = bf16x8{};
+    }
+  }
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[db][e] = 0.f;
+  float m_run = kNegBig, l_run = 0.f;
+
+  const int32_t* btr = bt + size_t(T.req) * bt_stride;
+  const int kvh = T.kvh;
+  const int kv_end = T.kv_end;
+  const int ntiles = (kv_end + kPTileKeys - 1) / kPTileKeys;
+
+  bf16x8 pk[PER], pv[PER];
+  // gather tile j into registers: K chunk t -> (key t / KCH, 8 d-values), V chunk t ->
+  // (d = t / 8, keys 8*(t % 8) .. +7)
+  auto load_tile = [&](int j) {
+    const int k0 = j * kPTileKeys;
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const int t = tid + r * 64 * NW;
+      const int kk = min(k0 + t / KCH, kv_end - 1);
+      pk[r] = *reinterpret_cast<const bf16x8*>(kpool + pg.k_row(pg.page_of(btr, kk), kvh, pg.slot_of(kk)) +
+                                               8 * (t % KCH));
+      const int d = t / 8;
+      const int vkey = k0 + 8 * (t % 8);
+      const int vk = min(vkey, (kv_end - 1) & ~7);
+      pv[r] = *reinterpret_cast<const bf16x8*>(vpool + pg.v_elem(pg.page_of(btr, vk), kvh, d, pg.slot_of(vk)));
+      const int valid = kv_end - vkey;   // positions past the tile's end may be unwritten slots
+      if (valid < 8) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (e >= valid) pv[r][e] = bf16(0.f);
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const int t = tid + r * 64 * NW;
+      const int key = t / KCH, kc = t % KCH;
+      sK[buf][key * KCH + (kc ^ (key & (KCH - 1)))] = pk[r];
+      const int d = t / 8, vc = t % 8;
+      sV[buf][d * 8 + (vc ^ (d & 7))] = pv[r];
+    }
+  };
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  const int rho = lane & 31;
+  const int kap = (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1);   // swap bits 2 and 3
+  for (int j = 0; j < ntiles; ++j) {
+    const int buf = j & 1;
+    const bool has_next = j + 1 < ntiles;
+    if (has_next) load_tile(j + 1);
+    const int k0 = j * kPTileKeys;
+    if (k0 <= w_max_limit) {
+      // ---- S^T for the tile's two 32-key blocks
+      f32x16 s[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[b][e] = 0.f;
+        const int key = 32 * b + kap;
+#pragma unroll
+        for (int kc = 0; kc < D / 16; ++kc) {
+          const int cc = 2 * kc + h;
+          s[b] = mfma32_bf16(sK[buf][key * KCH + (cc ^ (key & (KCH - 1)))], qb[kc], s[b]);
+        }
+      }
+      // ---- mask (diagonal and ragged tiles only)
+      if (k0 + kPTileKeys - 1 > w_min_limit) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int ii = e >> 2, jj = e & 3;
+            const int key = k0 + 32 * b + 16 * (ii >> 1) + 8 * h + 4 * (ii & 1) + jj;
+            if (key > limit) s[b][e] = -INFINITY;
+          }
+      }
+      // ---- online softmax
+      float mx = s[0][0];
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[b][e]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_tile = mx * scale_log2;
+      const bool need = m_tile > m_run + kRescaleSlack;
+      if (__any(need)) {
+        const float m_new = need ? m_tile : m_run;
+        const float alpha = fast_exp2(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
+      }
+      bf16x8 p[2][2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) p[b][t][e] = bf16(fast_exp2(fmaf(s[b][8 * t + e], scale_log2, -m_run)));
+          l_run += sum8_bf16(p[b][t]);
+        }
+      // ---- O^T += V^T . P^T
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const int d = 32 * db + rho;
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int vc = 4 * b + 2 * t + h;
+            acc[db] = mfma32_bf16(sV[buf][d * 8 + (vc ^ (d & 7))], p[b][t], acc[db]);
+          }
+      }
+    }
+    if (has_next) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+  // ---- normalise and write: acc[db][4*ii + jj] is d = 32*db + 8*ii + 4*h + jj of this column
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (cvalid) {
+    const float inv = 1.f / l_tot;
+    bf16* op = out + (size_t(row) * Hq + head) * D + 4 * h;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        bf16x4 o4;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) o4[jj] = bf16(acc[db][4 * ii + jj] * inv);
+        *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * ii) = o4;
+      }
+  }
+}
+
 // ------------------------------------------------------------------------ combine --
 // out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s with M = max_s m_s.
 template <int D, typename OutT>
@@ -342,7 +556,9 @@ static va_status hip_fail(const char* what, hipError_t e) {
   return fail(VA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-bool prefill_kernel_available(const va_params&) { return false; }
+bool prefill_kernel_available(const va_params& p) {
+  return p.dtype == VA_DTYPE_BF16 && (p.head_dim == 64 || p.head_dim == 128);
+}
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -440,7 +656,24 @@ static va_status run_impl(const va_plan* plan, const void* q, const void* k_pool
     return events ? hipEventRecord(static_cast<hipEvent_t>(events[i]), s) : hipSuccess;
   };
   if ((e = mark(0)) != hipSuccess) return hip_fail("hipEventRecord", e);
-  // (prefill tiles are launched here once the MFMA prefill kernel exists)
+  const int ntiles = int(plan->tiles.size());
+  if (ntiles) {
+    const dim3 grid(ntiles), block(64 * kPrefillWaves);
+    auto* qq = static_cast<const bf16*>(q);
+    auto* kk = static_cast<const bf16*>(k_pool);
+    auto* vv = static_cast<const bf16*>(v_pool);
+    auto* oo = static_cast<bf16*>(out);
+    if (D == 128)
+      prefill_bf16_kernel<128, kPrefillWaves><<<grid, block, 0, s>>>(plan->d_tiles, qq, kk, vv, block_table_dev,
+                                                                   bt_stride, oo, p.num_q_heads, plan->g, pg,
+                                                                   scale_log2);
+    else
+      prefill_bf16_kernel<64, kPrefillWaves><<<grid, block, 0, s>>>(plan->d_tiles, qq, kk, vv, block_table_dev,
+                                                                  bt_stride, oo, p.num_q_heads, plan->g, pg,
+                                                                  scale_log2);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail("prefill kernel launch", e);
+  }
   if ((e = mark(1)) != hipSuccess) return hip_fail("hipEventRecord", e);
   if (nitems) {
     const dim3 grid((nitems + kSplitWaves - 1) / kSplitWaves), block(64 * kSplitWaves);

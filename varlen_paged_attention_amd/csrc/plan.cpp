@@ -135,7 +135,10 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
   for (int r = 0; r < num_reqs; ++r) plan->kv_offset[r + 1] = plan->kv_offset[r] + kv_len[r];
 
   auto bt = [&](int r, int64_t j) { return block_table_host[int64_t(r) * p.max_pages_per_req + j]; };
-  const int prefill_min = p.prefill_min_rows > 0 ? p.prefill_min_rows : 64;
+  // default: a request gets prefill tiles once its new rows fill half a tile's columns
+  auto is_prefill = [&](int m) {
+    return p.prefill_min_rows > 0 ? m >= p.prefill_min_rows : int64_t(m) * g >= kPrefillCols / 2;
+  };
   const bool use_prefill = !(p.flags & VA_FLAG_NO_PREFILL_KERNEL) && prefill_kernel_available(p);
 
   // ---- classify requests -------------------------------------------------------
@@ -144,7 +147,7 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
     const int m = q_end[r] - q_start[r];
     if (m == 0) continue;
     const int S0 = kv_len[r] - m;
-    if (use_prefill && m >= prefill_min) {
+    if (use_prefill && is_prefill(m)) {
       const int ncol = m * g;
       for (int kvh = 0; kvh < Hkv; ++kvh)
         for (int c0 = 0; c0 < ncol; c0 += kPrefillCols) {

@@ -39,7 +39,8 @@ struct PrefillTile {
 
 constexpr int kSplitCols = 16;       // query columns per split-KV item (MFMA N)
 constexpr int kSplitWaves = 4;       // items (wavefronts) per split-KV workgroup
-constexpr int kPrefillCols = 128;    // query columns per prefill tile
+constexpr int kPrefillWaves = 4;     // wavefronts per prefill workgroup (32 columns each)
+constexpr int kPrefillCols = 32 * kPrefillWaves;   // query columns per prefill tile
 constexpr int kStepKeys = 64;        // kv positions per split-KV loop step
 
 }  // namespace va

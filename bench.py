@@ -181,6 +181,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--traffic", default=None, help="JSON file with measured HBM bytes per launch")
+    ap.add_argument("--only", type=int, default=None,
+                    help="profile mode: time only this workload (2, 3, 4, 5 or 51) and print its line")
+    ap.add_argument("--copy-only", action="store_true",
+                    help="profile mode: 10 device copies of 1 GiB (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no multi-GPU path.",
@@ -191,6 +195,14 @@ def main():
     from varlen_paged_attention_amd import api, workloads as W
     torch.cuda.set_device(0)
     api.lib()
+    if args.copy_only:
+        print(json.dumps({"copy_GBps": hbm_copy_gbps(), "bytes_per_copy": 2 * (1 << 30)}), flush=True)
+        return
+    if args.only is not None:
+        flags = api.VA_FLAG_SHARED_PREFIX if args.only in (5, 51) else 0
+        res = secondary(api, W, args.only, flags, args.steps, W.CONFIG_NAMES[args.only], None)
+        print(json.dumps(res), flush=True)
+        return
 
     log("[bench] building the ORCA mixed iteration (4096 prefill + decodes 1500, 1700)")
     w = W.config(2)

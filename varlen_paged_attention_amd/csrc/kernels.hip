@@ -326,8 +326,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     int g, Paged pg, float scale_log2) {
   constexpr int KCH = D / 8;                          // 16-byte chunks per K row
   constexpr int TCH = kPTileKeys * D / 8;             // chunks per K (or V) tile
-  constexpr int PER = TCH / (64 * NW);                // chunks per thread per tile
-  static_assert(PER * 64 * NW == TCH, "tile must split evenly over the threads");
   __shared__ bf16x8 sK[2][TCH];
   __shared__ bf16x8 sV[2][TCH];
 
@@ -368,41 +366,85 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int kv_end = T.kv_end;
   const int ntiles = (kv_end + kPTileKeys - 1) / kPTileKeys;
 
-  bf16x8 pk[PER], pv[PER];
-  // gather tile j into registers: K chunk t -> (key t / KCH, 8 d-values), V chunk t ->
-  // (d = t / 8, keys 8*(t % 8) .. +7)
-  auto load_tile = [&](int j) {
-    const int k0 = j * kPTileKeys;
+  // Staging: wave w copies keys [WK*w, WK*w + WK) of every 64-key tile into LDS.  The
+  // slice is page-aligned and page_size >= 16 >= WK, so it lies in one page: the page id
+  // and the slice's base address are wave-uniform (scalar loads and arithmetic), and page
+  // ids are fetched two tiles ahead.  Per lane: K chunk u = lane + 64*r is key u / KCH of
+  // the slice, d-values 8*(u % KCH) .. +7; V chunk u is row d = u / VH, keys 8*(u % VH) .. +7
+  // of the slice (VH = WK / 8).
+  constexpr int WK = kPTileKeys / NW;
+  constexpr int VH = WK / 8;
+  constexpr int KPER = WK * KCH / 64;
+  constexpr int VPER = D * VH / 64;
+  static_assert(KPER * 64 == WK * KCH && VPER * 64 == D * VH, "slice must split evenly over a wave");
+  const int ps_mask = (1 << pg.ps_shift) - 1;
+  const size_t page_elems = (size_t(pg.Hkv) * D) << pg.ps_shift;
+  const bf16* kbase = kpool + pg.k_row(0, kvh, 0);
+  const bf16* vbase = vpool + pg.v_elem(0, kvh, 0, 0);
+  bf16x8 pk[KPER], pv[VPER];
+  // LDS writes are serviced 8 lanes (128 bytes) at a time: with two chunks per V^T row per
+  // wave, lanes 4k .. 4k+3 take rows whose swizzles differ in bits 1-2 (rows 0,2,4,6 then
+  // 1,3,5,7 of each group of 8) so every 8-lane group hits 8 distinct chunk positions.
+  auto vrow = [](int j) { return VH == 2 ? (((j & 3) << 1) | ((j >> 2) & 1) | (j & ~7)) : j; };
+  auto page_for = [&](int j) -> int {
+    const int k0w = j * kPTileKeys + wv * WK;
+    return pg.page_of(btr, min(k0w, kv_end - 1));
+  };
+  auto load_tile = [&](int j, int page) {
+    const int k0w = j * kPTileKeys + wv * WK;
+    if (k0w < kv_end) {
+      const bf16* kp = kbase + size_t(page) * page_elems + size_t(k0w & ps_mask) * D;
 #pragma unroll
-    for (int r = 0; r < PER; ++r) {
-      const int t = tid + r * 64 * NW;
-      const int kk = min(k0 + t / KCH, kv_end - 1);
-      pk[r] = *reinterpret_cast<const bf16x8*>(kpool + pg.k_row(pg.page_of(btr, kk), kvh, pg.slot_of(kk)) +
-                                               8 * (t % KCH));
-      const int d = t / 8;
-      const int vkey = k0 + 8 * (t % 8);
-      const int vk = min(vkey, (kv_end - 1) & ~7);
-      pv[r] = *reinterpret_cast<const bf16x8*>(vpool + pg.v_elem(pg.page_of(btr, vk), kvh, d, pg.slot_of(vk)));
-      const int valid = kv_end - vkey;   // positions past the tile's end may be unwritten slots
-      if (valid < 8) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (e >= valid) pv[r][e] = bf16(0.f);
+      for (int r = 0; r < KPER; ++r) {
+        const int u = lane + 64 * r;
+        pk[r] = *reinterpret_cast<const bf16x8*>(kp + (u / KCH) * D + 8 * (u % KCH));
       }
+      const bf16* vp = vbase + size_t(page) * page_elems + (k0w & ps_mask);
+#pragma unroll
+      for (int r = 0; r < VPER; ++r) {
+        const int u = lane + 64 * r;
+        pv[r] = *reinterpret_cast<const bf16x8*>(vp + (vrow(u / VH) << pg.ps_shift) + 8 * (u % VH));
+      }
+      if (k0w + WK > kv_end) {
+        // positions past the tile's end may be unwritten slots: zero their V so that
+        // 0 * garbage cannot reach the accumulator (their scores are masked)
+#pragma unroll
+        for (int r = 0; r < VPER; ++r) {
+          const int valid = kv_end - (k0w + 8 * ((lane + 64 * r) % VH));
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (e >= valid) pv[r][e] = bf16(0.f);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < KPER; ++r) pk[r] = bf16x8{};
+#pragma unroll
+      for (int r = 0; r < VPER; ++r) pv[r] = bf16x8{};
     }
   };
+  // V^T rows are 128 bytes; the chunk swizzle (d & 7) ^ ((d >> 3) & 1) keeps any 8 or 16
+  // consecutive rows read at one chunk position on distinct banks.
+  auto vswz = [](int d) { return (d & 7) ^ ((d >> 3) & 1); };
   auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int r = 0; r < PER; ++r) {
-      const int t = tid + r * 64 * NW;
-      const int key = t / KCH, kc = t % KCH;
+    for (int r = 0; r < KPER; ++r) {
+      const int u = lane + 64 * r;
+      const int key = wv * WK + u / KCH, kc = u % KCH;
       sK[buf][key * KCH + (kc ^ (key & (KCH - 1)))] = pk[r];
-      const int d = t / 8, vc = t % 8;
-      sV[buf][d * 8 + (vc ^ (d & 7))] = pv[r];
+    }
+#pragma unroll
+    for (int r = 0; r < VPER; ++r) {
+      const int u = lane + 64 * r;
+      const int d = vrow(u / VH), vc = wv * VH + u % VH;
+      sV[buf][d * 8 + (vc ^ vswz(d))] = pv[r];
     }
   };
 
-  load_tile(0);
+  int page_next = page_for(0);
+  load_tile(0, page_next);
+  if (ntiles > 1) page_next = page_for(1);
+  int page_after = ntiles > 2 ? page_for(2) : 0;
   store_tile(0);
   __syncthreads();
   const int rho = lane & 31;
@@ -410,7 +452,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   for (int j = 0; j < ntiles; ++j) {
     const int buf = j & 1;
     const bool has_next = j + 1 < ntiles;
-    if (has_next) load_tile(j + 1);
+    if (has_next) {
+      load_tile(j + 1, page_next);
+      page_next = page_after;
+      if (j + 3 < ntiles) page_after = page_for(j + 3);
+    }
     const int k0 = j * kPTileKeys;
     if (k0 <= w_max_limit) {
       // ---- S^T for the tile's two 32-key blocks
@@ -472,7 +518,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
             const int vc = 4 * b + 2 * t + h;
-            acc[db] = mfma32_bf16(sV[buf][d * 8 + (vc ^ (d & 7))], p[b][t], acc[db]);
+            acc[db] = mfma32_bf16(sV[buf][d * 8 + (vc ^ vswz(d))], p[b][t], acc[db]);
           }
       }
     }

@@ -283,29 +283,45 @@ __global__ __launch_bounds__(256) void split_kv_f32_kernel(
 }
 
 // ------------------------------------------------------------ MFMA prefill, bf16 --
-// One workgroup = one PrefillTile of up to 32*NW query columns (new rows x query heads of
-// one KV head, row-major), NW wavefronts of 32 columns each.  KV tiles of 64 positions are
-// gathered through the block table into double-buffered LDS (K as [key][d], V^T as
-// [d][key], 16-byte chunks XOR-swizzled by row against bank conflicts) and shared by all
-// waves.  Per wave, v_mfma_f32_32x32x16_bf16 computes S^T = K . Q^T for two 32-key blocks
-// (keys on M, the wave's 32 columns on N) and O^T += V^T . P^T.
+// One workgroup = one PrefillTile of up to 128 query columns (new rows x query heads of one
+// KV head, row-major), 4 wavefronts of 32 columns each.  KV tiles of 64 positions are
+// copied by LDS-DMA loads (buffer_load ... lds: lane i's 16 bytes land at the
+// instruction's LDS base + 16*i, from a per-lane source address) into double-buffered LDS
+// shared by the 4 waves; no staging registers.  Wave w copies keys [16w, 16w+16) of each
+// tile, which lie in one page (page_size >= 16), so its page lookup and source base are
+// wave-uniform.
 //
-// 32x32x16 layouts: A/B operands give lane l row/column (l % 32) and k-elements
-// 8*(l/32) .. +7; the 32x32 f32 result gives lane l column (l % 32) and rows
-// 8*i + 4*(l/32) + j at element 4*i + j.  A-operand row rho of an S^T block holds key
-// kappa(rho) = rho with bits 2 and 3 swapped, which puts keys 16*t + 8*(l/32) .. +7 of the
-// block in elements 8*t .. 8*t+7 of lane l: the k-slice the P^T operand of the t-th PV
-// MFMA needs.  So P stays in registers.
+// LDS layouts (16-byte chunks):
+//   K   [key][KCH+1]: rows padded by one chunk, so the 16 lanes of an MFMA operand read
+//       (16 different keys, same d-chunk) hit 16 distinct bank groups and every read is a
+//       per-lane base plus an immediate offset.  The pad chunk receives a duplicate.
+//   V^T [slice w][d][2]: keys 16w .. 16w+15 of row d as two chunks, the chunk order
+//       flipped when bit 3 of d is set so the 16 rows read at one key-chunk position fall
+//       on 16 distinct bank groups.
+//
+// Per wave, v_mfma_f32_32x32x16_bf16 computes S^T = K . Q^T for two 32-key blocks (keys
+// on M, the wave's 32 columns on N) and O^T += V^T . P^T.  32x32x16 layouts: A/B operands
+// give lane l row/column (l % 32) and k-elements 8*(l/32) .. +7; the 32x32 f32 result
+// gives lane l column (l % 32) and rows 8*i + 4*(l/32) + j at element 4*i + j.  A-operand
+// row rho of an S^T block holds key kappa(rho) = rho with bits 2 and 3 swapped, which
+// puts keys 16*t + 8*(l/32) .. +7 of the block in elements 8*t .. 8*t+7 of lane l: the
+// k-slice the P^T operand of the t-th PV MFMA needs.  So P stays in registers.
+//
+// Software pipeline: iteration j issues the copies of K(j+2) and V(j+1), exponentiates
+// tile j's scores while the MFMAs of tile j+1's scores run, accumulates P(j) . V(j), then
+// waits for its copies and meets the other waves at the one barrier per tile.
 //
 // Online softmax in base 2 with lazy rescaling: the reference max of a column only moves
 // when a tile's max exceeds it by more than 8 (p <= 2^8 otherwise); the final division
 // by the running sum makes the result independent of the reference.
 constexpr int kPTileKeys = 64;
+constexpr int kPSliceKeys = kPTileKeys / kPrefillWaves;   // keys each wave copies per tile
 constexpr float kRescaleSlack = 8.f;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ f32x16 mfma32_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -319,22 +335,63 @@ __device__ __forceinline__ float sum8_bf16(bf16x8 p) {
   return s;
 }
 
-template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_bf16_kernel(
+// value of the other half-wave (lane l <-> lane l ^ 32)
+__device__ __forceinline__ float other_half(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(threadIdx.x & 32 ? r[0] : r[1]);
+}
+
+// Buffer resource over one page slice (wave-uniform base, raw addressing).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slice_rsrc(const bf16* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base), (short)0, 0x7fffffff, 0x00020000);
+}
+// 16 bytes per lane from rs + voff + soff into LDS at dst + 16 * lane.
+__device__ __forceinline__ void dma_b128(__amdgpu_buffer_rsrc_t rs, bf16x8* dst, uint32_t voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+template <int D>
+struct PrefillLds {
+  static constexpr int KCH = D / 8;                    // 16-byte chunks per K row
+  static constexpr int KROW = KCH + 1;                 // padded K row
+  static constexpr int KBUF = kPTileKeys * KROW;       // chunks per K buffer
+  static constexpr int VBUF = kPTileKeys / 8 * D;      // chunks per V^T buffer
+  static constexpr int bytes = 2 * (KBUF + VBUF) * 16;
+};
+
+template <int D>
+constexpr int prefill_lds_bytes() {
+  return PrefillLds<D>::bytes;
+}
+
+template <int D>
+__global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_bf16_kernel(
     const PrefillTile* __restrict__ tiles, const bf16* __restrict__ q, const bf16* __restrict__ kpool,
     const bf16* __restrict__ vpool, const int32_t* __restrict__ bt, int bt_stride, bf16* __restrict__ out, int Hq,
     int g, Paged pg, float scale_log2) {
-  constexpr int KCH = D / 8;                          // 16-byte chunks per K row
-  constexpr int TCH = kPTileKeys * D / 8;             // chunks per K (or V) tile
-  __shared__ bf16x8 sK[2][TCH];
-  __shared__ bf16x8 sV[2][TCH];
+  using Lay = PrefillLds<D>;
+  constexpr int KCH = Lay::KCH, KROW = Lay::KROW, KBUF = Lay::KBUF, VBUF = Lay::VBUF;
+  constexpr int WK = kPSliceKeys;                      // 16 keys per wave slice
+  static_assert(WK == 16, "slice layout assumes 16 keys per wave");
+  constexpr int KSC = WK * KROW;                       // K slice chunks (with pad)
+  constexpr int KNI = (KSC + 63) / 64;                 // DMA instructions per K slice
+  constexpr int KLAST = KSC - 64 * (KNI - 1);          // lanes active in the last one
+  constexpr int VSC = WK / 8 * D;                      // V^T slice chunks
+  constexpr int VNI = VSC / 64;
+  static_assert(VNI * 64 == VSC, "V^T slice must be whole instructions");
+  extern __shared__ bf16x8 smem[];
+  bf16x8* sK = smem;                                   // [2][KBUF]
+  bf16x8* sV = smem + 2 * KBUF;                        // [2][VBUF]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const PrefillTile T = tiles[blockIdx.x];
   const int h = lane >> 5;
-  const int col = wv * 32 + (lane & 31);
+  const int rho = lane & 31;
+  const int kap = (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1);   // swap bits 2 and 3
+  const int col = wv * 32 + rho;
   const bool cvalid = col < T.ncols;
   const int c = T.c0 + (cvalid ? col : 0);
   const int i = c / g;
@@ -365,114 +422,125 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int kvh = T.kvh;
   const int kv_end = T.kv_end;
   const int ntiles = (kv_end + kPTileKeys - 1) / kPTileKeys;
-
-  // Staging: wave w copies keys [WK*w, WK*w + WK) of every 64-key tile into LDS.  The
-  // slice is page-aligned and page_size >= 16 >= WK, so it lies in one page: the page id
-  // and the slice's base address are wave-uniform (scalar loads and arithmetic), and page
-  // ids are fetched two tiles ahead.  Per lane: K chunk u = lane + 64*r is key u / KCH of
-  // the slice, d-values 8*(u % KCH) .. +7; V chunk u is row d = u / VH, keys 8*(u % VH) .. +7
-  // of the slice (VH = WK / 8).
-  constexpr int WK = kPTileKeys / NW;
-  constexpr int VH = WK / 8;
-  constexpr int KPER = WK * KCH / 64;
-  constexpr int VPER = D * VH / 64;
-  static_assert(KPER * 64 == WK * KCH && VPER * 64 == D * VH, "slice must split evenly over a wave");
   const int ps_mask = (1 << pg.ps_shift) - 1;
   const size_t page_elems = (size_t(pg.Hkv) * D) << pg.ps_shift;
   const bf16* kbase = kpool + pg.k_row(0, kvh, 0);
   const bf16* vbase = vpool + pg.v_elem(0, kvh, 0, 0);
-  bf16x8 pk[KPER], pv[VPER];
-  // LDS writes are serviced 8 lanes (128 bytes) at a time: with two chunks per V^T row per
-  // wave, lanes 4k .. 4k+3 take rows whose swizzles differ in bits 1-2 (rows 0,2,4,6 then
-  // 1,3,5,7 of each group of 8) so every 8-lane group hits 8 distinct chunk positions.
-  auto vrow = [](int j) { return VH == 2 ? (((j & 3) << 1) | ((j >> 2) & 1) | (j & ~7)) : j; };
-  auto page_for = [&](int j) -> int {
-    const int k0w = j * kPTileKeys + wv * WK;
-    return pg.page_of(btr, min(k0w, kv_end - 1));
+
+  // ---- per-lane DMA source offsets (bytes from the slice base)
+  // K instruction r, lane -> slice chunk L = 64r + lane = (key L / KROW, d-chunk L % KROW);
+  // the pad chunk copies d-chunk 0 again.
+  uint32_t koff[KNI];
+#pragma unroll
+  for (int r = 0; r < KNI; ++r) {
+    const int L = min(64 * r + lane, KSC - 1);
+    koff[r] = uint32_t(((L / KROW) * D + 8 * min(L % KROW, KCH - 1)) * 2);
+  }
+  // V^T instruction r, lane -> slice chunk 64r + lane = (row d = 32r + lane/2, position
+  // lane & 1), holding the slice's key-chunk (lane & 1) ^ bit 3 of d; r adds 32 rows.
+  const int vd = lane >> 1;
+  const int vkc = (lane & 1) ^ ((vd >> 3) & 1);
+  const uint32_t voff = uint32_t(((vd << pg.ps_shift) + 8 * vkc) * 2);
+  const int vrstep = (32 << pg.ps_shift) * 2;
+
+  auto page_for = [&](int t) -> int {
+    return pg.page_of(btr, min(t * kPTileKeys + wv * WK, kv_end - 1));
   };
-  auto load_tile = [&](int j, int page) {
-    const int k0w = j * kPTileKeys + wv * WK;
-    if (k0w < kv_end) {
-      const bf16* kp = kbase + size_t(page) * page_elems + size_t(k0w & ps_mask) * D;
+  auto issue_k = [&](int t, int page, int buf) {
+    const int k0w = t * kPTileKeys + wv * WK;
+    if (k0w >= kv_end) return;               // positions past the end: scores are masked
+    const auto rs = slice_rsrc(kbase + size_t(page) * page_elems + size_t(k0w & ps_mask) * D);
+    bf16x8* dst = sK + buf * KBUF + wv * KSC;
 #pragma unroll
-      for (int r = 0; r < KPER; ++r) {
-        const int u = lane + 64 * r;
-        pk[r] = *reinterpret_cast<const bf16x8*>(kp + (u / KCH) * D + 8 * (u % KCH));
-      }
-      const bf16* vp = vbase + size_t(page) * page_elems + (k0w & ps_mask);
-#pragma unroll
-      for (int r = 0; r < VPER; ++r) {
-        const int u = lane + 64 * r;
-        pv[r] = *reinterpret_cast<const bf16x8*>(vp + (vrow(u / VH) << pg.ps_shift) + 8 * (u % VH));
-      }
-      if (k0w + WK > kv_end) {
-        // positions past the tile's end may be unwritten slots: zero their V so that
-        // 0 * garbage cannot reach the accumulator (their scores are masked)
-#pragma unroll
-        for (int r = 0; r < VPER; ++r) {
-          const int valid = kv_end - (k0w + 8 * ((lane + 64 * r) % VH));
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (e >= valid) pv[r][e] = bf16(0.f);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < KPER; ++r) pk[r] = bf16x8{};
-#pragma unroll
-      for (int r = 0; r < VPER; ++r) pv[r] = bf16x8{};
-    }
+    for (int r = 0; r < KNI; ++r)
+      if (r < KNI - 1 || lane < KLAST) dma_b128(rs, dst + 64 * r, koff[r], 0);
   };
-  // V^T rows are 128 bytes; the chunk swizzle (d & 7) ^ ((d >> 3) & 1) keeps any 8 or 16
-  // consecutive rows read at one chunk position on distinct banks.
-  auto vswz = [](int d) { return (d & 7) ^ ((d >> 3) & 1); };
-  auto store_tile = [&](int buf) {
+  auto issue_v = [&](int t, int page, int buf) {
+    const int k0w = t * kPTileKeys + wv * WK;
+    bf16x8* dst = sV + buf * VBUF + wv * VSC;
+    if (k0w >= kv_end) {                      // never read garbage into V: write zeros
 #pragma unroll
-    for (int r = 0; r < KPER; ++r) {
-      const int u = lane + 64 * r;
-      const int key = wv * WK + u / KCH, kc = u % KCH;
-      sK[buf][key * KCH + (kc ^ (key & (KCH - 1)))] = pk[r];
+      for (int r = 0; r < VNI; ++r) dst[64 * r + lane] = bf16x8{};
+      return;
     }
+    const auto rs = slice_rsrc(vbase + size_t(page) * page_elems + (k0w & ps_mask));
 #pragma unroll
-    for (int r = 0; r < VPER; ++r) {
-      const int u = lane + 64 * r;
-      const int d = vrow(u / VH), vc = wv * VH + u % VH;
-      sV[buf][d * 8 + (vc ^ vswz(d))] = pv[r];
+    for (int r = 0; r < VNI; ++r) dma_b128(rs, dst + 64 * r, voff, r * vrstep);
+  };
+  // after the copy of V(t) landed: zero the positions at or past the tile's end (they may
+  // be unwritten slots; their scores are masked, but 0 * NaN would still be NaN)
+  auto fix_v_tail = [&](int t, int buf) {
+    const int k0w = t * kPTileKeys + wv * WK;
+    if (k0w >= kv_end || k0w + WK <= kv_end) return;
+    bf16x8* dst = sV + buf * VBUF + wv * VSC;
+    const int valid = kv_end - (k0w + 8 * vkc);
+#pragma unroll
+    for (int r = 0; r < VNI; ++r) {
+      bf16x8 x = dst[64 * r + lane];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (e >= valid) x[e] = bf16(0.f);
+      dst[64 * r + lane] = x;
     }
   };
 
-  int page_next = page_for(0);
-  load_tile(0, page_next);
-  if (ntiles > 1) page_next = page_for(1);
-  int page_after = ntiles > 2 ? page_for(2) : 0;
-  store_tile(0);
-  __syncthreads();
-  const int rho = lane & 31;
-  const int kap = (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1);   // swap bits 2 and 3
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    const bool has_next = j + 1 < ntiles;
-    if (has_next) {
-      load_tile(j + 1, page_next);
-      page_next = page_after;
-      if (j + 3 < ntiles) page_after = page_for(j + 3);
+  // ---- per-wave compute pieces
+  const int kread = kap * KROW + h;                                 // + 32*b*KROW + 2*kc
+  const int vread = rho * 2 + (h ^ ((rho >> 3) & 1));               // + (2b+t)*VSC + 64*db
+  auto qk_block = [&](int buf, int b, f32x16& sn) {
+    const bf16x8* kb = sK + buf * KBUF + kread + 32 * b * KROW;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sn[e] = 0.f;
+#pragma unroll
+    for (int kc = 0; kc < D / 16; ++kc) sn = mfma32_bf16(kb[2 * kc], qb[kc], sn);
+  };
+  auto exp_block = [&](const f32x16& sc, bf16x8 (&pb)[2]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[t][e] = bf16(fast_exp2(fmaf(sc[8 * t + e], scale_log2, -m_run)));
+      l_run += sum8_bf16(pb[t]);
     }
+  };
+  auto pv_tile = [&](int buf, const bf16x8 (&p)[2][2]) {
+    const bf16x8* vb = sV + buf * VBUF + vread;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) acc[db] = mfma32_bf16(vb[(2 * b + t) * VSC + 64 * db], p[b][t], acc[db]);
+  };
+
+  // ---- prologue: K(0), K(1), V(0) in LDS; scores of tile 0
+  int p1 = ntiles > 1 ? page_for(1) : 0;
+  {
+    const int p0 = page_for(0);
+    issue_k(0, p0, 0);
+    issue_v(0, p0, 0);
+    if (ntiles > 1) issue_k(1, p1, 1);
+    wait_vmem();
+    fix_v_tail(0, 0);
+  }
+  int p2 = ntiles > 2 ? page_for(2) : 0;
+  int p3 = ntiles > 3 ? page_for(3) : 0;
+  __syncthreads();
+  f32x16 sc[2];
+  if (w_max_limit >= 0) {
+    qk_block(0, 0, sc[0]);
+    qk_block(0, 1, sc[1]);
+  }
+  __syncthreads();
+
+  for (int j = 0; j < ntiles; ++j) {
+    const bool ld_k = j + 2 < ntiles, ld_v = j + 1 < ntiles;
+    if (ld_k) issue_k(j + 2, p2, j & 1);
+    if (ld_v) issue_v(j + 1, p1, (j + 1) & 1);
+    p1 = p2;
+    p2 = p3;
+    if (j + 4 < ntiles) p3 = page_for(j + 4);
     const int k0 = j * kPTileKeys;
     if (k0 <= w_max_limit) {
-      // ---- S^T for the tile's two 32-key blocks
-      f32x16 s[2];
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s[b][e] = 0.f;
-        const int key = 32 * b + kap;
-#pragma unroll
-        for (int kc = 0; kc < D / 16; ++kc) {
-          const int cc = 2 * kc + h;
-          s[b] = mfma32_bf16(sK[buf][key * KCH + (cc ^ (key & (KCH - 1)))], qb[kc], s[b]);
-        }
-      }
-      // ---- mask (diagonal and ragged tiles only)
       if (k0 + kPTileKeys - 1 > w_min_limit) {
 #pragma unroll
         for (int b = 0; b < 2; ++b)
@@ -480,16 +548,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
           for (int e = 0; e < 16; ++e) {
             const int ii = e >> 2, jj = e & 3;
             const int key = k0 + 32 * b + 16 * (ii >> 1) + 8 * h + 4 * (ii & 1) + jj;
-            if (key > limit) s[b][e] = -INFINITY;
+            if (key > limit) sc[b][e] = -INFINITY;
           }
       }
-      // ---- online softmax
-      float mx = s[0][0];
+      float mx = sc[0][0];
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[b][e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[b][e]);
+      mx = fmaxf(mx, other_half(mx));
       const float m_tile = mx * scale_log2;
       const bool need = m_tile > m_run + kRescaleSlack;
       if (__any(need)) {
@@ -501,32 +568,27 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
       }
       bf16x8 p[2][2];
+      if (k0 + kPTileKeys <= w_max_limit) {
+        // the MFMAs of tile j+1's block b overlap the exponentials of tile j's block b
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) p[b][t][e] = bf16(fast_exp2(fmaf(s[b][8 * t + e], scale_log2, -m_run)));
-          l_run += sum8_bf16(p[b][t]);
+        for (int b = 0; b < 2; ++b) {
+          f32x16 sn;
+          qk_block((j + 1) & 1, b, sn);
+          exp_block(sc[b], p[b]);
+          sc[b] = sn;
         }
-      // ---- O^T += V^T . P^T
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const int d = 32 * db + rho;
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const int vc = 4 * b + 2 * t + h;
-            acc[db] = mfma32_bf16(sV[buf][d * 8 + (vc ^ vswz(d))], p[b][t], acc[db]);
-          }
+      } else {
+        exp_block(sc[0], p[0]);
+        exp_block(sc[1], p[1]);
       }
+      pv_tile(j & 1, p);
     }
-    if (has_next) store_tile(buf ^ 1);
+    wait_vmem();
+    if (ld_v) fix_v_tail(j + 1, (j + 1) & 1);
     __syncthreads();
   }
   // ---- normalise and write: acc[db][4*ii + jj] is d = 32*db + 8*ii + 4*h + jj of this column
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = l_run + other_half(l_run);
   if (cvalid) {
     const float inv = 1.f / l_tot;
     bf16* op = out + (size_t(row) * Hq + head) * D + 4 * h;
@@ -608,7 +670,21 @@ bool prefill_kernel_available(const va_params& p) {
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+static va_status prepare_kernels() {
+  // the prefill kernel's dynamic LDS exceeds the 64 KiB default limit
+  static hipError_t once = [] {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_bf16_kernel<128>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, prefill_lds_bytes<128>());
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_bf16_kernel<64>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, prefill_lds_bytes<64>());
+    return e;
+  }();
+  return once == hipSuccess ? VA_OK : hip_fail("hipFuncSetAttribute(max dynamic LDS)", once);
+}
+
 va_status upload_plan(va_plan* plan) {
+  if (va_status st = prepare_kernels(); st != VA_OK) return st;
   const size_t b_items = align256(plan->items.size() * sizeof(SplitItem));
   const size_t b_cols = align256(plan->cols.size() * sizeof(Column));
   const size_t b_comb = align256(plan->combine.size() * sizeof(CombineRow));
@@ -710,11 +786,11 @@ static va_status run_impl(const va_plan* plan, const void* q, const void* k_pool
     auto* vv = static_cast<const bf16*>(v_pool);
     auto* oo = static_cast<bf16*>(out);
     if (D == 128)
-      prefill_bf16_kernel<128, kPrefillWaves><<<grid, block, 0, s>>>(plan->d_tiles, qq, kk, vv, block_table_dev,
+      prefill_bf16_kernel<128><<<grid, block, prefill_lds_bytes<128>(), s>>>(plan->d_tiles, qq, kk, vv, block_table_dev,
                                                                    bt_stride, oo, p.num_q_heads, plan->g, pg,
                                                                    scale_log2);
     else
-      prefill_bf16_kernel<64, kPrefillWaves><<<grid, block, 0, s>>>(plan->d_tiles, qq, kk, vv, block_table_dev,
+      prefill_bf16_kernel<64><<<grid, block, prefill_lds_bytes<64>(), s>>>(plan->d_tiles, qq, kk, vv, block_table_dev,
                                                                   bt_stride, oo, p.num_q_heads, plan->g, pg,
                                                                   scale_log2);
     e = hipGetLastError();

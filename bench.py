@@ -13,6 +13,7 @@ chunked-prefill-mix and shared-prefix workloads (HBM GB/s of algorithmic bytes, 
 Prints progress on stderr and ONE JSON line on stdout.
 """
 import argparse
+import hashlib
 import json
 import os
 import platform
@@ -29,6 +30,34 @@ PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E
 PEAK_BF16 = 2.5e15         # FLOP/s, MI355X dense bf16 MFMA
 STAGES = ("prefill", "split_kv", "combine")
 KERNEL_NAMES = {"prefill": "prefill_bf16_kernel", "split_kv": "split_kv_bf16_kernel", "combine": "combine_kernel"}
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def kernel_source_hash():
+    """sha256 (first 16 hex digits) over the library sources, in name order."""
+    csrc = os.path.join(ROOT, "varlen_paged_attention_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".cpp", ".h")):
+            h.update(name.encode())
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` on `workload` from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE passes (already scaled by the copy-kernel calibration), or None when the
+    counters were taken on other kernel sources."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("sources_sha256_16") != kernel_source_hash():
+        return None
+    e = t.get(workload, {}).get(kernel)
+    return None if not e else e.get("hbm_bytes")
 
 
 def log(*a):
@@ -51,14 +80,16 @@ def time_runs(api, plan, tensors, steps, warmup, flush=None):
     import torch
     q, k, v, bt, out, ws = tensors
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    run = api.RunCall(plan, q, k, v, bt, out, ws)
+    calls = [run.with_events(e) for e in evs]
     for _ in range(warmup):
-        api.varlen_attn_run(plan, q, k, v, bt, out, ws)
+        run()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         if flush is not None:
             flush()
-        api.varlen_attn_run_events(plan, q, k, v, bt, out, ws, evs[i])
+        calls[i]()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
     stage = {s: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, s in enumerate(STAGES)}
@@ -91,8 +122,9 @@ def dominant(stats, stage_ms):
     return name, ms, work, bound
 
 
-def roofline(stats, stage_ms, traffic=None):
+def roofline(stats, stage_ms, workload=None):
     name, ms, work, bound = dominant(stats, stage_ms)
+    traffic = measured_traffic(workload, KERNEL_NAMES[name]) if workload else None
     sec = ms * 1e-3
     if bound == "mfma":
         a, p, unit = work / sec / 1e12, PEAK_BF16 / 1e12, "TFLOP/s"
@@ -154,7 +186,7 @@ def hbm_copy_gbps():
     return round(2 * n * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
 
 
-def secondary(api, W, cid, flags, reps, label, flush):
+def secondary(api, W, cid, flags, reps, label, flush, key=None):
     plan, tensors = None, None
     w = W.config(cid)
     plan, tensors = setup(api, w, flags)
@@ -168,7 +200,7 @@ def secondary(api, W, cid, flags, reps, label, flush):
            "algorithmic_bytes": byts, "logical_kv_bytes": st["logical_kv_bytes"],
            "physical_kv_bytes": st["physical_kv_bytes"], "flops": st["flops"],
            "stage_ms": {k: round(v, 5) for k, v in stage.items()},
-           "roofline": roofline(st, stage), "l2_flushed": flush is not None}
+           "roofline": roofline(st, stage, key), "l2_flushed": flush is not None}
     del tensors
     return res
 
@@ -180,7 +212,6 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--traffic", default=None, help="JSON file with measured HBM bytes per launch")
     ap.add_argument("--only", type=int, default=None,
                     help="profile mode: time only this workload (2, 3, 4, 5 or 51) and print its line")
     ap.add_argument("--copy-only", action="store_true",
@@ -200,7 +231,8 @@ def main():
         return
     if args.only is not None:
         flags = api.VA_FLAG_SHARED_PREFIX if args.only in (5, 51) else 0
-        res = secondary(api, W, args.only, flags, args.steps, W.CONFIG_NAMES[args.only], None)
+        key = {2: "orca", 3: "decode", 4: "chunk", 5: "shared6", 51: "shared64"}.get(args.only)
+        res = secondary(api, W, args.only, flags, args.steps, W.CONFIG_NAMES[args.only], None, key)
         print(json.dumps(res), flush=True)
         return
 
@@ -213,10 +245,7 @@ def main():
     wall, stage, totals = time_runs(api, plan, tensors, args.steps, args.warmup)
     ms = wall
     value = st["flops"] / (ms * 1e-3) / 1e12
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        traffic = json.load(open(args.traffic)).get("orca-mixed")
-    roof = roofline(st, stage, traffic)
+    roof = roofline(st, stage, "orca")
     log(f"[bench] {ms:.4f} ms/step  {value:.1f} TFLOP/s  stages {stage}")
 
     rec = {"metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -239,13 +268,13 @@ def main():
             flush_buf.zero_()     # 512 MiB write evicts the 256 MB last-level cache
 
         sec = []
-        for cid, flags, label, fl in ((3, 0, "decode-heavy-gqa (256 decodes, kv U[1024,8192], g=4, page 64)", None),
-                                      (4, 0, "chunked-prefill-mix (2048@S0=30720 + 64 decodes, g=8)", None),
-                                      (5, api.VA_FLAG_SHARED_PREFIX, "shared-prefix-6 (4096 shared + 1024 each)", flush),
-                                      (51, api.VA_FLAG_SHARED_PREFIX, "shared-prefix-64 (16384 shared + 1024 each)",
-                                       flush)):
+        for cid, flags, label, fl, key in (
+                (3, 0, "decode-heavy-gqa (256 decodes, kv U[1024,8192], g=4, page 64)", None, "decode"),
+                (4, 0, "chunked-prefill-mix (2048@S0=30720 + 64 decodes, g=8)", None, "chunk"),
+                (5, api.VA_FLAG_SHARED_PREFIX, "shared-prefix-6 (4096 shared + 1024 each)", flush, "shared6"),
+                (51, api.VA_FLAG_SHARED_PREFIX, "shared-prefix-64 (16384 shared + 1024 each)", flush, "shared64")):
             log(f"[bench] secondary: {label}")
-            sec.append(secondary(api, W, cid, flags, 20, label, fl))
+            sec.append(secondary(api, W, cid, flags, 20, label, fl, key))
             torch.cuda.empty_cache()
         sec.append({"workload": "torch copy 1 GiB (read+write) for reference", "hbm_GBps": hbm_copy_gbps()})
         rec["secondary"] = sec

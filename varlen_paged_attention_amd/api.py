@@ -259,3 +259,40 @@ def run_workload(w, flags: int = 0, plan: Optional[Plan] = None, device="cuda", 
     varlen_attn_run(plan, q, k, v, bt, out, ws)
     torch.cuda.synchronize()
     return out, plan
+
+
+class RunCall:
+    """``varlen_attn_run`` with its arguments marshalled once, for launch loops where the
+    per-call ctypes conversion would cost more than the GPU work (same checks as
+    ``varlen_attn_run`` at construction)."""
+
+    def __init__(self, plan: Plan, q, k_pool, v_pool, block_table_dev, out, workspace=None, stream=None):
+        import torch
+        dt = _elem_dtype(plan)
+        self._s = torch.cuda.current_stream() if stream is None else stream
+        self._args = (plan.handle, _dev_ptr(q, "q", dt), _dev_ptr(k_pool, "k_pool", dt),
+                      _dev_ptr(v_pool, "v_pool", dt), _dev_ptr(block_table_dev, "block_table", torch.int32),
+                      _dev_ptr(out, "out", dt), _dev_ptr(workspace, "workspace"),
+                      0 if workspace is None else workspace.numel() * workspace.element_size(),
+                      ctypes.c_void_p(self._s.cuda_stream))
+        self._keep = (plan, q, k_pool, v_pool, block_table_dev, out, workspace)
+
+    def __call__(self) -> None:
+        _check(lib().varlen_attn_run(*self._args))
+
+    def with_events(self, events):
+        """A callable that runs with ``varlen_attn_run_events`` and these VA_RUN_EVENTS
+        torch.cuda.Event(enable_timing=True) objects."""
+        if len(events) != VA_RUN_EVENTS:
+            raise ValueError(f"need {VA_RUN_EVENTS} events")
+        for ev in events:
+            if ev.cuda_event == 0:
+                ev.record(self._s)
+        arr = (ctypes.c_void_p * VA_RUN_EVENTS)(*[ev.cuda_event for ev in events])
+        args = self._args + (arr,)
+        L = lib()
+
+        def call():
+            _check(L.varlen_attn_run_events(*args))
+        call._keep = (events, arr)
+        return call

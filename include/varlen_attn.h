@@ -118,6 +118,7 @@ typedef struct {
   int64_t prefill_kv_bytes;   /* distinct KV bytes the prefill tiles' requests read */
   int64_t split_kv_bytes;     /* distinct KV bytes the split-KV requests read */
   int64_t split_q_bytes;      /* query bytes of the split-KV requests */
+  int64_t direct_items;       /* split-KV items that write output rows directly (no combine) */
 } va_plan_stats;
 
 typedef struct va_plan va_plan;   /* opaque, immutable after creation */
@@ -168,6 +169,8 @@ va_status varlen_attn_debug_gather(const va_plan* plan, const void* k_pool, cons
 
 /* Introspection for tests: the plan's host work lists as int32 records.
  * which = 0: split-KV items {req, kvh, col0, ncols, k0, k1, slot, flags}
+ *            (flags bit 0: some column's causal limit falls inside [k0, k1); bit 1: the
+ *            item writes its columns' output rows directly)
  *         1: query columns {q_row, q_head, limit, pbase}
  *         2: combine rows {q_row, q_head, pbase, nparts}
  *         3: prefill tiles {req, kvh, c0, ncols, q0, S0, kv_end, key_diag}

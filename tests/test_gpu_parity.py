@@ -210,6 +210,8 @@ EDGE = [
     ("long-decode", dict(q_rows=[1, 1], kv=[40000, 77], hq=8, hkv=1, d=128, ps=64)),
     ("d64-bf16-prefill", dict(q_rows=[130, 2], kv=[200, 2], hq=6, hkv=3, d=64, ps=16)),
     ("f32-d128", dict(q_rows=[17, 1], kv=[40, 90], hq=4, hkv=2, d=128, ps=16, dtype="f32")),
+    # prefill tiles plus decode items written directly (short kv) and split (long kv)
+    ("prefill+direct+split", dict(q_rows=[600, 1, 1, 1], kv=[700, 100, 160, 30000], hq=8, hkv=2, d=128, ps=32)),
 ]
 
 
@@ -240,7 +242,8 @@ def test_edge_cases(label, spec):
 def test_run_errors():
     import torch
     w = W.config(1)
-    plan = api.plan_for(w)
+    plan = api.plan_for(w, split_len=64)      # several parts per output: a workspace is needed
+    assert plan.workspace_bytes > 0
     q, k, v, bt = api.to_device(w)
     out = torch.zeros_like(q)
     small = torch.empty(max(1, plan.workspace_bytes - 1), dtype=torch.uint8, device="cuda")

@@ -86,8 +86,11 @@ def test_status_strings_and_null_args():
 
 def test_empty_and_zero_row_requests_plan():
     w = W.build("z", [0, 3, 0], [5, 7, 0], num_q_heads=2, num_kv_heads=1, head_dim=64, page_size=16, seed=2)
-    st = api.varlen_attn_plan_stats(_plan(w))
-    assert st["combine_rows"] == 3 * 2
+    plan = _plan(w)
+    st = api.varlen_attn_plan_stats(plan)
+    items = api.varlen_attn_plan_export(plan, 0)
+    direct_cols = int(sum(it[3] for it in items if it[7] & 2))
+    assert st["combine_rows"] + direct_cols == 3 * 2
     assert st["visible_pairs"] == 3 * 4 + 6
 
 
@@ -105,6 +108,7 @@ def check_coverage(w, plan):
     cover = {}                 # (row, head) -> list of (k0, k1) intervals
     slots = {}
     comb_map = {(int(c[0]), int(c[1])): (int(c[2]), int(c[3])) for c in comb}
+    direct = {}
     for it in items:
         req, kvh, col0, ncols, k0, k1, slot, flags = (int(x) for x in it)
         assert 1 <= ncols <= 16 and k0 < k1 and k0 % 8 == 0
@@ -120,11 +124,17 @@ def check_coverage(w, plan):
                 pages = range(k0 // ps, (hi - 1) // ps + 1)
                 assert all(w.block_table[req, p] == w.block_table[r, p] for p in pages)
                 cover.setdefault((row, head), []).append((k0, hi))
-            pb, npart = comb_map[(row, head)]
-            assert pb == pbase and 0 <= slot < npart
-            slots.setdefault((row, head), []).append(slot)
+            if flags & 2:          # written directly: the item is the output's only part
+                assert (row, head) not in comb_map and pbase == -1
+                direct[(row, head)] = direct.get((row, head), 0) + 1
+            else:
+                pb, npart = comb_map[(row, head)]
+                assert pb == pbase and 0 <= slot < npart
+                slots.setdefault((row, head), []).append(slot)
             if not (flags & 1):
                 assert k1 - 1 <= limit
+    assert all(n == 1 for n in direct.values())
+    assert not (set(direct) & set(slots))
     for t in tiles:
         req, kvh, c0, ncols, q0, S0, kv_end, key_diag = (int(x) for x in t)
         for c in range(c0, c0 + ncols):
@@ -156,6 +166,11 @@ CASES = [
     ("shared-scaled", lambda: W.config(51, scale=8), api.VA_FLAG_SHARED_PREFIX),
     ("mtp-g8", lambda: W.build("m", [4, 3, 1], [100, 64, 33], num_q_heads=16, num_kv_heads=2, head_dim=128,
                                page_size=32, seed=3), 0),
+    ("prefill+decodes", lambda: W.build("fd", [2048, 1, 1, 1], [2048, 100, 160, 3000], num_q_heads=8, num_kv_heads=2,
+                                     head_dim=128, page_size=32, seed=4), 0),
+    ("orca-full", lambda: W.config(2), 0),
+    ("chunk-like", lambda: W.build("cl", [2048, 1, 1, 1, 1], [32768, 600, 5000, 16384, 70], num_q_heads=8,
+                                   num_kv_heads=1, head_dim=128, page_size=64, seed=5), 0),
 ]
 
 

@@ -41,7 +41,8 @@ class VaPlanStats(ctypes.Structure):
                                               "table_bytes", "workspace_bytes")] + \
                [("plan_host_us", ctypes.c_double), ("prefill_flops", ctypes.c_double),
                 ("split_flops", ctypes.c_double)] + \
-               [(n, ctypes.c_int64) for n in ("prefill_kv_bytes", "split_kv_bytes", "split_q_bytes")]
+               [(n, ctypes.c_int64) for n in ("prefill_kv_bytes", "split_kv_bytes", "split_q_bytes",
+                                              "direct_items")]
 
 
 class VarlenAttnError(RuntimeError):

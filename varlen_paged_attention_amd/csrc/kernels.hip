@@ -70,6 +70,18 @@ __device__ __forceinline__ void store_partial(float* ws_ml, float* ws_acc, int s
   for (int db = 0; db < D / 16; ++db) *reinterpret_cast<f32x4*>(wa + 16 * db) = acc[db];
 }
 
+// Write one column's finished output row (an item that covers the column's whole kv
+// range): acc / l, rounded to the output type.
+template <int D, typename OutT>
+__device__ __forceinline__ void store_output(OutT* out, size_t row_off, int grp, float l, const f32x4* acc) {
+  const float inv = 1.f / l;
+  OutT* op = out + row_off + 4 * grp;
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) op[16 * db + r] = OutT(acc[db][r] * inv);
+}
+
 // ----------------------------------------------------------------- split-KV, bf16 --
 // MFMA v_mfma_f32_16x16x32_bf16 operand layout: lane l holds row/column (l % 16) and
 // k-elements 8*(l/16) .. 8*(l/16)+7; the 16x16 f32 result gives lane l column (l % 16),
@@ -81,18 +93,16 @@ __device__ __forceinline__ void store_partial(float* ws_ml, float* ws_acc, int s
 // 32u + 8*grp .. +7 of sub-step u -- exactly the k-slice the P^T operand of the
 // O^T += V^T . P^T MFMA needs -- so P never leaves registers.  V^T's 8-key slices are
 // contiguous because V pages are stored transposed.
+// One wavefront runs item `idx`.
 template <int D>
-__global__ __launch_bounds__(256) void split_kv_bf16_kernel(
-    const SplitItem* __restrict__ items, int nitems, const Column* __restrict__ cols,
+__device__ __forceinline__ void split_kv_bf16_wave(
+    int idx, const SplitItem* __restrict__ items, const Column* __restrict__ cols,
     const bf16* __restrict__ q, const bf16* __restrict__ kpool, const bf16* __restrict__ vpool,
     const int32_t* __restrict__ bt, int bt_stride, float* __restrict__ ws_ml, float* __restrict__ ws_acc,
-    int Hq, Paged pg, float scale_log2) {
+    bf16* __restrict__ out, int Hq, Paged pg, float scale_log2) {
   constexpr int KC = D / 32;
   constexpr int DB = D / 16;
   const int lane = threadIdx.x & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int idx = blockIdx.x * kSplitWaves + wv;
-  if (idx >= nitems) return;
   const SplitItem it = items[idx];
   const int n = lane & 15, grp = lane >> 4;
   const bool cvalid = n < it.ncols;
@@ -200,7 +210,21 @@ __global__ __launch_bounds__(256) void split_kv_bf16_kernel(
   }
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
-  if (cvalid) store_partial<D>(ws_ml, ws_acc, c.pbase + it.slot, grp, m_run, l_tot, acc);
+  if (cvalid) {
+    if (it.flags & kItemDirect) store_output<D>(out, (size_t(c.q_row) * Hq + c.q_head) * D, grp, l_tot, acc);
+    else store_partial<D>(ws_ml, ws_acc, c.pbase + it.slot, grp, m_run, l_tot, acc);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void split_kv_bf16_kernel(
+    const SplitItem* __restrict__ items, int nitems, const Column* __restrict__ cols,
+    const bf16* __restrict__ q, const bf16* __restrict__ kpool, const bf16* __restrict__ vpool,
+    const int32_t* __restrict__ bt, int bt_stride, float* __restrict__ ws_ml, float* __restrict__ ws_acc,
+    bf16* __restrict__ out, int Hq, Paged pg, float scale_log2) {
+  const int idx = blockIdx.x * kSplitWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (idx < nitems)
+    split_kv_bf16_wave<D>(idx, items, cols, q, kpool, vpool, bt, bt_stride, ws_ml, ws_acc, out, Hq, pg, scale_log2);
 }
 
 // ------------------------------------------------------------------ split-KV, fp32 --
@@ -212,7 +236,7 @@ __global__ __launch_bounds__(256) void split_kv_f32_kernel(
     const SplitItem* __restrict__ items, int nitems, const Column* __restrict__ cols,
     const float* __restrict__ q, const float* __restrict__ kpool, const float* __restrict__ vpool,
     const int32_t* __restrict__ bt, int bt_stride, float* __restrict__ ws_ml, float* __restrict__ ws_acc,
-    int Hq, Paged pg, float scale_log2) {
+    float* __restrict__ out, int Hq, Paged pg, float scale_log2) {
   constexpr int KC = D / 4;
   constexpr int DB = D / 16;
   const int lane = threadIdx.x & 63;
@@ -279,7 +303,10 @@ __global__ __launch_bounds__(256) void split_kv_f32_kernel(
   }
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
-  if (cvalid) store_partial<D>(ws_ml, ws_acc, c.pbase + it.slot, grp, m_run, l_tot, acc);
+  if (cvalid) {
+    if (it.flags & kItemDirect) store_output<D>(out, (size_t(c.q_row) * Hq + c.q_head) * D, grp, l_tot, acc);
+    else store_partial<D>(ws_ml, ws_acc, c.pbase + it.slot, grp, m_run, l_tot, acc);
+  }
 }
 
 // ------------------------------------------------------------ MFMA prefill, bf16 --
@@ -604,6 +631,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
   }
 }
 
+
 // ------------------------------------------------------------------------ combine --
 // out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s with M = max_s m_s.
 template <int D, typename OutT>
@@ -806,11 +834,11 @@ static va_status run_impl(const va_plan* plan, const void* q, const void* k_pool
       if (D == 128)
         split_kv_bf16_kernel<128><<<grid, block, 0, s>>>(plan->d_items, nitems, plan->d_cols, qq, kk, vv,
                                                          block_table_dev, bt_stride, ws_ml, ws_acc,
-                                                         p.num_q_heads, pg, scale_log2);
+                                                         static_cast<bf16*>(out), p.num_q_heads, pg, scale_log2);
       else
         split_kv_bf16_kernel<64><<<grid, block, 0, s>>>(plan->d_items, nitems, plan->d_cols, qq, kk, vv,
                                                         block_table_dev, bt_stride, ws_ml, ws_acc,
-                                                        p.num_q_heads, pg, scale_log2);
+                                                        static_cast<bf16*>(out), p.num_q_heads, pg, scale_log2);
     } else {
       auto* qq = static_cast<const float*>(q);
       auto* kk = static_cast<const float*>(k_pool);
@@ -818,11 +846,11 @@ static va_status run_impl(const va_plan* plan, const void* q, const void* k_pool
       if (D == 128)
         split_kv_f32_kernel<128><<<grid, block, 0, s>>>(plan->d_items, nitems, plan->d_cols, qq, kk, vv,
                                                         block_table_dev, bt_stride, ws_ml, ws_acc,
-                                                        p.num_q_heads, pg, scale_log2);
+                                                        static_cast<float*>(out), p.num_q_heads, pg, scale_log2);
       else
         split_kv_f32_kernel<64><<<grid, block, 0, s>>>(plan->d_items, nitems, plan->d_cols, qq, kk, vv,
                                                        block_table_dev, bt_stride, ws_ml, ws_acc,
-                                                       p.num_q_heads, pg, scale_log2);
+                                                       static_cast<float*>(out), p.num_q_heads, pg, scale_log2);
     }
     e = hipGetLastError();
     if (e != hipSuccess) return hip_fail("split-KV kernel launch", e);

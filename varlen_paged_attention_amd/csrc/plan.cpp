@@ -47,10 +47,13 @@ struct Block {          // a set of <= 16 query columns scored against one kv ra
   std::vector<int32_t> outs;   // output ids (q_row * Hq + q_head)
   std::vector<int32_t> limits;
   bool shared;
+  bool direct;
   int32_t nchunks;
+  int32_t chunk;     // kv positions per item (the last one may be shorter)
 };
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
 
 }  // namespace
 }  // namespace va
@@ -215,6 +218,7 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
       B.kvh = kvh;
       B.kstart = kstart;
       B.shared = shared;
+      B.direct = false;
       B.max_limit = -1;
       B.min_limit = INT32_MAX;
       for (size_t c = b0; c < std::min(rowhead.size(), b0 + kSplitCols); ++c) {
@@ -262,17 +266,30 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
     L = std::min<int64_t>(std::max<int64_t>(L, 256), 8192);
   }
   plan->split_len = int32_t(L);
-  for (auto& B : blocks) B.nchunks = int32_t(ceil_div(std::max(0, B.kend - B.kstart), L));
+  for (auto& B : blocks) {
+    const int64_t keys = std::max(0, B.kend - B.kstart);
+    B.nchunks = int32_t(ceil_div(keys, L));
+    B.chunk = int32_t(L);
+  }
 
-  // ---- partial slots: every (row, head) output of the split path ----------------------
+  // ---- partial slots: every (row, head) output of the split path that is not written
+  // directly (an output whose one part comes from an item that covers only such outputs)
   std::vector<int32_t> nparts(size_t(total_rows) * Hq, 0);
   for (auto& B : blocks)
     for (int32_t o : B.outs) nparts[o] += B.nchunks;
+  std::vector<char> needs_slot(nparts.size(), 0);
+  for (auto& B : blocks) {
+    bool direct = B.nchunks == 1;
+    for (int32_t o : B.outs) direct = direct && nparts[o] == 1;
+    B.direct = direct;
+    if (!direct)
+      for (int32_t o : B.outs) needs_slot[o] = 1;
+  }
   std::vector<int32_t> pbase(nparts.size(), -1);
   std::vector<int32_t> shared_n(nparts.size(), 0);   // slots taken by group items
   int64_t slots = 0;
   for (size_t o = 0; o < nparts.size(); ++o)
-    if (nparts[o] > 0) {
+    if (nparts[o] > 0 && needs_slot[o]) {
       pbase[o] = int32_t(slots);
       slots += nparts[o];
       CombineRow cr;
@@ -309,10 +326,10 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
       it.kvh = B.kvh;
       it.col0 = col0;
       it.ncols = int32_t(B.outs.size());
-      it.k0 = int32_t(B.kstart + j * L);
-      it.k1 = int32_t(std::min<int64_t>(B.kend, B.kstart + (j + 1) * L));
+      it.k0 = int32_t(B.kstart + int64_t(j) * B.chunk);
+      it.k1 = int32_t(std::min<int64_t>(B.kend, B.kstart + int64_t(j + 1) * B.chunk));
       it.slot = B.shared ? j : shared_n[B.outs[0]] + j;
-      it.flags = (B.min_limit < it.k1 - 1) ? kItemMasked : 0;
+      it.flags = ((B.min_limit < it.k1 - 1) ? kItemMasked : 0) | (B.direct ? kItemDirect : 0);
       (B.shared ? shared_items : own_items).push_back(it);
     }
   }
@@ -368,6 +385,9 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
   st.prefill_kv_bytes = phys_pf * pos_bytes;
   st.split_kv_bytes = phys_sp * pos_bytes;
   st.split_q_bytes = rows_sp * Hq * D * elem;
+  st.direct_items = std::count_if(plan->items.begin(), plan->items.end(),
+                                  [](const SplitItem& it) { return (it.flags & kItemDirect) != 0; });
+
   st.visible_pairs = pairs;
   st.flops = 4.0 * D * Hq * double(pairs);
   st.logical_kv_bytes = logical_pos * pos_bytes;

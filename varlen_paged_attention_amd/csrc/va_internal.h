@@ -11,12 +11,13 @@ namespace va {
 // One split-KV work item = one wavefront.  It reads kv positions [k0, k1) of request
 // `req`'s block table for KV head `kvh` and scores them against up to 16 query columns
 // cols[col0 .. col0+ncols).  Each column's partial result goes to workspace slot
-// cols[c].pbase + slot.
+// cols[c].pbase + slot, or, with kItemDirect (the item covers its columns' whole kv range),
+// straight to the output rows.
 struct SplitItem {
   int32_t req, kvh, col0, ncols;
-  int32_t k0, k1, slot, flags;  // flags: kItemMasked if some column's limit < k1 - 1
+  int32_t k0, k1, slot, flags;  // flags: kItemMasked if some column's limit < k1 - 1; kItemDirect
 };
-enum { kItemMasked = 1 };
+enum { kItemMasked = 1, kItemDirect = 2 };
 
 // A query column: flat Q row, query head, last visible kv position (S0 + i), and the
 // first workspace slot of this (row, head) output.

@@ -127,40 +127,51 @@ __device__ __forceinline__ void split_kv_bf16_wave(
   const int klast = it.k1 - 1;
   const bool masked_item = (it.flags & kItemMasked) != 0;
 
-  for (int k = it.k0; k < it.k1; k += kStepKeys) {
-    const bool tail = k + kStepKeys > it.k1;
-    // ---- loads: K rows (4 blocks x KC chunks) and V^T slices (2 sub-steps x DB rows)
-    bf16x8 ka[4][KC];
+  // Page ids: lane i holds the page of the item's (pbase + i)-th page, fetched with one
+  // vector load per 64 pages, and a lane finds its key's page with a cross-lane read, so
+  // no K/V load waits for a block-table load of its own.
+  const int last_page = klast >> pg.ps_shift;
+  int pbase = it.k0 >> pg.ps_shift;
+  int pids = btr[min(pbase + lane, last_page)];
+  auto cover = [&](int k) {            // make the 64 keys from k addressable
+    if (((min(k + kStepKeys, it.k1) - 1) >> pg.ps_shift) - pbase >= 64) {
+      pbase = k >> pg.ps_shift;
+      pids = btr[min(pbase + lane, last_page)];
+    }
+  };
+  auto page_at = [&](int pos) -> int { return __shfl(pids, (pos >> pg.ps_shift) - pbase); };
+
+  // K rows (4 blocks x KC chunks) and V^T slices (2 sub-steps x DB rows) of a 64-key step.
+  // The loop is rotated: step k+64's K loads are issued as soon as step k's scores are
+  // computed, its V loads once step k's P . V is issued, so a load is in flight while
+  // the previous step computes.
+  bf16x8 ka[4][KC], va[2][DB];
+  auto load_k = [&](int k) {
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const int key = k + 32 * (b >> 1) + 8 * (n >> 2) + 4 * (b & 1) + (n & 3);
       const int kk = min(key, klast);
-      const bf16* kr = kpool + pg.k_row(pg.page_of(btr, kk), kvh, pg.slot_of(kk)) + 8 * grp;
+      const bf16* kr = kpool + pg.k_row(page_at(kk), kvh, pg.slot_of(kk)) + 8 * grp;
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) ka[b][kc] = *reinterpret_cast<const bf16x8*>(kr + 32 * kc);
     }
-    bf16x8 va[2][DB];
+  };
+  auto load_v = [&](int k) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int vkey = k + 32 * u + 8 * grp;
-      const int vk = min(vkey, klast & ~7);
-      const bf16* vr = vpool + pg.v_elem(pg.page_of(btr, vk), kvh, n, pg.slot_of(vk));
+      const int vk = min(k + 32 * u + 8 * grp, klast & ~7);
+      const bf16* vr = vpool + pg.v_elem(page_at(vk), kvh, n, pg.slot_of(vk));
 #pragma unroll
       for (int db = 0; db < DB; ++db)
         va[u][db] = *reinterpret_cast<const bf16x8*>(vr + (size_t(16 * db) << pg.ps_shift));
-      if (tail) {
-        // positions at or past k1 may lie past kv_len (unwritten slots): zero them so
-        // 0 * garbage cannot reach the accumulator
-        const int valid = it.k1 - vkey;
-        if (valid < 8) {
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (e >= valid) va[u][db][e] = bf16(0.f);
-        }
-      }
     }
+  };
+  cover(it.k0);
+  load_k(it.k0);
+  load_v(it.k0);
+  for (int k = it.k0; k < it.k1; k += kStepKeys) {
+    const bool tail = k + kStepKeys > it.k1;
+    const bool more = k + kStepKeys < it.k1;
     // ---- scores S^T for 64 keys: lane holds v[4b + r] = key k + 32(b>>1) + 8grp + 4(b&1) + r
     float v[16];
 #pragma unroll
@@ -170,6 +181,10 @@ __device__ __forceinline__ void split_kv_bf16_wave(
       for (int kc = 0; kc < KC; ++kc) s = mfma16_bf16(ka[b][kc], qb[kc], s);
 #pragma unroll
       for (int r = 0; r < 4; ++r) v[4 * b + r] = s[r] * scale_log2;
+    }
+    if (more) {
+      cover(k + kStepKeys);
+      load_k(k + kStepKeys);
     }
     if (masked_item || tail) {
 #pragma unroll
@@ -200,6 +215,21 @@ __device__ __forceinline__ void split_kv_bf16_wave(
         sum += float(pe);
       }
     l_run = l_run * alpha + sum;
+    if (tail) {
+      // positions at or past k1 may lie past kv_len (unwritten slots): zero them so
+      // 0 * garbage cannot reach the accumulator
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int valid = it.k1 - (k + 32 * u + 8 * grp);
+        if (valid < 8) {
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (e >= valid) va[u][db][e] = bf16(0.f);
+        }
+      }
+    }
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[db] *= alpha;
     // ---- O^T += V^T . P^T
@@ -207,6 +237,7 @@ __device__ __forceinline__ void split_kv_bf16_wave(
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int db = 0; db < DB; ++db) acc[db] = mfma16_bf16(va[u][db], pb[u], acc[db]);
+    if (more) load_v(k + kStepKeys);
   }
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
@@ -217,7 +248,7 @@ __device__ __forceinline__ void split_kv_bf16_wave(
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void split_kv_bf16_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void split_kv_bf16_kernel(
     const SplitItem* __restrict__ items, int nitems, const Column* __restrict__ cols,
     const bf16* __restrict__ q, const bf16* __restrict__ kpool, const bf16* __restrict__ vpool,
     const int32_t* __restrict__ bt, int bt_stride, float* __restrict__ ws_ml, float* __restrict__ ws_acc,

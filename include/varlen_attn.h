@@ -119,6 +119,7 @@ typedef struct {
   int64_t split_kv_bytes;     /* distinct KV bytes the split-KV requests read */
   int64_t split_q_bytes;      /* query bytes of the split-KV requests */
   int64_t direct_items;       /* split-KV items that write output rows directly (no combine) */
+  int64_t shared_tiles;       /* MFMA tiles scoring shared-prefix chunks for stacked member rows */
 } va_plan_stats;
 
 typedef struct va_plan va_plan;   /* opaque, immutable after creation */
@@ -174,6 +175,9 @@ va_status varlen_attn_debug_gather(const va_plan* plan, const void* k_pool, cons
  *         1: query columns {q_row, q_head, limit, pbase}
  *         2: combine rows {q_row, q_head, pbase, nparts}
  *         3: prefill tiles {req, kvh, c0, ncols, q0, S0, kv_end, key_diag}
+ *         4: shared-prefix group tiles {req, kvh, col0, ncols, slot, k0, k1, k1}: query
+ *            columns cols[col0 .. col0+ncols) scored against positions [k0, k1) of request
+ *            req's block table, partial results to slot pbase + slot
  * *data stays valid until the plan is destroyed. */
 va_status varlen_attn_plan_export(const va_plan* plan, int32_t which, const int32_t** data,
                                   int64_t* count, int32_t* ints_per_entry);

@@ -66,6 +66,7 @@ SMALL = [
     ("chunk-mix/8", 4, 8, 0),
     ("shared-6", 5, 1, api.VA_FLAG_SHARED_PREFIX),
     ("shared-6 plain", 5, 1, 0),
+    ("shared-6 split items", 5, 1, api.VA_FLAG_SHARED_PREFIX | api.VA_FLAG_NO_PREFILL_KERNEL),
     ("shared-64/8", 51, 8, api.VA_FLAG_SHARED_PREFIX),
 ]
 

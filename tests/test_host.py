@@ -135,6 +135,19 @@ def check_coverage(w, plan):
                 assert k1 - 1 <= limit
     assert all(n == 1 for n in direct.values())
     assert not (set(direct) & set(slots))
+    for t in api.varlen_attn_plan_export(plan, 4):        # shared-prefix group tiles
+        req, kvh, col0, ncols, slot, k0, k1, _ = (int(x) for x in t)
+        assert 1 <= ncols <= 128 and k0 < k1
+        for c in cols[col0:col0 + ncols]:
+            row, head, limit, pbase = (int(x) for x in c)
+            r = req_of_row[row]
+            assert head // g == kvh and k1 - 1 <= limit
+            pages = range(k0 // ps, (k1 - 1) // ps + 1)
+            assert all(w.block_table[req, p] == w.block_table[r, p] for p in pages)
+            cover.setdefault((row, head), []).append((k0, k1))
+            pb, npart = comb_map[(row, head)]
+            assert pb == pbase and 0 <= slot < npart
+            slots.setdefault((row, head), []).append(slot)
     for t in tiles:
         req, kvh, c0, ncols, q0, S0, kv_end, key_diag = (int(x) for x in t)
         for c in range(c0, c0 + ncols):
@@ -164,6 +177,7 @@ CASES = [
     ("chunk-mix", lambda: W.config(4, scale=16), 0),
     ("shared", lambda: W.config(5), api.VA_FLAG_SHARED_PREFIX),
     ("shared-scaled", lambda: W.config(51, scale=8), api.VA_FLAG_SHARED_PREFIX),
+    ("shared-split-items", lambda: W.config(5), api.VA_FLAG_SHARED_PREFIX | api.VA_FLAG_NO_PREFILL_KERNEL),
     ("mtp-g8", lambda: W.build("m", [4, 3, 1], [100, 64, 33], num_q_heads=16, num_kv_heads=2, head_dim=128,
                                page_size=32, seed=3), 0),
     ("prefill+decodes", lambda: W.build("fd", [2048, 1, 1, 1], [2048, 100, 160, 3000], num_q_heads=8, num_kv_heads=2,
@@ -195,7 +209,7 @@ def test_plan_counters_match_oracle(name, make, flags):
 def test_shared_prefix_groups_found():
     w = W.config(5)
     st = api.varlen_attn_plan_stats(_plan(w, api.VA_FLAG_SHARED_PREFIX))
-    assert st["shared_groups"] == 1 and st["shared_items"] > 0
+    assert st["shared_groups"] == 1 and st["shared_tiles"] > 0 and st["shared_items"] == 0
     assert st["physical_kv_bytes"] == 40 * 2 ** 20 and st["logical_kv_bytes"] == 120 * 2 ** 20
     st0 = api.varlen_attn_plan_stats(_plan(w))
     assert st0["shared_groups"] == 0

@@ -423,11 +423,17 @@ constexpr int prefill_lds_bytes() {
   return PrefillLds<D>::bytes;
 }
 
-template <int D>
+// GROUP = true: the same kernel scores a shared-prefix chunk for several requests' rows.
+// The tile's columns come from cols[c0 ..] (rows of different requests), its keys are
+// [S0, kv_end) of request req's block table (pages every member shares, all visible to
+// every member row), and each column's unnormalised partial (m, l, acc) goes to workspace
+// slot pbase + q0 for the combine pass.
+template <int D, bool GROUP>
 __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_bf16_kernel(
-    const PrefillTile* __restrict__ tiles, const bf16* __restrict__ q, const bf16* __restrict__ kpool,
-    const bf16* __restrict__ vpool, const int32_t* __restrict__ bt, int bt_stride, bf16* __restrict__ out, int Hq,
-    int g, Paged pg, float scale_log2) {
+    const PrefillTile* __restrict__ tiles, const Column* __restrict__ cols, const bf16* __restrict__ q,
+    const bf16* __restrict__ kpool, const bf16* __restrict__ vpool, const int32_t* __restrict__ bt, int bt_stride,
+    bf16* __restrict__ out, float* __restrict__ ws_ml, float* __restrict__ ws_acc, int Hq, int g, Paged pg,
+    float scale_log2) {
   using Lay = PrefillLds<D>;
   constexpr int KCH = Lay::KCH, KROW = Lay::KROW, KBUF = Lay::KBUF, VBUF = Lay::VBUF;
   constexpr int WK = kPSliceKeys;                      // 16 keys per wave slice
@@ -452,13 +458,28 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
   const int col = wv * 32 + rho;
   const bool cvalid = col < T.ncols;
   const int c = T.c0 + (cvalid ? col : 0);
-  const int i = c / g;
-  const int row = T.q0 + i, head = T.kvh * g + c % g;
-  const int limit = cvalid ? T.S0 + i : -1;
-  // the wave's first and last visible positions bound its causal work
-  const int wcol_last = min(wv * 32 + 31, T.ncols - 1);
-  const int w_min_limit = T.S0 + (T.c0 + wv * 32) / g;
-  const int w_max_limit = (wv * 32 < T.ncols) ? T.S0 + (T.c0 + wcol_last) / g : -1;
+  int row, head, limit, w_min_limit, w_max_limit, kbeg, pslot;
+  if constexpr (GROUP) {
+    const Column cc = cols[c];
+    row = cc.q_row;
+    head = cc.q_head;
+    pslot = cc.pbase + T.q0;
+    kbeg = T.S0;
+    limit = cvalid ? T.kv_end - 1 : -1;
+    w_min_limit = T.kv_end - 1;
+    w_max_limit = (wv * 32 < T.ncols) ? T.kv_end - 1 : -1;
+  } else {
+    const int i = c / g;
+    row = T.q0 + i;
+    head = T.kvh * g + c % g;
+    pslot = 0;
+    kbeg = 0;
+    limit = cvalid ? T.S0 + i : -1;
+    // the wave's first and last visible positions bound its causal work
+    const int wcol_last = min(wv * 32 + 31, T.ncols - 1);
+    w_min_limit = T.S0 + (T.c0 + wv * 32) / g;
+    w_max_limit = (wv * 32 < T.ncols) ? T.S0 + (T.c0 + wcol_last) / g : -1;
+  }
 
   bf16x8 qb[D / 16];
   {
@@ -479,7 +500,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
   const int32_t* btr = bt + size_t(T.req) * bt_stride;
   const int kvh = T.kvh;
   const int kv_end = T.kv_end;
-  const int ntiles = (kv_end + kPTileKeys - 1) / kPTileKeys;
+  const int ntiles = (kv_end - kbeg + kPTileKeys - 1) / kPTileKeys;   // tile t: keys kbeg + 64t ..
   const int ps_mask = (1 << pg.ps_shift) - 1;
   const size_t page_elems = (size_t(pg.Hkv) * D) << pg.ps_shift;
   const bf16* kbase = kpool + pg.k_row(0, kvh, 0);
@@ -502,10 +523,10 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
   const int vrstep = (32 << pg.ps_shift) * 2;
 
   auto page_for = [&](int t) -> int {
-    return pg.page_of(btr, min(t * kPTileKeys + wv * WK, kv_end - 1));
+    return pg.page_of(btr, min(kbeg + t * kPTileKeys + wv * WK, kv_end - 1));
   };
   auto issue_k = [&](int t, int page, int buf) {
-    const int k0w = t * kPTileKeys + wv * WK;
+    const int k0w = kbeg + t * kPTileKeys + wv * WK;
     if (k0w >= kv_end) return;               // positions past the end: scores are masked
     const auto rs = slice_rsrc(kbase + size_t(page) * page_elems + size_t(k0w & ps_mask) * D);
     bf16x8* dst = sK + buf * KBUF + wv * KSC;
@@ -514,7 +535,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
       if (r < KNI - 1 || lane < KLAST) dma_b128(rs, dst + 64 * r, koff[r], 0);
   };
   auto issue_v = [&](int t, int page, int buf) {
-    const int k0w = t * kPTileKeys + wv * WK;
+    const int k0w = kbeg + t * kPTileKeys + wv * WK;
     bf16x8* dst = sV + buf * VBUF + wv * VSC;
     if (k0w >= kv_end) {                      // never read garbage into V: write zeros
 #pragma unroll
@@ -528,7 +549,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
   // after the copy of V(t) landed: zero the positions at or past the tile's end (they may
   // be unwritten slots; their scores are masked, but 0 * NaN would still be NaN)
   auto fix_v_tail = [&](int t, int buf) {
-    const int k0w = t * kPTileKeys + wv * WK;
+    const int k0w = kbeg + t * kPTileKeys + wv * WK;
     if (k0w >= kv_end || k0w + WK <= kv_end) return;
     bf16x8* dst = sV + buf * VBUF + wv * VSC;
     const int valid = kv_end - (k0w + 8 * vkc);
@@ -597,7 +618,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
     p1 = p2;
     p2 = p3;
     if (j + 4 < ntiles) p3 = page_for(j + 4);
-    const int k0 = j * kPTileKeys;
+    const int k0 = kbeg + j * kPTileKeys;
     if (k0 <= w_max_limit) {
       if (k0 + kPTileKeys - 1 > w_min_limit) {
 #pragma unroll
@@ -647,6 +668,22 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
   }
   // ---- normalise and write: acc[db][4*ii + jj] is d = 32*db + 8*ii + 4*h + jj of this column
   const float l_tot = l_run + other_half(l_run);
+  if constexpr (GROUP) {
+    if (cvalid) {
+      if (h == 0) {
+        ws_ml[2 * size_t(pslot)] = m_run;
+        ws_ml[2 * size_t(pslot) + 1] = l_tot;
+      }
+      float* wa = ws_acc + size_t(pslot) * D + 4 * h;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+          *reinterpret_cast<f32x4*>(wa + 32 * db + 8 * ii) =
+              f32x4{acc[db][4 * ii], acc[db][4 * ii + 1], acc[db][4 * ii + 2], acc[db][4 * ii + 3]};
+    }
+    return;
+  }
   if (cvalid) {
     const float inv = 1.f / l_tot;
     bf16* op = out + (size_t(row) * Hq + head) * D + 4 * h;
@@ -732,12 +769,16 @@ static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 static va_status prepare_kernels() {
   // the prefill kernel's dynamic LDS exceeds the 64 KiB default limit
   static hipError_t once = [] {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_bf16_kernel<128>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, prefill_lds_bytes<128>());
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_bf16_kernel<64>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, prefill_lds_bytes<64>());
-    return e;
+    const std::pair<const void*, int> kernels[] = {
+        {reinterpret_cast<const void*>(&prefill_bf16_kernel<128, false>), prefill_lds_bytes<128>()},
+        {reinterpret_cast<const void*>(&prefill_bf16_kernel<64, false>), prefill_lds_bytes<64>()},
+        {reinterpret_cast<const void*>(&prefill_bf16_kernel<128, true>), prefill_lds_bytes<128>()},
+        {reinterpret_cast<const void*>(&prefill_bf16_kernel<64, true>), prefill_lds_bytes<64>()}};
+    for (const auto& k : kernels) {
+      const hipError_t e = hipFuncSetAttribute(k.first, hipFuncAttributeMaxDynamicSharedMemorySize, k.second);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
   }();
   return once == hipSuccess ? VA_OK : hip_fail("hipFuncSetAttribute(max dynamic LDS)", once);
 }
@@ -749,7 +790,8 @@ va_status upload_plan(va_plan* plan) {
   const size_t b_comb = align256(plan->combine.size() * sizeof(CombineRow));
   const size_t b_tiles = align256(plan->tiles.size() * sizeof(PrefillTile));
   const size_t b_off = align256(plan->kv_offset.size() * sizeof(int64_t));
-  const size_t total = b_items + b_cols + b_comb + b_tiles + b_off;
+  const size_t b_gtiles = align256(plan->gtiles.size() * sizeof(PrefillTile));
+  const size_t total = b_items + b_cols + b_comb + b_tiles + b_off + b_gtiles;
   std::vector<char> host(total, 0);
   size_t o = 0;
   auto put = [&](const void* src, size_t n, size_t span) {
@@ -763,6 +805,7 @@ va_status upload_plan(va_plan* plan) {
   const size_t o_comb = put(plan->combine.data(), plan->combine.size() * sizeof(CombineRow), b_comb);
   const size_t o_tiles = put(plan->tiles.data(), plan->tiles.size() * sizeof(PrefillTile), b_tiles);
   const size_t o_off = put(plan->kv_offset.data(), plan->kv_offset.size() * sizeof(int64_t), b_off);
+  const size_t o_gtiles = put(plan->gtiles.data(), plan->gtiles.size() * sizeof(PrefillTile), b_gtiles);
   hipError_t e = hipGetDevice(&plan->device);
   if (e != hipSuccess) return hip_fail("hipGetDevice", e);
   e = hipMalloc(&plan->dev, total);
@@ -783,6 +826,7 @@ va_status upload_plan(va_plan* plan) {
   plan->d_combine = reinterpret_cast<const CombineRow*>(base + o_comb);
   plan->d_tiles = reinterpret_cast<const PrefillTile*>(base + o_tiles);
   plan->d_kv_offset = reinterpret_cast<const int64_t*>(base + o_off);
+  plan->d_gtiles = reinterpret_cast<const PrefillTile*>(base + o_gtiles);
   return VA_OK;
 }
 
@@ -806,7 +850,7 @@ static va_status run_impl(const va_plan* plan, const void* q, const void* k_pool
                           void* stream, void* const* events) {
   if (!plan) return fail(VA_ERR_INVALID_ARG, "plan is NULL");
   if (!plan->dev) return fail(VA_ERR_INVALID_ARG, "plan has no device buffer (built with VA_FLAG_HOST_ONLY)");
-  const bool any = !plan->items.empty() || !plan->tiles.empty();
+  const bool any = !plan->items.empty() || !plan->tiles.empty() || !plan->gtiles.empty();
   if (!any && !events) return VA_OK;
   if (any && (!q || !k_pool || !v_pool || !block_table_dev || !out))
     return fail(VA_ERR_INVALID_ARG, "q, k_pool, v_pool, block_table_dev and out must be non-NULL");
@@ -837,24 +881,28 @@ static va_status run_impl(const va_plan* plan, const void* q, const void* k_pool
     return events ? hipEventRecord(static_cast<hipEvent_t>(events[i]), s) : hipSuccess;
   };
   if ((e = mark(0)) != hipSuccess) return hip_fail("hipEventRecord", e);
-  const int ntiles = int(plan->tiles.size());
-  if (ntiles) {
-    const dim3 grid(ntiles), block(64 * kPrefillWaves);
+  const int ntiles = int(plan->tiles.size()), ngtiles = int(plan->gtiles.size());
+  auto launch_tiles = [&](auto group, const PrefillTile* tl, int n) {
+    constexpr bool G = decltype(group)::value;
+    const dim3 grid(n), block(64 * kPrefillWaves);
     auto* qq = static_cast<const bf16*>(q);
     auto* kk = static_cast<const bf16*>(k_pool);
     auto* vv = static_cast<const bf16*>(v_pool);
     auto* oo = static_cast<bf16*>(out);
     if (D == 128)
-      prefill_bf16_kernel<128><<<grid, block, prefill_lds_bytes<128>(), s>>>(plan->d_tiles, qq, kk, vv, block_table_dev,
-                                                                   bt_stride, oo, p.num_q_heads, plan->g, pg,
-                                                                   scale_log2);
+      prefill_bf16_kernel<128, G><<<grid, block, prefill_lds_bytes<128>(), s>>>(
+          tl, plan->d_cols, qq, kk, vv, block_table_dev, bt_stride, oo, ws_ml, ws_acc, p.num_q_heads, plan->g, pg,
+          scale_log2);
     else
-      prefill_bf16_kernel<64><<<grid, block, prefill_lds_bytes<64>(), s>>>(plan->d_tiles, qq, kk, vv, block_table_dev,
-                                                                  bt_stride, oo, p.num_q_heads, plan->g, pg,
-                                                                  scale_log2);
-    e = hipGetLastError();
-    if (e != hipSuccess) return hip_fail("prefill kernel launch", e);
-  }
+      prefill_bf16_kernel<64, G><<<grid, block, prefill_lds_bytes<64>(), s>>>(
+          tl, plan->d_cols, qq, kk, vv, block_table_dev, bt_stride, oo, ws_ml, ws_acc, p.num_q_heads, plan->g, pg,
+          scale_log2);
+    return hipGetLastError();
+  };
+  if (ntiles && (e = launch_tiles(std::false_type{}, plan->d_tiles, ntiles)) != hipSuccess)
+    return hip_fail("prefill kernel launch", e);
+  if (ngtiles && (e = launch_tiles(std::true_type{}, plan->d_gtiles, ngtiles)) != hipSuccess)
+    return hip_fail("shared-prefix tile kernel launch", e);
   if ((e = mark(1)) != hipSuccess) return hip_fail("hipEventRecord", e);
   if (nitems) {
     const dim3 grid((nitems + kSplitWaves - 1) / kSplitWaves), block(64 * kSplitWaves);

@@ -47,6 +47,7 @@ struct Block {          // a set of <= 16 query columns scored against one kv ra
   std::vector<int32_t> outs;   // output ids (q_row * Hq + q_head)
   std::vector<int32_t> limits;
   bool shared;
+  bool tile;         // scored by group tiles (MFMA) rather than split items
   bool direct;
   int32_t nchunks;
   int32_t chunk;     // kv positions per item (the last one may be shorter)
@@ -211,17 +212,19 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
   // ---- column blocks ------------------------------------------------------------------
   std::vector<Block> blocks;
   auto add_blocks = [&](const std::vector<std::pair<int, int>>& rowhead,   // (req, local col)
-                        int kvh, int32_t kstart, bool shared, int32_t req_for_table) {
-    for (size_t b0 = 0; b0 < rowhead.size(); b0 += kSplitCols) {
+                        int kvh, int32_t kstart, bool shared, int32_t req_for_table, bool tile) {
+    const size_t width = tile ? size_t(kPrefillCols) : size_t(kSplitCols);
+    for (size_t b0 = 0; b0 < rowhead.size(); b0 += width) {
       Block B;
       B.req = req_for_table;
       B.kvh = kvh;
       B.kstart = kstart;
       B.shared = shared;
+      B.tile = tile;
       B.direct = false;
       B.max_limit = -1;
       B.min_limit = INT32_MAX;
-      for (size_t c = b0; c < std::min(rowhead.size(), b0 + kSplitCols); ++c) {
+      for (size_t c = b0; c < std::min(rowhead.size(), b0 + width); ++c) {
         const int r = rowhead[c].first, lc = rowhead[c].second;
         const int m = q_end[r] - q_start[r];
         const int i = lc / g, hh = lc % g;
@@ -235,6 +238,9 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
       blocks.push_back(std::move(B));
     }
   };
+  // A group's shared range is scored by MFMA tiles of up to 128 stacked member columns
+  // (the prefill kernel in group mode) where that kernel exists, else by split items.
+  const bool group_tiles = use_prefill;
   for (auto& mem : groups) {
     const int32_t kend = shared_pages[mem[0]] * ps;
     for (int kvh = 0; kvh < Hkv; ++kvh) {
@@ -242,7 +248,7 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
       for (int r : mem)
         for (int lc = 0; lc < (q_end[r] - q_start[r]) * g; ++lc) rh.push_back({r, lc});
       const size_t first = blocks.size();
-      add_blocks(rh, kvh, 0, true, mem[0]);
+      add_blocks(rh, kvh, 0, true, mem[0], group_tiles);
       for (size_t b = first; b < blocks.size(); ++b) blocks[b].kend = kend;
     }
   }
@@ -251,13 +257,20 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
     for (int kvh = 0; kvh < Hkv; ++kvh) {
       std::vector<std::pair<int, int>> rh;
       for (int lc = 0; lc < ncol; ++lc) rh.push_back({r, lc});
-      add_blocks(rh, kvh, shared_pages[r] * ps, false, r);
+      add_blocks(rh, kvh, shared_pages[r] * ps, false, r, false);
     }
   }
 
   // ---- split length: about 8192 items over the whole iteration ------------------------
-  int64_t work = 0;
-  for (auto& B : blocks) work += std::max(0, B.kend - B.kstart);
+  int64_t work = 0, tile_cols = 0, tile_keys = 0;
+  for (auto& B : blocks) {
+    if (B.tile) {
+      tile_cols += 1;
+      tile_keys = std::max<int64_t>(tile_keys, B.kend - B.kstart);
+    } else {
+      work += std::max(0, B.kend - B.kstart);
+    }
+  }
   int64_t L;
   if (p.split_len > 0) {
     L = ceil_div(p.split_len, kStepKeys) * kStepKeys;
@@ -266,10 +279,13 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
     L = std::min<int64_t>(std::max<int64_t>(L, 256), 8192);
   }
   plan->split_len = int32_t(L);
+  // group tiles: key chunks sized for about 512 tiles in all (one per resident workgroup)
+  const int64_t Lt = std::min<int64_t>(
+      4096, std::max<int64_t>(256, ceil_div(ceil_div(tile_keys * tile_cols, 512), kStepKeys) * kStepKeys));
   for (auto& B : blocks) {
     const int64_t keys = std::max(0, B.kend - B.kstart);
-    B.nchunks = int32_t(ceil_div(keys, L));
-    B.chunk = int32_t(L);
+    B.chunk = int32_t(B.tile ? Lt : L);
+    B.nchunks = int32_t(ceil_div(keys, B.chunk));
   }
 
   // ---- partial slots: every (row, head) output of the split path that is not written
@@ -279,7 +295,7 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
     for (int32_t o : B.outs) nparts[o] += B.nchunks;
   std::vector<char> needs_slot(nparts.size(), 0);
   for (auto& B : blocks) {
-    bool direct = B.nchunks == 1;
+    bool direct = B.nchunks == 1 && !B.tile;
     for (int32_t o : B.outs) direct = direct && nparts[o] == 1;
     B.direct = direct;
     if (!direct)
@@ -311,6 +327,30 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
   std::vector<SplitItem> shared_items, own_items;
   for (auto& B : blocks) {
     if (B.nchunks == 0) continue;
+    if (B.tile) {
+      const int32_t col0 = int32_t(plan->cols.size());
+      for (size_t c = 0; c < B.outs.size(); ++c) {
+        Column C;
+        C.q_row = B.outs[c] / Hq;
+        C.q_head = B.outs[c] % Hq;
+        C.limit = B.limits[c];
+        C.pbase = pbase[B.outs[c]];
+        plan->cols.push_back(C);
+      }
+      for (int32_t j = 0; j < B.nchunks; ++j) {
+        PrefillTile t;
+        t.req = B.req;
+        t.kvh = B.kvh;
+        t.c0 = col0;
+        t.ncols = int32_t(B.outs.size());
+        t.q0 = j;                                       // partial slot of this chunk
+        t.S0 = int32_t(B.kstart + int64_t(j) * B.chunk);
+        t.kv_end = int32_t(std::min<int64_t>(B.kend, B.kstart + int64_t(j + 1) * B.chunk));
+        t.key_diag = t.kv_end;
+        plan->gtiles.push_back(t);
+      }
+      continue;
+    }
     const int32_t col0 = int32_t(plan->cols.size());
     for (size_t c = 0; c < B.outs.size(); ++c) {
       Column C;
@@ -385,6 +425,7 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
   st.prefill_kv_bytes = phys_pf * pos_bytes;
   st.split_kv_bytes = phys_sp * pos_bytes;
   st.split_q_bytes = rows_sp * Hq * D * elem;
+  st.shared_tiles = int64_t(plan->gtiles.size());
   st.direct_items = std::count_if(plan->items.begin(), plan->items.end(),
                                   [](const SplitItem& it) { return (it.flags & kItemDirect) != 0; });
 
@@ -445,8 +486,14 @@ extern "C" va_status varlen_attn_plan_export(const va_plan* plan, int32_t which,
       *count = int64_t(plan->tiles.size());
       *ints_per_entry = sizeof(PrefillTile) / 4;
       return VA_OK;
+    case 4:
+      *data = reinterpret_cast<const int32_t*>(plan->gtiles.data());
+      *count = int64_t(plan->gtiles.size());
+      *ints_per_entry = sizeof(PrefillTile) / 4;
+      return VA_OK;
   }
-  return fail(VA_ERR_INVALID_ARG, "which must be 0 (items), 1 (columns), 2 (combine rows) or 3 (tiles)");
+  return fail(VA_ERR_INVALID_ARG,
+              "which must be 0 (items), 1 (columns), 2 (combine rows), 3 (prefill tiles) or 4 (group tiles)");
 }
 
 extern "C" void varlen_attn_plan_destroy(va_plan* plan) {

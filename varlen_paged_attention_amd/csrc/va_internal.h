@@ -31,7 +31,9 @@ struct CombineRow {
 };
 
 // One MFMA prefill tile: query columns c0 .. c0+ncols of request `req` under KV head
-// `kvh`, where column c is new row i = c / g with query head kvh*g + c % g.
+// `kvh`, where column c is new row i = c / g with query head kvh*g + c % g.  As a
+// shared-prefix group tile the fields mean: columns cols[c0 .. c0+ncols), partial slot q0,
+// keys [S0, kv_end) of request req's block table.
 struct PrefillTile {
   int32_t req, kvh, c0, ncols;
   int32_t q0, S0, kv_end, key_diag;  // q_start of the request; S0; keys read [0, kv_end);
@@ -62,6 +64,7 @@ struct va_plan {
   std::vector<va::Column> cols;
   std::vector<va::CombineRow> combine;
   std::vector<va::PrefillTile> tiles;
+  std::vector<va::PrefillTile> gtiles;        // shared-prefix group tiles (columns from `cols`)
   va_plan_stats stats{};
   // device copies (one allocation)
   void* dev = nullptr;
@@ -70,6 +73,7 @@ struct va_plan {
   const va::Column* d_cols = nullptr;
   const va::CombineRow* d_combine = nullptr;
   const va::PrefillTile* d_tiles = nullptr;
+  const va::PrefillTile* d_gtiles = nullptr;
   const int64_t* d_kv_offset = nullptr;
   int device = -1;
   size_t ws_ml_off = 0, ws_acc_off = 0, ws_bytes = 0;

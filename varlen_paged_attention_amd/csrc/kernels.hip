@@ -711,20 +711,43 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineRow* __restri
   const int idx = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (idx >= nrows) return;
   const CombineRow r = rows[idx];
+  // lane s holds part s0 + s's (m, l), so the per-part scalars load in parallel; the
+  // accumulator rows (lane d holds d, d + 64, ..) are loaded eight parts at a time
   float M = -INFINITY;
-  for (int s = 0; s < r.nparts; ++s) M = fmaxf(M, ws_ml[2 * size_t(r.pbase + s)]);
+  for (int s0 = 0; s0 < r.nparts; s0 += 64)
+    if (s0 + lane < r.nparts) M = fmaxf(M, ws_ml[2 * size_t(r.pbase + s0 + lane)]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   float L = 0.f;
   float o[D / 64];
 #pragma unroll
   for (int j = 0; j < D / 64; ++j) o[j] = 0.f;
-  for (int s = 0; s < r.nparts; ++s) {
-    const size_t slot = size_t(r.pbase + s);
-    const float w = fast_exp2(ws_ml[2 * slot] - M);
-    L += w * ws_ml[2 * slot + 1];
-    const float* a = ws_acc + slot * D + lane;
+  for (int s0 = 0; s0 < r.nparts; s0 += 64) {
+    float w = 0.f;
+    if (s0 + lane < r.nparts) {
+      const size_t slot = size_t(r.pbase + s0 + lane);
+      w = fast_exp2(ws_ml[2 * slot] - M);
+      L += w * ws_ml[2 * slot + 1];
+    }
+    const int n = min(64, r.nparts - s0);
+    for (int t = 0; t < n; t += 8) {
+      float a[8][D / 64], wt[8];
 #pragma unroll
-    for (int j = 0; j < D / 64; ++j) o[j] += w * a[64 * j];
+      for (int u = 0; u < 8; ++u) {
+        const bool ok = t + u < n;
+        wt[u] = ok ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), t + u)) : 0.f;
+        const float* ap = ws_acc + size_t(r.pbase + s0 + (ok ? t + u : 0)) * D + lane;
+#pragma unroll
+        for (int j = 0; j < D / 64; ++j) a[u][j] = ap[64 * j];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int j = 0; j < D / 64; ++j) o[j] += wt[u] * a[u][j];
+    }
   }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
   const float inv = 1.f / L;
   OutT* op = out + (size_t(r.q_row) * Hq + r.q_head) * D + lane;
 #pragma unroll

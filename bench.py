@@ -110,11 +110,12 @@ def dominant(stats, stage_ms):
     """The stage with the largest time, with its algorithmic work and roofline bound."""
     name = max(stage_ms, key=stage_ms.get)
     ms = stage_ms[name]
-    if name == "prefill":
-        work, bound = stats["prefill_flops"], "mfma"
+    if name == "prefill":      # prefill tiles and shared-prefix group tiles
+        work, bound = stats["prefill_flops"] + stats["shared_tile_flops"], "mfma"
     elif name == "split_kv":
         # bandwidth-bound unless it also carries the prefill rows (then it is a contraction)
-        flops, byts = stats["split_flops"], stats["split_kv_bytes"] + stats["split_q_bytes"] + stats["table_bytes"]
+        flops = stats["split_flops"] - stats["shared_tile_flops"]
+        byts = stats["split_item_kv_bytes"] + stats["split_q_bytes"] + stats["table_bytes"]
         bound = "mfma" if flops / PEAK_BF16 > byts / PEAK_HBM else "hbm"
         work = flops if bound == "mfma" else byts
     else:

@@ -120,6 +120,8 @@ typedef struct {
   int64_t split_q_bytes;      /* query bytes of the split-KV requests */
   int64_t direct_items;       /* split-KV items that write output rows directly (no combine) */
   int64_t shared_tiles;       /* MFMA tiles scoring shared-prefix chunks for stacked member rows */
+  double shared_tile_flops;   /* part of split_flops done by those tiles (in the prefill stage) */
+  int64_t split_item_kv_bytes; /* distinct KV bytes the split-KV items read */
 } va_plan_stats;
 
 typedef struct va_plan va_plan;   /* opaque, immutable after creation */

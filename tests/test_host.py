@@ -211,8 +211,11 @@ def test_shared_prefix_groups_found():
     st = api.varlen_attn_plan_stats(_plan(w, api.VA_FLAG_SHARED_PREFIX))
     assert st["shared_groups"] == 1 and st["shared_tiles"] > 0 and st["shared_items"] == 0
     assert st["physical_kv_bytes"] == 40 * 2 ** 20 and st["logical_kv_bytes"] == 120 * 2 ** 20
+    # split items read only the 6 private ranges of 1024 positions (8 KV heads, K and V, bf16)
+    assert st["split_item_kv_bytes"] == 6 * 1024 * 8 * 128 * 2 * 2
+    assert st["shared_tile_flops"] == 4 * 128 * (6 * 4) * 4096 * 8
     st0 = api.varlen_attn_plan_stats(_plan(w))
-    assert st0["shared_groups"] == 0
+    assert st0["shared_groups"] == 0 and st0["split_item_kv_bytes"] == st0["physical_kv_bytes"]
 
 
 def test_config_shapes():

@@ -42,7 +42,8 @@ class VaPlanStats(ctypes.Structure):
                [("plan_host_us", ctypes.c_double), ("prefill_flops", ctypes.c_double),
                 ("split_flops", ctypes.c_double)] + \
                [(n, ctypes.c_int64) for n in ("prefill_kv_bytes", "split_kv_bytes", "split_q_bytes",
-                                              "direct_items", "shared_tiles")]
+                                              "direct_items", "shared_tiles")] + \
+               [("shared_tile_flops", ctypes.c_double), ("split_item_kv_bytes", ctypes.c_int64)]
 
 
 class VarlenAttnError(RuntimeError):

@@ -425,7 +425,35 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
   st.prefill_kv_bytes = phys_pf * pos_bytes;
   st.split_kv_bytes = phys_sp * pos_bytes;
   st.split_q_bytes = rows_sp * Hq * D * elem;
+  // distinct positions the split items read (with group tiles, the shared pages are theirs)
+  {
+    std::vector<std::pair<int64_t, int64_t>> iv;      // [page*ps + lo, page*ps + hi)
+    for (const SplitItem& it : plan->items) {
+      if (it.kvh != 0) continue;                      // every KV head reads the same positions
+      for (int64_t k = it.k0; k < it.k1;) {
+        const int64_t j = k / ps, hi = std::min<int64_t>(it.k1, (j + 1) * ps);
+        const int64_t base = int64_t(bt(it.req, j)) * ps - j * ps;
+        iv.push_back({base + k, base + hi});
+        k = hi;
+      }
+    }
+    std::sort(iv.begin(), iv.end());
+    int64_t n = 0, cur_lo = -1, cur_hi = -1;
+    for (auto& x : iv) {
+      if (x.first > cur_hi) {
+        n += cur_hi - cur_lo;
+        cur_lo = x.first;
+        cur_hi = x.second;
+      } else {
+        cur_hi = std::max(cur_hi, x.second);
+      }
+    }
+    n += cur_hi - cur_lo;
+    st.split_item_kv_bytes = n * pos_bytes;
+  }
   st.shared_tiles = int64_t(plan->gtiles.size());
+  st.shared_tile_flops = 0;
+  for (const PrefillTile& t : plan->gtiles) st.shared_tile_flops += 4.0 * D * t.ncols * double(t.kv_end - t.S0);
   st.direct_items = std::count_if(plan->items.begin(), plan->items.end(),
                                   [](const SplitItem& it) { return (it.flags & kItemDirect) != 0; });
 

@@ -429,3 +429,67 @@ def test_mutants_are_caught(monkeypatch):
     with monkeypatch.context() as mp:
         mp.setattr(OA, "attention_rows", rows_mod)
         assert _fails(check_gqa_replication)
+
+
+# ------------------------------------------------------------ KV append ----------
+
+def test_append_slots_worked_example():
+    """Hand-derived slot mapping ("GLM-5.3 推理全链路(八)", stage 4; tests/golden)."""
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "kv_append_slots.txt"))
+            if l.strip() and not l.startswith("#")]
+    want = np.array([int(r[1]) for r in rows], np.int64)
+    bt = np.array([[5, 2], [7, -1], [1, 0]], np.int32)
+    got = oracle.slots_for_new_rows([0, 2, 3], [2, 3, 5], [5, 1, 8], bt, 4, 6)
+    assert np.array_equal(got, want)
+
+
+def _bits_equal(a, b):
+    return np.array_equal(np.ascontiguousarray(a).view(np.uint8), np.ascontiguousarray(b).view(np.uint8))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_append_then_gather_round_trip(dtype):
+    """Writing the new rows' K/V back through the slot mapping restores the pools bit for
+    bit, and the request's gather reads them at positions S0 .. kv_len-1 ("ORCA 和 chunked
+    prefill", section 3: append, then attention reads the whole prefix)."""
+    w = W.build("a", [5, 1, 3], [9, 40, 3], num_q_heads=4, num_kv_heads=2, head_dim=8, page_size=4,
+                dtype=dtype, seed=11)
+    loc = oracle.slots_for_new_rows(w.q_start, w.q_end, w.kv_len, w.block_table, w.page_size, w.total_q_rows)
+    Hkv, D = w.num_kv_heads, w.head_dim
+    k_new = np.zeros((w.total_q_rows, Hkv, D), w.k_pool.dtype)
+    v_new = np.zeros_like(k_new)
+    for r in range(w.num_reqs):
+        m = int(w.q_end[r] - w.q_start[r])
+        S0 = int(w.kv_len[r]) - m
+        for i in range(m):
+            pos = S0 + i
+            page, slot = w.block_table[r][pos // w.page_size], pos % w.page_size
+            k_new[w.q_start[r] + i] = w.k_pool[page, :, slot, :]
+            v_new[w.q_start[r] + i] = w.v_pool[page, :, :, slot]
+    # blank the new slots, then append: the original pools come back
+    kb, vb = w.k_pool.copy(), w.v_pool.copy()
+    for t, l in enumerate(loc):
+        if l >= 0:
+            kb[l // w.page_size, :, l % w.page_size, :] = 0
+            vb[l // w.page_size, :, :, l % w.page_size] = 0
+    assert not _bits_equal(kb, w.k_pool)
+    k2, v2 = oracle.append_kv(kb, vb, k_new, v_new, loc, w.page_size)
+    assert _bits_equal(k2, w.k_pool) and _bits_equal(v2, w.v_pool)
+    # and the gather of request r reads token t's rows at position S0 + i
+    for r in range(w.num_reqs):
+        m = int(w.q_end[r] - w.q_start[r])
+        for kvh in range(Hkv):
+            K, V = OA.gather_kv(k2, v2, w.block_table[r], int(w.kv_len[r]), kvh, w.page_size)
+            assert np.array_equal(K[-m:], OA.to_f64(k_new[w.q_start[r]:w.q_end[r], kvh, :]))
+            assert np.array_equal(V[-m:], OA.to_f64(v_new[w.q_start[r]:w.q_end[r], kvh, :]))
+
+
+def test_append_padding_writes_nothing():
+    w = W.build("p", [2], [6], num_q_heads=2, num_kv_heads=1, head_dim=8, page_size=4, dtype="f32", seed=2)
+    k_new = np.full((3, 1, 8), 9.0, np.float32)
+    v_new = np.full((3, 1, 8), 9.0, np.float32)
+    k2, v2 = oracle.append_kv(w.k_pool, w.v_pool, k_new, v_new, np.array([-1, -1, -1]), 4)
+    assert _bits_equal(k2, w.k_pool) and _bits_equal(v2, w.v_pool)
+    # one real entry changes exactly D values in each pool
+    k3, v3 = oracle.append_kv(w.k_pool, w.v_pool, k_new, v_new, np.array([-1, 5, -1]), 4)
+    assert int((k3 != w.k_pool).sum()) <= 8 and np.all(k3[1, 0, 1, :] == 9.0) and np.all(v3[1, 0, :, 1] == 9.0)

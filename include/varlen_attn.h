@@ -160,6 +160,31 @@ va_status varlen_attn_run_events(const va_plan* plan, const void* q, const void*
                                  void* workspace, size_t workspace_bytes, void* stream,
                                  void* const* events);
 
+/* Write one iteration's new K and V into the paged pools ("ORCA 和 chunked prefill",
+ * section 3: the layer's K/V of the new rows are appended to each request's cache before
+ * attention reads the whole prefix; "GLM-5.3 推理全链路(八)", stage 4: out_cache_loc gives
+ * every new token the page and slot it is written to).
+ *   params:        layout of the pools (num_kv_heads, head_dim, page_size, num_pages, dtype;
+ *                  the other fields are ignored)
+ *   num_tokens:    new tokens (>= 0)
+ *   k_new, v_new:  device [num_tokens][num_kv_heads][head_dim], element type params->dtype
+ *   out_cache_loc: device int64 [num_tokens]: token t goes to page loc / page_size, slot
+ *                  loc % page_size of both pools; loc < 0 is padding and writes nothing
+ *   k_pool, v_pool: device pools in the layouts above (K rows, V pages transposed)
+ *   bad_loc_count: optional device int32 (NULL: not reported); every token whose loc is
+ *                  >= num_pages * page_size is skipped and counted here (atomically added,
+ *                  the caller zeroes it)
+ * Values are copied bit for bit.  Enqueue only (no allocation, no synchronisation); two
+ * tokens naming the same slot leave one of them, unspecified which. */
+va_status varlen_attn_append_kv(const va_params* params, int64_t num_tokens, const void* k_new,
+                                const void* v_new, const int64_t* out_cache_loc, void* k_pool,
+                                void* v_pool, int32_t* bad_loc_count, void* stream);
+
+/* The out_cache_loc of the planned iteration (host int64 [total_q_rows]): flat row
+ * q_start[r] + i of request r is logical position kv_len[r] - q_rows + i, in page
+ * block_table[r][pos / page_size], slot pos % page_size; rows outside every request get -1. */
+va_status varlen_attn_plan_slots(const va_plan* plan, int64_t* out_cache_loc_host);
+
 /* Counters of the planned work (no device access). */
 va_status varlen_attn_plan_stats(const va_plan* plan, va_plan_stats* out);
 

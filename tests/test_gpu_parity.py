@@ -253,3 +253,109 @@ def test_run_errors():
     assert ei.value.status == api.VA_ERR_WORKSPACE_TOO_SMALL
     L = api.lib()
     assert L.varlen_attn_run(plan.handle, None, None, None, None, None, None, 0, None) == api.VA_ERR_INVALID_ARG
+
+
+# ------------------------------------------------------------------ KV append --
+
+def _new_rows_kv(w):
+    """The new rows' K/V ([total_q_rows, Hkv, D], raw element bits) read from the pools by
+    the definition: row q_start[r] + i is position kv_len[r] - q_rows + i."""
+    k_new = np.zeros((w.total_q_rows, w.num_kv_heads, w.head_dim), w.k_pool.dtype)
+    v_new = np.zeros_like(k_new)
+    for r in range(w.num_reqs):
+        m = int(w.q_end[r] - w.q_start[r])
+        S0 = int(w.kv_len[r]) - m
+        for i in range(m):
+            pos = S0 + i
+            page, slot = w.block_table[r][pos // w.page_size], pos % w.page_size
+            k_new[w.q_start[r] + i] = w.k_pool[page, :, slot, :]
+            v_new[w.q_start[r] + i] = w.v_pool[page, :, :, slot]
+    return k_new, v_new
+
+
+def _to_dev(a):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    return (t.view(torch.bfloat16) if a.dtype == np.uint16 else t).cuda()
+
+
+def _raw(t):
+    import torch
+    return t.view(torch.int16).cpu().numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.cpu().numpy()
+
+
+@pytest.mark.parametrize("dtype,d,ps", [("bf16", 128, 16), ("bf16", 64, 64), ("f32", 128, 32)])
+def test_append_bit_exact(dtype, d, ps):
+    """GPU append == oracle append, bit for bit, with padding (-1) and random new values."""
+    import torch
+    w = W.build("ap", [37, 1, 5, 0, 200], [90, 300, 5, 10, 200], num_q_heads=8, num_kv_heads=4, head_dim=d,
+                page_size=ps, dtype=dtype, seed=23, extra_pages=3)
+    _say(f"[gpu] append {dtype} d={d} ps={ps}")
+    plan = api.plan_for(w, flags=api.VA_FLAG_HOST_ONLY)
+    loc = api.varlen_attn_plan_slots(plan)
+    rng = np.random.default_rng(5)
+    shape = (w.total_q_rows, w.num_kv_heads, w.head_dim)
+    if dtype == "bf16":
+        k_new = rng.integers(0, 1 << 16, size=shape, dtype=np.uint16)
+        v_new = rng.integers(0, 1 << 16, size=shape, dtype=np.uint16)
+    else:
+        k_new = rng.standard_normal(shape).astype(np.float32)
+        v_new = rng.standard_normal(shape).astype(np.float32)
+    loc[3] = -1                                          # a padding row inside a request
+    want_k, want_v = oracle.append_kv(w.k_pool, w.v_pool, k_new, v_new, loc, w.page_size)
+    kp, vp = _to_dev(w.k_pool), _to_dev(w.v_pool)
+    bad = torch.zeros(1, dtype=torch.int32, device="cuda")
+    api.varlen_attn_append_kv(num_kv_heads=w.num_kv_heads, head_dim=d, page_size=ps, num_pages=w.num_pages,
+                              k_new=_to_dev(k_new), v_new=_to_dev(v_new), out_cache_loc=torch.from_numpy(loc).cuda(),
+                              k_pool=kp, v_pool=vp, bad_loc_count=bad, dtype=dtype)
+    torch.cuda.synchronize()
+    assert int(bad.item()) == 0
+    assert np.array_equal(_raw(kp).view(np.uint8), np.ascontiguousarray(want_k).view(np.uint8))
+    assert np.array_equal(_raw(vp).view(np.uint8), np.ascontiguousarray(want_v).view(np.uint8))
+
+
+def test_append_out_of_range_counted_and_skipped():
+    import torch
+    w = W.build("ob", [4], [20], num_q_heads=4, num_kv_heads=2, head_dim=64, page_size=16, seed=3)
+    _say("[gpu] append out of range")
+    n = w.num_pages * w.page_size
+    loc = np.array([n, 5, n + 100, 17], np.int64)
+    k_new = np.full((4, 2, 64), 0x3F80, np.uint16)
+    v_new = np.full((4, 2, 64), 0x4000, np.uint16)
+    want_k, want_v = oracle.append_kv(w.k_pool, w.v_pool, k_new, v_new, np.where(loc < n, loc, -1), w.page_size)
+    kp, vp = _to_dev(w.k_pool), _to_dev(w.v_pool)
+    bad = torch.zeros(1, dtype=torch.int32, device="cuda")
+    api.varlen_attn_append_kv(num_kv_heads=2, head_dim=64, page_size=16, num_pages=w.num_pages, k_new=_to_dev(k_new),
+                              v_new=_to_dev(v_new), out_cache_loc=torch.from_numpy(loc).cuda(), k_pool=kp, v_pool=vp,
+                              bad_loc_count=bad)
+    torch.cuda.synchronize()
+    assert int(bad.item()) == 2
+    assert np.array_equal(_raw(kp), want_k) and np.array_equal(_raw(vp), want_v)
+
+
+@pytest.mark.parametrize("cid,scale", [(2, 8), (4, 16), (3, 16)])
+def test_append_then_attend(cid, scale):
+    """Poison the new rows' slots, append their K/V on the GPU, run attention: the result
+    matches the oracle on the original pools (the append puts every new row where the
+    attention reads it)."""
+    import torch
+    w = W.config(cid, scale=scale)
+    _say(f"[gpu] append then attend config {cid}/{scale}")
+    plan = api.plan_for(w)
+    loc = api.varlen_attn_plan_slots(plan)
+    k_new, v_new = _new_rows_kv(w)
+    poison = np.uint16(0x7FC0) if w.dtype == "bf16" else np.float32(np.nan)
+    kb, vb = w.k_pool.copy(), w.v_pool.copy()
+    for l in loc[loc >= 0]:
+        kb[l // w.page_size, :, l % w.page_size, :] = poison
+        vb[l // w.page_size, :, :, l % w.page_size] = poison
+    q, _, _, bt = api.to_device(w)
+    kp, vp = _to_dev(kb), _to_dev(vb)
+    api.varlen_attn_append_kv(num_kv_heads=w.num_kv_heads, head_dim=w.head_dim, page_size=w.page_size,
+                              num_pages=w.num_pages, k_new=_to_dev(k_new), v_new=_to_dev(v_new),
+                              out_cache_loc=torch.from_numpy(loc).cuda(), k_pool=kp, v_pool=vp, dtype=w.dtype)
+    out = torch.zeros_like(q)
+    api.varlen_attn_run(plan, q, kp, vp, bt, out, api.new_workspace(plan))
+    torch.cuda.synchronize()
+    assert np.array_equal(_raw(kp).view(np.uint8), np.ascontiguousarray(w.k_pool).view(np.uint8))
+    _check_full(w, out, f"append+attend {cid}/{scale}")

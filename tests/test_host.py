@@ -225,3 +225,23 @@ def test_config_shapes():
     assert w.num_pages == 256 + 94 + 107
     w = W.config(5)
     assert w.num_pages == 64 + 6 * 16 and w.shared_prefix_pages == 64
+
+
+@pytest.mark.parametrize("name,make,flags", CASES[:6], ids=[c[0] for c in CASES[:6]])
+def test_plan_slots_match_oracle(name, make, flags):
+    """The plan's out_cache_loc equals the oracle's slot mapping of the new rows."""
+    w = make()
+    got = api.varlen_attn_plan_slots(_plan(w, flags))
+    want = oracle.slots_for_new_rows(w.q_start, w.q_end, w.kv_len, w.block_table, w.page_size, w.total_q_rows)
+    assert np.array_equal(got, want)
+
+
+def test_append_argument_errors():
+    L = api.lib()
+    assert L.varlen_attn_append_kv(None, 1, None, None, None, None, None, None, None) == api.VA_ERR_INVALID_ARG
+    p = api.VaParams(0, 2, 64, 16, 8, 0, api.VA_DTYPE_BF16, 0.0, 0, 0, 0)
+    assert L.varlen_attn_append_kv(p, -1, None, None, None, None, None, None, None) == api.VA_ERR_INVALID_ARG
+    assert L.varlen_attn_append_kv(p, 0, None, None, None, None, None, None, None) == api.VA_OK
+    assert L.varlen_attn_append_kv(p, 3, None, None, None, None, None, None, None) == api.VA_ERR_INVALID_ARG
+    p.head_dim = 96
+    assert L.varlen_attn_append_kv(p, 3, None, None, None, None, None, None, None) == api.VA_ERR_UNSUPPORTED

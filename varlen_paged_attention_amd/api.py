@@ -21,7 +21,7 @@ VA_FLAG_SHARED_PREFIX, VA_FLAG_NO_PREFILL_KERNEL, VA_FLAG_HOST_ONLY = 1, 2, 4
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvarlen_attn.so")
 EXPORTED = ["varlen_attn_plan", "varlen_attn_run", "varlen_attn_run_events", "varlen_attn_plan_stats", "varlen_attn_plan_export",
             "varlen_attn_debug_gather", "varlen_attn_plan_destroy", "varlen_attn_status_string",
-            "varlen_attn_last_error"]
+            "varlen_attn_last_error", "varlen_attn_append_kv", "varlen_attn_plan_slots"]
 
 
 class VaParams(ctypes.Structure):
@@ -83,6 +83,10 @@ def lib():
         L.varlen_attn_plan_export.restype = ctypes.c_int
         L.varlen_attn_debug_gather.argtypes = [P, P, P, P, P, P, P]
         L.varlen_attn_debug_gather.restype = ctypes.c_int
+        L.varlen_attn_append_kv.argtypes = [ctypes.POINTER(VaParams), ctypes.c_int64, P, P, P, P, P, P, P]
+        L.varlen_attn_append_kv.restype = ctypes.c_int
+        L.varlen_attn_plan_slots.argtypes = [P, ctypes.POINTER(ctypes.c_int64)]
+        L.varlen_attn_plan_slots.restype = ctypes.c_int
         L.varlen_attn_plan_destroy.argtypes = [P]
         L.varlen_attn_plan_destroy.restype = None
         L.varlen_attn_status_string.argtypes = [ctypes.c_int]
@@ -231,6 +235,32 @@ def varlen_attn_debug_gather(plan: Plan, k_pool, v_pool, block_table_dev, k_out,
                                           _dev_ptr(block_table_dev, "block_table", torch.int32),
                                           _dev_ptr(k_out, "k_out", dt), _dev_ptr(v_out, "v_out", dt),
                                           _stream_ptr(stream)))
+
+
+def varlen_attn_plan_slots(plan: Plan) -> np.ndarray:
+    """out_cache_loc of the planned iteration: int64 [total_q_rows], -1 outside requests."""
+    n = int(varlen_attn_plan_stats(plan)["total_q_rows"])
+    out = np.empty(n, np.int64)
+    _check(lib().varlen_attn_plan_slots(plan.handle, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))))
+    return out
+
+
+def varlen_attn_append_kv(*, num_kv_heads: int, head_dim: int, page_size: int, num_pages: int, k_new, v_new,
+                          out_cache_loc, k_pool, v_pool, bad_loc_count=None, dtype: str = "bf16", stream=None) -> None:
+    """Write k_new/v_new ([T, Hkv, D] GPU tensors) into the pools at out_cache_loc (int64 [T] GPU
+    tensor); bad_loc_count: optional int32 [1] GPU tensor counting out-of-range entries."""
+    import torch
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    p = VaParams(0, num_kv_heads, head_dim, page_size, num_pages, 0,
+                 VA_DTYPE_BF16 if dtype == "bf16" else VA_DTYPE_F32, 0.0, 0, 0, 0)
+    T = int(out_cache_loc.numel())
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if tuple(t.shape) != (T, num_kv_heads, head_dim):
+            raise ValueError(f"{name} must be [{T}, {num_kv_heads}, {head_dim}]")
+    _check(lib().varlen_attn_append_kv(ctypes.byref(p), T, _dev_ptr(k_new, "k_new", dt), _dev_ptr(v_new, "v_new", dt),
+                                       _dev_ptr(out_cache_loc, "out_cache_loc", torch.int64),
+                                       _dev_ptr(k_pool, "k_pool", dt), _dev_ptr(v_pool, "v_pool", dt),
+                                       _dev_ptr(bad_loc_count, "bad_loc_count", torch.int32), _stream_ptr(stream)))
 
 
 def new_workspace(plan: Plan, device="cuda"):

@@ -135,6 +135,7 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
   plan->q_start.assign(q_start, q_start + num_reqs);
   plan->q_end.assign(q_end, q_end + num_reqs);
   plan->kv_len.assign(kv_len, kv_len + num_reqs);
+  plan->block_table.assign(block_table_host, block_table_host + int64_t(num_reqs) * p.max_pages_per_req);
   plan->kv_offset.resize(num_reqs + 1, 0);
   for (int r = 0; r < num_reqs; ++r) plan->kv_offset[r + 1] = plan->kv_offset[r] + kv_len[r];
 
@@ -481,6 +482,23 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
       std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t0).count();
   *plan_out = plan;
   if (workspace_bytes_out) *workspace_bytes_out = plan->ws_bytes;
+  return VA_OK;
+}
+
+extern "C" va_status varlen_attn_plan_slots(const va_plan* plan, int64_t* out) {
+  if (!plan || !out) return fail(VA_ERR_INVALID_ARG, "plan or out is NULL");
+  const int64_t rows = plan->stats.total_q_rows;
+  for (int64_t t = 0; t < rows; ++t) out[t] = -1;
+  const int ps = plan->p.page_size;
+  for (int r = 0; r < plan->num_reqs; ++r) {
+    const int32_t* row = plan->block_table.data() + int64_t(r) * plan->p.max_pages_per_req;
+    const int m = plan->q_end[r] - plan->q_start[r];
+    const int S0 = plan->kv_len[r] - m;
+    for (int i = 0; i < m; ++i) {
+      const int pos = S0 + i;
+      out[plan->q_start[r] + i] = int64_t(row[pos / ps]) * ps + pos % ps;
+    }
+  }
   return VA_OK;
 }
 

@@ -59,6 +59,7 @@ struct va_plan {
   int32_t g = 1;
   int32_t split_len = 0;
   std::vector<int32_t> q_start, q_end, kv_len;
+  std::vector<int32_t> block_table;          // host copy [num_reqs][max_pages_per_req]
   std::vector<int64_t> kv_offset;            // prefix sum of kv_len (gather output rows)
   std::vector<va::SplitItem> items;
   std::vector<va::Column> cols;

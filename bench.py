@@ -187,6 +187,35 @@ def hbm_copy_gbps():
     return round(2 * n * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
 
 
+def append_line(api, W, cid, label, reps=50):
+    """Time varlen_attn_append_kv for one iteration's new rows (their slots from the plan);
+    algorithmic bytes = new K/V read + the same bytes written + the slot indices."""
+    import torch
+    w = W.config(cid)
+    plan = api.plan_for(w, flags=api.VA_FLAG_HOST_ONLY)
+    loc = torch.from_numpy(api.varlen_attn_plan_slots(plan)).cuda()
+    _, k, v, _ = api.to_device(w)
+    T = int(loc.numel())
+    dt = k.dtype
+    k_new = torch.randn(T, w.num_kv_heads, w.head_dim, device="cuda").to(dt)
+    v_new = torch.randn_like(k_new)
+    args = dict(num_kv_heads=w.num_kv_heads, head_dim=w.head_dim, page_size=w.page_size, num_pages=w.num_pages,
+                k_new=k_new, v_new=v_new, out_cache_loc=loc, k_pool=k, v_pool=v, dtype=w.dtype)
+    for _ in range(5):
+        api.varlen_attn_append_kv(**args)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        api.varlen_attn_append_kv(**args)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    byts = 2 * 2 * k_new.numel() * k_new.element_size() + 8 * T
+    return {"workload": label, "us_per_step": round(us, 2), "hbm_GBps": round(byts / (us * 1e-6) / 1e9, 1),
+            "hbm_frac": round(byts / (us * 1e-6) / PEAK_HBM, 4), "algorithmic_bytes": byts, "tokens": T}
+
+
 def make_flush():
     """A callable that evicts the 256 MB last-level cache by reading 1 GiB (a read leaves no
     dirty lines whose write-back the timed kernels would pay for)."""
@@ -286,6 +315,11 @@ def main():
                 (51, api.VA_FLAG_SHARED_PREFIX, "shared-prefix-64 (16384 shared + 1024 each)", flush, "shared64")):
             log(f"[bench] secondary: {label}")
             sec.append(secondary(api, W, cid, flags, 20, label, fl, key))
+            torch.cuda.empty_cache()
+        for cid, label in ((2, "kv-append: the ORCA iteration's 4098 new rows (32 KV heads, page 16)"),
+                           (3, "kv-append: the decode-heavy iteration's 256 new rows (8 KV heads, page 64)")):
+            log(f"[bench] secondary: {label}")
+            sec.append(append_line(api, W, cid, label))
             torch.cuda.empty_cache()
         sec.append({"workload": "torch copy 1 GiB (read+write) for reference", "hbm_GBps": hbm_copy_gbps()})
         rec["secondary"] = sec

@@ -1,0 +1,221 @@
+"""Pins for the oracle's fp8 KV storage (e4m3fn codes with per-token float32 scales).
+
+The decoder is pinned to the format's closed-form values and to torch's own
+float8_e4m3fn conversion on all 256 codes; the dequantising gather is pinned by
+constructed pools whose values name their own page, head and slot; attention over
+fp8 pools is pinned by the scalar brute force on pools decoded by torch, and by the
+exact scaling laws of the scales.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import fp8 as OF
+from varlen_paged_attention_amd import workloads as W
+
+
+def _torch_decode(codes: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(codes, np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
+
+
+def check_closed_forms():
+    """Values fixed by the e4m3fn definition: bias 7, 3 mantissa bits, no infinities."""
+    table = {
+        0x00: 0.0, 0x38: 1.0, 0x40: 2.0, 0x3C: 1.5, 0x30: 0.5, 0x7E: 448.0, 0x7D: 416.0,
+        0x08: 2.0 ** -6, 0x07: 7 * 2.0 ** -9, 0x01: 2.0 ** -9, 0xB8: -1.0, 0xFE: -448.0,
+        0x81: -(2.0 ** -9), 0x48: 4.0, 0x4F: 7.5,
+    }
+    got = OF.e4m3fn_to_f64(np.array(list(table), np.uint8))
+    np.testing.assert_array_equal(got, np.array(list(table.values())))
+    neg0 = OF.e4m3fn_to_f64(np.array([0x80], np.uint8))[0]
+    assert neg0 == 0.0 and math.copysign(1.0, neg0) == -1.0
+    nan = OF.e4m3fn_to_f64(np.array([0x7F, 0xFF], np.uint8))
+    assert np.isnan(nan).all()
+
+
+def check_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    got = OF.e4m3fn_to_f64(codes)
+    want = _torch_decode(codes)
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    np.testing.assert_array_equal(got[ok], want[ok])
+    np.testing.assert_array_equal(np.signbit(got[ok]), np.signbit(want[ok]))
+
+
+def check_grid_shape():
+    """The 126 positive finite codes increase strictly with their code; the spacing in
+    exponent field e is 2^(max(e,1)-10) (subnormals share the first binade's 2^-9),
+    the step into a new binade is the previous binade's spacing, and the negative half
+    mirrors the positive half."""
+    pos = OF.e4m3fn_to_f64(np.arange(1, 0x7F, dtype=np.uint8))
+    assert np.all(np.diff(pos) > 0)
+    steps = np.diff(np.concatenate([[0.0], pos]))
+
+    def spacing(e):
+        return 2.0 ** (max(e, 1) - 10)
+
+    for c, st in zip(range(1, 0x7F), steps):
+        e = c >> 3
+        want = spacing(e - 1) if (c & 7) == 0 else spacing(e)
+        assert st == want, (hex(c), st, want)
+    neg = OF.e4m3fn_to_f64(np.arange(0x81, 0xFF, dtype=np.uint8))
+    np.testing.assert_array_equal(neg, -pos)
+
+
+def _layout_pools(P=3, H=2, ps=4, D=5):
+    """Pools whose codes are all 1.0 and whose scales encode (page, head, slot)."""
+    k = np.full((P, H, ps, D), 0x38, np.uint8)
+    v = np.full((P, H, D, ps), 0x38, np.uint8)
+    tag = (np.arange(P)[:, None, None] * 100 + np.arange(H)[None, :, None] * 10
+           + np.arange(ps)[None, None, :]).astype(np.float32)
+    return k, tag + 1000, v, tag + 2000
+
+
+def check_dequantize_axes():
+    """K row (p, h, s) is scaled by k_scale[p, h, s]; V column (p, h, :, s) by
+    v_scale[p, h, s]; K and V scales are not exchanged."""
+    k, ks, v, vs = _layout_pools()
+    K, V = OF.dequantize_pools(k, ks, v, vs)
+    P, H, ps, D = k.shape
+    for p in range(P):
+        for h in range(H):
+            for s in range(ps):
+                assert np.all(K[p, h, s, :] == 1000 + 100 * p + 10 * h + s)
+                assert np.all(V[p, h, :, s] == 2000 + 100 * p + 10 * h + s)
+
+
+def check_dequantize_random():
+    rng = np.random.default_rng(5)
+    k = rng.integers(0, 256, (4, 2, 8, 16), dtype=np.uint8)
+    v = rng.integers(0, 256, (4, 2, 16, 8), dtype=np.uint8)
+    k[k & 0x7F == 0x7F] = 0x38
+    v[v & 0x7F == 0x7F] = 0x38
+    ks = rng.uniform(0.01, 2.0, (4, 2, 8)).astype(np.float32)
+    vs = rng.uniform(0.01, 2.0, (4, 2, 8)).astype(np.float32)
+    K, V = OF.dequantize_pools(k, ks, v, vs)
+    np.testing.assert_array_equal(K, _torch_decode(k) * ks.astype(np.float64)[..., None])
+    np.testing.assert_array_equal(V, _torch_decode(v) * vs.astype(np.float64)[:, :, None, :])
+
+
+def _fp8_workload(seed=3, q_rows=(3, 1, 2), kv=(9, 6, 5), hq=4, hkv=2, d=8, ps=4):
+    return W.build("fp8", list(q_rows), list(kv), num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                   page_size=ps, dtype="fp8", seed=seed)
+
+
+def _oracle_fp8(w, k_scale=None, v_scale=None, softmax_scale=None):
+    K, V = oracle.dequantize_pools(w.k_pool, w.k_scale if k_scale is None else k_scale,
+                                   w.v_pool, w.v_scale if v_scale is None else v_scale)
+    return oracle.varlen_paged_attention(w.q, K, V, w.block_table, w.q_start, w.q_end, w.kv_len,
+                                         w.page_size, softmax_scale)
+
+
+def check_fp8_attention_brute_force():
+    """Attention over dequantised pools equals the scalar brute force over pools
+    decoded by torch and scaled per token."""
+    w = _fp8_workload()
+    got = _oracle_fp8(w)
+    K = _torch_decode(w.k_pool) * w.k_scale.astype(np.float64)[..., None]
+    V = _torch_decode(w.v_pool) * w.v_scale.astype(np.float64)[:, :, None, :]
+    want = np.array(oracle.brute_force_attention(w.q, K, V, w.block_table, w.q_start, w.q_end,
+                                                 w.kv_len, w.page_size))
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+def check_scale_laws():
+    """Multiplying every V scale by c multiplies every output by c; multiplying every K
+    scale by c is the same as multiplying the softmax scale by c."""
+    w = _fp8_workload(seed=4)
+    base = _oracle_fp8(w)
+    np.testing.assert_allclose(_oracle_fp8(w, v_scale=w.v_scale * 4), 4 * base, rtol=1e-12, atol=1e-14)
+    s = 1 / math.sqrt(w.head_dim)
+    np.testing.assert_allclose(_oracle_fp8(w, k_scale=w.k_scale.astype(np.float64) * 3),
+                               _oracle_fp8(w, softmax_scale=3 * s), rtol=1e-12, atol=1e-14)
+    # a per-token K scale moves only that token's scores: doubling one token's scale
+    # changes the outputs of the rows that see it and of no other row
+    k2 = w.k_scale.copy()
+    r = 1
+    p = int(w.block_table[r][0])
+    k2[p, :, 0] *= 2
+    out = _oracle_fp8(w, k_scale=k2)
+    rows = slice(int(w.q_start[r]), int(w.q_end[r]))
+    others = np.ones(w.q.shape[0], bool)
+    others[rows] = False
+    np.testing.assert_array_equal(out[others], base[others])
+    assert np.abs(out[rows] - base[rows]).max() > 1e-6
+
+
+def check_generator_round_trip():
+    """The generator's codes and scales reproduce its float32 draws to within e4m3fn
+    rounding: half a step of the code's binade (relative 2^-4 for normal values,
+    absolute 2^-10 * scale below the normal range), and the largest |x| of each token
+    maps to +-448 exactly."""
+    w = _fp8_workload(seed=6, q_rows=(2,), kv=(16,), d=32)
+    P, H, ps, D = w.k_pool.shape
+    kf = W._normal_fill(6, W.STREAM_K, P * H * ps * D, False).reshape(P, H, ps, D).astype(np.float64)
+    K, _ = oracle.dequantize_pools(w.k_pool, w.k_scale, w.v_pool, w.v_scale)
+    sc = w.k_scale.astype(np.float64)[..., None]
+    y = np.abs(kf) / sc
+    bound = np.where(y >= 2.0 ** -6, y * 2.0 ** -4, 2.0 ** -10) * sc
+    assert np.all(np.abs(K - kf) <= bound * (1 + 1e-6))
+    assert np.all(np.abs(OF.e4m3fn_to_f64(w.k_pool)).max(axis=3) == 448.0)
+
+
+ALL_CHECKS = [check_closed_forms, check_all_codes_match_torch, check_grid_shape,
+              check_dequantize_axes, check_dequantize_random, check_fp8_attention_brute_force,
+              check_scale_laws, check_generator_round_trip]
+
+
+@pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda c: c.__name__[6:])
+def test_fp8_pin(check):
+    check()
+
+
+def _fails(check) -> bool:
+    try:
+        check()
+    except AssertionError:
+        return True
+    return False
+
+
+def test_fp8_mutants_are_caught(monkeypatch):
+    """Plausible mistakes in the fp8 oracle each fail at least one pin."""
+    real_decode, real_deq = OF.e4m3fn_to_f64, OF.dequantize_pools
+
+    def bias8(codes):
+        c = np.asarray(codes, np.uint8)
+        return real_decode(c) / 2.0
+
+    def no_subnormals(codes):
+        c = np.asarray(codes, np.uint8).astype(np.int64)
+        e, m, s = (c >> 3) & 0xF, c & 7, (c >> 7) & 1
+        mag = np.ldexp(1.0 + m / 8.0, e - 7)
+        return np.where(s == 1, -mag, mag)
+
+    def nan_as_480(codes):
+        out = real_decode(codes)
+        return np.where(np.isnan(out), np.copysign(480.0, out), out)
+
+    def v_with_k_scale(k, ks, v, vs):
+        return real_deq(k, ks, v, ks)
+
+    def v_scales_of_wrong_head(k, ks, v, vs):
+        return real_deq(k, ks, v, np.asarray(vs)[:, ::-1, :])
+
+    mutants = {"exponent bias 8": ("e4m3fn_to_f64", bias8),
+               "subnormals read as normals": ("e4m3fn_to_f64", no_subnormals),
+               "NaN codes read as numbers": ("e4m3fn_to_f64", nan_as_480),
+               "V scaled by K's scales": ("dequantize_pools", v_with_k_scale),
+               "V scales of the wrong head": ("dequantize_pools", v_scales_of_wrong_head)}
+    for name, (attr, fn) in mutants.items():
+        with monkeypatch.context() as mp:
+            mp.setattr(OF, attr, fn)
+            mp.setattr(oracle, attr, fn)
+            assert any(_fails(c) for c in ALL_CHECKS), f"no pin catches mutant: {name}"

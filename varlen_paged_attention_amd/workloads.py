@@ -37,6 +37,21 @@ import numpy as np
 CHUNK = 1 << 22
 STREAM_LENGTHS, STREAM_PERM, STREAM_Q, STREAM_K, STREAM_V = 0, 1, 2, 3, 4
 BF16_NAN = np.uint16(0x7FC0)
+FP8_NAN = np.uint8(0x7F)
+FP8_MAX = 448.0             # largest finite e4m3fn value
+
+
+def quantize_fp8(x: np.ndarray, axis: int):
+    """Per-vector fp8 e4m3fn storage of float32 ``x``: one float32 scale per vector along
+    ``axis`` (its absolute maximum / 448, 1 for an all-zero vector) and the codes of
+    x / scale rounded to nearest even by torch's float8_e4m3fn conversion.  Returns
+    (uint8 codes shaped like x, float32 scales with ``axis`` removed)."""
+    import torch
+    amax = np.abs(x).max(axis=axis)
+    scale = np.where(amax > 0, amax / np.float32(FP8_MAX), np.float32(1.0)).astype(np.float32)
+    y = (x / np.expand_dims(scale, axis)).astype(np.float32)
+    codes = torch.from_numpy(np.ascontiguousarray(y)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return codes, scale
 
 
 def _threads() -> int:
@@ -86,7 +101,7 @@ class Workload:
     num_kv_heads: int
     head_dim: int
     page_size: int
-    dtype: str                      # "bf16" or "f32"
+    dtype: str                      # "bf16", "f32" or "fp8" (bf16 Q/out, fp8 e4m3fn K/V + scales)
     q_start: np.ndarray             # int32 [R]
     q_end: np.ndarray               # int32 [R]
     kv_len: np.ndarray              # int32 [R]
@@ -97,6 +112,8 @@ class Workload:
     v_pool: np.ndarray              # [P, Hkv, D, ps]
     softmax_scale: float = 0.0      # <= 0 means 1/sqrt(head_dim)
     shared_prefix_pages: int = 0    # leading pages shared by every request (0: none)
+    k_scale: Optional[np.ndarray] = None   # fp8 only: float32 [P, Hkv, ps], one per K row
+    v_scale: Optional[np.ndarray] = None   # fp8 only: float32 [P, Hkv, ps], one per V column
     notes: dict = field(default_factory=dict)
 
     @property
@@ -113,7 +130,8 @@ class Workload:
 
     @property
     def elem_bytes(self) -> int:
-        return 2 if self.dtype == "bf16" else 4
+        """Bytes of one stored K or V element."""
+        return {"bf16": 2, "f32": 4, "fp8": 1}[self.dtype]
 
 
 def build(name: str, q_rows: Sequence[int], kv_lens: Sequence[int], *, num_q_heads: int,
@@ -134,7 +152,8 @@ def build(name: str, q_rows: Sequence[int], kv_lens: Sequence[int], *, num_q_hea
     kv = np.asarray(kv_lens, np.int64)
     R = len(kv)
     assert q_rows.shape == (R,)
-    bf16 = dtype == "bf16"
+    fp8 = dtype == "fp8"
+    bf16 = dtype == "bf16" or fp8
     ps = page_size
     npg = (kv + ps - 1) // ps
     sp = shared_prefix_pages
@@ -156,23 +175,36 @@ def build(name: str, q_rows: Sequence[int], kv_lens: Sequence[int], *, num_q_hea
     T = int(q_rows.sum())
     D = head_dim
     q = _normal_fill(seed, STREAM_Q, T * num_q_heads * D, bf16).reshape(T, num_q_heads, D)
-    k = _normal_fill(seed, STREAM_K, P * num_kv_heads * ps * D, bf16).reshape(P, num_kv_heads, ps, D)
-    v = _normal_fill(seed, STREAM_V, P * num_kv_heads * D * ps, bf16).reshape(P, num_kv_heads, D, ps)
+    k_scale = v_scale = None
+    if fp8:
+        kf = _normal_fill(seed, STREAM_K, P * num_kv_heads * ps * D, False).reshape(P, num_kv_heads, ps, D)
+        vf = _normal_fill(seed, STREAM_V, P * num_kv_heads * D * ps, False).reshape(P, num_kv_heads, D, ps)
+        k, k_scale = quantize_fp8(kf, axis=3)
+        v, v_scale = quantize_fp8(vf, axis=2)
+    else:
+        k = _normal_fill(seed, STREAM_K, P * num_kv_heads * ps * D, bf16).reshape(P, num_kv_heads, ps, D)
+        v = _normal_fill(seed, STREAM_V, P * num_kv_heads * D * ps, bf16).reshape(P, num_kv_heads, D, ps)
     if poison_tail:
-        nanv = BF16_NAN if bf16 else np.float32(np.nan)
+        nanv = FP8_NAN if fp8 else (BF16_NAN if bf16 else np.float32(np.nan))
         for r in range(R):
             valid = int(kv[r]) - (int(npg[r]) - 1) * ps
             if int(npg[r]) > 0 and valid < ps:
                 p = bt[r, int(npg[r]) - 1]
                 k[p, :, valid:, :] = nanv
                 v[p, :, :, valid:] = nanv
+                if fp8:
+                    k_scale[p, :, valid:] = np.nan
+                    v_scale[p, :, valid:] = np.nan
         for u in range(P - extra_pages, P):
             k[perm[u]] = nanv
             v[perm[u]] = nanv
+            if fp8:
+                k_scale[perm[u]] = np.nan
+                v_scale[perm[u]] = np.nan
     return Workload(name=name, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, head_dim=D,
                     page_size=ps, dtype=dtype, q_start=qs, q_end=qe, kv_len=kv.astype(np.int32),
                     block_table=bt, num_pages=P, q=q, k_pool=k, v_pool=v, softmax_scale=softmax_scale,
-                    shared_prefix_pages=sp)
+                    shared_prefix_pages=sp, k_scale=k_scale, v_scale=v_scale)
 
 
 def uniform_lengths(seed: int, n: int, lo: int, hi: int) -> np.ndarray:

@@ -28,6 +28,7 @@
  *   q, out   [total_q_rows][num_q_heads][head_dim]
  *   k_pool   [num_pages][num_kv_heads][page_size][head_dim]
  *   v_pool   [num_pages][num_kv_heads][head_dim][page_size]   (V pages are transposed)
+ *   k_scale, v_scale  float32 [num_pages][num_kv_heads][page_size]   (fp8 pools only)
  *   block table  int32 [num_reqs][max_pages_per_req]; only the first
  *                ceil(kv_len[r] / page_size) entries of row r are read.
  *
@@ -65,7 +66,15 @@ typedef enum {
   VA_ERR_WORKSPACE_TOO_SMALL = -5   /* workspace_bytes below what the plan reported */
 } va_status;
 
-typedef enum { VA_DTYPE_BF16 = 0, VA_DTYPE_F32 = 1 } va_dtype;
+/* VA_DTYPE_FP8_E4M3: q and out are bf16; k_pool and v_pool hold OCP fp8 e4m3fn codes
+ * (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; S.1111.111 is NaN) in the
+ * layouts above, and every position of every KV head has one float32 scale for its K row
+ * and one for its V row: element d of that position is decode(code) * scale ("How To
+ * Scale Your Model 笔记(7-8)", section 4: a storage format widened on chip, the arithmetic
+ * in the wider format; "GLM-5.3 推理全链路(八)", on the costs outside the 656-byte
+ * ledger: FP32 scales stored with each token's FP8 data, both read to dequantise).
+ * Such plans run with varlen_attn_run_fp8 and use the split-KV path for every row. */
+typedef enum { VA_DTYPE_BF16 = 0, VA_DTYPE_F32 = 1, VA_DTYPE_FP8_E4M3 = 2 } va_dtype;
 
 enum {
   /* Find requests whose block tables start with the same physical pages and read those
@@ -106,7 +115,8 @@ typedef struct {
   int64_t combine_rows;       /* (row, head) outputs merged by the combine pass */
   int64_t visible_pairs;      /* sum over requests of m*S0 + m(m+1)/2 */
   double flops;               /* 4 * head_dim * num_q_heads * visible_pairs */
-  int64_t logical_kv_bytes;   /* sum kv_len * Hkv * head_dim * 2 (K and V) * elem */
+  int64_t logical_kv_bytes;   /* sum kv_len * Hkv * head_dim * 2 (K and V) * elem;
+                                 fp8: sum kv_len * Hkv * 2 * (head_dim + 4) (codes + scales) */
   int64_t physical_kv_bytes;  /* distinct (page, slot) positions read, same units */
   int64_t q_bytes;            /* query rows read */
   int64_t o_bytes;            /* output rows written */
@@ -147,6 +157,15 @@ va_status varlen_attn_plan(const va_params* params, int32_t num_reqs, const int3
 va_status varlen_attn_run(const va_plan* plan, const void* q, const void* k_pool, const void* v_pool,
                           const int32_t* block_table_dev, void* out, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/* varlen_attn_run for a plan built with dtype VA_DTYPE_FP8_E4M3: k_pool and v_pool hold
+ * the fp8 codes, k_scale and v_scale (device float32 [num_pages][num_kv_heads][page_size],
+ * 16-byte aligned) their scales; q and out are bf16.  events: NULL, or VA_RUN_EVENTS
+ * events recorded as by varlen_attn_run_events.  Any other plan dtype is refused. */
+va_status varlen_attn_run_fp8(const va_plan* plan, const void* q, const void* k_pool, const void* v_pool,
+                              const float* k_scale, const float* v_scale, const int32_t* block_table_dev,
+                              void* out, void* workspace, size_t workspace_bytes, void* stream,
+                              void* const* events);
 
 /* Same as varlen_attn_run, and also records the VA_RUN_EVENTS hipEvent_t handles in
  * `events` on `stream` around its kernel stages, for per-kernel timing:
@@ -194,6 +213,11 @@ va_status varlen_attn_plan_stats(const va_plan* plan, va_plan_stats* out);
 va_status varlen_attn_debug_gather(const va_plan* plan, const void* k_pool, const void* v_pool,
                                    const int32_t* block_table_dev, void* k_out, void* v_out,
                                    void* stream);
+
+/* Widen n fp8 e4m3fn codes (device, 8-byte aligned; n a multiple of 8) to bf16 bit
+ * patterns (device uint16 [n], 16-byte aligned) with the converter the fp8 attention
+ * kernel uses.  Exists to test that conversion against the format's definition. */
+va_status varlen_attn_debug_fp8_to_bf16(const uint8_t* codes, uint16_t* out, int64_t n, void* stream);
 
 /* Introspection for tests: the plan's host work lists as int32 records.
  * which = 0: split-KV items {req, kvh, col0, ncols, k0, k1, slot, flags}

@@ -12,6 +12,11 @@
   head, i.e. 4·H per pair ("ORCA 和 chunked prefill", section 3 cost model;
   "How To Scale Your Model 笔记(7-8)", section 2: about 4·S·H per query head reading S
   sources).
+* Quantised storage: with p_kv = 1 byte (fp8) every stored vector also carries its
+  float32 scale, so each of the 2·L·N_KV vectors of a position takes H·p_kv + s bytes
+  ("GLM-5.3 推理全链路(八)": the indexer cache holds 128 FP8 bytes plus a 4-byte
+  scale per token and layer, 132 bytes; and the scales of the main KV are read along
+  with its data).
 * Logical vs physical KV bytes: logical counts every request's positions; physical
   counts each distinct (page, slot) once ("How To Scale Your Model 笔记(7-8)",
   section 3, shared-prefix example).
@@ -21,8 +26,9 @@ from __future__ import annotations
 import numpy as np
 
 
-def kv_bytes_per_position(layers: int, kv_heads: int, head_dim: int, elem_bytes: int) -> int:
-    return 2 * layers * kv_heads * head_dim * elem_bytes
+def kv_bytes_per_position(layers: int, kv_heads: int, head_dim: int, elem_bytes: int,
+                          scale_bytes: int = 0) -> int:
+    return 2 * layers * kv_heads * (head_dim * elem_bytes + scale_bytes)
 
 
 def visible_pairs(q_rows, kv_len) -> int:
@@ -37,13 +43,14 @@ def attention_flops(q_rows, kv_len, num_q_heads: int, head_dim: int) -> int:
     return 4 * head_dim * num_q_heads * visible_pairs(q_rows, kv_len)
 
 
-def logical_kv_bytes(kv_len, kv_heads: int, head_dim: int, elem_bytes: int, layers: int = 1) -> int:
+def logical_kv_bytes(kv_len, kv_heads: int, head_dim: int, elem_bytes: int, layers: int = 1,
+                     scale_bytes: int = 0) -> int:
     return int(np.sum(np.asarray(kv_len, np.int64))) * kv_bytes_per_position(layers, kv_heads, head_dim,
-                                                                              elem_bytes)
+                                                                              elem_bytes, scale_bytes)
 
 
 def physical_kv_bytes(block_table, kv_len, page_size: int, kv_heads: int, head_dim: int,
-                      elem_bytes: int, layers: int = 1) -> int:
+                      elem_bytes: int, layers: int = 1, scale_bytes: int = 0) -> int:
     """Bytes of the distinct (physical page, slot) positions the requests read."""
     seen = set()
     for r, L in enumerate(np.asarray(kv_len, np.int64)):
@@ -54,4 +61,4 @@ def physical_kv_bytes(block_table, kv_len, page_size: int, kv_heads: int, head_d
             seen.update((int(row[p]), s) for s in range(page_size))
         if tail:
             seen.update((int(row[full]), s) for s in range(tail))
-    return len(seen) * kv_bytes_per_position(layers, kv_heads, head_dim, elem_bytes)
+    return len(seen) * kv_bytes_per_position(layers, kv_heads, head_dim, elem_bytes, scale_bytes)

@@ -1,0 +1,220 @@
+"""GPU parity of the fp8 KV path (e4m3fn codes with per-position float32 scales) through
+the C ABI, against the oracle on the dequantised pools.
+
+Tolerance: max |gpu - oracle| <= 2e-2, as for the bf16 path: the codes widen to bf16
+exactly, the scales are applied in fp32, and the remaining roundings are those of the
+bf16 path (P rounded to bf16 for the P.V product, bf16 output).  The code widening is
+compared bit for bit on all 256 codes, and the page gather of the codes bit for bit."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from varlen_paged_attention_amd import api, workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    torch.cuda.set_device(0)
+    api.lib()
+    yield
+
+
+def _oracle_full(w):
+    K, V = oracle.dequantize_pools(w.k_pool, w.k_scale, w.v_pool, w.v_scale)
+    return oracle.varlen_paged_attention(w.q, K, V, w.block_table, w.q_start, w.q_end, w.kv_len, w.page_size,
+                                         w.softmax_scale or None)
+
+
+def _oracle_rows(w, r, rows):
+    """Oracle rows of request r from its own pages only (dequantising the whole pool of a
+    full-size workload would not fit in memory)."""
+    npg = -(-int(w.kv_len[r]) // w.page_size)
+    pages = np.asarray(w.block_table[r][:npg], np.int64)
+    K, V = oracle.dequantize_pools(w.k_pool[pages], w.k_scale[pages], w.v_pool[pages], w.v_scale[pages])
+    bt = np.arange(npg, dtype=np.int32)[None, :]
+    qs = np.array([w.q_start[r]], np.int32)
+    return oracle.attention_rows(w.q, K, V, bt, qs, np.array([w.q_end[r]], np.int32),
+                                 np.array([w.kv_len[r]], np.int32), w.page_size, 0, rows)
+
+
+def _run(w, flags=0, out_fill=None, **kw):
+    import torch
+    plan = api.plan_for(w, flags=flags, **kw)
+    q, k, v, bt = api.to_device(w)
+    ks, vs = api.scales_to_device(w)
+    out = torch.zeros_like(q) if out_fill is None else torch.full_like(q, out_fill)
+    ws = api.new_workspace(plan)
+    api.varlen_attn_run_fp8(plan, q, k, v, ks, vs, bt, out, ws)
+    torch.cuda.synchronize()
+    return out, plan
+
+
+def _covered_rows(w):
+    rows = np.zeros(w.total_q_rows, bool)
+    for r in range(w.num_reqs):
+        rows[w.q_start[r]:w.q_end[r]] = True
+    return rows
+
+
+def _check_full(w, out, label):
+    got = out.float().cpu().numpy().astype(np.float64)
+    ref = _oracle_full(w)
+    rows = _covered_rows(w)
+    err = np.abs(got[rows] - ref[rows])
+    e = float(err.max()) if err.size else 0.0
+    _say(f"[parity] {label}: max|gpu-oracle| = {e:.3e} (tol {TOL})")
+    assert np.isfinite(got[rows]).all(), f"{label}: non-finite output"
+    assert e <= TOL, f"{label}: max error {e}"
+
+
+def test_fp8_widening_all_codes_bit_exact():
+    """Every code at every byte position of an 8-code group widens to the bf16 value the
+    format defines (NaN codes to a NaN)."""
+    import torch
+    codes = np.concatenate([np.roll(np.arange(256, dtype=np.uint8), s) for s in range(8)])
+    _say("[gpu] fp8 widening of all codes")
+    dev = torch.from_numpy(codes).cuda()
+    out = torch.empty(codes.size, dtype=torch.int16, device="cuda")
+    api.varlen_attn_debug_fp8_to_bf16(dev, out)
+    torch.cuda.synchronize()
+    got_bits = out.cpu().numpy().view(np.uint16)
+    got = oracle.bf16_bits_to_f64(got_bits)
+    want = oracle.e4m3fn_to_f64(codes)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))     # -0 stays -0
+
+
+SMALL = [
+    ("tiny-d64", 1, 1, 0),
+    ("orca-mixed/4", 2, 4, 0),
+    ("decode-heavy/8", 3, 8, 0),
+    ("chunk-mix/8", 4, 8, 0),
+    ("shared-6", 5, 1, api.VA_FLAG_SHARED_PREFIX),
+    ("shared-6 plain", 5, 1, 0),
+]
+
+
+@pytest.mark.parametrize("label,cid,scale,flags", SMALL, ids=[s[0] for s in SMALL])
+def test_fp8_parity_small_elementwise(label, cid, scale, flags):
+    w = W.config(cid, scale=scale, poison_tail=True, dtype="fp8")
+    _say(f"[gpu] fp8 run {label} rows={w.total_q_rows} kv={list(w.kv_len[:4])}...")
+    out, plan = _run(w, flags)
+    _check_full(w, out, "fp8 " + label)
+
+
+def test_fp8_parity_split_len_64():
+    """Many parts per output (every 64-key step its own item) through the combine pass."""
+    w = W.config(4, scale=16, poison_tail=True, dtype="fp8")
+    _say("[gpu] fp8 split_len=64")
+    out, plan = _run(w, split_len=64)
+    assert api.varlen_attn_plan_stats(plan)["combine_rows"] > 0
+    _check_full(w, out, "fp8 chunk-mix/16 split 64")
+
+
+FULL = [("decode-heavy", 3, 0), ("orca-mixed", 2, 0), ("shared-64", 51, api.VA_FLAG_SHARED_PREFIX)]
+
+
+@pytest.mark.parametrize("label,cid,flags", FULL, ids=[f[0] for f in FULL])
+def test_fp8_parity_full_size_sampled(label, cid, flags):
+    w = W.config(cid, dtype="fp8")
+    _say(f"[gpu] fp8 run full {label}: reqs={w.num_reqs} rows={w.total_q_rows} pages={w.num_pages}")
+    out, plan = _run(w, flags)
+    got = out.float().cpu().numpy()
+    rng = np.random.default_rng(200 + cid)
+    R = w.num_reqs
+    reqs = sorted({0, R - 1, int(np.argmax(w.kv_len))} | set(int(x) for x in rng.choice(R, min(R, 6), False)))
+    worst = 0.0
+    for r in reqs:
+        m = int(w.q_end[r] - w.q_start[r])
+        rows = sorted({0, m - 1} | set(int(x) for x in rng.choice(m, min(m, 8), False)))
+        for h, o in _oracle_rows(w, r, rows).items():
+            g = got[int(w.q_start[r]) + np.asarray(rows), h, :]
+            assert np.isfinite(g).all()
+            worst = max(worst, float(np.abs(g - o).max()))
+    _say(f"[parity] fp8 full {label}: sampled max|gpu-oracle| = {worst:.3e}")
+    assert worst <= TOL
+
+
+EDGE = [
+    ("gap+zero-row+kv1", dict(q_rows=[3, 0, 1, 1, 5], kv=[3, 9, 1, 2, 40], hq=4, hkv=4, d=64, ps=16)),
+    ("g16-multi-row-ps256", dict(q_rows=[3, 1], kv=[700, 257], hq=32, hkv=2, d=128, ps=256)),
+    ("mtp-g8-ps32", dict(q_rows=[5, 4, 1], kv=[300, 64, 31], hq=16, hkv=2, d=128, ps=32)),
+    ("long-decode", dict(q_rows=[1, 1], kv=[40000, 77], hq=8, hkv=1, d=128, ps=64)),
+    ("prefill-rows-d64", dict(q_rows=[130, 2], kv=[200, 2], hq=6, hkv=3, d=64, ps=16)),
+]
+
+
+@pytest.mark.parametrize("label,spec", EDGE, ids=[e[0] for e in EDGE])
+def test_fp8_edge_cases(label, spec):
+    w = W.build(label, spec["q_rows"], spec["kv"], num_q_heads=spec["hq"], num_kv_heads=spec["hkv"],
+                head_dim=spec["d"], page_size=spec["ps"], dtype="fp8", seed=19, poison_tail=True, extra_pages=2)
+    w.q_start = w.q_start.copy()
+    w.q_end = w.q_end.copy()
+    w.q_start[1:] += 2
+    w.q_end[1:] += 2
+    w.q = np.concatenate([w.q[:w.q_end[0]], np.zeros((2,) + w.q.shape[1:], w.q.dtype), w.q[w.q_end[0]:]])
+    _say(f"[gpu] fp8 edge {label}")
+    out, plan = _run(w, out_fill=7.0)
+    _check_full(w, out, "fp8 " + label)
+    gap = out[w.q_end[0]:w.q_start[1]].float().cpu().numpy()
+    assert (gap == 7.0).all(), "rows outside every request were written"
+
+
+def test_fp8_deterministic_and_gather():
+    import torch
+    w = W.config(3, scale=8, dtype="fp8")
+    _say("[gpu] fp8 determinism + gather")
+    a, plan = _run(w)
+    b, _ = _run(w)
+    assert np.array_equal(a.view(torch.int16).cpu().numpy(), b.view(torch.int16).cpu().numpy())
+    q, k, v, bt = api.to_device(w)
+    tot = int(w.kv_len.sum())
+    ko = torch.empty((tot, w.num_kv_heads, w.head_dim), dtype=torch.uint8, device="cuda")
+    vo = torch.empty_like(ko)
+    api.varlen_attn_debug_gather(plan, k, v, bt, ko, vo)
+    torch.cuda.synchronize()
+    ks, vs = [], []
+    for r in range(w.num_reqs):
+        j = np.arange(int(w.kv_len[r]))
+        pages, slots = w.block_table[r][j // w.page_size], j % w.page_size
+        ks.append(w.k_pool[pages, :, slots, :])
+        vs.append(w.v_pool[pages, :, :, slots])
+    assert np.array_equal(ko.cpu().numpy(), np.concatenate(ks))
+    assert np.array_equal(vo.cpu().numpy(), np.concatenate(vs))
+
+
+def test_fp8_run_errors():
+    import torch
+    w = W.config(3, scale=64, dtype="fp8")
+    plan = api.plan_for(w)
+    q, k, v, bt = api.to_device(w)
+    ks, vs = api.scales_to_device(w)
+    out = torch.zeros_like(q)
+    ws = api.new_workspace(plan)
+    L = api.lib()
+    P = lambda t: None if t is None else t.data_ptr()          # noqa: E731
+    base = [plan.handle, P(q), P(k), P(v), P(ks), P(vs), P(bt), P(out), P(ws), ws.numel(), None, None]
+    no_scale = list(base)
+    no_scale[4] = None
+    assert L.varlen_attn_run_fp8(*no_scale) == api.VA_ERR_INVALID_ARG
+    misaligned = list(base)
+    misaligned[5] = P(vs) + 4
+    assert L.varlen_attn_run_fp8(*misaligned) == api.VA_ERR_INVALID_ARG
+    assert "aligned" in L.varlen_attn_last_error().decode()
+    assert L.varlen_attn_run_fp8(*base) == api.VA_OK
+    torch.cuda.synchronize()

@@ -111,7 +111,7 @@ def check_coverage(w, plan):
     direct = {}
     for it in items:
         req, kvh, col0, ncols, k0, k1, slot, flags = (int(x) for x in it)
-        assert 1 <= ncols <= 16 and k0 < k1 and k0 % 8 == 0
+        assert 1 <= ncols <= 16 and k0 < k1 and k0 % 16 == 0     # 16-key runs stay in one page
         for c in cols[col0:col0 + ncols]:
             row, head, limit, pbase = (int(x) for x in c)
             r = req_of_row[row]
@@ -185,6 +185,9 @@ CASES = [
     ("orca-full", lambda: W.config(2), 0),
     ("chunk-like", lambda: W.build("cl", [2048, 1, 1, 1, 1], [32768, 600, 5000, 16384, 70], num_q_heads=8,
                                    num_kv_heads=1, head_dim=128, page_size=64, seed=5), 0),
+    ("orca-small-fp8", lambda: W.config(2, scale=16, dtype="fp8"), 0),
+    ("decode-fp8", lambda: W.config(3, scale=16, dtype="fp8"), 0),
+    ("shared-fp8", lambda: W.config(5, dtype="fp8"), api.VA_FLAG_SHARED_PREFIX),
 ]
 
 
@@ -201,9 +204,15 @@ def test_plan_counters_match_oracle(name, make, flags):
     m = w.q_end - w.q_start
     assert st["visible_pairs"] == oracle.visible_pairs(m, w.kv_len)
     assert st["flops"] == oracle.attention_flops(m, w.kv_len, w.num_q_heads, w.head_dim)
-    assert st["logical_kv_bytes"] == oracle.logical_kv_bytes(w.kv_len, w.num_kv_heads, w.head_dim, w.elem_bytes)
+    assert st["logical_kv_bytes"] == oracle.logical_kv_bytes(w.kv_len, w.num_kv_heads, w.head_dim, w.elem_bytes,
+                                                             scale_bytes=w.scale_bytes)
     assert st["physical_kv_bytes"] == oracle.physical_kv_bytes(w.block_table, w.kv_len, w.page_size,
-                                                               w.num_kv_heads, w.head_dim, w.elem_bytes)
+                                                               w.num_kv_heads, w.head_dim, w.elem_bytes,
+                                                               scale_bytes=w.scale_bytes)
+    if w.dtype == "fp8":
+        # every row runs on the split-KV kernel: no MFMA prefill or shared-prefix tiles
+        assert st["prefill_tiles"] == 0 and st["shared_tiles"] == 0 and st["prefill_flops"] == 0
+        assert st["q_bytes"] == int(m.sum()) * w.num_q_heads * w.head_dim * 2
 
 
 def test_shared_prefix_groups_found():
@@ -244,4 +253,38 @@ def test_append_argument_errors():
     assert L.varlen_attn_append_kv(p, 0, None, None, None, None, None, None, None) == api.VA_OK
     assert L.varlen_attn_append_kv(p, 3, None, None, None, None, None, None, None) == api.VA_ERR_INVALID_ARG
     p.head_dim = 96
+    assert L.varlen_attn_append_kv(p, 3, None, None, None, None, None, None, None) == api.VA_ERR_UNSUPPORTED
+
+
+def test_fp8_run_entry_points_check_the_plan_dtype():
+    """An fp8 plan is refused by varlen_attn_run / run_events and a bf16 plan by
+    varlen_attn_run_fp8, before any device work."""
+    L = api.lib()
+    wf = W.config(3, scale=64, dtype="fp8")
+    pf = _plan(wf)
+    assert L.varlen_attn_run(pf.handle, None, None, None, None, None, None, 0, None) == api.VA_ERR_INVALID_ARG
+    assert "varlen_attn_run_fp8" in L.varlen_attn_last_error().decode()
+    ev = (ctypes.c_void_p * api.VA_RUN_EVENTS)(1, 1, 1, 1)
+    assert L.varlen_attn_run_events(pf.handle, None, None, None, None, None, None, 0, None, ev) == \
+        api.VA_ERR_INVALID_ARG
+    pb = _plan(W.config(3, scale=64))
+    assert L.varlen_attn_run_fp8(pb.handle, None, None, None, None, None, None, None, None, 0, None, None) == \
+        api.VA_ERR_INVALID_ARG
+    assert "VA_DTYPE_FP8_E4M3" in L.varlen_attn_last_error().decode()
+    # host-only fp8 plan: refused for lack of a device buffer
+    assert L.varlen_attn_run_fp8(pf.handle, None, None, None, None, None, None, None, None, 0, None, None) == \
+        api.VA_ERR_INVALID_ARG
+
+
+def test_fp8_debug_convert_argument_errors():
+    L = api.lib()
+    assert L.varlen_attn_debug_fp8_to_bf16(None, None, 12, None) == api.VA_ERR_INVALID_ARG
+    assert L.varlen_attn_debug_fp8_to_bf16(None, None, -8, None) == api.VA_ERR_INVALID_ARG
+    assert L.varlen_attn_debug_fp8_to_bf16(None, None, 0, None) == api.VA_OK
+    assert L.varlen_attn_debug_fp8_to_bf16(None, None, 8, None) == api.VA_ERR_INVALID_ARG
+
+
+def test_fp8_append_is_refused():
+    L = api.lib()
+    p = api.VaParams(0, 2, 64, 16, 8, 0, api.VA_DTYPE_FP8_E4M3, 0.0, 0, 0, 0)
     assert L.varlen_attn_append_kv(p, 3, None, None, None, None, None, None, None) == api.VA_ERR_UNSUPPORTED

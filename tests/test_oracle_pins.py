@@ -298,6 +298,17 @@ def test_kv_bytes_closed_forms():
     assert oracle.kv_bytes_per_position(32, 32, 128, 2) == 512 * 1024
 
 
+def test_fp8_scale_bytes_closed_forms():
+    """An fp8 vector of 128 elements with its float32 scale is 132 bytes, and 21 layers of
+    such one-vector-per-token entries over 1M positions are about 2.9 GB ("GLM-5.3
+    推理全链路(八)", the indexer-cache figures)."""
+    per_token_layer = oracle.kv_bytes_per_position(1, 1, 128, 1, 4) // 2     # K only
+    assert per_token_layer == 132
+    assert round(21 * per_token_layer * 1048576 / 1e9, 1) == 2.9
+    # K and V of 8 KV heads x 128 in fp8 with scales: 2 * 8 * 132 bytes per position
+    assert oracle.kv_bytes_per_position(1, 8, 128, 1, 4) == 2112
+
+
 def test_shared_prefix_bytes():
     """Six requests sharing 4096 positions + 1024 private each, 32 layers x 8 KV heads x
     H=128 bf16: 3.75 GiB read naively vs 1.25 GiB stored ("How To Scale Your Model

@@ -15,13 +15,15 @@ import numpy as np
 
 VA_OK, VA_ERR_INVALID_ARG, VA_ERR_UNSUPPORTED, VA_ERR_OUT_OF_MEMORY, VA_ERR_HIP, VA_ERR_WORKSPACE_TOO_SMALL = \
     0, -1, -2, -3, -4, -5
-VA_DTYPE_BF16, VA_DTYPE_F32 = 0, 1
+VA_DTYPE_BF16, VA_DTYPE_F32, VA_DTYPE_FP8_E4M3 = 0, 1, 2
+DTYPE_CODES = {"bf16": VA_DTYPE_BF16, "f32": VA_DTYPE_F32, "fp8": VA_DTYPE_FP8_E4M3}
 VA_FLAG_SHARED_PREFIX, VA_FLAG_NO_PREFILL_KERNEL, VA_FLAG_HOST_ONLY = 1, 2, 4
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvarlen_attn.so")
 EXPORTED = ["varlen_attn_plan", "varlen_attn_run", "varlen_attn_run_events", "varlen_attn_plan_stats", "varlen_attn_plan_export",
             "varlen_attn_debug_gather", "varlen_attn_plan_destroy", "varlen_attn_status_string",
-            "varlen_attn_last_error", "varlen_attn_append_kv", "varlen_attn_plan_slots"]
+            "varlen_attn_last_error", "varlen_attn_append_kv", "varlen_attn_plan_slots", "varlen_attn_run_fp8",
+            "varlen_attn_debug_fp8_to_bf16"]
 
 
 class VaParams(ctypes.Structure):
@@ -76,6 +78,10 @@ def lib():
         L.varlen_attn_run.restype = ctypes.c_int
         L.varlen_attn_run_events.argtypes = [P, P, P, P, P, P, P, ctypes.c_size_t, P, ctypes.POINTER(P)]
         L.varlen_attn_run_events.restype = ctypes.c_int
+        L.varlen_attn_run_fp8.argtypes = [P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P, ctypes.POINTER(P)]
+        L.varlen_attn_run_fp8.restype = ctypes.c_int
+        L.varlen_attn_debug_fp8_to_bf16.argtypes = [P, P, ctypes.c_int64, P]
+        L.varlen_attn_debug_fp8_to_bf16.restype = ctypes.c_int
         L.varlen_attn_plan_stats.argtypes = [P, ctypes.POINTER(VaPlanStats)]
         L.varlen_attn_plan_stats.restype = ctypes.c_int
         L.varlen_attn_plan_export.argtypes = [P, ctypes.c_int32, ctypes.POINTER(i32p),
@@ -135,8 +141,7 @@ def varlen_attn_plan(*, num_q_heads: int, num_kv_heads: int, head_dim: int, page
     if bt.ndim != 2 or not (len(qs) == len(qe) == len(kv) == bt.shape[0]):
         raise ValueError("q_start/q_end/kv_len must be [R] and block_table [R, max_pages]")
     p = VaParams(num_q_heads, num_kv_heads, head_dim, page_size, num_pages, bt.shape[1],
-                 VA_DTYPE_BF16 if dtype == "bf16" else VA_DTYPE_F32, softmax_scale, flags,
-                 prefill_min_rows, split_len)
+                 DTYPE_CODES[dtype], softmax_scale, flags, prefill_min_rows, split_len)
     h = ctypes.c_void_p()
     ws = ctypes.c_size_t()
     _check(lib().varlen_attn_plan(ctypes.byref(p), len(kv), _ptr32(qs), _ptr32(qe), _ptr32(kv), _ptr32(bt),
@@ -189,8 +194,15 @@ def _stream_ptr(stream):
 
 
 def _elem_dtype(plan: Plan):
+    """torch dtype of q and out."""
     import torch
-    return torch.bfloat16 if plan.params.dtype == VA_DTYPE_BF16 else torch.float32
+    return torch.float32 if plan.params.dtype == VA_DTYPE_F32 else torch.bfloat16
+
+
+def _pool_dtype(plan: Plan):
+    """torch dtype of the K/V pools (fp8 codes travel as uint8)."""
+    import torch
+    return torch.uint8 if plan.params.dtype == VA_DTYPE_FP8_E4M3 else _elem_dtype(plan)
 
 
 def varlen_attn_run(plan: Plan, q, k_pool, v_pool, block_table_dev, out, workspace=None, stream=None) -> None:
@@ -228,9 +240,46 @@ def varlen_attn_run_events(plan: Plan, q, k_pool, v_pool, block_table_dev, out, 
                                         ctypes.c_void_p(s.cuda_stream), arr))
 
 
+def varlen_attn_run_fp8(plan: Plan, q, k_pool, v_pool, k_scale, v_scale, block_table_dev, out, workspace=None,
+                        stream=None, events=None) -> None:
+    """Run an fp8 plan: k_pool/v_pool uint8 e4m3fn codes, k_scale/v_scale float32
+    [num_pages, Hkv, page_size], q/out bf16.  ``events``: None or VA_RUN_EVENTS
+    torch.cuda.Event(enable_timing=True) objects."""
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    arr = None
+    if events is not None:
+        if len(events) != VA_RUN_EVENTS:
+            raise ValueError(f"need {VA_RUN_EVENTS} events")
+        for ev in events:
+            if ev.cuda_event == 0:
+                ev.record(s)
+        arr = (ctypes.c_void_p * VA_RUN_EVENTS)(*[ev.cuda_event for ev in events])
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().varlen_attn_run_fp8(plan.handle, _dev_ptr(q, "q", torch.bfloat16),
+                                     _dev_ptr(k_pool, "k_pool", torch.uint8), _dev_ptr(v_pool, "v_pool", torch.uint8),
+                                     _dev_ptr(k_scale, "k_scale", torch.float32),
+                                     _dev_ptr(v_scale, "v_scale", torch.float32),
+                                     _dev_ptr(block_table_dev, "block_table", torch.int32),
+                                     _dev_ptr(out, "out", torch.bfloat16), _dev_ptr(workspace, "workspace"), ws_bytes,
+                                     ctypes.c_void_p(s.cuda_stream), arr))
+
+
+def varlen_attn_debug_fp8_to_bf16(codes, out, stream=None) -> None:
+    """Widen uint8 e4m3fn codes (GPU tensor, numel % 8 == 0) into ``out`` (bf16 or int16
+    GPU tensor of the same numel) with the attention kernel's converter."""
+    import torch
+    if out.numel() != codes.numel():
+        raise ValueError("out must have as many elements as codes")
+    if out.element_size() != 2:
+        raise ValueError("out must hold 2-byte elements")
+    _check(lib().varlen_attn_debug_fp8_to_bf16(_dev_ptr(codes, "codes", torch.uint8), _dev_ptr(out, "out"),
+                                               codes.numel(), _stream_ptr(stream)))
+
+
 def varlen_attn_debug_gather(plan: Plan, k_pool, v_pool, block_table_dev, k_out, v_out, stream=None) -> None:
     import torch
-    dt = _elem_dtype(plan)
+    dt = _pool_dtype(plan)
     _check(lib().varlen_attn_debug_gather(plan.handle, _dev_ptr(k_pool, "k_pool", dt), _dev_ptr(v_pool, "v_pool", dt),
                                           _dev_ptr(block_table_dev, "block_table", torch.int32),
                                           _dev_ptr(k_out, "k_out", dt), _dev_ptr(v_out, "v_out", dt),
@@ -250,9 +299,8 @@ def varlen_attn_append_kv(*, num_kv_heads: int, head_dim: int, page_size: int, n
     """Write k_new/v_new ([T, Hkv, D] GPU tensors) into the pools at out_cache_loc (int64 [T] GPU
     tensor); bad_loc_count: optional int32 [1] GPU tensor counting out-of-range entries."""
     import torch
-    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
-    p = VaParams(0, num_kv_heads, head_dim, page_size, num_pages, 0,
-                 VA_DTYPE_BF16 if dtype == "bf16" else VA_DTYPE_F32, 0.0, 0, 0, 0)
+    dt = {"bf16": torch.bfloat16, "f32": torch.float32, "fp8": torch.uint8}[dtype]
+    p = VaParams(0, num_kv_heads, head_dim, page_size, num_pages, 0, DTYPE_CODES[dtype], 0.0, 0, 0, 0)
     T = int(out_cache_loc.numel())
     for name, t in (("k_new", k_new), ("v_new", v_new)):
         if tuple(t.shape) != (T, num_kv_heads, head_dim):
@@ -281,6 +329,13 @@ def to_device(w, device="cuda"):
     return conv(w.q), conv(w.k_pool), conv(w.v_pool), torch.from_numpy(_i32(w.block_table)).to(device)
 
 
+def scales_to_device(w, device="cuda"):
+    """An fp8 workload's (k_scale, v_scale) as float32 GPU tensors."""
+    import torch
+    return (torch.from_numpy(np.ascontiguousarray(w.k_scale, np.float32)).to(device),
+            torch.from_numpy(np.ascontiguousarray(w.v_scale, np.float32)).to(device))
+
+
 def run_workload(w, flags: int = 0, plan: Optional[Plan] = None, device="cuda", **kw):
     """Plan + run one workload; returns (out tensor, plan)."""
     import torch
@@ -288,7 +343,11 @@ def run_workload(w, flags: int = 0, plan: Optional[Plan] = None, device="cuda", 
     q, k, v, bt = to_device(w, device)
     out = torch.zeros_like(q)
     ws = new_workspace(plan, device)
-    varlen_attn_run(plan, q, k, v, bt, out, ws)
+    if plan.params.dtype == VA_DTYPE_FP8_E4M3:
+        ks, vs = scales_to_device(w, device)
+        varlen_attn_run_fp8(plan, q, k, v, ks, vs, bt, out, ws)
+    else:
+        varlen_attn_run(plan, q, k, v, bt, out, ws)
     torch.cuda.synchronize()
     return out, plan
 
@@ -298,19 +357,28 @@ class RunCall:
     per-call ctypes conversion would cost more than the GPU work (same checks as
     ``varlen_attn_run`` at construction)."""
 
-    def __init__(self, plan: Plan, q, k_pool, v_pool, block_table_dev, out, workspace=None, stream=None):
+    def __init__(self, plan: Plan, q, k_pool, v_pool, block_table_dev, out, workspace=None, stream=None,
+                 k_scale=None, v_scale=None):
         import torch
-        dt = _elem_dtype(plan)
+        dt, pdt = _elem_dtype(plan), _pool_dtype(plan)
+        self._fp8 = plan.params.dtype == VA_DTYPE_FP8_E4M3
         self._s = torch.cuda.current_stream() if stream is None else stream
-        self._args = (plan.handle, _dev_ptr(q, "q", dt), _dev_ptr(k_pool, "k_pool", dt),
-                      _dev_ptr(v_pool, "v_pool", dt), _dev_ptr(block_table_dev, "block_table", torch.int32),
+        scales = ()
+        if self._fp8:
+            scales = (_dev_ptr(k_scale, "k_scale", torch.float32), _dev_ptr(v_scale, "v_scale", torch.float32))
+        self._args = (plan.handle, _dev_ptr(q, "q", dt), _dev_ptr(k_pool, "k_pool", pdt),
+                      _dev_ptr(v_pool, "v_pool", pdt)) + scales + (
+                      _dev_ptr(block_table_dev, "block_table", torch.int32),
                       _dev_ptr(out, "out", dt), _dev_ptr(workspace, "workspace"),
                       0 if workspace is None else workspace.numel() * workspace.element_size(),
                       ctypes.c_void_p(self._s.cuda_stream))
-        self._keep = (plan, q, k_pool, v_pool, block_table_dev, out, workspace)
+        self._keep = (plan, q, k_pool, v_pool, block_table_dev, out, workspace, k_scale, v_scale)
 
     def __call__(self) -> None:
-        _check(lib().varlen_attn_run(*self._args))
+        if self._fp8:
+            _check(lib().varlen_attn_run_fp8(*self._args, None))
+        else:
+            _check(lib().varlen_attn_run(*self._args))
 
     def with_events(self, events):
         """A callable that runs with ``varlen_attn_run_events`` and these VA_RUN_EVENTS
@@ -323,8 +391,9 @@ class RunCall:
         arr = (ctypes.c_void_p * VA_RUN_EVENTS)(*[ev.cuda_event for ev in events])
         args = self._args + (arr,)
         L = lib()
+        fn = L.varlen_attn_run_fp8 if self._fp8 else L.varlen_attn_run_events
 
         def call():
-            _check(L.varlen_attn_run_events(*args))
+            _check(fn(*args))
         call._keep = (events, arr)
         return call

@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libvarlen_attn.so")
-SOURCES = ["plan.cpp", "kernels.hip", "append.hip"]
+SOURCES = ["plan.cpp", "kernels.hip", "append.hip", "kv_fp8.hip"]
 
 
 def hipcc() -> str:

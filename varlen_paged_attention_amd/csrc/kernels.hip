@@ -19,68 +19,10 @@
 #include <string>
 #include <vector>
 
+#include "device_common.h"
 #include "va_internal.h"
 
 namespace va {
-
-typedef __bf16 bf16;
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kNegBig = -1e30f;   // running-max start: finite, so fully masked steps keep alpha = 1
-
-// ---------------------------------------------------------------- page addressing --
-// Pools: K [page][kv_head][slot][d], V [page][kv_head][d][slot] (transposed page).
-// Logical position j of a request is slot j % page_size of page block_table[j / page_size].
-struct Paged {
-  int Hkv, ps_shift, D;
-  __device__ __forceinline__ int ps() const { return 1 << ps_shift; }
-  __device__ __forceinline__ int page_of(const int32_t* bt_row, int pos) const { return bt_row[pos >> ps_shift]; }
-  __device__ __forceinline__ int slot_of(int pos) const { return pos & ((1 << ps_shift) - 1); }
-  // element offset of K[page, kvh, slot, 0]
-  __device__ __forceinline__ size_t k_row(int page, int kvh, int slot) const {
-    return ((size_t(page) * Hkv + kvh) * (size_t(1) << ps_shift) + slot) * D;
-  }
-  // element offset of V[page, kvh, d, slot]
-  __device__ __forceinline__ size_t v_elem(int page, int kvh, int d, int slot) const {
-    return ((size_t(page) * Hkv + kvh) * D + d) * (size_t(1) << ps_shift) + slot;
-  }
-};
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-__device__ __forceinline__ f32x4 mfma16_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mfma16_f32(float a, float b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-// Write one column's partial result.  acc[db][r] holds d = 16*db + 4*grp + r.
-template <int D>
-__device__ __forceinline__ void store_partial(float* ws_ml, float* ws_acc, int slot, int grp, float m, float l,
-                                              const f32x4* acc) {
-  if (grp == 0) {
-    ws_ml[2 * size_t(slot)] = m;
-    ws_ml[2 * size_t(slot) + 1] = l;
-  }
-  float* wa = ws_acc + size_t(slot) * D + 4 * grp;
-#pragma unroll
-  for (int db = 0; db < D / 16; ++db) *reinterpret_cast<f32x4*>(wa + 16 * db) = acc[db];
-}
-
-// Write one column's finished output row (an item that covers the column's whole kv
-// range): acc / l, rounded to the output type.
-template <int D, typename OutT>
-__device__ __forceinline__ void store_output(OutT* out, size_t row_off, int grp, float l, const f32x4* acc) {
-  const float inv = 1.f / l;
-  OutT* op = out + row_off + 4 * grp;
-#pragma unroll
-  for (int db = 0; db < D / 16; ++db)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) op[16 * db + r] = OutT(acc[db][r] * inv);
-}
 
 // ----------------------------------------------------------------- split-KV, bf16 --
 // MFMA v_mfma_f32_16x16x32_bf16 operand layout: lane l holds row/column (l % 16) and
@@ -839,7 +781,7 @@ va_status upload_plan(va_plan* plan) {
   plan->dev_bytes = total;
   e = hipMemcpy(plan->dev, host.data(), total, hipMemcpyHostToDevice);
   if (e != hipSuccess) {
-    hipFree(plan->dev);
+    (void)hipFree(plan->dev);
     plan->dev = nullptr;
     return hip_fail("hipMemcpy of the plan buffer", e);
   }
@@ -854,7 +796,7 @@ va_status upload_plan(va_plan* plan) {
 }
 
 void free_plan_device(va_plan* plan) {
-  if (plan->dev) hipFree(plan->dev);
+  if (plan->dev) (void)hipFree(plan->dev);
   plan->dev = nullptr;
 }
 
@@ -868,15 +810,23 @@ static int log2i(int x) {
 
 using namespace va;
 
+// k_scale / v_scale: the scale pools of an fp8 plan (NULL otherwise).
 static va_status run_impl(const va_plan* plan, const void* q, const void* k_pool, const void* v_pool,
-                          const int32_t* block_table_dev, void* out, void* workspace, size_t workspace_bytes,
-                          void* stream, void* const* events) {
+                          const float* k_scale, const float* v_scale, const int32_t* block_table_dev, void* out,
+                          void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
   if (!plan) return fail(VA_ERR_INVALID_ARG, "plan is NULL");
   if (!plan->dev) return fail(VA_ERR_INVALID_ARG, "plan has no device buffer (built with VA_FLAG_HOST_ONLY)");
+  const bool fp8 = plan->p.dtype == VA_DTYPE_FP8_E4M3;
   const bool any = !plan->items.empty() || !plan->tiles.empty() || !plan->gtiles.empty();
   if (!any && !events) return VA_OK;
   if (any && (!q || !k_pool || !v_pool || !block_table_dev || !out))
     return fail(VA_ERR_INVALID_ARG, "q, k_pool, v_pool, block_table_dev and out must be non-NULL");
+  if (any && fp8) {
+    if (!k_scale || !v_scale) return fail(VA_ERR_INVALID_ARG, "k_scale and v_scale must be non-NULL");
+    if ((reinterpret_cast<uintptr_t>(k_scale) | reinterpret_cast<uintptr_t>(v_scale) |
+         reinterpret_cast<uintptr_t>(k_pool) | reinterpret_cast<uintptr_t>(v_pool)) & 15)
+      return fail(VA_ERR_INVALID_ARG, "fp8 pools and scale pools must be 16-byte aligned");
+  }
   if (workspace_bytes < plan->ws_bytes)
     return fail(VA_ERR_WORKSPACE_TOO_SMALL, "workspace has " + std::to_string(workspace_bytes) + " bytes, plan needs " +
                                                 std::to_string(plan->ws_bytes));
@@ -897,7 +847,7 @@ static va_status run_impl(const va_plan* plan, const void* q, const void* k_pool
   const int nitems = int(plan->items.size());
   const int ncomb = int(plan->combine.size());
   const int bt_stride = p.max_pages_per_req;
-  const bool bf = p.dtype == VA_DTYPE_BF16;
+  const bool bf = p.dtype != VA_DTYPE_F32;     // bf16 Q and output (bf16 and fp8 plans)
 
   (void)hipGetLastError();   // clear a stale error left by earlier, unrelated calls
   auto mark = [&](int i) -> hipError_t {
@@ -929,7 +879,11 @@ static va_status run_impl(const va_plan* plan, const void* q, const void* k_pool
   if ((e = mark(1)) != hipSuccess) return hip_fail("hipEventRecord", e);
   if (nitems) {
     const dim3 grid((nitems + kSplitWaves - 1) / kSplitWaves), block(64 * kSplitWaves);
-    if (bf) {
+    e = hipSuccess;
+    if (fp8) {
+      e = launch_split_kv_fp8(D, nitems, s, plan->d_items, plan->d_cols, q, k_pool, v_pool, k_scale, v_scale,
+                          block_table_dev, bt_stride, ws_ml, ws_acc, out, p.num_q_heads, pg, scale_log2);
+    } else if (bf) {
       auto* qq = static_cast<const bf16*>(q);
       auto* kk = static_cast<const bf16*>(k_pool);
       auto* vv = static_cast<const bf16*>(v_pool);
@@ -954,7 +908,7 @@ static va_status run_impl(const va_plan* plan, const void* q, const void* k_pool
                                                        block_table_dev, bt_stride, ws_ml, ws_acc,
                                                        static_cast<float*>(out), p.num_q_heads, pg, scale_log2);
     }
-    e = hipGetLastError();
+    if (e == hipSuccess) e = hipGetLastError();
     if (e != hipSuccess) return hip_fail("split-KV kernel launch", e);
   }
   if ((e = mark(2)) != hipSuccess) return hip_fail("hipEventRecord", e);
@@ -983,7 +937,23 @@ static va_status run_impl(const va_plan* plan, const void* q, const void* k_pool
 extern "C" va_status varlen_attn_run(const va_plan* plan, const void* q, const void* k_pool, const void* v_pool,
                                      const int32_t* block_table_dev, void* out, void* workspace,
                                      size_t workspace_bytes, void* stream) {
-  return run_impl(plan, q, k_pool, v_pool, block_table_dev, out, workspace, workspace_bytes, stream, nullptr);
+  if (plan && plan->p.dtype == VA_DTYPE_FP8_E4M3)
+    return fail(VA_ERR_INVALID_ARG, "an fp8 plan runs with varlen_attn_run_fp8 (it needs the scale pools)");
+  return run_impl(plan, q, k_pool, v_pool, nullptr, nullptr, block_table_dev, out, workspace, workspace_bytes, stream,
+                  nullptr);
+}
+
+extern "C" va_status varlen_attn_run_fp8(const va_plan* plan, const void* q, const void* k_pool, const void* v_pool,
+                                         const float* k_scale, const float* v_scale,
+                                         const int32_t* block_table_dev, void* out, void* workspace,
+                                         size_t workspace_bytes, void* stream, void* const* events) {
+  if (plan && plan->p.dtype != VA_DTYPE_FP8_E4M3)
+    return fail(VA_ERR_INVALID_ARG, "varlen_attn_run_fp8 needs a plan built with dtype VA_DTYPE_FP8_E4M3");
+  if (events)
+    for (int i = 0; i < VA_RUN_EVENTS; ++i)
+      if (!events[i]) return fail(VA_ERR_INVALID_ARG, "events[" + std::to_string(i) + "] is NULL");
+  return run_impl(plan, q, k_pool, v_pool, k_scale, v_scale, block_table_dev, out, workspace, workspace_bytes, stream,
+                  events);
 }
 
 extern "C" va_status varlen_attn_run_events(const va_plan* plan, const void* q, const void* k_pool,
@@ -993,7 +963,10 @@ extern "C" va_status varlen_attn_run_events(const va_plan* plan, const void* q, 
   if (!events) return fail(VA_ERR_INVALID_ARG, "events is NULL");
   for (int i = 0; i < VA_RUN_EVENTS; ++i)
     if (!events[i]) return fail(VA_ERR_INVALID_ARG, "events[" + std::to_string(i) + "] is NULL");
-  return run_impl(plan, q, k_pool, v_pool, block_table_dev, out, workspace, workspace_bytes, stream, events);
+  if (plan && plan->p.dtype == VA_DTYPE_FP8_E4M3)
+    return fail(VA_ERR_INVALID_ARG, "an fp8 plan runs with varlen_attn_run_fp8 (it needs the scale pools)");
+  return run_impl(plan, q, k_pool, v_pool, nullptr, nullptr, block_table_dev, out, workspace, workspace_bytes, stream,
+                  events);
 }
 
 extern "C" va_status varlen_attn_debug_gather(const va_plan* plan, const void* k_pool, const void* v_pool,
@@ -1010,7 +983,12 @@ extern "C" va_status varlen_attn_debug_gather(const va_plan* plan, const void* k
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid(unsigned((total + 255) / 256)), block(256);
   (void)hipGetLastError();
-  if (p.dtype == VA_DTYPE_BF16)
+  if (p.dtype == VA_DTYPE_FP8_E4M3)
+    gather_kernel<uint8_t><<<grid, block, 0, s>>>(plan->d_kv_offset, plan->num_reqs, total, block_table_dev,
+                                                  p.max_pages_per_req, static_cast<const uint8_t*>(k_pool),
+                                                  static_cast<const uint8_t*>(v_pool), static_cast<uint8_t*>(k_out),
+                                                  static_cast<uint8_t*>(v_out), pg);
+  else if (p.dtype == VA_DTYPE_BF16)
     gather_kernel<bf16><<<grid, block, 0, s>>>(plan->d_kv_offset, plan->num_reqs, total, block_table_dev,
                                                p.max_pages_per_req, static_cast<const bf16*>(k_pool),
                                                static_cast<const bf16*>(v_pool), static_cast<bf16*>(k_out),

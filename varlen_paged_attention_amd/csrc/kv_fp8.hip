@@ -1,0 +1,255 @@
+// Split-KV attention over fp8 KV pools (gfx950).
+//
+// K and V are stored as OCP fp8 e4m3fn codes in the same page layouts as the bf16 pools
+// (K [page][kv_head][slot][d], V [page][kv_head][d][slot]) plus one float32 scale per
+// (page, kv_head, slot) for K and one for V: the stored value of a position's element d
+// is code * scale.  The codes are widened to bf16 on chip (exactly: every e4m3fn value is
+// a bf16 value) and the products run on the bf16 MFMA with fp32 accumulation, so the
+// fp8 storage halves the bytes read and leaves the arithmetic as in the bf16 path.
+// The scales are applied in fp32 outside the MFMAs: a K scale multiplies its key's scores
+// before the softmax, a V scale multiplies its key's probability before P is rounded to
+// bf16 for the P.V product (the row sum uses the unscaled probability).
+#include <hip/hip_runtime.h>
+
+#include <string>
+
+#include "device_common.h"
+#include "va_internal.h"
+
+namespace va {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Eight fp8 e4m3fn codes (bytes 0..3 of w0, then of w1, low byte first) -> bf16x8 with
+// the hardware converter at scale 1 (exact).
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// One wavefront runs item `idx` (same item / column records and partial layout as the
+// bf16 split-KV kernel).
+//
+// Lane (n = lane % 16, grp = lane / 16).  The head dimension is split into four
+// contiguous quarters, one per lane group: MFMA chunk kc of lane group grp contracts
+// d = (D/4)*grp + 8*kc .. +7, for Q and K alike, so a lane's K bytes of one row are one
+// contiguous run of D/4 bytes.  Key rows of the four 16-key blocks b of a 64-key step
+// are key(b, i) = k + 16*(i/4) + 4*b + i%4, so after S^T = K . Q^T lane group grp holds
+// the scores of the 16 consecutive keys k + 16*grp .. +15 (v[4b + r] is key
+// k + 16*grp + 4b + r); those are also the keys of its V^T slice (16 contiguous bytes of
+// a transposed V page row) and of its 16 scales, and P sub-step u element e is key
+// k + 16*grp + 8*u + e.  Items start at multiples of 16 and pages hold >= 16 positions,
+// so each 16-key run lies in one page.
+template <int D>
+__device__ __forceinline__ void split_kv_fp8_wave(
+    int idx, const SplitItem* __restrict__ items, const Column* __restrict__ cols, const bf16* __restrict__ q,
+    const uint8_t* __restrict__ kpool, const uint8_t* __restrict__ vpool, const float* __restrict__ kscale,
+    const float* __restrict__ vscale, const int32_t* __restrict__ bt, int bt_stride, float* __restrict__ ws_ml,
+    float* __restrict__ ws_acc, bf16* __restrict__ out, int Hq, Paged pg, float scale_log2) {
+  constexpr int KC = D / 32;        // MFMA k-chunks of 8 per lane
+  constexpr int NL = D / 64;        // 16-byte K loads per lane and key row
+  constexpr int DB = D / 16;
+  constexpr int QD = D / 4;         // head-dim quarter of a lane group
+  const int lane = threadIdx.x & 63;
+  const SplitItem it = items[idx];
+  const int n = lane & 15, grp = lane >> 4;
+  const bool cvalid = n < it.ncols;
+  const Column c = cols[it.col0 + (cvalid ? n : 0)];
+  const int limit = cvalid ? c.limit : -1;
+
+  bf16x8 qb[KC];
+  {
+    const bf16* qp = q + (size_t(c.q_row) * Hq + c.q_head) * D + QD * grp;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      qb[kc] = *reinterpret_cast<const bf16x8*>(qp + 8 * kc);
+      if (!cvalid) qb[kc] = bf16x8{};
+    }
+  }
+  f32x4 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = kNegBig, l_run = 0.f;
+  const int32_t* btr = bt + size_t(it.req) * bt_stride;
+  const int kvh = it.kvh;
+  const int klast = it.k1 - 1;
+  const bool masked_item = (it.flags & kItemMasked) != 0;
+
+  const int last_page = klast >> pg.ps_shift;
+  int pbase = it.k0 >> pg.ps_shift;
+  int pids = btr[min(pbase + lane, last_page)];
+  auto cover = [&](int k) {
+    if (((min(k + kStepKeys, it.k1) - 1) >> pg.ps_shift) - pbase >= 64) {
+      pbase = k >> pg.ps_shift;
+      pids = btr[min(pbase + lane, last_page)];
+    }
+  };
+  auto page_at = [&](int pos) -> int { return __shfl(pids, (pos >> pg.ps_shift) - pbase); };
+
+  // first key of the lane group's 16-key run, clamped to the run holding the last key
+  auto run_start = [&](int k) { return min(k + 16 * grp, klast & ~15); };
+  u32x4 ka[4][NL], va[DB];
+  f32x4 ks[4], vs[4];
+  auto load_k = [&](int k) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int key = min(k + 16 * (n >> 2) + 4 * b + (n & 3), klast);
+      const uint8_t* kr = kpool + pg.k_row(page_at(key), kvh, pg.slot_of(key)) + QD * grp;
+#pragma unroll
+      for (int j = 0; j < NL; ++j) ka[b][j] = *reinterpret_cast<const u32x4*>(kr + 16 * j);
+    }
+    const int kb = run_start(k);
+    const float* sp = kscale + pg.scale_idx(page_at(kb), kvh, pg.slot_of(kb));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ks[i] = *reinterpret_cast<const f32x4*>(sp + 4 * i);
+  };
+  auto load_v = [&](int k) {
+    const int kb = run_start(k);
+    const int page = page_at(kb), slot = pg.slot_of(kb);
+    const uint8_t* vr = vpool + pg.v_elem(page, kvh, n, slot);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) va[db] = *reinterpret_cast<const u32x4*>(vr + (size_t(16 * db) << pg.ps_shift));
+    const float* sp = vscale + pg.scale_idx(page, kvh, slot);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vs[i] = *reinterpret_cast<const f32x4*>(sp + 4 * i);
+  };
+  cover(it.k0);
+  load_k(it.k0);
+  load_v(it.k0);
+  for (int k = it.k0; k < it.k1; k += kStepKeys) {
+    const bool tail = k + kStepKeys > it.k1;
+    const bool more = k + kStepKeys < it.k1;
+    // ---- scores S^T for 64 keys, times the keys' K scales
+    float v[16];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < NL; ++j) {
+        s = mfma16_bf16(fp8x8_to_bf16(ka[b][j][0], ka[b][j][1]), qb[2 * j], s);
+        s = mfma16_bf16(fp8x8_to_bf16(ka[b][j][2], ka[b][j][3]), qb[2 * j + 1], s);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[4 * b + r] = s[r] * (ks[b][r] * scale_log2);
+    }
+    if (more) {
+      cover(k + kStepKeys);
+      load_k(k + kStepKeys);
+    }
+    float vsc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) vsc[i] = vs[i >> 2][i & 3];
+    if (masked_item || tail) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = k + 16 * grp + i;
+        if (key > klast || key > limit) v[i] = -INFINITY;
+        // scales past the item's end may belong to unwritten slots: keep them out of P
+        if (key > klast) vsc[i] = 0.f;
+      }
+    }
+    // ---- online softmax (max shared by the 4 lane groups of a column)
+    float mx = v[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, v[e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = fast_exp2(m_run - m_new);
+    m_run = m_new;
+    bf16x8 pb[2];
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = fast_exp2(v[i] - m_new);
+      sum += p;
+      pb[i >> 3][i & 7] = bf16(p * vsc[i]);
+    }
+    l_run = l_run * alpha + sum;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+    // ---- O^T += V^T . P^T; codes at or past k1 may be unwritten slots: zeroed
+    const int valid = it.k1 - (k + 16 * grp);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      bf16x8 v0 = fp8x8_to_bf16(va[db][0], va[db][1]);
+      bf16x8 v1 = fp8x8_to_bf16(va[db][2], va[db][3]);
+      if (tail && valid < 16) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (e >= valid) v0[e] = bf16(0.f);
+          if (8 + e >= valid) v1[e] = bf16(0.f);
+        }
+      }
+      acc[db] = mfma16_bf16(v0, pb[0], acc[db]);
+      acc[db] = mfma16_bf16(v1, pb[1], acc[db]);
+    }
+    if (more) load_v(k + kStepKeys);
+  }
+  float l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  if (cvalid) {
+    if (it.flags & kItemDirect) store_output<D>(out, (size_t(c.q_row) * Hq + c.q_head) * D, grp, l_tot, acc);
+    else store_partial<D>(ws_ml, ws_acc, c.pbase + it.slot, grp, m_run, l_tot, acc);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void split_kv_fp8_kernel(
+    const SplitItem* __restrict__ items, int nitems, const Column* __restrict__ cols, const bf16* __restrict__ q,
+    const uint8_t* __restrict__ kpool, const uint8_t* __restrict__ vpool, const float* __restrict__ kscale,
+    const float* __restrict__ vscale, const int32_t* __restrict__ bt, int bt_stride, float* __restrict__ ws_ml,
+    float* __restrict__ ws_acc, bf16* __restrict__ out, int Hq, Paged pg, float scale_log2) {
+  const int idx = blockIdx.x * kSplitWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (idx < nitems)
+    split_kv_fp8_wave<D>(idx, items, cols, q, kpool, vpool, kscale, vscale, bt, bt_stride, ws_ml, ws_acc, out, Hq,
+                         pg, scale_log2);
+}
+
+hipError_t launch_split_kv_fp8(int D, int nitems, hipStream_t s, const SplitItem* items, const Column* cols,
+                               const void* q, const void* kpool, const void* vpool, const float* kscale,
+                               const float* vscale, const int32_t* bt, int bt_stride, float* ws_ml, float* ws_acc,
+                               void* out, int Hq, Paged pg, float scale_log2) {
+  const dim3 grid((nitems + kSplitWaves - 1) / kSplitWaves), block(64 * kSplitWaves);
+  auto* qq = static_cast<const bf16*>(q);
+  auto* kk = static_cast<const uint8_t*>(kpool);
+  auto* vv = static_cast<const uint8_t*>(vpool);
+  auto* oo = static_cast<bf16*>(out);
+  if (D == 128)
+    split_kv_fp8_kernel<128><<<grid, block, 0, s>>>(items, nitems, cols, qq, kk, vv, kscale, vscale, bt, bt_stride,
+                                                    ws_ml, ws_acc, oo, Hq, pg, scale_log2);
+  else
+    split_kv_fp8_kernel<64><<<grid, block, 0, s>>>(items, nitems, cols, qq, kk, vv, kscale, vscale, bt, bt_stride,
+                                                   ws_ml, ws_acc, oo, Hq, pg, scale_log2);
+  return hipGetLastError();
+}
+
+// Thread t widens codes 8t .. 8t+7 with the same converter the attention kernel uses.
+__global__ __launch_bounds__(256) void fp8_to_bf16_kernel(const uint32_t* __restrict__ codes, int64_t groups,
+                                                          bf16x8* __restrict__ out) {
+  const int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (t < groups) out[t] = fp8x8_to_bf16(codes[2 * t], codes[2 * t + 1]);
+}
+
+}  // namespace va
+
+using namespace va;
+
+extern "C" va_status varlen_attn_debug_fp8_to_bf16(const uint8_t* codes, uint16_t* out, int64_t n, void* stream) {
+  if (n < 0 || n % 8 != 0) return fail(VA_ERR_INVALID_ARG, "n must be a non-negative multiple of 8");
+  if (n == 0) return VA_OK;
+  if (!codes || !out) return fail(VA_ERR_INVALID_ARG, "codes and out must be non-NULL");
+  if ((reinterpret_cast<uintptr_t>(codes) & 7) || (reinterpret_cast<uintptr_t>(out) & 15))
+    return fail(VA_ERR_INVALID_ARG, "codes must be 8-byte and out 16-byte aligned");
+  const int64_t groups = n / 8;
+  (void)hipGetLastError();
+  fp8_to_bf16_kernel<<<dim3(unsigned((groups + 255) / 256)), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
+      reinterpret_cast<const uint32_t*>(codes), groups, reinterpret_cast<bf16x8*>(out));
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(VA_ERR_HIP, std::string("fp8 conversion kernel launch: ") + hipGetErrorString(e));
+  return VA_OK;
+}

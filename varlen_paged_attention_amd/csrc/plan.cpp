@@ -90,7 +90,8 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
   if (p.num_q_heads < 1 || p.num_kv_heads < 1) return fail(VA_ERR_INVALID_ARG, "head counts must be >= 1");
   if (p.num_q_heads % p.num_kv_heads != 0)
     return fail(VA_ERR_INVALID_ARG, "num_q_heads must be a multiple of num_kv_heads");
-  if (p.dtype != VA_DTYPE_BF16 && p.dtype != VA_DTYPE_F32) return fail(VA_ERR_INVALID_ARG, "unknown dtype");
+  if (p.dtype != VA_DTYPE_BF16 && p.dtype != VA_DTYPE_F32 && p.dtype != VA_DTYPE_FP8_E4M3)
+    return fail(VA_ERR_INVALID_ARG, "unknown dtype");
   if (p.head_dim != 64 && p.head_dim != 128) return fail(VA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
   const int ps = p.page_size;
   if (ps != 16 && ps != 32 && ps != 64 && ps != 128 && ps != 256)
@@ -383,7 +384,10 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
 
   // ---- counters ---------------------------------------------------------------------
   va_plan_stats& st = plan->stats;
-  const int64_t elem = p.dtype == VA_DTYPE_BF16 ? 2 : 4;
+  // bytes of one Q / output element, and of one position of one KV head's K and V
+  // (fp8: one byte per element plus a float32 scale each for K and V)
+  const int64_t elem = p.dtype == VA_DTYPE_F32 ? 4 : 2;
+  const int64_t head_pos_bytes = p.dtype == VA_DTYPE_FP8_E4M3 ? 2 * (int64_t(D) + 4) : 2 * int64_t(D) * elem;
   st.num_reqs = num_reqs;
   st.total_q_rows = total_rows;
   st.prefill_tiles = int64_t(plan->tiles.size());
@@ -420,7 +424,7 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
   for (int32_t v : max_slot) phys_pos += v;
   for (int32_t v : max_slot_pf) phys_pf += v;
   for (int32_t v : max_slot_sp) phys_sp += v;
-  const int64_t pos_bytes = int64_t(Hkv) * D * 2 * elem;
+  const int64_t pos_bytes = int64_t(Hkv) * head_pos_bytes;
   st.prefill_flops = 4.0 * D * Hq * double(pairs_pf);
   st.split_flops = 4.0 * D * Hq * double(pairs - pairs_pf);
   st.prefill_kv_bytes = phys_pf * pos_bytes;

@@ -72,15 +72,31 @@ def f32_to_bf16_bits(x: np.ndarray, out: np.ndarray) -> None:
     out[...] = r
 
 
-def _normal_fill(seed: int, stream: int, n: int, bf16: bool) -> np.ndarray:
-    out = np.empty(n, np.uint16 if bf16 else np.float32)
+def _normal_fill(seed: int, stream: int, n: int, bf16: bool, fp8_vec: Optional[tuple] = None):
+    """n standard normal float32 draws (chunk c from its own seeded stream), stored as
+    float32, as bf16 bits, or -- with ``fp8_vec`` = (D, stride) -- as e4m3fn codes with
+    one scale per vector of D elements spaced ``stride`` apart inside blocks of D*stride
+    elements (stride 1: K rows, stride page_size: V columns of a transposed page); then
+    returns (codes, scales).  Chunks hold whole blocks, so the draws do not depend on the
+    storage type."""
+    if fp8_vec is not None:
+        D, stride = fp8_vec
+        assert CHUNK % (D * stride) == 0 and n % (D * stride) == 0
+        out = np.empty(n, np.uint8)
+        scales = np.empty(n // D, np.float32)
+    else:
+        out = np.empty(n, np.uint16 if bf16 else np.float32)
     nchunks = (n + CHUNK - 1) // CHUNK
 
     def job(c: int) -> None:
         lo, hi = c * CHUNK, min(n, (c + 1) * CHUNK)
         g = _rng(seed, stream, c)
         x = g.standard_normal(hi - lo, dtype=np.float32)
-        if bf16:
+        if fp8_vec is not None:
+            codes, sc = quantize_fp8(x.reshape(-1, D, stride), axis=1)
+            out[lo:hi] = codes.reshape(-1)
+            scales[lo // D:hi // D] = sc.reshape(-1)
+        elif bf16:
             f32_to_bf16_bits(x, out[lo:hi])
         else:
             out[lo:hi] = x
@@ -91,7 +107,7 @@ def _normal_fill(seed: int, stream: int, n: int, bf16: bool) -> np.ndarray:
     else:
         with ThreadPoolExecutor(_threads()) as ex:
             list(ex.map(job, range(nchunks)))
-    return out
+    return out if fp8_vec is None else (out, scales)
 
 
 @dataclass
@@ -132,6 +148,11 @@ class Workload:
     def elem_bytes(self) -> int:
         """Bytes of one stored K or V element."""
         return {"bf16": 2, "f32": 4, "fp8": 1}[self.dtype]
+
+    @property
+    def scale_bytes(self) -> int:
+        """Bytes of the scale stored with each K or V vector (fp8: one float32)."""
+        return 4 if self.dtype == "fp8" else 0
 
 
 def build(name: str, q_rows: Sequence[int], kv_lens: Sequence[int], *, num_q_heads: int,
@@ -177,10 +198,10 @@ def build(name: str, q_rows: Sequence[int], kv_lens: Sequence[int], *, num_q_hea
     q = _normal_fill(seed, STREAM_Q, T * num_q_heads * D, bf16).reshape(T, num_q_heads, D)
     k_scale = v_scale = None
     if fp8:
-        kf = _normal_fill(seed, STREAM_K, P * num_kv_heads * ps * D, False).reshape(P, num_kv_heads, ps, D)
-        vf = _normal_fill(seed, STREAM_V, P * num_kv_heads * D * ps, False).reshape(P, num_kv_heads, D, ps)
-        k, k_scale = quantize_fp8(kf, axis=3)
-        v, v_scale = quantize_fp8(vf, axis=2)
+        k, k_scale = _normal_fill(seed, STREAM_K, P * num_kv_heads * ps * D, False, fp8_vec=(D, 1))
+        v, v_scale = _normal_fill(seed, STREAM_V, P * num_kv_heads * D * ps, False, fp8_vec=(D, ps))
+        k, k_scale = k.reshape(P, num_kv_heads, ps, D), k_scale.reshape(P, num_kv_heads, ps)
+        v, v_scale = v.reshape(P, num_kv_heads, D, ps), v_scale.reshape(P, num_kv_heads, ps)
     else:
         k = _normal_fill(seed, STREAM_K, P * num_kv_heads * ps * D, bf16).reshape(P, num_kv_heads, ps, D)
         v = _normal_fill(seed, STREAM_V, P * num_kv_heads * D * ps, bf16).reshape(P, num_kv_heads, D, ps)
@@ -223,42 +244,48 @@ CONFIG_NAMES = {
 
 
 def config(cid: int, seed: Optional[int] = None, poison_tail: bool = False,
-           scale: int = 1) -> Workload:
+           scale: int = 1, dtype: Optional[str] = None) -> Workload:
     """The five workloads of the pages (plus 51: the scaled shared-prefix variant).
 
     ``scale`` > 1 shrinks the lengths (integer division, min 1) and keeps the head
-    layout, for parity runs the oracle finishes quickly.
+    layout, for parity runs the oracle finishes quickly.  ``dtype`` replaces the
+    configuration's element type (e.g. "fp8" for the same shapes in fp8 storage).
     """
     s = cid if seed is None else seed
+
+    def mk(*a, **kw):
+        if dtype is not None:
+            kw["dtype"] = dtype
+        return build(*a, **kw)
 
     def sh(x):
         return np.maximum(1, np.asarray(x, np.int64) // scale)
 
     if cid == 1:
         # A uncached prefill 64/64, B decode 1/100, C chunk 16 rows on S0=32
-        return build(CONFIG_NAMES[1], [64, 1, 16], [64, 100, 48], num_q_heads=4, num_kv_heads=2,
+        return mk(CONFIG_NAMES[1], [64, 1, 16], [64, 100, 48], num_q_heads=4, num_kv_heads=2,
                      head_dim=64, page_size=16, dtype="f32", seed=s, permute_pages=False,
                      poison_tail=poison_tail)
     if cid == 2:
         a = int(sh(4096))
-        return build(CONFIG_NAMES[2], [a, 1, 1], [a, int(sh(1500)), int(sh(1700))], num_q_heads=32,
+        return mk(CONFIG_NAMES[2], [a, 1, 1], [a, int(sh(1500)), int(sh(1700))], num_q_heads=32,
                      num_kv_heads=32, head_dim=128, page_size=16, seed=s, poison_tail=poison_tail)
     if cid == 3:
         n = max(1, 256 // scale)
         kv = sh(uniform_lengths(s, n, 1024, 8192))
-        return build(CONFIG_NAMES[3], [1] * n, kv, num_q_heads=32, num_kv_heads=8, head_dim=128,
+        return mk(CONFIG_NAMES[3], [1] * n, kv, num_q_heads=32, num_kv_heads=8, head_dim=128,
                      page_size=64, seed=s, poison_tail=poison_tail)
     if cid == 4:
         n = max(1, 64 // scale)
         kv = sh(uniform_lengths(s, n, 512, 16384))
         chunk, total = int(sh(2048)), int(sh(32768))
-        return build(CONFIG_NAMES[4], [chunk] + [1] * n, [total] + list(kv), num_q_heads=64,
+        return mk(CONFIG_NAMES[4], [chunk] + [1] * n, [total] + list(kv), num_q_heads=64,
                      num_kv_heads=8, head_dim=128, page_size=64, seed=s, poison_tail=poison_tail)
     if cid in (5, 51):
         nreq, shared = (6, 4096) if cid == 5 else (64, 16384)
         shared = max(64, (shared // scale) // 64 * 64)
         priv = int(sh(1024))
-        return build(CONFIG_NAMES[cid], [1] * nreq, [shared + priv] * nreq, num_q_heads=32,
+        return mk(CONFIG_NAMES[cid], [1] * nreq, [shared + priv] * nreq, num_q_heads=32,
                      num_kv_heads=8, head_dim=128, page_size=64, seed=s,
                      shared_prefix_pages=shared // 64, poison_tail=poison_tail)
     raise ValueError(f"unknown config {cid}")

@@ -30,6 +30,7 @@ PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E
 PEAK_BF16 = 2.5e15         # FLOP/s, MI355X dense bf16 MFMA
 STAGES = ("prefill", "split_kv", "combine")
 KERNEL_NAMES = {"prefill": "prefill_bf16_kernel", "split_kv": "split_kv_bf16_kernel", "combine": "combine_kernel"}
+KERNEL_NAMES_FP8 = {**KERNEL_NAMES, "split_kv": "split_kv_fp8_kernel"}
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
@@ -78,9 +79,10 @@ def time_runs(api, plan, tensors, steps, warmup, flush=None):
     """Run warmup + steps iterations with per-stage HIP events; returns (wall ms/step,
     per-stage mean ms, per-step total ms list)."""
     import torch
-    q, k, v, bt, out, ws = tensors
+    q, k, v, bt, out, ws = tensors[:6]
+    scales = dict(zip(("k_scale", "v_scale"), tensors[6:]))
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
-    run = api.RunCall(plan, q, k, v, bt, out, ws)
+    run = api.RunCall(plan, q, k, v, bt, out, ws, **scales)
     calls = [run.with_events(e) for e in evs]
     for _ in range(warmup):
         run()
@@ -103,7 +105,8 @@ def setup(api, w, flags=0):
     q, k, v, bt = api.to_device(w)
     out = torch.zeros_like(q)
     ws = api.new_workspace(plan)
-    return plan, (q, k, v, bt, out, ws)
+    scales = api.scales_to_device(w) if w.dtype == "fp8" else ()
+    return plan, (q, k, v, bt, out, ws) + tuple(scales)
 
 
 def dominant(stats, stage_ms):
@@ -123,16 +126,17 @@ def dominant(stats, stage_ms):
     return name, ms, work, bound
 
 
-def roofline(stats, stage_ms, workload=None):
+def roofline(stats, stage_ms, workload=None, fp8=False):
+    names = KERNEL_NAMES_FP8 if fp8 else KERNEL_NAMES
     name, ms, work, bound = dominant(stats, stage_ms)
-    traffic = measured_traffic(workload, KERNEL_NAMES[name]) if workload else None
+    traffic = measured_traffic(workload, names[name]) if workload else None
     sec = ms * 1e-3
     if bound == "mfma":
         a, p, unit = work / sec / 1e12, PEAK_BF16 / 1e12, "TFLOP/s"
     else:
         a, p, unit = work / sec / 1e9, PEAK_HBM / 1e9, "GB/s"
     return {"bound": bound, "achieved": round(a, 2), "peak": p, "unit": unit, "frac": round(a / p, 4),
-            "traffic": traffic, "kernel": KERNEL_NAMES[name], "kernel_ms": round(ms, 5),
+            "traffic": traffic, "kernel": names[name], "kernel_ms": round(ms, 5),
             "algorithmic_per_launch": work}
 
 
@@ -228,9 +232,9 @@ def make_flush():
     return flush
 
 
-def secondary(api, W, cid, flags, reps, label, flush, key=None):
+def secondary(api, W, cid, flags, reps, label, flush, key=None, dtype=None):
     plan, tensors = None, None
-    w = W.config(cid)
+    w = W.config(cid, dtype=dtype)
     plan, tensors = setup(api, w, flags)
     st = api.varlen_attn_plan_stats(plan)
     _, stage, totals = time_runs(api, plan, tensors, reps, 3, flush)
@@ -242,7 +246,8 @@ def secondary(api, W, cid, flags, reps, label, flush, key=None):
            "algorithmic_bytes": byts, "logical_kv_bytes": st["logical_kv_bytes"],
            "physical_kv_bytes": st["physical_kv_bytes"], "flops": st["flops"],
            "stage_ms": {k: round(v, 5) for k, v in stage.items()},
-           "roofline": roofline(st, stage, key), "l2_flushed": flush is not None}
+           "roofline": roofline(st, stage, key, fp8=w.dtype == "fp8"), "l2_flushed": flush is not None,
+           "dtype": w.dtype}
     del tensors
     return res
 
@@ -256,6 +261,7 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--only", type=int, default=None,
                     help="profile mode: time only this workload (2, 3, 4, 5 or 51) and print its line")
+    ap.add_argument("--fp8", action="store_true", help="with --only: the workload in fp8 KV storage")
     ap.add_argument("--copy-only", action="store_true",
                     help="profile mode: 10 device copies of 1 GiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -274,8 +280,11 @@ def main():
     if args.only is not None:
         flags = api.VA_FLAG_SHARED_PREFIX if args.only in (5, 51) else 0
         key = {2: "orca", 3: "decode", 4: "chunk", 5: "shared6", 51: "shared64"}.get(args.only)
+        if args.fp8:
+            key += "_fp8"
         fl = make_flush() if args.only in (5, 51) else None     # as in the secondary lines
-        res = secondary(api, W, args.only, flags, args.steps, W.CONFIG_NAMES[args.only], fl, key)
+        res = secondary(api, W, args.only, flags, args.steps, W.CONFIG_NAMES[args.only], fl, key,
+                        "fp8" if args.fp8 else None)
         print(json.dumps(res), flush=True)
         return
 
@@ -308,13 +317,17 @@ def main():
         flush = make_flush()
 
         sec = []
-        for cid, flags, label, fl, key in (
-                (3, 0, "decode-heavy-gqa (256 decodes, kv U[1024,8192], g=4, page 64)", None, "decode"),
-                (4, 0, "chunked-prefill-mix (2048@S0=30720 + 64 decodes, g=8)", None, "chunk"),
-                (5, api.VA_FLAG_SHARED_PREFIX, "shared-prefix-6 (4096 shared + 1024 each)", flush, "shared6"),
-                (51, api.VA_FLAG_SHARED_PREFIX, "shared-prefix-64 (16384 shared + 1024 each)", flush, "shared64")):
+        for cid, flags, label, fl, key, dt in (
+                (3, 0, "decode-heavy-gqa (256 decodes, kv U[1024,8192], g=4, page 64)", None, "decode", None),
+                (4, 0, "chunked-prefill-mix (2048@S0=30720 + 64 decodes, g=8)", None, "chunk", None),
+                (5, api.VA_FLAG_SHARED_PREFIX, "shared-prefix-6 (4096 shared + 1024 each)", flush, "shared6", None),
+                (51, api.VA_FLAG_SHARED_PREFIX, "shared-prefix-64 (16384 shared + 1024 each)", flush, "shared64",
+                 None),
+                (3, 0, "decode-heavy-gqa in fp8 e4m3fn KV + per-position fp32 scales", None, "decode_fp8", "fp8"),
+                (51, api.VA_FLAG_SHARED_PREFIX, "shared-prefix-64 in fp8 e4m3fn KV + scales", flush, "shared64_fp8",
+                 "fp8")):
             log(f"[bench] secondary: {label}")
-            sec.append(secondary(api, W, cid, flags, 20, label, fl, key))
+            sec.append(secondary(api, W, cid, flags, 20, label, fl, key, dt))
             torch.cuda.empty_cache()
         for cid, label in ((2, "kv-append: the ORCA iteration's 4098 new rows (32 KV heads, page 16)"),
                            (3, "kv-append: the decode-heavy iteration's 256 new rows (8 KV heads, page 64)")):

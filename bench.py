@@ -279,7 +279,7 @@ def main():
         return
     if args.only is not None:
         flags = api.VA_FLAG_SHARED_PREFIX if args.only in (5, 51) else 0
-        key = {2: "orca", 3: "decode", 4: "chunk", 5: "shared6", 51: "shared64"}.get(args.only)
+        key = {2: "orca", 3: "decode", 4: "chunk", 5: "shared6", 51: "shared64", 6: "mtp3", 7: "mtp7"}.get(args.only)
         if args.fp8:
             key += "_fp8"
         fl = make_flush() if args.only in (5, 51) else None     # as in the secondary lines
@@ -322,6 +322,10 @@ def main():
                 (4, 0, "chunked-prefill-mix (2048@S0=30720 + 64 decodes, g=8)", None, "chunk", None),
                 (5, api.VA_FLAG_SHARED_PREFIX, "shared-prefix-6 (4096 shared + 1024 each)", flush, "shared6", None),
                 (51, api.VA_FLAG_SHARED_PREFIX, "shared-prefix-64 (16384 shared + 1024 each)", flush, "shared64",
+                 None),
+                (6, 0, "spec-decode verify, 4 rows/request (256 requests, kv U[1024,8192], g=4)", None, "mtp3",
+                 None),
+                (7, 0, "spec-decode verify, 8 rows/request (256 requests, kv U[1024,8192], g=4)", None, "mtp7",
                  None),
                 (3, 0, "decode-heavy-gqa in fp8 e4m3fn KV + per-position fp32 scales", None, "decode_fp8", "fp8"),
                 (51, api.VA_FLAG_SHARED_PREFIX, "shared-prefix-64 in fp8 e4m3fn KV + scales", flush, "shared64_fp8",

@@ -185,6 +185,8 @@ CASES = [
     ("orca-full", lambda: W.config(2), 0),
     ("chunk-like", lambda: W.build("cl", [2048, 1, 1, 1, 1], [32768, 600, 5000, 16384, 70], num_q_heads=8,
                                    num_kv_heads=1, head_dim=128, page_size=64, seed=5), 0),
+    ("spec-decode-mtp3", lambda: W.config(6, scale=16), 0),
+    ("spec-decode-mtp7", lambda: W.config(7, scale=16), 0),
     ("orca-small-fp8", lambda: W.config(2, scale=16, dtype="fp8"), 0),
     ("decode-fp8", lambda: W.config(3, scale=16, dtype="fp8"), 0),
     ("shared-fp8", lambda: W.config(5, dtype="fp8"), api.VA_FLAG_SHARED_PREFIX),

@@ -240,12 +240,15 @@ CONFIG_NAMES = {
     4: "chunked-prefill-mix-gqa8",
     5: "shared-prefix-6",
     51: "shared-prefix-64",
+    6: "spec-decode-mtp3",
+    7: "spec-decode-mtp7",
 }
 
 
 def config(cid: int, seed: Optional[int] = None, poison_tail: bool = False,
            scale: int = 1, dtype: Optional[str] = None) -> Workload:
-    """The five workloads of the pages (plus 51: the scaled shared-prefix variant).
+    """The five workloads of the pages (plus 51: the scaled shared-prefix variant; 6 and 7:
+    multi-row speculative-decode verify steps with 4 and 8 rows per request).
 
     ``scale`` > 1 shrinks the lengths (integer division, min 1) and keeps the head
     layout, for parity runs the oracle finishes quickly.  ``dtype`` replaces the
@@ -288,4 +291,13 @@ def config(cid: int, seed: Optional[int] = None, poison_tail: bool = False,
         return mk(CONFIG_NAMES[cid], [1] * nreq, [shared + priv] * nreq, num_q_heads=32,
                      num_kv_heads=8, head_dim=128, page_size=64, seed=s,
                      shared_prefix_pages=shared // 64, poison_tail=poison_tail)
+    if cid in (6, 7):
+        # speculative / MTP verify: each request checks k draft tokens plus one, so it has
+        # k+1 new rows, causal among themselves (k = 3 or 7); otherwise the decode-heavy shape
+        n = max(1, 256 // scale)
+        kv = sh(uniform_lengths(s, n, 1024, 8192))
+        rows = 4 if cid == 6 else 8
+        kv = np.maximum(kv, rows)
+        return mk(CONFIG_NAMES[cid], [rows] * n, kv, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                  page_size=64, seed=s, poison_tail=poison_tail)
     raise ValueError(f"unknown config {cid}")

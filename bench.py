@@ -220,6 +220,65 @@ def append_line(api, W, cid, label, reps=50):
             "hbm_frac": round(byts / (us * 1e-6) / PEAK_HBM, 4), "algorithmic_bytes": byts, "tokens": T}
 
 
+def long_context_line(api, W, reps=10):
+    """256 decodes at 128K context (524,288 block-table entries, 137 GB of bf16 K/V made on
+    the device): planner time, block-table upload, eager per-stage times and the
+    graph-captured step."""
+    import torch
+    w = W.config(8)
+    plan = api.plan_for(w)                    # first plan of the process loads the kernels
+    t0 = time.perf_counter()
+    plan = api.plan_for(w)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    t0 = time.perf_counter()
+    api.plan_for(w, flags=api.VA_FLAG_HOST_ONLY)
+    plan_host_only_ms = (time.perf_counter() - t0) * 1e3
+    st = api.varlen_attn_plan_stats(plan)
+    q, k, v, bt = api.to_device(w)
+    out = torch.zeros_like(q)
+    ws = api.new_workspace(plan)
+    # block-table upload from pinned host memory (what a serving loop copies every step)
+    bt_host = torch.from_numpy(np.ascontiguousarray(w.block_table)).pin_memory()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    bt.copy_(bt_host, non_blocking=True)
+    e0.record()
+    for _ in range(reps):
+        bt.copy_(bt_host, non_blocking=True)
+    e1.record()
+    torch.cuda.synchronize()
+    h2d_us = e0.elapsed_time(e1) * 1e3 / reps
+    _, stage, totals = time_runs(api, plan, (q, k, v, bt, out, ws), reps, 2)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call = api.RunCall(plan, q, k, v, bt, out, ws, stream=s)
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    g.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    graph_us = e0.elapsed_time(e1) * 1e3 / reps
+    byts = st["physical_kv_bytes"] + st["q_bytes"] + st["o_bytes"] + st["table_bytes"]
+    res = {"workload": "long-context decode: 256 x 128K positions (524,288 table entries), Hq=32 Hkv=8 D=128, "
+                       "page 64, bf16 (hashed page values made on the device)",
+           "us_per_step_graph": round(graph_us, 1), "us_per_step_eager": round(float(np.median(totals)) * 1e3, 1),
+           "hbm_GBps": round(byts / (graph_us * 1e-6) / 1e9, 1), "hbm_frac": round(byts / (graph_us * 1e-6) / PEAK_HBM, 4),
+           "algorithmic_bytes": byts, "plan_ms": round(plan_ms, 2), "plan_ms_host_only": round(plan_host_only_ms, 2),
+           "plan_host_us_lib": round(st["plan_host_us"], 1),
+           "split_items": st["split_items"], "block_table_h2d_us": round(h2d_us, 2), "table_bytes": st["table_bytes"],
+           "stage_ms": {kk: round(vv, 5) for kk, vv in stage.items()}, "roofline": roofline(st, stage, "long128k")}
+    del q, k, v, bt, out, ws, g
+    return res
+
+
 def make_flush():
     """A callable that evicts the 256 MB last-level cache by reading 1 GiB (a read leaves no
     dirty lines whose write-back the timed kernels would pay for)."""
@@ -260,7 +319,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--only", type=int, default=None,
-                    help="profile mode: time only this workload (2, 3, 4, 5 or 51) and print its line")
+                    help="profile mode: time only this workload (2-8 or 51) and print its line")
     ap.add_argument("--fp8", action="store_true", help="with --only: the workload in fp8 KV storage")
     ap.add_argument("--copy-only", action="store_true",
                     help="profile mode: 10 device copies of 1 GiB (HBM counter calibration)")
@@ -276,6 +335,9 @@ def main():
     api.lib()
     if args.copy_only:
         print(json.dumps({"copy_GBps": hbm_copy_gbps(), "bytes_per_copy": 2 * (1 << 30)}), flush=True)
+        return
+    if args.only == 8:
+        print(json.dumps(long_context_line(api, W, max(2, args.steps))), flush=True)
         return
     if args.only is not None:
         flags = api.VA_FLAG_SHARED_PREFIX if args.only in (5, 51) else 0
@@ -333,6 +395,9 @@ def main():
             log(f"[bench] secondary: {label}")
             sec.append(secondary(api, W, cid, flags, 20, label, fl, key, dt))
             torch.cuda.empty_cache()
+        log("[bench] secondary: long-context decode 256 x 128K")
+        sec.append(long_context_line(api, W))
+        torch.cuda.empty_cache()
         for cid, label in ((2, "kv-append: the ORCA iteration's 4098 new rows (32 KV heads, page 16)"),
                            (3, "kv-append: the decode-heavy iteration's 256 new rows (8 KV heads, page 64)")):
             log(f"[bench] secondary: {label}")

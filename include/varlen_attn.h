@@ -204,7 +204,10 @@ va_status varlen_attn_append_kv(const va_params* params, int64_t num_tokens, con
  * block_table[r][pos / page_size], slot pos % page_size; rows outside every request get -1. */
 va_status varlen_attn_plan_slots(const va_plan* plan, int64_t* out_cache_loc_host);
 
-/* Counters of the planned work (no device access). */
+/* Counters of the planned work (no device access).  The distinct-position counters
+ * (physical_kv_bytes, prefill_kv_bytes, split_kv_bytes, split_item_kv_bytes) walk every
+ * block-table entry and are computed on the first call for a plan (thread-safe), so
+ * plan_host_us does not include them. */
 va_status varlen_attn_plan_stats(const va_plan* plan, va_plan_stats* out);
 
 /* Copy every request's K and V into logical order through the same page-address code the

@@ -326,7 +326,12 @@ def to_device(w, device="cuda"):
             t = t.view(torch.bfloat16)
         return t.to(device)
 
-    return conv(w.q), conv(w.k_pool), conv(w.v_pool), torch.from_numpy(_i32(w.block_table)).to(device)
+    bt = torch.from_numpy(_i32(w.block_table)).to(device)
+    if getattr(w, "hashed_kv", False):          # pools made on the device from the page hash
+        from .workloads import hashed_pools_device
+        k, v = hashed_pools_device(w, device)
+        return conv(w.q), k, v, bt
+    return conv(w.q), conv(w.k_pool), conv(w.v_pool), bt
 
 
 def scales_to_device(w, device="cuda"):

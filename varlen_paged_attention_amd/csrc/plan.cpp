@@ -16,6 +16,7 @@
 //    Model 笔记(7-8)", section 3, 物理存一份，不保证从 HBM 只读一次).
 #include <algorithm>
 #include <chrono>
+#include <mutex>
 #include <cmath>
 #include <cstring>
 #include <map>
@@ -396,9 +397,8 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
   st.shared_groups = int64_t(groups.size());
   st.partial_slots = slots;
   st.combine_rows = int64_t(plan->combine.size());
-  // distinct positions read: all requests, and each class (prefill tiles / split items)
-  std::vector<int32_t> max_slot(p.num_pages, 0), max_slot_pf(p.num_pages, 0), max_slot_sp(p.num_pages, 0);
-  std::vector<char> is_split(num_reqs, 0);
+  std::vector<char>& is_split = plan->is_split;
+  is_split.assign(num_reqs, 0);
   for (int r : split_reqs) is_split[r] = 1;
   int64_t pairs = 0, logical_pos = 0, rows = 0, table_entries = 0, pairs_pf = 0, rows_sp = 0;
   for (int r = 0; r < num_reqs; ++r) {
@@ -410,52 +410,13 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
     if (!is_split[r]) pairs_pf += pr; else rows_sp += m;
     logical_pos += kv;
     rows += m;
-    const int64_t npg = ceil_div(kv, ps);
-    table_entries += npg;
-    for (int64_t j = 0; j < npg; ++j) {
-      const int32_t used = int32_t(std::min<int64_t>(ps, kv - j * ps));
-      for (auto* v : {&max_slot, is_split[r] ? &max_slot_sp : &max_slot_pf}) {
-        int32_t& ms = (*v)[bt(r, j)];
-        ms = std::max(ms, used);
-      }
-    }
+    table_entries += ceil_div(kv, ps);
   }
-  int64_t phys_pos = 0, phys_pf = 0, phys_sp = 0;
-  for (int32_t v : max_slot) phys_pos += v;
-  for (int32_t v : max_slot_pf) phys_pf += v;
-  for (int32_t v : max_slot_sp) phys_sp += v;
   const int64_t pos_bytes = int64_t(Hkv) * head_pos_bytes;
+  plan->pos_bytes = pos_bytes;
   st.prefill_flops = 4.0 * D * Hq * double(pairs_pf);
   st.split_flops = 4.0 * D * Hq * double(pairs - pairs_pf);
-  st.prefill_kv_bytes = phys_pf * pos_bytes;
-  st.split_kv_bytes = phys_sp * pos_bytes;
   st.split_q_bytes = rows_sp * Hq * D * elem;
-  // distinct positions the split items read (with group tiles, the shared pages are theirs)
-  {
-    std::vector<std::pair<int64_t, int64_t>> iv;      // [page*ps + lo, page*ps + hi)
-    for (const SplitItem& it : plan->items) {
-      if (it.kvh != 0) continue;                      // every KV head reads the same positions
-      for (int64_t k = it.k0; k < it.k1;) {
-        const int64_t j = k / ps, hi = std::min<int64_t>(it.k1, (j + 1) * ps);
-        const int64_t base = int64_t(bt(it.req, j)) * ps - j * ps;
-        iv.push_back({base + k, base + hi});
-        k = hi;
-      }
-    }
-    std::sort(iv.begin(), iv.end());
-    int64_t n = 0, cur_lo = -1, cur_hi = -1;
-    for (auto& x : iv) {
-      if (x.first > cur_hi) {
-        n += cur_hi - cur_lo;
-        cur_lo = x.first;
-        cur_hi = x.second;
-      } else {
-        cur_hi = std::max(cur_hi, x.second);
-      }
-    }
-    n += cur_hi - cur_lo;
-    st.split_item_kv_bytes = n * pos_bytes;
-  }
   st.shared_tiles = int64_t(plan->gtiles.size());
   st.shared_tile_flops = 0;
   for (const PrefillTile& t : plan->gtiles) st.shared_tile_flops += 4.0 * D * t.ncols * double(t.kv_end - t.S0);
@@ -465,7 +426,6 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
   st.visible_pairs = pairs;
   st.flops = 4.0 * D * Hq * double(pairs);
   st.logical_kv_bytes = logical_pos * pos_bytes;
-  st.physical_kv_bytes = phys_pos * pos_bytes;
   st.q_bytes = rows * Hq * D * elem;
   st.o_bytes = st.q_bytes;
   st.table_bytes = table_entries * 4;
@@ -506,8 +466,57 @@ extern "C" va_status varlen_attn_plan_slots(const va_plan* plan, int64_t* out) {
   return VA_OK;
 }
 
+// Distinct-position counters.  They walk every block-table entry, so they are computed on
+// the first varlen_attn_plan_stats call instead of in the planner (a serving loop that
+// plans every iteration does not pay for them).
+static void page_counters(const va_plan* plan) {
+  const va_params& p = plan->p;
+  const int ps = p.page_size;
+  va_plan_stats& st = plan->stats;
+  auto bt = [&](int r, int64_t j) { return plan->block_table[int64_t(r) * p.max_pages_per_req + j]; };
+  // distinct positions read: all requests, and each class (prefill tiles / split items)
+  std::vector<int32_t> max_slot(p.num_pages, 0), max_slot_pf(p.num_pages, 0), max_slot_sp(p.num_pages, 0);
+  for (int r = 0; r < plan->num_reqs; ++r) {
+    if (plan->q_end[r] == plan->q_start[r]) continue;
+    const int64_t kv = plan->kv_len[r];
+    std::vector<int32_t>& cls = plan->is_split[r] ? max_slot_sp : max_slot_pf;
+    for (int64_t j = 0, npg = ceil_div(kv, ps); j < npg; ++j) {
+      const int32_t used = int32_t(std::min<int64_t>(ps, kv - j * ps));
+      const int32_t page = bt(r, j);
+      max_slot[page] = std::max(max_slot[page], used);
+      cls[page] = std::max(cls[page], used);
+    }
+  }
+  int64_t phys_pos = 0, phys_pf = 0, phys_sp = 0;
+  for (int32_t v : max_slot) phys_pos += v;
+  for (int32_t v : max_slot_pf) phys_pf += v;
+  for (int32_t v : max_slot_sp) phys_sp += v;
+  st.physical_kv_bytes = phys_pos * plan->pos_bytes;
+  st.prefill_kv_bytes = phys_pf * plan->pos_bytes;
+  st.split_kv_bytes = phys_sp * plan->pos_bytes;
+  // distinct positions the split items read (with group tiles, the shared pages are theirs).
+  // Every item range starts on a page boundary or right after another item of the same
+  // block, so the slots read in one page form one run [lo, hi): per-page bounds suffice.
+  std::vector<int32_t> lo(p.num_pages, INT32_MAX), hi(p.num_pages, 0);
+  for (const SplitItem& it : plan->items) {
+    if (it.kvh != 0) continue;                      // every KV head reads the same positions
+    for (int64_t k = it.k0; k < it.k1;) {
+      const int64_t j = k / ps, e = std::min<int64_t>(it.k1, (j + 1) * ps);
+      const int32_t page = bt(it.req, j);
+      lo[page] = std::min<int32_t>(lo[page], int32_t(k - j * ps));
+      hi[page] = std::max<int32_t>(hi[page], int32_t(e - j * ps));
+      k = e;
+    }
+  }
+  int64_t n = 0;
+  for (int32_t pg = 0; pg < p.num_pages; ++pg)
+    if (hi[pg] > 0) n += hi[pg] - lo[pg];
+  st.split_item_kv_bytes = n * plan->pos_bytes;
+}
+
 extern "C" va_status varlen_attn_plan_stats(const va_plan* plan, va_plan_stats* out) {
   if (!plan || !out) return fail(VA_ERR_INVALID_ARG, "plan or out is NULL");
+  std::call_once(plan->page_counters_once, page_counters, plan);
   *out = plan->stats;
   return VA_OK;
 }

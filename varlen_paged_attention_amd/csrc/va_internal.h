@@ -50,6 +50,7 @@ constexpr int kStepKeys = 64;        // kv positions per split-KV loop step
 
 // Plan object (host side).  Defined here so kernels.hip can read the device pointers.
 #ifdef __cplusplus
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -66,7 +67,10 @@ struct va_plan {
   std::vector<va::CombineRow> combine;
   std::vector<va::PrefillTile> tiles;
   std::vector<va::PrefillTile> gtiles;        // shared-prefix group tiles (columns from `cols`)
-  va_plan_stats stats{};
+  std::vector<char> is_split;               // per request: rows run as split-KV items
+  int64_t pos_bytes = 0;                     // K+V bytes of one position over all KV heads
+  mutable va_plan_stats stats{};             // page-level counters filled on first query
+  mutable std::once_flag page_counters_once;
   // device copies (one allocation)
   void* dev = nullptr;
   size_t dev_bytes = 0;

@@ -128,6 +128,8 @@ class Workload:
     v_pool: np.ndarray              # [P, Hkv, D, ps]
     softmax_scale: float = 0.0      # <= 0 means 1/sqrt(head_dim)
     shared_prefix_pages: int = 0    # leading pages shared by every request (0: none)
+    hashed_kv: bool = False         # K/V not held on the host: made page by page by hashed_pages*
+    seed: int = 0
     k_scale: Optional[np.ndarray] = None   # fp8 only: float32 [P, Hkv, ps], one per K row
     v_scale: Optional[np.ndarray] = None   # fp8 only: float32 [P, Hkv, ps], one per V column
     notes: dict = field(default_factory=dict)
@@ -158,7 +160,7 @@ class Workload:
 def build(name: str, q_rows: Sequence[int], kv_lens: Sequence[int], *, num_q_heads: int,
           num_kv_heads: int, head_dim: int, page_size: int, dtype: str = "bf16", seed: int = 0,
           permute_pages: bool = True, shared_prefix_pages: int = 0, poison_tail: bool = False,
-          extra_pages: int = 0, softmax_scale: float = 0.0) -> Workload:
+          extra_pages: int = 0, softmax_scale: float = 0.0, hashed_kv: bool = False) -> Workload:
     """Build a workload from per-request (q_rows, kv_length) pairs.
 
     Requests' Q rows are laid out back to back in request order.  Each request owns
@@ -168,6 +170,10 @@ def build(name: str, q_rows: Sequence[int], kv_lens: Sequence[int], *, num_q_hea
     never referenced), permuted by a seeded permutation when ``permute_pages``.
     With ``poison_tail`` the slots past kv_len in each tail page (and the extra pages)
     hold NaN, so any read beyond a request's length shows in its output.
+    With ``hashed_kv`` (bf16 only) the K/V pools are not built on the host: every page's
+    values come from a counter-based hash of (seed, pool, page, element), made on the
+    device by ``hashed_pools_device`` and for any pages on the host by
+    ``hashed_pages_host`` (pools too large for host memory).
     """
     q_rows = np.asarray(q_rows, np.int64)
     kv = np.asarray(kv_lens, np.int64)
@@ -197,7 +203,10 @@ def build(name: str, q_rows: Sequence[int], kv_lens: Sequence[int], *, num_q_hea
     D = head_dim
     q = _normal_fill(seed, STREAM_Q, T * num_q_heads * D, bf16).reshape(T, num_q_heads, D)
     k_scale = v_scale = None
-    if fp8:
+    if hashed_kv:
+        assert dtype == "bf16" and not poison_tail and not extra_pages
+        k = v = None
+    elif fp8:
         k, k_scale = _normal_fill(seed, STREAM_K, P * num_kv_heads * ps * D, False, fp8_vec=(D, 1))
         v, v_scale = _normal_fill(seed, STREAM_V, P * num_kv_heads * D * ps, False, fp8_vec=(D, ps))
         k, k_scale = k.reshape(P, num_kv_heads, ps, D), k_scale.reshape(P, num_kv_heads, ps)
@@ -205,7 +214,7 @@ def build(name: str, q_rows: Sequence[int], kv_lens: Sequence[int], *, num_q_hea
     else:
         k = _normal_fill(seed, STREAM_K, P * num_kv_heads * ps * D, bf16).reshape(P, num_kv_heads, ps, D)
         v = _normal_fill(seed, STREAM_V, P * num_kv_heads * D * ps, bf16).reshape(P, num_kv_heads, D, ps)
-    if poison_tail:
+    if poison_tail and not hashed_kv:
         nanv = FP8_NAN if fp8 else (BF16_NAN if bf16 else np.float32(np.nan))
         for r in range(R):
             valid = int(kv[r]) - (int(npg[r]) - 1) * ps
@@ -225,7 +234,87 @@ def build(name: str, q_rows: Sequence[int], kv_lens: Sequence[int], *, num_q_hea
     return Workload(name=name, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, head_dim=D,
                     page_size=ps, dtype=dtype, q_start=qs, q_end=qe, kv_len=kv.astype(np.int32),
                     block_table=bt, num_pages=P, q=q, k_pool=k, v_pool=v, softmax_scale=softmax_scale,
-                    shared_prefix_pages=sp, k_scale=k_scale, v_scale=v_scale)
+                    shared_prefix_pages=sp, k_scale=k_scale, v_scale=v_scale, hashed_kv=hashed_kv, seed=seed)
+
+
+# ---- counter-based page values (pools too large to build on the host) ----------------
+# Element e of physical page p of pool s (3 = K, 4 = V) is a function of (seed, s, p, e)
+# only: key = h(h(seed) ^ s), page key = h(p ^ key), u = h(e ^ page key), where h is the
+# 32-bit "lowbias32" integer hash (xor-shift 16, multiply 0x7feb352d, xor-shift 15,
+# multiply 0x846ca68b, xor-shift 16, all modulo 2^32; C. Wellons, "Prospecting for hash
+# functions").  The value is (byte0(u) + byte1(u) - 255) / 128: a triangular
+# distribution on [-1.99, 1.99] (std 0.82) whose every value is exact in bf16.  The same
+# integer steps run in NumPy (host) and in torch (device), with products split so that no
+# intermediate exceeds 2^48, so both give identical bits.
+_M32 = 0xFFFFFFFF
+_H1, _H2 = 0x7FEB352D, 0x846CA68B
+
+
+def _mul32(x, c: int):
+    """(x * c) mod 2^32 for 0 <= x < 2^32 without intermediates above 2^48 (x: int64
+    array or tensor)."""
+    lo, hi = c & 0xFFFF, c >> 16
+    return ((((x * hi) & 0xFFFF) << 16) + x * lo) & _M32
+
+
+def _lowbias32(x):
+    x = x ^ (x >> 16)
+    x = _mul32(x, _H1)
+    x = x ^ (x >> 15)
+    x = _mul32(x, _H2)
+    return x ^ (x >> 16)
+
+
+def _pool_key(seed: int, stream: int) -> int:
+    k = int(_lowbias32(np.array([seed & _M32], np.int64))[0])
+    return int(_lowbias32(np.array([k ^ stream], np.int64))[0])
+
+
+def _page_elems(w: "Workload") -> int:
+    return w.num_kv_heads * w.page_size * w.head_dim
+
+
+def hashed_pages_host(w: "Workload", pages, stream: int) -> np.ndarray:
+    """bf16 bits (uint16) of the given physical pages of pool ``stream`` (STREAM_K or
+    STREAM_V) of a hashed workload: [len(pages), Hkv, ps, D] for K, [len(pages), Hkv, D, ps]
+    for V."""
+    key = _pool_key(w.seed, stream)
+    pk = _lowbias32(np.asarray(pages, np.int64)[:, None] ^ key)
+    u = _lowbias32(np.arange(_page_elems(w), dtype=np.int64)[None, :] ^ pk)
+    vals = ((u & 0xFF) + ((u >> 8) & 0xFF) - 255).astype(np.float32) / np.float32(128.0)
+    bits = np.empty(vals.shape, np.uint16)
+    f32_to_bf16_bits(np.ascontiguousarray(vals), bits)
+    H, ps, D = w.num_kv_heads, w.page_size, w.head_dim
+    return bits.reshape((len(pages), H, ps, D) if stream == STREAM_K else (len(pages), H, D, ps))
+
+
+def hashed_pools_device(w: "Workload", device="cuda", pages_per_chunk: int = 1024):
+    """The K and V pools of a hashed workload, made on the device (bf16 torch tensors)."""
+    import torch
+    E = _page_elems(w)
+    H, ps, D = w.num_kv_heads, w.page_size, w.head_dim
+    elems = torch.arange(E, dtype=torch.int64, device=device)[None, :]
+    out = []
+    for stream, shape in ((STREAM_K, (w.num_pages, H, ps, D)), (STREAM_V, (w.num_pages, H, D, ps))):
+        pool = torch.empty(shape, dtype=torch.bfloat16, device=device)
+        flat = pool.view(w.num_pages, E)
+        key = _pool_key(w.seed, stream)
+        for p0 in range(0, w.num_pages, pages_per_chunk):
+            p1 = min(w.num_pages, p0 + pages_per_chunk)
+            pk = _lowbias32(torch.arange(p0, p1, dtype=torch.int64, device=device)[:, None] ^ key)
+            u = _lowbias32(elems ^ pk)
+            flat[p0:p1] = (((u & 0xFF) + ((u >> 8) & 0xFF) - 255).to(torch.float32) / 128.0).to(torch.bfloat16)
+            del pk, u
+        out.append(pool)
+    return out[0], out[1]
+
+
+def host_kv_pages(w: "Workload", pages):
+    """(K, V) host values of the given physical pages, for any workload."""
+    pages = np.asarray(pages, np.int64)
+    if w.hashed_kv:
+        return hashed_pages_host(w, pages, STREAM_K), hashed_pages_host(w, pages, STREAM_V)
+    return w.k_pool[pages], w.v_pool[pages]
 
 
 def uniform_lengths(seed: int, n: int, lo: int, hi: int) -> np.ndarray:
@@ -242,6 +331,7 @@ CONFIG_NAMES = {
     51: "shared-prefix-64",
     6: "spec-decode-mtp3",
     7: "spec-decode-mtp7",
+    8: "long-context-decode-128k",
 }
 
 
@@ -300,4 +390,12 @@ def config(cid: int, seed: Optional[int] = None, poison_tail: bool = False,
         kv = np.maximum(kv, rows)
         return mk(CONFIG_NAMES[cid], [rows] * n, kv, num_q_heads=32, num_kv_heads=8, head_dim=128,
                   page_size=64, seed=s, poison_tail=poison_tail)
+    if cid == 8:
+        # 256 decodes at 128K context each, page 64: 256 x 2048 = 524,288 block-table entries
+        # ("GLM-5.3 推理全链路(八)", stage 4); the decode-heavy head layout.  K/V (137 GB in
+        # bf16) are hashed page values made on the device.
+        n = max(1, 256 // scale)
+        L = max(64, 131072 // scale)
+        return mk(CONFIG_NAMES[8], [1] * n, [L] * n, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                  page_size=64, seed=s, hashed_kv=True)
     raise ValueError(f"unknown config {cid}")

@@ -288,7 +288,7 @@ def hashed_pages_host(w: "Workload", pages, stream: int) -> np.ndarray:
     return bits.reshape((len(pages), H, ps, D) if stream == STREAM_K else (len(pages), H, D, ps))
 
 
-def hashed_pools_device(w: "Workload", device="cuda", pages_per_chunk: int = 1024):
+def hashed_pools_device(w: "Workload", device="cuda", pages_per_chunk: int = 4096):
     """The K and V pools of a hashed workload, made on the device (bf16 torch tensors)."""
     import torch
     E = _page_elems(w)

@@ -13,7 +13,8 @@ Modules
 ``accounting`` : closed-form counters (KV bytes per position, visible pairs, FLOPs,
                  logical vs physical KV bytes).
 ``kv_append``  : writing the iteration's new K/V into the paged pools (slot mapping).
-``fp8``        : fp8 e4m3fn KV storage with per-token float32 scales (decode, dequantise).
+``fp8``        : fp8 e4m3fn KV storage with per-token float32 scales (decode, dequantise,
+                 quantise and append new rows).
 
 Every function is pinned by a ``-m "not gpu"`` test in ``tests/test_oracle_pins.py``;
 none is "parity unpinned".
@@ -24,11 +25,12 @@ from .accounting import (kv_bytes_per_position, visible_pairs, attention_flops,
                          logical_kv_bytes, physical_kv_bytes)
 from .brute import brute_force_attention
 from .kv_append import slots_for_new_rows, append_kv
-from .fp8 import e4m3fn_to_f64, dequantize_pools
+from .fp8 import e4m3fn_to_f64, dequantize_pools, e4m3fn_round, quantize_rows, append_kv_fp8
 
 __all__ = [
     "bf16_bits_to_f64", "to_f64", "visibility_mask", "gather_kv", "attend",
     "varlen_paged_attention", "attention_rows", "kv_bytes_per_position", "visible_pairs",
     "attention_flops", "logical_kv_bytes", "physical_kv_bytes", "brute_force_attention",
-    "slots_for_new_rows", "append_kv", "e4m3fn_to_f64", "dequantize_pools",
+    "slots_for_new_rows", "append_kv", "e4m3fn_to_f64", "dequantize_pools", "e4m3fn_round", "quantize_rows",
+    "append_kv_fp8",
 ]

@@ -167,9 +167,91 @@ def check_generator_round_trip():
     assert np.all(np.abs(OF.e4m3fn_to_f64(w.k_pool)).max(axis=3) == 448.0)
 
 
+def _midpoints():
+    """Every value halfway between adjacent finite codes (float32-exact), both signs."""
+    v = OF.e4m3fn_to_f64(np.arange(0, 0x7F, dtype=np.uint8))
+    mid = ((v[:-1] + v[1:]) / 2).astype(np.float32)
+    assert np.array_equal(mid.astype(np.float64), (v[:-1] + v[1:]) / 2)
+    return np.concatenate([mid, -mid])
+
+
+def check_rounding_matches_torch():
+    """Nearest-even rounding to e4m3fn agrees with torch's float8_e4m3fn cast on random
+    magnitudes across the whole range, on every tie and on values one float32 ulp around
+    every tie."""
+    rng = np.random.default_rng(11)
+    y = (rng.standard_normal(100000) * rng.choice([1e-5, 1e-3, 0.1, 1, 30, 300], 100000)).astype(np.float32)
+    y = np.clip(y, -448, 448)
+    m = _midpoints()
+    y = np.concatenate([y, m, np.nextafter(m, np.float32(np.inf)), np.nextafter(m, np.float32(-np.inf)),
+                        np.array([0.0, -0.0, 448.0, -448.0, 2.0 ** -10, 2.0 ** -9], np.float32)])
+    want = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(OF.e4m3fn_round(y), want)
+
+
+def check_rounding_ties_and_round_trip():
+    """Every finite code's value rounds to itself; a tie between codes c and c+1 picks the
+    even one; 449 saturates to 448."""
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], np.uint8)
+    vals = OF.e4m3fn_to_f64(codes).astype(np.float32)
+    assert np.array_equal(OF.e4m3fn_round(vals), codes)
+    m = _midpoints()[:126]
+    got = OF.e4m3fn_round(m)
+    assert np.all(got % 2 == 0) and np.all((got == np.arange(126)) | (got == np.arange(1, 127)))
+    assert OF.e4m3fn_round(np.array([449.0, -449.0], np.float32)).tolist() == [0x7E, 0xFE]
+
+
+def check_quantize_rows():
+    """The largest magnitude of each vector maps to +-448; every element is within half a
+    step of x / scale; an all-zero vector has scale 1 and zero codes; the workload
+    generator's codes and scales are the same function."""
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((50, 3, 64)).astype(np.float32)
+    x[7, 1] = 0.0
+    codes, sc = OF.quantize_rows(x)
+    assert sc[7, 1] == 1.0 and not codes[7, 1].any()
+    dec = OF.e4m3fn_to_f64(codes)
+    nz = np.ones(x.shape[:2], bool)
+    nz[7, 1] = False
+    assert np.all(np.abs(dec).max(axis=-1)[nz] == 448.0)
+    y = x.astype(np.float64) / sc[..., None]
+    step = np.where(np.abs(y) >= 2.0 ** -6, np.abs(y) * 2.0 ** -4, 2.0 ** -10)
+    assert np.all(np.abs(dec - y) <= step * (1 + 1e-6))
+    gc, gs = W.quantize_fp8(x, axis=2)
+    assert np.array_equal(gc, codes) and np.array_equal(gs, sc)
+
+
+def check_append_fp8_slots():
+    """Quantised rows land in the slots out_cache_loc names (K row, transposed V column,
+    both scales); padding writes nothing; other slots keep their bits."""
+    P, H, ps, D = 4, 2, 16, 8
+    rng = np.random.default_rng(13)
+    k = rng.integers(0, 0x7F, (P, H, ps, D), dtype=np.uint8)
+    v = rng.integers(0, 0x7F, (P, H, D, ps), dtype=np.uint8)
+    ks = rng.uniform(0.1, 1, (P, H, ps)).astype(np.float32)
+    vs = rng.uniform(0.1, 1, (P, H, ps)).astype(np.float32)
+    kn = rng.standard_normal((3, H, D)).astype(np.float32)
+    vn = rng.standard_normal((3, H, D)).astype(np.float32)
+    loc = np.array([2 * ps + 5, -1, 0 * ps + 15])
+    k2, v2, ks2, vs2 = OF.append_kv_fp8(k, v, ks, vs, kn, vn, loc, ps)
+    kc, kq = OF.quantize_rows(kn)
+    vc, vq = OF.quantize_rows(vn)
+    assert np.array_equal(k2[2, :, 5, :], kc[0]) and np.array_equal(v2[2, :, :, 5], vc[0])
+    assert np.array_equal(ks2[2, :, 5], kq[0]) and np.array_equal(vs2[2, :, 5], vq[0])
+    assert np.array_equal(k2[0, :, 15, :], kc[2]) and np.array_equal(vs2[0, :, 15], vq[2])
+    touched = np.zeros((P, ps), bool)
+    touched[2, 5] = touched[0, 15] = True
+    for p in range(P):
+        for sl in range(ps):
+            if not touched[p, sl]:
+                assert np.array_equal(k2[p, :, sl], k[p, :, sl]) and np.array_equal(v2[p, :, :, sl], v[p, :, :, sl])
+                assert np.array_equal(ks2[p, :, sl], ks[p, :, sl]) and np.array_equal(vs2[p, :, sl], vs[p, :, sl])
+
+
 ALL_CHECKS = [check_closed_forms, check_all_codes_match_torch, check_grid_shape,
               check_dequantize_axes, check_dequantize_random, check_fp8_attention_brute_force,
-              check_scale_laws, check_generator_round_trip]
+              check_scale_laws, check_generator_round_trip, check_rounding_matches_torch,
+              check_rounding_ties_and_round_trip, check_quantize_rows, check_append_fp8_slots]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda c: c.__name__[6:])
@@ -209,7 +291,30 @@ def test_fp8_mutants_are_caught(monkeypatch):
     def v_scales_of_wrong_head(k, ks, v, vs):
         return real_deq(k, ks, v, np.asarray(vs)[:, ::-1, :])
 
-    mutants = {"exponent bias 8": ("e4m3fn_to_f64", bias8),
+    def round_ties_up(y):
+        c = real_round(y)
+        up = np.minimum((c & 0x7F) + 1, 0x7E) | (c & 0x80)
+        m = np.abs(np.asarray(y, np.float64))
+        hit = m == (OF.e4m3fn_to_f64(c & 0x7F) + OF.e4m3fn_to_f64(up & 0x7F)) / 2
+        return np.where(hit, up, c).astype(np.uint8)
+
+    def round_truncate(y):
+        c = real_round(y)
+        v = OF.e4m3fn_to_f64(c & 0x7F)
+        down = np.where((v > np.abs(np.asarray(y, np.float64))) & ((c & 0x7F) > 0), c - 1, c)
+        return down.astype(np.uint8)
+
+    def scale_by_max_not_448(x):
+        xx = np.asarray(x, np.float32)
+        amax = np.abs(xx).max(axis=-1)
+        sc = np.where(amax > 0, amax / np.float32(240.0), np.float32(1.0)).astype(np.float32)
+        return OF.e4m3fn_round(xx / sc[..., None]), sc
+
+    real_round = OF.e4m3fn_round
+    mutants = {"ties rounded up": ("e4m3fn_round", round_ties_up),
+               "truncating rounding": ("e4m3fn_round", round_truncate),
+               "scale for the wrong maximum": ("quantize_rows", scale_by_max_not_448),
+               "exponent bias 8": ("e4m3fn_to_f64", bias8),
                "subnormals read as normals": ("e4m3fn_to_f64", no_subnormals),
                "NaN codes read as numbers": ("e4m3fn_to_f64", nan_as_480),
                "V scaled by K's scales": ("dequantize_pools", v_with_k_scale),

@@ -191,31 +191,42 @@ def hbm_copy_gbps():
     return round(2 * n * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
 
 
-def append_line(api, W, cid, label, reps=50):
-    """Time varlen_attn_append_kv for one iteration's new rows (their slots from the plan);
-    algorithmic bytes = new K/V read + the same bytes written + the slot indices."""
+def append_line(api, W, cid, label, reps=50, dtype=None):
+    """Time varlen_attn_append_kv (fp8: varlen_attn_append_kv_fp8, which also quantises) for
+    one iteration's new rows (their slots from the plan); algorithmic bytes = new K/V read +
+    what is written (the same bytes; fp8: codes + one float32 scale per vector) + the slot
+    indices."""
     import torch
-    w = W.config(cid)
+    w = W.config(cid, dtype=dtype)
     plan = api.plan_for(w, flags=api.VA_FLAG_HOST_ONLY)
     loc = torch.from_numpy(api.varlen_attn_plan_slots(plan)).cuda()
     _, k, v, _ = api.to_device(w)
     T = int(loc.numel())
-    dt = k.dtype
+    fp8 = w.dtype == "fp8"
+    dt = torch.bfloat16 if fp8 else k.dtype
     k_new = torch.randn(T, w.num_kv_heads, w.head_dim, device="cuda").to(dt)
     v_new = torch.randn_like(k_new)
     args = dict(num_kv_heads=w.num_kv_heads, head_dim=w.head_dim, page_size=w.page_size, num_pages=w.num_pages,
-                k_new=k_new, v_new=v_new, out_cache_loc=loc, k_pool=k, v_pool=v, dtype=w.dtype)
+                k_new=k_new, v_new=v_new, out_cache_loc=loc, k_pool=k, v_pool=v)
+    if fp8:
+        ks, vs = api.scales_to_device(w)
+        args.update(k_scale=ks, v_scale=vs)
+        call = api.varlen_attn_append_kv_fp8
+    else:
+        args.update(dtype=w.dtype)
+        call = api.varlen_attn_append_kv
     for _ in range(5):
-        api.varlen_attn_append_kv(**args)
+        call(**args)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
     for _ in range(reps):
-        api.varlen_attn_append_kv(**args)
+        call(**args)
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / reps
-    byts = 2 * 2 * k_new.numel() * k_new.element_size() + 8 * T
+    written = 2 * k_new.numel() * (1 if fp8 else k_new.element_size()) + (2 * 4 * T * w.num_kv_heads if fp8 else 0)
+    byts = 2 * k_new.numel() * k_new.element_size() + written + 8 * T
     return {"workload": label, "us_per_step": round(us, 2), "hbm_GBps": round(byts / (us * 1e-6) / 1e9, 1),
             "hbm_frac": round(byts / (us * 1e-6) / PEAK_HBM, 4), "algorithmic_bytes": byts, "tokens": T}
 
@@ -398,10 +409,13 @@ def main():
         log("[bench] secondary: long-context decode 256 x 128K")
         sec.append(long_context_line(api, W))
         torch.cuda.empty_cache()
-        for cid, label in ((2, "kv-append: the ORCA iteration's 4098 new rows (32 KV heads, page 16)"),
-                           (3, "kv-append: the decode-heavy iteration's 256 new rows (8 KV heads, page 64)")):
+        for cid, label, dt in ((2, "kv-append: the ORCA iteration's 4098 new rows (32 KV heads, page 16)", None),
+                               (3, "kv-append: the decode-heavy iteration's 256 new rows (8 KV heads, page 64)", None),
+                               (2, "kv-append fp8 (quantise + scatter): the ORCA iteration's 4098 new rows", "fp8"),
+                               (3, "kv-append fp8 (quantise + scatter): the decode-heavy iteration's 256 new rows",
+                                "fp8")):
             log(f"[bench] secondary: {label}")
-            sec.append(append_line(api, W, cid, label))
+            sec.append(append_line(api, W, cid, label, dtype=dt))
             torch.cuda.empty_cache()
         sec.append({"workload": "torch copy 1 GiB (read+write) for reference", "hbm_GBps": hbm_copy_gbps()})
         rec["secondary"] = sec

@@ -73,7 +73,8 @@ typedef enum {
  * Scale Your Model 笔记(7-8)", section 4: a storage format widened on chip, the arithmetic
  * in the wider format; "GLM-5.3 推理全链路(八)", on the costs outside the 656-byte
  * ledger: FP32 scales stored with each token's FP8 data, both read to dequantise).
- * Such plans run with varlen_attn_run_fp8 and use the split-KV path for every row. */
+ * Such plans run with varlen_attn_run_fp8 and use the split-KV path for every row; new rows
+ * are stored with varlen_attn_append_kv_fp8. */
 typedef enum { VA_DTYPE_BF16 = 0, VA_DTYPE_F32 = 1, VA_DTYPE_FP8_E4M3 = 2 } va_dtype;
 
 enum {
@@ -198,6 +199,19 @@ va_status varlen_attn_run_events(const va_plan* plan, const void* q, const void*
 va_status varlen_attn_append_kv(const va_params* params, int64_t num_tokens, const void* k_new,
                                 const void* v_new, const int64_t* out_cache_loc, void* k_pool,
                                 void* v_pool, int32_t* bad_loc_count, void* stream);
+
+/* varlen_attn_append_kv for fp8 pools (params->dtype VA_DTYPE_FP8_E4M3): k_new, v_new are
+ * bf16 [num_tokens][num_kv_heads][head_dim] (finite values).  Each token's K vector and V
+ * vector of each KV head is stored as e4m3fn codes with its own float32 scale: scale =
+ * max|x| / 448 (float32 division; 1 for an all-zero vector) and code = x / scale rounded
+ * to the nearest e4m3fn value, ties to even ("GLM-5.3 推理全链路(八)", on the costs outside
+ * the 656-byte ledger: each token's FP8 data carries FP32 scales).  The codes go to
+ * k_pool / v_pool and the scales to k_scale / v_scale ([num_pages][num_kv_heads][page_size])
+ * at the token's out_cache_loc; padding, out-of-range entries and bad_loc_count behave as
+ * in varlen_attn_append_kv.  Enqueue only. */
+va_status varlen_attn_append_kv_fp8(const va_params* params, int64_t num_tokens, const void* k_new,
+                                    const void* v_new, const int64_t* out_cache_loc, void* k_pool, void* v_pool,
+                                    float* k_scale, float* v_scale, int32_t* bad_loc_count, void* stream);
 
 /* The out_cache_loc of the planned iteration (host int64 [total_q_rows]): flat row
  * q_start[r] + i of request r is logical position kv_len[r] - q_rows + i, in page

@@ -218,3 +218,102 @@ def test_fp8_run_errors():
     assert "aligned" in L.varlen_attn_last_error().decode()
     assert L.varlen_attn_run_fp8(*base) == api.VA_OK
     torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ fp8 append --
+
+def _bf16_rows(rng, shape, special=True):
+    """bf16 bit patterns of test rows: N(0,1) draws, plus (``special``) rows that reach the
+    subnormal codes (magnitudes spread over 2^-20 .. 4) and rows whose maximum is 448 so
+    that the scale is 1 and every other element sits exactly halfway between two codes."""
+    x = rng.standard_normal(shape).astype(np.float32)
+    T, H, D = shape
+    if not special:
+        bits = np.empty(shape, np.uint16)
+        W.f32_to_bf16_bits(x, bits)
+        return bits
+    x[0, 0] = np.ldexp(1.0, rng.integers(-20, 3, D)) * rng.choice([-1, 1], D)
+    mids = (oracle.e4m3fn_to_f64(np.arange(0, 0x7E, dtype=np.uint8)) +
+            oracle.e4m3fn_to_f64(np.arange(1, 0x7F, dtype=np.uint8))) / 2
+    row = rng.choice(mids, D) * rng.choice([-1, 1], D)
+    row[0] = 448.0
+    x[1 % T, H - 1] = row
+    x[min(2, T - 1), 0] = 0.0                        # all-zero vector: scale 1, zero codes
+    bits = np.empty(shape, np.uint16)
+    W.f32_to_bf16_bits(x, bits)
+    assert np.array_equal((bits[1 % T, H - 1].astype(np.uint32) << 16).view(np.float32), row.astype(np.float32))
+    return bits
+
+
+def _f32(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+@pytest.mark.parametrize("d,ps", [(128, 16), (64, 64), (128, 256)])
+def test_fp8_append_bit_exact(d, ps):
+    """GPU quantise-and-append == the oracle's, bit for bit (codes and scales), with
+    padding, an out-of-range entry (skipped and counted) and untouched slots kept."""
+    import torch
+    w = W.build("ap8", [37, 1, 5, 0, 200], [90, 300, 5, 10, 200], num_q_heads=8, num_kv_heads=4, head_dim=d,
+                page_size=ps, dtype="fp8", seed=29, extra_pages=3)
+    _say(f"[gpu] fp8 append d={d} ps={ps}")
+    plan = api.plan_for(w, flags=api.VA_FLAG_HOST_ONLY)
+    loc = api.varlen_attn_plan_slots(plan)
+    loc[3] = -1
+    loc[7] = w.num_pages * ps + 5                       # out of range: skipped, counted
+    rng = np.random.default_rng(7)
+    shape = (w.total_q_rows, w.num_kv_heads, d)
+    k_new, v_new = _bf16_rows(rng, shape), _bf16_rows(rng, shape)
+    ok = np.where(loc < w.num_pages * ps, loc, -1)
+    want = oracle.append_kv_fp8(w.k_pool, w.v_pool, w.k_scale, w.v_scale, _f32(k_new), _f32(v_new), ok, ps)
+    kp, vp = torch.from_numpy(w.k_pool.copy()).cuda(), torch.from_numpy(w.v_pool.copy()).cuda()
+    ks, vs = api.scales_to_device(w)
+    bad = torch.zeros(1, dtype=torch.int32, device="cuda")
+    api.varlen_attn_append_kv_fp8(num_kv_heads=w.num_kv_heads, head_dim=d, page_size=ps, num_pages=w.num_pages,
+                                  k_new=torch.from_numpy(k_new).view(torch.bfloat16).cuda(),
+                                  v_new=torch.from_numpy(v_new).view(torch.bfloat16).cuda(),
+                                  out_cache_loc=torch.from_numpy(loc).cuda(), k_pool=kp, v_pool=vp, k_scale=ks,
+                                  v_scale=vs, bad_loc_count=bad)
+    torch.cuda.synchronize()
+    assert int(bad.item()) == 1
+    for got, exp, name in zip((kp, vp, ks, vs), want, ("k codes", "v codes", "k scales", "v scales")):
+        g = got.cpu().numpy()
+        assert np.array_equal(g.view(np.uint8), np.ascontiguousarray(exp).view(np.uint8)), name
+
+
+@pytest.mark.parametrize("cid,scale", [(3, 16), (4, 16)])
+def test_fp8_append_then_attend(cid, scale):
+    """Quantise and append the iteration's new rows on the GPU into pools whose new-row
+    slots hold NaN codes, then attend: the output matches the oracle on the pools the
+    oracle's own append produces."""
+    import torch
+    w = W.config(cid, scale=scale, dtype="fp8")
+    _say(f"[gpu] fp8 append then attend config {cid}/{scale}")
+    plan = api.plan_for(w)
+    loc = api.varlen_attn_plan_slots(plan)
+    rng = np.random.default_rng(31)
+    shape = (w.total_q_rows, w.num_kv_heads, w.head_dim)
+    # N(0,1) rows: outputs of order 1, where the bf16 tolerance applies
+    k_new, v_new = _bf16_rows(rng, shape, special=False), _bf16_rows(rng, shape, special=False)
+    kb, vb = w.k_pool.copy(), w.v_pool.copy()
+    ksb, vsb = w.k_scale.copy(), w.v_scale.copy()
+    for l in loc[loc >= 0]:
+        kb[l // w.page_size, :, l % w.page_size, :] = W.FP8_NAN
+        vb[l // w.page_size, :, :, l % w.page_size] = W.FP8_NAN
+        ksb[l // w.page_size, :, l % w.page_size] = np.nan
+        vsb[l // w.page_size, :, l % w.page_size] = np.nan
+    w.k_pool, w.v_pool, w.k_scale, w.v_scale = oracle.append_kv_fp8(kb, vb, ksb, vsb, _f32(k_new), _f32(v_new), loc,
+                                                                     w.page_size)
+    q, _, _, bt = api.to_device(w)
+    kp, vp = torch.from_numpy(kb).cuda(), torch.from_numpy(vb).cuda()
+    ks, vs = torch.from_numpy(ksb).cuda(), torch.from_numpy(vsb).cuda()
+    api.varlen_attn_append_kv_fp8(num_kv_heads=w.num_kv_heads, head_dim=w.head_dim, page_size=w.page_size,
+                                  num_pages=w.num_pages, k_new=torch.from_numpy(k_new).view(torch.bfloat16).cuda(),
+                                  v_new=torch.from_numpy(v_new).view(torch.bfloat16).cuda(),
+                                  out_cache_loc=torch.from_numpy(loc).cuda(), k_pool=kp, v_pool=vp, k_scale=ks, v_scale=vs)
+    out = torch.zeros_like(q)
+    api.varlen_attn_run_fp8(plan, q, kp, vp, ks, vs, bt, out, api.new_workspace(plan))
+    torch.cuda.synchronize()
+    assert np.array_equal(kp.cpu().numpy(), w.k_pool) and np.array_equal(vs.cpu().numpy().view(np.uint32),
+                                                                          w.v_scale.view(np.uint32))
+    _check_full(w, out, f"fp8 append+attend {cid}/{scale}")

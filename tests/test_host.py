@@ -286,7 +286,18 @@ def test_fp8_debug_convert_argument_errors():
     assert L.varlen_attn_debug_fp8_to_bf16(None, None, 8, None) == api.VA_ERR_INVALID_ARG
 
 
-def test_fp8_append_is_refused():
+def test_fp8_append_argument_errors():
+    """fp8 pools take varlen_attn_append_kv_fp8 (codes and scales), and it takes only them."""
     L = api.lib()
     p = api.VaParams(0, 2, 64, 16, 8, 0, api.VA_DTYPE_FP8_E4M3, 0.0, 0, 0, 0)
-    assert L.varlen_attn_append_kv(p, 3, None, None, None, None, None, None, None) == api.VA_ERR_UNSUPPORTED
+    assert L.varlen_attn_append_kv(p, 3, None, None, None, None, None, None, None) == api.VA_ERR_INVALID_ARG
+    assert "varlen_attn_append_kv_fp8" in L.varlen_attn_last_error().decode()
+    n = (None,) * 9
+    assert L.varlen_attn_append_kv_fp8(None, 1, *n) == api.VA_ERR_INVALID_ARG
+    assert L.varlen_attn_append_kv_fp8(p, -1, *n) == api.VA_ERR_INVALID_ARG
+    assert L.varlen_attn_append_kv_fp8(p, 0, *n) == api.VA_OK
+    assert L.varlen_attn_append_kv_fp8(p, 3, *n) == api.VA_ERR_INVALID_ARG
+    pb = api.VaParams(0, 2, 64, 16, 8, 0, api.VA_DTYPE_BF16, 0.0, 0, 0, 0)
+    assert L.varlen_attn_append_kv_fp8(pb, 3, *n) == api.VA_ERR_INVALID_ARG
+    p.head_dim = 96
+    assert L.varlen_attn_append_kv_fp8(p, 3, *n) == api.VA_ERR_UNSUPPORTED

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvarlen_a
 EXPORTED = ["varlen_attn_plan", "varlen_attn_run", "varlen_attn_run_events", "varlen_attn_plan_stats", "varlen_attn_plan_export",
             "varlen_attn_debug_gather", "varlen_attn_plan_destroy", "varlen_attn_status_string",
             "varlen_attn_last_error", "varlen_attn_append_kv", "varlen_attn_plan_slots", "varlen_attn_run_fp8",
-            "varlen_attn_debug_fp8_to_bf16"]
+            "varlen_attn_debug_fp8_to_bf16", "varlen_attn_append_kv_fp8"]
 
 
 class VaParams(ctypes.Structure):
@@ -82,6 +82,8 @@ def lib():
         L.varlen_attn_run_fp8.restype = ctypes.c_int
         L.varlen_attn_debug_fp8_to_bf16.argtypes = [P, P, ctypes.c_int64, P]
         L.varlen_attn_debug_fp8_to_bf16.restype = ctypes.c_int
+        L.varlen_attn_append_kv_fp8.argtypes = [ctypes.POINTER(VaParams), ctypes.c_int64, P, P, P, P, P, P, P, P, P]
+        L.varlen_attn_append_kv_fp8.restype = ctypes.c_int
         L.varlen_attn_plan_stats.argtypes = [P, ctypes.POINTER(VaPlanStats)]
         L.varlen_attn_plan_stats.restype = ctypes.c_int
         L.varlen_attn_plan_export.argtypes = [P, ctypes.c_int32, ctypes.POINTER(i32p),
@@ -309,6 +311,25 @@ def varlen_attn_append_kv(*, num_kv_heads: int, head_dim: int, page_size: int, n
                                        _dev_ptr(out_cache_loc, "out_cache_loc", torch.int64),
                                        _dev_ptr(k_pool, "k_pool", dt), _dev_ptr(v_pool, "v_pool", dt),
                                        _dev_ptr(bad_loc_count, "bad_loc_count", torch.int32), _stream_ptr(stream)))
+
+
+def varlen_attn_append_kv_fp8(*, num_kv_heads: int, head_dim: int, page_size: int, num_pages: int, k_new, v_new,
+                              out_cache_loc, k_pool, v_pool, k_scale, v_scale, bad_loc_count=None,
+                              stream=None) -> None:
+    """Quantise k_new/v_new (bf16 [T, Hkv, D] GPU tensors) per (token, KV head) and write codes
+    into the uint8 pools and scales into the float32 scale pools at out_cache_loc."""
+    import torch
+    p = VaParams(0, num_kv_heads, head_dim, page_size, num_pages, 0, VA_DTYPE_FP8_E4M3, 0.0, 0, 0, 0)
+    T = int(out_cache_loc.numel())
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if tuple(t.shape) != (T, num_kv_heads, head_dim):
+            raise ValueError(f"{name} must be [{T}, {num_kv_heads}, {head_dim}]")
+    _check(lib().varlen_attn_append_kv_fp8(
+        ctypes.byref(p), T, _dev_ptr(k_new, "k_new", torch.bfloat16), _dev_ptr(v_new, "v_new", torch.bfloat16),
+        _dev_ptr(out_cache_loc, "out_cache_loc", torch.int64), _dev_ptr(k_pool, "k_pool", torch.uint8),
+        _dev_ptr(v_pool, "v_pool", torch.uint8), _dev_ptr(k_scale, "k_scale", torch.float32),
+        _dev_ptr(v_scale, "v_scale", torch.float32), _dev_ptr(bad_loc_count, "bad_loc_count", torch.int32),
+        _stream_ptr(stream)))
 
 
 def new_workspace(plan: Plan, device="cuda"):

@@ -81,7 +81,8 @@ extern "C" va_status varlen_attn_append_kv(const va_params* params, int64_t num_
   const int ps = p.page_size;
   if (ps != 16 && ps != 32 && ps != 64 && ps != 128 && ps != 256)
     return fail(VA_ERR_UNSUPPORTED, "page_size must be 16, 32, 64, 128 or 256");
-  if (p.dtype == VA_DTYPE_FP8_E4M3) return fail(VA_ERR_UNSUPPORTED, "append of fp8 pools is not built");
+  if (p.dtype == VA_DTYPE_FP8_E4M3)
+    return fail(VA_ERR_INVALID_ARG, "fp8 pools are written with varlen_attn_append_kv_fp8 (codes and scales)");
   if (p.dtype != VA_DTYPE_BF16 && p.dtype != VA_DTYPE_F32) return fail(VA_ERR_INVALID_ARG, "unknown dtype");
   if (num_tokens == 0) return VA_OK;
   if (!k_new || !v_new || !out_cache_loc || !k_pool || !v_pool)

@@ -9,6 +9,7 @@
 // The scales are applied in fp32 outside the MFMAs: a K scale multiplies its key's scores
 // before the softmax, a V scale multiplies its key's probability before P is rounded to
 // bf16 for the P.V product (the row sum uses the unscaled probability).
+// The file also holds the append of new rows into fp8 pools (quantisation + scatter).
 #include <hip/hip_runtime.h>
 
 #include <string>
@@ -235,9 +236,168 @@ __global__ __launch_bounds__(256) void fp8_to_bf16_kernel(const uint32_t* __rest
   if (t < groups) out[t] = fp8x8_to_bf16(codes[2 * t], codes[2 * t + 1]);
 }
 
+// ---------------------------------------------------------------- fp8 append --
+// Storing new rows: per (token, KV head) vector, scale = max|x| / 448 in float32 (IEEE
+// division; 1 for an all-zero vector), code = x / scale rounded to the nearest e4m3fn
+// value with ties to the even code, magnitudes from 448 up taking the largest finite code.
+
+// Nearest-even e4m3fn code of a finite float32, from the format's definition.
+__device__ __forceinline__ uint32_t f32_to_e4m3fn(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  const float fa = __uint_as_float(a);
+  if (!(fa < 448.f)) return sign | 0x7eu;
+  if (fa >= 0.015625f) {                       // normal e4m3fn range, 2^-6 and up
+    const uint32_t e = (a >> 23) - 127u + 7u;  // biased e4m3 exponent, 1..15
+    const uint32_t keep = (a >> 20) & 7u, rem = a & 0xfffffu;
+    uint32_t code = (e << 3) | keep;
+    if (rem > 0x80000u || (rem == 0x80000u && (keep & 1u))) code += 1u;   // carries into the exponent
+    return sign | code;
+  }
+  return sign | uint32_t(rintf(fa * 512.f));   // subnormal steps of 2^-9; 8 is the code of 2^-6
+}
+
+constexpr int kAppendFp8Tok = 64;
+
+// One workgroup per (KV head, up to 64 consecutive tokens).  Each wave quantises four rows
+// at a time: lane group grp = lane / 16 takes token tt = 4*wave + 16*i + grp (i = 0..3), lane
+// s = lane % 16 its elements EPS*s .. +EPS-1 (one 16- or 8-byte load); the maximum is
+// reduced over the 16 lanes of the group.  All of a wave's loads are issued before any
+// row is quantised.  K codes and both scales are written directly, V codes go through LDS
+// so that the transposed V pages are written with the token index fastest (tokens that
+// fill consecutive slots of a page write consecutive bytes).
+template <int D>
+__global__ __launch_bounds__(256) void append_kv_fp8_kernel(
+    const bf16* __restrict__ k_new, const bf16* __restrict__ v_new, const int64_t* __restrict__ loc, int64_t ntok,
+    int tpw_log2, int Hkv, int ps, int64_t nslots, uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
+    float* __restrict__ k_scale, float* __restrict__ v_scale, int32_t* __restrict__ bad) {
+  constexpr int EPS = D / 16;                    // elements per lane of a row group
+  constexpr int IT = kAppendFp8Tok / 16;         // row groups per wave
+  constexpr int VROW = D + 4;                    // padded code row: token-strided reads spread over banks
+  typedef __bf16 row_t __attribute__((ext_vector_type(EPS)));
+  __shared__ uint8_t vcode[kAppendFp8Tok * VROW];
+  __shared__ int64_t tloc[kAppendFp8Tok];
+  const int kvh = blockIdx.y;
+  const int tpw = 1 << tpw_log2;
+  const int64_t t0 = int64_t(blockIdx.x) << tpw_log2;
+  const int n = int(min<int64_t>(tpw, ntok - t0));
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = lane >> 4, sub = lane & 15;
+  if (tid < kAppendFp8Tok) {
+    int64_t l = tid < n ? loc[t0 + tid] : -1;
+    if (l >= nslots) {
+      if (bad && kvh == 0) atomicAdd(bad, 1);
+      l = -1;
+    }
+    tloc[tid] = l;
+  }
+  row_t kx[IT], vx[IT];
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    if (4 * wave + 16 * i >= n) break;              // wave-uniform
+    const int tt = min(4 * wave + 16 * i + grp, n - 1);   // rows past n: loaded, not stored
+    const size_t src = size_t((t0 + tt) * Hkv + kvh) * D + EPS * sub;
+    kx[i] = *reinterpret_cast<const row_t*>(k_new + src);
+    vx[i] = *reinterpret_cast<const row_t*>(v_new + src);
+  }
+  __syncthreads();
+  auto quant = [&](const row_t& row, uint32_t (&c)[EPS]) -> float {
+    float x[EPS], amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPS; ++e) {
+      x[e] = float(row[e]);
+      amax = fmaxf(amax, fabsf(x[e]));
+    }
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    const float scale = amax > 0.f ? amax / 448.f : 1.f;
+#pragma unroll
+    for (int e = 0; e < EPS; ++e) c[e] = f32_to_e4m3fn(x[e] / scale);
+    return scale;
+  };
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const int tt = 4 * wave + 16 * i + grp;
+    if (4 * wave + 16 * i >= n) break;            // wave-uniform: no row of this group exists
+    uint32_t kc[EPS], vc[EPS];
+    const float ks = quant(kx[i], kc);
+    const float vs = quant(vx[i], vc);
+    if (tt >= n) continue;
+#pragma unroll
+    for (int e = 0; e < EPS; ++e) vcode[tt * VROW + EPS * sub + e] = uint8_t(vc[e]);
+    const int64_t l = tloc[tt];
+    if (l < 0) continue;
+    const int64_t page = l / ps, slot = l % ps;
+    const size_t srow = size_t(page * Hkv + kvh) * ps + slot;
+    uint32_t w[EPS / 4];
+#pragma unroll
+    for (int j = 0; j < EPS / 4; ++j)
+      w[j] = kc[4 * j] | (kc[4 * j + 1] << 8) | (kc[4 * j + 2] << 16) | (kc[4 * j + 3] << 24);
+    uint8_t* kd = k_pool + srow * D + EPS * sub;
+    if constexpr (EPS == 8)
+      *reinterpret_cast<uint2*>(kd) = uint2{w[0], w[1]};
+    else
+      *reinterpret_cast<uint32_t*>(kd) = w[0];
+    if (sub == 0) {
+      k_scale[srow] = ks;
+      v_scale[srow] = vs;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < tpw * D; e += blockDim.x) {
+    const int tt = e & (tpw - 1), d = e >> tpw_log2;
+    if (tt >= n) continue;
+    const int64_t l = tloc[tt];
+    if (l < 0) continue;
+    const int64_t page = l / ps, slot = l % ps;
+    v_pool[(size_t(page * Hkv + kvh) * D + d) * ps + slot] = vcode[tt * VROW + d];
+  }
+}
+
 }  // namespace va
 
 using namespace va;
+
+extern "C" va_status varlen_attn_append_kv_fp8(const va_params* params, int64_t num_tokens, const void* k_new,
+                                               const void* v_new, const int64_t* out_cache_loc, void* k_pool,
+                                               void* v_pool, float* k_scale, float* v_scale,
+                                               int32_t* bad_loc_count, void* stream) {
+  if (!params) return fail(VA_ERR_INVALID_ARG, "params is NULL");
+  const va_params& p = *params;
+  if (num_tokens < 0) return fail(VA_ERR_INVALID_ARG, "num_tokens < 0");
+  if (p.num_kv_heads < 1 || p.num_pages < 1) return fail(VA_ERR_INVALID_ARG, "num_kv_heads and num_pages must be >= 1");
+  if (p.dtype != VA_DTYPE_FP8_E4M3)
+    return fail(VA_ERR_INVALID_ARG, "varlen_attn_append_kv_fp8 needs dtype VA_DTYPE_FP8_E4M3");
+  if (p.head_dim != 64 && p.head_dim != 128) return fail(VA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  const int ps = p.page_size;
+  if (ps != 16 && ps != 32 && ps != 64 && ps != 128 && ps != 256)
+    return fail(VA_ERR_UNSUPPORTED, "page_size must be 16, 32, 64, 128 or 256");
+  if (num_tokens == 0) return VA_OK;
+  if (!k_new || !v_new || !out_cache_loc || !k_pool || !v_pool || !k_scale || !v_scale)
+    return fail(VA_ERR_INVALID_ARG, "k_new, v_new, out_cache_loc, the pools and the scale pools must be non-NULL");
+  const int Hkv = p.num_kv_heads;
+  const int64_t nslots = int64_t(p.num_pages) * ps;
+  int tpw_log2 = 6;
+  while (tpw_log2 > 0 && ((num_tokens * Hkv) >> tpw_log2) < 1024) --tpw_log2;
+  const int tpw = 1 << tpw_log2;
+  const dim3 block(256), grid(unsigned((num_tokens + tpw - 1) / tpw), unsigned(Hkv));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto* kn = static_cast<const bf16*>(k_new);
+  auto* vn = static_cast<const bf16*>(v_new);
+  auto* kp = static_cast<uint8_t*>(k_pool);
+  auto* vp = static_cast<uint8_t*>(v_pool);
+  (void)hipGetLastError();
+  if (p.head_dim == 128)
+    append_kv_fp8_kernel<128><<<grid, block, 0, s>>>(kn, vn, out_cache_loc, num_tokens, tpw_log2, Hkv, ps, nslots, kp, vp,
+                                                      k_scale, v_scale, bad_loc_count);
+  else
+    append_kv_fp8_kernel<64><<<grid, block, 0, s>>>(kn, vn, out_cache_loc, num_tokens, tpw_log2, Hkv, ps, nslots, kp, vp,
+                                                     k_scale, v_scale, bad_loc_count);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(VA_ERR_HIP, std::string("fp8 append kernel launch: ") + hipGetErrorString(e));
+  return VA_OK;
+}
 
 extern "C" va_status varlen_attn_debug_fp8_to_bf16(const uint8_t* codes, uint16_t* out, int64_t n, void* stream) {
   if (n < 0 || n % 8 != 0) return fail(VA_ERR_INVALID_ARG, "n must be a non-negative multiple of 8");

@@ -402,7 +402,9 @@ def main():
                  None),
                 (3, 0, "decode-heavy-gqa in fp8 e4m3fn KV + per-position fp32 scales", None, "decode_fp8", "fp8"),
                 (51, api.VA_FLAG_SHARED_PREFIX, "shared-prefix-64 in fp8 e4m3fn KV + scales", flush, "shared64_fp8",
-                 "fp8")):
+                 "fp8"),
+                (4, 0, "chunked-prefill-mix in fp8 e4m3fn KV + scales", None, "chunk_fp8", "fp8"),
+                (2, 0, "orca-mixed in fp8 e4m3fn KV + scales", None, "orca_fp8", "fp8")):
             log(f"[bench] secondary: {label}")
             sec.append(secondary(api, W, cid, flags, 20, label, fl, key, dt))
             torch.cuda.empty_cache()

@@ -212,9 +212,7 @@ def test_plan_counters_match_oracle(name, make, flags):
                                                                w.num_kv_heads, w.head_dim, w.elem_bytes,
                                                                scale_bytes=w.scale_bytes)
     if w.dtype == "fp8":
-        # every row runs on the split-KV kernel: no MFMA prefill or shared-prefix tiles
-        assert st["prefill_tiles"] == 0 and st["shared_tiles"] == 0 and st["prefill_flops"] == 0
-        assert st["q_bytes"] == int(m.sum()) * w.num_q_heads * w.head_dim * 2
+        assert st["q_bytes"] == int(m.sum()) * w.num_q_heads * w.head_dim * 2      # bf16 rows
 
 
 def test_shared_prefix_groups_found():

@@ -342,8 +342,12 @@ __device__ __forceinline__ float other_half(float x) {
 }
 
 // Buffer resource over one page slice (wave-uniform base, raw addressing).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t slice_rsrc(const bf16* base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base), (short)0, 0x7fffffff, 0x00020000);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slice_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
+}
+// 4 bytes per lane from rs + voff into LDS at dst + 4 * lane.
+__device__ __forceinline__ void dma_b32(__amdgpu_buffer_rsrc_t rs, void* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 4, voff, 0, 0, 0);
 }
 // 16 bytes per lane from rs + voff + soff into LDS at dst + 16 * lane.
 __device__ __forceinline__ void dma_b128(__amdgpu_buffer_rsrc_t rs, bf16x8* dst, uint32_t voff, int soff) {
@@ -370,12 +374,19 @@ constexpr int prefill_lds_bytes() {
 // [S0, kv_end) of request req's block table (pages every member shares, all visible to
 // every member row), and each column's unnormalised partial (m, l, acc) goes to workspace
 // slot pbase + q0 for the combine pass.
-template <int D, bool GROUP>
+//
+// F8 = true: the pools hold fp8 e4m3fn codes with per-position float32 scales.  Each wave
+// copies its 16-key slice of codes (and the 16 K or V scales) by LDS-DMA into the upper
+// part of the same slice's bf16 area, then, once its copies have landed, widens them in
+// place to bf16(code * scale) in the layouts above, so the MFMA loop is the bf16 one.
+// The slice is the wave's own, and all its reads precede its writes, so no other wave is
+// involved until the barrier that ends the iteration.
+template <int D, bool GROUP, bool F8>
 __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_bf16_kernel(
     const PrefillTile* __restrict__ tiles, const Column* __restrict__ cols, const bf16* __restrict__ q,
-    const bf16* __restrict__ kpool, const bf16* __restrict__ vpool, const int32_t* __restrict__ bt, int bt_stride,
-    bf16* __restrict__ out, float* __restrict__ ws_ml, float* __restrict__ ws_acc, int Hq, int g, Paged pg,
-    float scale_log2) {
+    const void* __restrict__ kpool, const void* __restrict__ vpool, const float* __restrict__ kscale,
+    const float* __restrict__ vscale, const int32_t* __restrict__ bt, int bt_stride, bf16* __restrict__ out,
+    float* __restrict__ ws_ml, float* __restrict__ ws_acc, int Hq, int g, Paged pg, float scale_log2) {
   using Lay = PrefillLds<D>;
   constexpr int KCH = Lay::KCH, KROW = Lay::KROW, KBUF = Lay::KBUF, VBUF = Lay::VBUF;
   constexpr int WK = kPSliceKeys;                      // 16 keys per wave slice
@@ -444,9 +455,16 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
   const int kv_end = T.kv_end;
   const int ntiles = (kv_end - kbeg + kPTileKeys - 1) / kPTileKeys;   // tile t: keys kbeg + 64t ..
   const int ps_mask = (1 << pg.ps_shift) - 1;
-  const size_t page_elems = (size_t(pg.Hkv) * D) << pg.ps_shift;
-  const bf16* kbase = kpool + pg.k_row(0, kvh, 0);
-  const bf16* vbase = vpool + pg.v_elem(0, kvh, 0, 0);
+  constexpr int EB = F8 ? 1 : 2;                       // bytes per stored element
+  const size_t page_bytes = ((size_t(pg.Hkv) * D) << pg.ps_shift) * EB;
+  const char* kbase = static_cast<const char*>(kpool) + pg.k_row(0, kvh, 0) * EB;
+  const char* vbase = static_cast<const char*>(vpool) + pg.v_elem(0, kvh, 0, 0) * EB;
+  // fp8: raw slice sizes (16-byte chunks) and where they sit inside the bf16 slices
+  constexpr int KR = WK * D / 16;                      // K codes of the slice
+  constexpr int VR = D;                                // V codes: one chunk (16 keys) per d
+  constexpr int KRAW = KSC - KR, KSCL = KRAW - 4;      // raw K codes, then 16 K scales before them
+  constexpr int VRAW = VSC - VR, VSCL = VRAW - 4;
+  static_assert(KSCL >= 0 && VSCL >= 0, "raw fp8 slices must fit in the bf16 slices");
 
   // ---- per-lane DMA source offsets (bytes from the slice base)
   // K instruction r, lane -> slice chunk L = 64r + lane = (key L / KROW, d-chunk L % KROW);
@@ -470,11 +488,19 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
   auto issue_k = [&](int t, int page, int buf) {
     const int k0w = kbeg + t * kPTileKeys + wv * WK;
     if (k0w >= kv_end) return;               // positions past the end: scores are masked
-    const auto rs = slice_rsrc(kbase + size_t(page) * page_elems + size_t(k0w & ps_mask) * D);
+    const auto rs = slice_rsrc(kbase + size_t(page) * page_bytes + size_t(k0w & ps_mask) * D * EB);
     bf16x8* dst = sK + buf * KBUF + wv * KSC;
+    if constexpr (F8) {
+      // codes: lane -> raw chunk L = 64r + lane = (key L / (D/16), 16-byte piece L % (D/16))
 #pragma unroll
-    for (int r = 0; r < KNI; ++r)
-      if (r < KNI - 1 || lane < KLAST) dma_b128(rs, dst + 64 * r, koff[r], 0);
+      for (int r = 0; r < KR / 64; ++r) dma_b128(rs, dst + KRAW + 64 * r, uint32_t(16 * (64 * r + lane)), 0);
+      const auto rsc = slice_rsrc(kscale + pg.scale_idx(page, kvh, k0w & ps_mask));
+      if (lane < WK) dma_b32(rsc, dst + KSCL, uint32_t(4 * lane));
+    } else {
+#pragma unroll
+      for (int r = 0; r < KNI; ++r)
+        if (r < KNI - 1 || lane < KLAST) dma_b128(rs, dst + 64 * r, koff[r], 0);
+    }
   };
   auto issue_v = [&](int t, int page, int buf) {
     const int k0w = kbeg + t * kPTileKeys + wv * WK;
@@ -484,13 +510,101 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
       for (int r = 0; r < VNI; ++r) dst[64 * r + lane] = bf16x8{};
       return;
     }
-    const auto rs = slice_rsrc(vbase + size_t(page) * page_elems + (k0w & ps_mask));
+    const auto rs = slice_rsrc(vbase + size_t(page) * page_bytes + (k0w & ps_mask) * EB);
+    if constexpr (F8) {
+      // codes: lane -> raw chunk d = 64r + lane, the 16 keys of V page row d
 #pragma unroll
-    for (int r = 0; r < VNI; ++r) dma_b128(rs, dst + 64 * r, voff, r * vrstep);
+      for (int r = 0; r < VR / 64; ++r) dma_b128(rs, dst + VRAW + 64 * r, uint32_t((64 * r + lane) << pg.ps_shift), 0);
+      const auto rsc = slice_rsrc(vscale + pg.scale_idx(page, kvh, k0w & ps_mask));
+      if (lane < WK) dma_b32(rsc, dst + VSCL, uint32_t(4 * lane));
+    } else {
+#pragma unroll
+      for (int r = 0; r < VNI; ++r) dma_b128(rs, dst + 64 * r, voff, r * vrstep);
+    }
+  };
+  // fp8: widen the slice's codes in place once its copies have landed (own slice only)
+  // the 16 codes of a raw chunk as floats (bytes 0..15 in order)
+  auto codes16 = [&](const bf16x8& raw, float (&f)[16]) {
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(&raw);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(int(w[i]), false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(int(w[i]), true);
+      f[4 * i] = lo[0];
+      f[4 * i + 1] = lo[1];
+      f[4 * i + 2] = hi[0];
+      f[4 * i + 3] = hi[1];
+    }
+  };
+  auto widen16 = [&](const bf16x8& raw, float sc, bf16x8 (&o)[2]) {
+    float f[16];
+    codes16(raw, f);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[e >> 3][e & 7] = bf16(f[e] * sc);
+  };
+  auto convert_k = [&](int t, int buf) {
+    if constexpr (F8) {
+      const int k0w = kbeg + t * kPTileKeys + wv * WK;
+      if (k0w >= kv_end) return;
+      bf16x8* sl = sK + buf * KBUF + wv * KSC;
+      constexpr int PER = KR / 64;                      // raw chunks per lane
+      bf16x8 raw[PER];
+      float sc[PER];
+      const float* scl = reinterpret_cast<const float*>(sl + KSCL);
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        raw[i] = sl[KRAW + 64 * i + lane];
+        sc[i] = scl[(64 * i + lane) / (D / 16)];
+      }
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int L = 64 * i + lane, key = L / (D / 16), pc = L % (D / 16);
+        bf16x8 o[2];
+        widen16(raw[i], sc[i], o);
+        sl[key * KROW + 2 * pc] = o[0];
+        sl[key * KROW + 2 * pc + 1] = o[1];
+      }
+    }
+  };
+  auto convert_v = [&](int t, int buf) {
+    if constexpr (F8) {
+      const int k0w = kbeg + t * kPTileKeys + wv * WK;
+      if (k0w >= kv_end) return;                        // zeros were written instead
+      bf16x8* sl = sV + buf * VBUF + wv * VSC;
+      constexpr int PER = VR / 64;
+      bf16x8 raw[PER];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) raw[i] = sl[VRAW + 64 * i + lane];
+      float sc[WK];
+      const f32x4* scl = reinterpret_cast<const f32x4*>(sl + VSCL);
+#pragma unroll
+      for (int i = 0; i < WK / 4; ++i) {
+        const f32x4 x = scl[i];
+        sc[4 * i] = x[0];
+        sc[4 * i + 1] = x[1];
+        sc[4 * i + 2] = x[2];
+        sc[4 * i + 3] = x[3];
+      }
+      const int valid = kv_end - k0w;                   // keys of the slice before the end
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int d = 64 * i + lane;
+        float f[16];
+        codes16(raw[i], f);
+        bf16x8 o[2];
+#pragma unroll
+        for (int k = 0; k < WK; ++k)   // positions at or past the end may be unwritten slots: zero, not 0 * NaN
+          o[k >> 3][k & 7] = k < valid ? bf16(f[k] * sc[k]) : bf16(0.f);
+        const int flip = (d >> 3) & 1;
+        sl[2 * d + flip] = o[0];
+        sl[2 * d + (flip ^ 1)] = o[1];
+      }
+    }
   };
   // after the copy of V(t) landed: zero the positions at or past the tile's end (they may
   // be unwritten slots; their scores are masked, but 0 * NaN would still be NaN)
   auto fix_v_tail = [&](int t, int buf) {
+    if constexpr (F8) return;                 // the widening zeroes those positions
     const int k0w = kbeg + t * kPTileKeys + wv * WK;
     if (k0w >= kv_end || k0w + WK <= kv_end) return;
     bf16x8* dst = sV + buf * VBUF + wv * VSC;
@@ -542,6 +656,9 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
     if (ntiles > 1) issue_k(1, p1, 1);
     wait_vmem();
     fix_v_tail(0, 0);
+    convert_k(0, 0);
+    convert_v(0, 0);
+    if (ntiles > 1) convert_k(1, 1);
   }
   int p2 = ntiles > 2 ? page_for(2) : 0;
   int p3 = ntiles > 3 ? page_for(3) : 0;
@@ -606,6 +723,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
     }
     wait_vmem();
     if (ld_v) fix_v_tail(j + 1, (j + 1) & 1);
+    if (ld_k) convert_k(j + 2, j & 1);
+    if (ld_v) convert_v(j + 1, (j + 1) & 1);
     __syncthreads();
   }
   // ---- normalise and write: acc[db][4*ii + jj] is d = 32*db + 8*ii + 4*h + jj of this column
@@ -726,7 +845,7 @@ static va_status hip_fail(const char* what, hipError_t e) {
 }
 
 bool prefill_kernel_available(const va_params& p) {
-  return p.dtype == VA_DTYPE_BF16 && (p.head_dim == 64 || p.head_dim == 128);
+  return (p.dtype == VA_DTYPE_BF16 || p.dtype == VA_DTYPE_FP8_E4M3) && (p.head_dim == 64 || p.head_dim == 128);
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -735,10 +854,14 @@ static va_status prepare_kernels() {
   // the prefill kernel's dynamic LDS exceeds the 64 KiB default limit
   static hipError_t once = [] {
     const std::pair<const void*, int> kernels[] = {
-        {reinterpret_cast<const void*>(&prefill_bf16_kernel<128, false>), prefill_lds_bytes<128>()},
-        {reinterpret_cast<const void*>(&prefill_bf16_kernel<64, false>), prefill_lds_bytes<64>()},
-        {reinterpret_cast<const void*>(&prefill_bf16_kernel<128, true>), prefill_lds_bytes<128>()},
-        {reinterpret_cast<const void*>(&prefill_bf16_kernel<64, true>), prefill_lds_bytes<64>()}};
+        {reinterpret_cast<const void*>(&prefill_bf16_kernel<128, false, false>), prefill_lds_bytes<128>()},
+        {reinterpret_cast<const void*>(&prefill_bf16_kernel<64, false, false>), prefill_lds_bytes<64>()},
+        {reinterpret_cast<const void*>(&prefill_bf16_kernel<128, true, false>), prefill_lds_bytes<128>()},
+        {reinterpret_cast<const void*>(&prefill_bf16_kernel<64, true, false>), prefill_lds_bytes<64>()},
+        {reinterpret_cast<const void*>(&prefill_bf16_kernel<128, false, true>), prefill_lds_bytes<128>()},
+        {reinterpret_cast<const void*>(&prefill_bf16_kernel<64, false, true>), prefill_lds_bytes<64>()},
+        {reinterpret_cast<const void*>(&prefill_bf16_kernel<128, true, true>), prefill_lds_bytes<128>()},
+        {reinterpret_cast<const void*>(&prefill_bf16_kernel<64, true, true>), prefill_lds_bytes<64>()}};
     for (const auto& k : kernels) {
       const hipError_t e = hipFuncSetAttribute(k.first, hipFuncAttributeMaxDynamicSharedMemorySize, k.second);
       if (e != hipSuccess) return e;
@@ -855,26 +978,27 @@ static va_status run_impl(const va_plan* plan, const void* q, const void* k_pool
   };
   if ((e = mark(0)) != hipSuccess) return hip_fail("hipEventRecord", e);
   const int ntiles = int(plan->tiles.size()), ngtiles = int(plan->gtiles.size());
-  auto launch_tiles = [&](auto group, const PrefillTile* tl, int n) {
-    constexpr bool G = decltype(group)::value;
+  auto launch_tiles = [&](auto group, auto f8, const PrefillTile* tl, int n) {
+    constexpr bool G = decltype(group)::value, F = decltype(f8)::value;
     const dim3 grid(n), block(64 * kPrefillWaves);
     auto* qq = static_cast<const bf16*>(q);
-    auto* kk = static_cast<const bf16*>(k_pool);
-    auto* vv = static_cast<const bf16*>(v_pool);
     auto* oo = static_cast<bf16*>(out);
     if (D == 128)
-      prefill_bf16_kernel<128, G><<<grid, block, prefill_lds_bytes<128>(), s>>>(
-          tl, plan->d_cols, qq, kk, vv, block_table_dev, bt_stride, oo, ws_ml, ws_acc, p.num_q_heads, plan->g, pg,
-          scale_log2);
+      prefill_bf16_kernel<128, G, F><<<grid, block, prefill_lds_bytes<128>(), s>>>(
+          tl, plan->d_cols, qq, k_pool, v_pool, k_scale, v_scale, block_table_dev, bt_stride, oo, ws_ml, ws_acc,
+          p.num_q_heads, plan->g, pg, scale_log2);
     else
-      prefill_bf16_kernel<64, G><<<grid, block, prefill_lds_bytes<64>(), s>>>(
-          tl, plan->d_cols, qq, kk, vv, block_table_dev, bt_stride, oo, ws_ml, ws_acc, p.num_q_heads, plan->g, pg,
-          scale_log2);
+      prefill_bf16_kernel<64, G, F><<<grid, block, prefill_lds_bytes<64>(), s>>>(
+          tl, plan->d_cols, qq, k_pool, v_pool, k_scale, v_scale, block_table_dev, bt_stride, oo, ws_ml, ws_acc,
+          p.num_q_heads, plan->g, pg, scale_log2);
     return hipGetLastError();
   };
-  if (ntiles && (e = launch_tiles(std::false_type{}, plan->d_tiles, ntiles)) != hipSuccess)
+  auto launch_kind = [&](auto group, const PrefillTile* tl, int n) {
+    return fp8 ? launch_tiles(group, std::true_type{}, tl, n) : launch_tiles(group, std::false_type{}, tl, n);
+  };
+  if (ntiles && (e = launch_kind(std::false_type{}, plan->d_tiles, ntiles)) != hipSuccess)
     return hip_fail("prefill kernel launch", e);
-  if (ngtiles && (e = launch_tiles(std::true_type{}, plan->d_gtiles, ngtiles)) != hipSuccess)
+  if (ngtiles && (e = launch_kind(std::true_type{}, plan->d_gtiles, ngtiles)) != hipSuccess)
     return hip_fail("shared-prefix tile kernel launch", e);
   if ((e = mark(1)) != hipSuccess) return hip_fail("hipEventRecord", e);
   if (nitems) {

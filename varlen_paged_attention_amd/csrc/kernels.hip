@@ -35,8 +35,10 @@ namespace va {
 // 32u + 8*grp .. +7 of sub-step u -- exactly the k-slice the P^T operand of the
 // O^T += V^T . P^T MFMA needs -- so P never leaves registers.  V^T's 8-key slices are
 // contiguous because V pages are stored transposed.
-// One wavefront runs item `idx`.
-template <int D>
+// One wavefront runs item `idx`.  NC = blocks of 16 query columns: with NC = 2 the item has
+// up to 32 columns (multi-row decode with g * rows > 16) and every K/V load serves both
+// blocks, so the kv range is read once instead of twice.
+template <int D, int NC>
 __device__ __forceinline__ void split_kv_bf16_wave(
     int idx, const SplitItem* __restrict__ items, const Column* __restrict__ cols,
     const bf16* __restrict__ q, const bf16* __restrict__ kpool, const bf16* __restrict__ vpool,
@@ -47,23 +49,28 @@ __device__ __forceinline__ void split_kv_bf16_wave(
   const int lane = threadIdx.x & 63;
   const SplitItem it = items[idx];
   const int n = lane & 15, grp = lane >> 4;
-  const bool cvalid = n < it.ncols;
-  const Column c = cols[it.col0 + (cvalid ? n : 0)];
-  const int limit = cvalid ? c.limit : -1;
-
-  bf16x8 qb[KC];
-  {
-    const bf16* qp = q + (size_t(c.q_row) * Hq + c.q_head) * D + 8 * grp;
+  bool cvalid[NC];
+  Column c[NC];
+  int limit[NC];
+  bf16x8 qb[NC][KC];
+  f32x4 acc[NC][DB];
+  float m_run[NC], l_run[NC];
+#pragma unroll
+  for (int cb = 0; cb < NC; ++cb) {
+    cvalid[cb] = 16 * cb + n < it.ncols;
+    c[cb] = cols[it.col0 + (cvalid[cb] ? 16 * cb + n : 0)];
+    limit[cb] = cvalid[cb] ? c[cb].limit : -1;
+    const bf16* qp = q + (size_t(c[cb].q_row) * Hq + c[cb].q_head) * D + 8 * grp;
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
-      qb[kc] = *reinterpret_cast<const bf16x8*>(qp + 32 * kc);
-      if (!cvalid) qb[kc] = bf16x8{};
+      qb[cb][kc] = *reinterpret_cast<const bf16x8*>(qp + 32 * kc);
+      if (!cvalid[cb]) qb[cb][kc] = bf16x8{};
     }
-  }
-  f32x4 acc[DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = kNegBig, l_run = 0.f;
+    for (int db = 0; db < DB; ++db) acc[cb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[cb] = kNegBig;
+    l_run[cb] = 0.f;
+  }
   const int32_t* btr = bt + size_t(it.req) * bt_stride;
   const int kvh = it.kvh;
   const int klast = it.k1 - 1;
@@ -114,15 +121,21 @@ __device__ __forceinline__ void split_kv_bf16_wave(
   for (int k = it.k0; k < it.k1; k += kStepKeys) {
     const bool tail = k + kStepKeys > it.k1;
     const bool more = k + kStepKeys < it.k1;
-    // ---- scores S^T for 64 keys: lane holds v[4b + r] = key k + 32(b>>1) + 8grp + 4(b&1) + r
-    float v[16];
+    // ---- scores S^T for 64 keys: lane holds v[cb][4b + r] = key k + 32(b>>1) + 8grp + 4(b&1) + r
+    float v[NC][16];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 s[NC];
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) s = mfma16_bf16(ka[b][kc], qb[kc], s);
+      for (int cb = 0; cb < NC; ++cb) s[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[4 * b + r] = s[r] * scale_log2;
+      for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+        for (int cb = 0; cb < NC; ++cb) s[cb] = mfma16_bf16(ka[b][kc], qb[cb][kc], s[cb]);
+#pragma unroll
+      for (int cb = 0; cb < NC; ++cb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[cb][4 * b + r] = s[cb][r] * scale_log2;
     }
     if (more) {
       cover(k + kStepKeys);
@@ -130,33 +143,15 @@ __device__ __forceinline__ void split_kv_bf16_wave(
     }
     if (masked_item || tail) {
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
+      for (int cb = 0; cb < NC; ++cb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = k + 32 * (b >> 1) + 8 * grp + 4 * (b & 1) + r;
-          if (key > klast || key > limit) v[4 * b + r] = -INFINITY;
-        }
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = k + 32 * (b >> 1) + 8 * grp + 4 * (b & 1) + r;
+            if (key > klast || key > limit[cb]) v[cb][4 * b + r] = -INFINITY;
+          }
     }
-    // ---- online softmax (max shared by the 4 lane groups of a column)
-    float mx = v[0];
-#pragma unroll
-    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, v[e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = fast_exp2(m_run - m_new);
-    m_run = m_new;
-    bf16x8 pb[2];
-    float sum = 0.f;
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const bf16 pe = bf16(fast_exp2(v[4 * (2 * u + (e >> 2)) + (e & 3)] - m_new));
-        pb[u][e] = pe;
-        sum += float(pe);
-      }
-    l_run = l_run * alpha + sum;
     if (tail) {
       // positions at or past k1 may lie past kv_len (unwritten slots): zero them so
       // 0 * garbage cannot reach the accumulator
@@ -172,32 +167,63 @@ __device__ __forceinline__ void split_kv_bf16_wave(
         }
       }
     }
+    // ---- online softmax per column block (max shared by the 4 lane groups of a column)
+    bf16x8 pb[NC][2];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+    for (int cb = 0; cb < NC; ++cb) {
+      float mx = v[cb][0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, v[cb][e]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run[cb], mx);
+      const float alpha = fast_exp2(m_run[cb] - m_new);
+      m_run[cb] = m_new;
+      float sum = 0.f;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const bf16 pe = bf16(fast_exp2(v[cb][4 * (2 * u + (e >> 2)) + (e & 3)] - m_new));
+          pb[cb][u][e] = pe;
+          sum += float(pe);
+        }
+      l_run[cb] = l_run[cb] * alpha + sum;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[cb][db] *= alpha;
+    }
     // ---- O^T += V^T . P^T
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) acc[db] = mfma16_bf16(va[u][db], pb[u], acc[db]);
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int cb = 0; cb < NC; ++cb) acc[cb][db] = mfma16_bf16(va[u][db], pb[cb][u], acc[cb][db]);
     if (more) load_v(k + kStepKeys);
   }
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  if (cvalid) {
-    if (it.flags & kItemDirect) store_output<D>(out, (size_t(c.q_row) * Hq + c.q_head) * D, grp, l_tot, acc);
-    else store_partial<D>(ws_ml, ws_acc, c.pbase + it.slot, grp, m_run, l_tot, acc);
+#pragma unroll
+  for (int cb = 0; cb < NC; ++cb) {
+    float l_tot = l_run[cb] + __shfl_xor(l_run[cb], 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    if (cvalid[cb]) {
+      if (it.flags & kItemDirect)
+        store_output<D>(out, (size_t(c[cb].q_row) * Hq + c[cb].q_head) * D, grp, l_tot, acc[cb]);
+      else
+        store_partial<D>(ws_ml, ws_acc, c[cb].pbase + it.slot, grp, m_run[cb], l_tot, acc[cb]);
+    }
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void split_kv_bf16_kernel(
+template <int D, int NC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3 - NC, 3 - NC))) void split_kv_bf16_kernel(
     const SplitItem* __restrict__ items, int nitems, const Column* __restrict__ cols,
     const bf16* __restrict__ q, const bf16* __restrict__ kpool, const bf16* __restrict__ vpool,
     const int32_t* __restrict__ bt, int bt_stride, float* __restrict__ ws_ml, float* __restrict__ ws_acc,
     bf16* __restrict__ out, int Hq, Paged pg, float scale_log2) {
   const int idx = blockIdx.x * kSplitWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (idx < nitems)
-    split_kv_bf16_wave<D>(idx, items, cols, q, kpool, vpool, bt, bt_stride, ws_ml, ws_acc, out, Hq, pg, scale_log2);
+    split_kv_bf16_wave<D, NC>(idx, items, cols, q, kpool, vpool, bt, bt_stride, ws_ml, ws_acc, out, Hq, pg,
+                              scale_log2);
 }
 
 // ------------------------------------------------------------------ split-KV, fp32 --
@@ -1011,14 +1037,29 @@ static va_status run_impl(const va_plan* plan, const void* q, const void* k_pool
       auto* qq = static_cast<const bf16*>(q);
       auto* kk = static_cast<const bf16*>(k_pool);
       auto* vv = static_cast<const bf16*>(v_pool);
-      if (D == 128)
-        split_kv_bf16_kernel<128><<<grid, block, 0, s>>>(plan->d_items, nitems, plan->d_cols, qq, kk, vv,
-                                                         block_table_dev, bt_stride, ws_ml, ws_acc,
-                                                         static_cast<bf16*>(out), p.num_q_heads, pg, scale_log2);
-      else
-        split_kv_bf16_kernel<64><<<grid, block, 0, s>>>(plan->d_items, nitems, plan->d_cols, qq, kk, vv,
-                                                        block_table_dev, bt_stride, ws_ml, ws_acc,
-                                                        static_cast<bf16*>(out), p.num_q_heads, pg, scale_log2);
+      // items of more than 16 columns (first in the list) on the two-block kernel
+      const int nw = plan->items_wide, nn = nitems - nw;
+      const dim3 gw((nw + kSplitWaves - 1) / kSplitWaves), gn((nn + kSplitWaves - 1) / kSplitWaves);
+      const SplitItem* in = plan->d_items + nw;
+      if (D == 128) {
+        if (nw)
+          split_kv_bf16_kernel<128, 2><<<gw, block, 0, s>>>(plan->d_items, nw, plan->d_cols, qq, kk, vv,
+                                                            block_table_dev, bt_stride, ws_ml, ws_acc,
+                                                            static_cast<bf16*>(out), p.num_q_heads, pg, scale_log2);
+        if (nn)
+          split_kv_bf16_kernel<128, 1><<<gn, block, 0, s>>>(in, nn, plan->d_cols, qq, kk, vv, block_table_dev,
+                                                            bt_stride, ws_ml, ws_acc, static_cast<bf16*>(out),
+                                                            p.num_q_heads, pg, scale_log2);
+      } else {
+        if (nw)
+          split_kv_bf16_kernel<64, 2><<<gw, block, 0, s>>>(plan->d_items, nw, plan->d_cols, qq, kk, vv,
+                                                           block_table_dev, bt_stride, ws_ml, ws_acc,
+                                                           static_cast<bf16*>(out), p.num_q_heads, pg, scale_log2);
+        if (nn)
+          split_kv_bf16_kernel<64, 1><<<gn, block, 0, s>>>(in, nn, plan->d_cols, qq, kk, vv, block_table_dev,
+                                                           bt_stride, ws_ml, ws_acc, static_cast<bf16*>(out),
+                                                           p.num_q_heads, pg, scale_log2);
+      }
     } else {
       auto* qq = static_cast<const float*>(q);
       auto* kk = static_cast<const float*>(k_pool);

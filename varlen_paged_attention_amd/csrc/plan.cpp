@@ -216,7 +216,11 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
   std::vector<Block> blocks;
   auto add_blocks = [&](const std::vector<std::pair<int, int>>& rowhead,   // (req, local col)
                         int kvh, int32_t kstart, bool shared, int32_t req_for_table, bool tile) {
-    const size_t width = tile ? size_t(kPrefillCols) : size_t(kSplitCols);
+    // split blocks of a bf16 plan take up to 32 columns (two MFMA column blocks per item)
+    // when there are more than 16, so the kv range is read once for all of them
+    const size_t width = tile ? size_t(kPrefillCols)
+                              : (p.dtype == VA_DTYPE_BF16 && rowhead.size() > size_t(kSplitCols) ? size_t(2 * kSplitCols)
+                                                                                               : size_t(kSplitCols));
     for (size_t b0 = 0; b0 < rowhead.size(); b0 += width) {
       Block B;
       B.req = req_for_table;
@@ -376,12 +380,17 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
       (B.shared ? shared_items : own_items).push_back(it);
     }
   }
-  // group items first (each chunk's blocks adjacent), then longest first
+  // items of more than 16 columns first (their own launch), then group items (each
+  // chunk's blocks adjacent), then longest first within each kind
   plan->items = shared_items;
   plan->items.insert(plan->items.end(), own_items.begin(), own_items.end());
   std::stable_sort(plan->items.begin(), plan->items.end(), [](const SplitItem& a, const SplitItem& b) {
+    const bool wa = a.ncols > kSplitCols, wb = b.ncols > kSplitCols;
+    if (wa != wb) return wa;
     return (a.k1 - a.k0) > (b.k1 - b.k0);
   });
+  plan->items_wide = int32_t(std::count_if(plan->items.begin(), plan->items.end(),
+                                           [](const SplitItem& it) { return it.ncols > kSplitCols; }));
 
   // ---- counters ---------------------------------------------------------------------
   va_plan_stats& st = plan->stats;

@@ -10,7 +10,7 @@ namespace va {
 
 // One split-KV work item = one wavefront.  It reads kv positions [k0, k1) of request
 // `req`'s block table for KV head `kvh` and scores them against up to 16 query columns
-// cols[col0 .. col0+ncols).  Each column's partial result goes to workspace slot
+// (up to 32 in bf16 plans, run by the two-block kernel) cols[col0 .. col0+ncols).  Each column's partial result goes to workspace slot
 // cols[c].pbase + slot, or, with kItemDirect (the item covers its columns' whole kv range),
 // straight to the output rows.
 struct SplitItem {
@@ -62,7 +62,8 @@ struct va_plan {
   std::vector<int32_t> q_start, q_end, kv_len;
   std::vector<int32_t> block_table;          // host copy [num_reqs][max_pages_per_req]
   std::vector<int64_t> kv_offset;            // prefix sum of kv_len (gather output rows)
-  std::vector<va::SplitItem> items;
+  std::vector<va::SplitItem> items;          // items of more than 16 columns first
+  int32_t items_wide = 0;                    // how many items have more than 16 columns
   std::vector<va::Column> cols;
   std::vector<va::CombineRow> combine;
   std::vector<va::PrefillTile> tiles;

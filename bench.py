@@ -336,7 +336,7 @@ def main():
                     help="profile mode: 10 device copies of 1 GiB (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no multi-GPU path.",
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); this library has no multi-GPU path.",
               file=sys.stderr)
         sys.exit(2)
 

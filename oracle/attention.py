@@ -18,7 +18,7 @@ Sources, cited by page title and section:
   weights.  Section 3 (paging): a block table maps logical positions to physical
   blocks; paging changes placement, not the result.
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
   scale = 1/sqrt(head_dim) unless given; query head h uses KV head h // g;
   the new rows' own K/V are the last q_rows logical positions (S0 = kv_len − q_rows);
   logical position j lives in page block_table[r][j // page_size], slot j % page_size;

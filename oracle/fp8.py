@@ -11,7 +11,7 @@ Sources, cited by page title and section:
   every token carries FP32 scales stored next to its FP8 data, and a kernel reading
   the cache needs both to dequantise.
 
-Readings where the pages are silent (listed in the design doc): the FP8 format is OCP
+Readings where the pages are silent: the FP8 format is OCP
 e4m3fn (1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits, no infinities, the
 all-ones exponent-and-mantissa codes are NaN, exponent 0 is subnormal); there is one
 float32 scale per (page, KV head, slot) for K and one for V, i.e. one per token and
@@ -57,7 +57,7 @@ def dequantize_pools(k_codes: np.ndarray, k_scale: np.ndarray, v_codes: np.ndarr
 
 
 # ---- storing new rows in fp8 ----------------------------------------------------------
-# Readings (listed in the design doc): a new K or V vector of one token and KV head is stored
+# Readings where the pages are silent: a new K or V vector of one token and KV head is stored
 # with scale = max|x| / 448 (the largest finite e4m3fn magnitude), computed in float32, or 1
 # for an all-zero vector; each element's code is x / scale (float32 division) rounded to
 # the nearest e4m3fn value, ties to the even code; magnitudes above 448 (reachable only by

@@ -10,7 +10,7 @@ Sources, cited by page title and section:
 * "GLM-5.3 推理全链路(八)", stage 4 (freezing the scheduler's result into GPU inputs):
   out_cache_loc tells, for every new token, the page and the slot it is written to.
 
-Readings where the pages are silent (listed in the design doc): an out_cache_loc entry is the
+Readings where the pages are silent: an out_cache_loc entry is the
 flat slot index page * page_size + slot, and a negative entry is padding that writes
 nothing; the new token of flat row t of request r is logical position
 S0 + (t - q_start[r]) with S0 = kv_len - q_rows (the new rows are the last positions).

@@ -299,3 +299,13 @@ def test_fp8_append_argument_errors():
     assert L.varlen_attn_append_kv_fp8(pb, 3, *n) == api.VA_ERR_INVALID_ARG
     p.head_dim = 96
     assert L.varlen_attn_append_kv_fp8(p, 3, *n) == api.VA_ERR_UNSUPPORTED
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py runs on one GPU; asked for more it exits with status 2 and says why."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""

@@ -268,7 +268,8 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
     }
   }
 
-  // ---- split length: about 8192 items over the whole iteration ------------------------
+  // ---- split length: about 8192 items over the whole iteration (fewer, longer ones when
+  // there is little work) ---------------------------------------------------------------
   int64_t work = 0, tile_cols = 0, tile_keys = 0;
   for (auto& B : blocks) {
     if (B.tile) {
@@ -283,7 +284,13 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
     L = ceil_div(p.split_len, kStepKeys) * kStepKeys;
   } else {
     L = ceil_div(std::max<int64_t>(1, ceil_div(work, 8192)), kStepKeys) * kStepKeys;
-    L = std::min<int64_t>(std::max<int64_t>(L, 256), 8192);
+    if (L < 256) {
+      // little split work: cut it into enough items to occupy every SIMD (about 2048
+      // resident waves) with short items, down to one 64-key step each, so the latency of
+      // a few long items does not set the time
+      L = std::min<int64_t>(256, ceil_div(std::max<int64_t>(1, ceil_div(work, 2048)), kStepKeys) * kStepKeys);
+    }
+    L = std::min<int64_t>(L, 8192);
   }
   plan->split_len = int32_t(L);
   // group tiles: key chunks sized for about 512 tiles in all (one per resident workgroup)

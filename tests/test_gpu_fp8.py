@@ -106,6 +106,8 @@ SMALL = [
     ("chunk-mix/8", 4, 8, 0),
     ("shared-6", 5, 1, api.VA_FLAG_SHARED_PREFIX),
     ("shared-6 plain", 5, 1, 0),
+    ("spec-decode-mtp7/8", 7, 8, 0),
+    ("shared-6 split items", 5, 1, api.VA_FLAG_SHARED_PREFIX | api.VA_FLAG_NO_PREFILL_KERNEL),
 ]
 
 

@@ -111,7 +111,7 @@ def check_coverage(w, plan):
     direct = {}
     for it in items:
         req, kvh, col0, ncols, k0, k1, slot, flags = (int(x) for x in it)
-        assert 1 <= ncols <= (32 if w.dtype == "bf16" else 16) and k0 < k1 and k0 % 16 == 0   # 16-key runs in one page
+        assert 1 <= ncols <= (16 if w.dtype == "f32" else 32) and k0 < k1 and k0 % 16 == 0   # 16-key runs in one page
         for c in cols[col0:col0 + ncols]:
             row, head, limit, pbase = (int(x) for x in c)
             r = req_of_row[row]

@@ -71,9 +71,10 @@ __device__ __forceinline__ void store_output(OutT* out, size_t row_off, int grp,
     for (int r = 0; r < 4; ++r) op[16 * db + r] = OutT(acc[db][r] * inv);
 }
 
-// Split-KV kernel over fp8 e4m3fn K/V pools with per-position float32 scales
-// (kv_fp8.hip); bf16 Q and output.  Returns the launch status.
-hipError_t launch_split_kv_fp8(int D, int nitems, hipStream_t s, const SplitItem* items, const Column* cols,
+// Split-KV kernels over fp8 e4m3fn K/V pools with per-position float32 scales
+// (kv_fp8.hip); bf16 Q and output.  The first nwide items have more than 16 columns.
+// Returns the launch status.
+hipError_t launch_split_kv_fp8(int D, int nitems, int nwide, hipStream_t s, const SplitItem* items, const Column* cols,
                                const void* q, const void* kpool, const void* vpool, const float* kscale,
                                const float* vscale, const int32_t* bt, int bt_stride, float* ws_ml, float* ws_acc,
                                void* out, int Hq, Paged pg, float scale_log2);

@@ -1031,7 +1031,7 @@ static va_status run_impl(const va_plan* plan, const void* q, const void* k_pool
     const dim3 grid((nitems + kSplitWaves - 1) / kSplitWaves), block(64 * kSplitWaves);
     e = hipSuccess;
     if (fp8) {
-      e = launch_split_kv_fp8(D, nitems, s, plan->d_items, plan->d_cols, q, k_pool, v_pool, k_scale, v_scale,
+      e = launch_split_kv_fp8(D, nitems, plan->items_wide, s, plan->d_items, plan->d_cols, q, k_pool, v_pool, k_scale, v_scale,
                           block_table_dev, bt_stride, ws_ml, ws_acc, out, p.num_q_heads, pg, scale_log2);
     } else if (bf) {
       auto* qq = static_cast<const bf16*>(q);

@@ -13,6 +13,7 @@
 #include <hip/hip_runtime.h>
 
 #include <string>
+#include <type_traits>
 
 #include "device_common.h"
 #include "va_internal.h"
@@ -44,8 +45,9 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
 // k + 16*grp + 4b + r); those are also the keys of its V^T slice (16 contiguous bytes of
 // a transposed V page row) and of its 16 scales, and P sub-step u element e is key
 // k + 16*grp + 8*u + e.  Items start at multiples of 16 and pages hold >= 16 positions,
-// so each 16-key run lies in one page.
-template <int D>
+// so each 16-key run lies in one page.  NC = blocks of 16 query columns per item (2 for
+// items of 17-32 columns): each widened K/V operand then feeds one MFMA per block.
+template <int D, int NC>
 __device__ __forceinline__ void split_kv_fp8_wave(
     int idx, const SplitItem* __restrict__ items, const Column* __restrict__ cols, const bf16* __restrict__ q,
     const uint8_t* __restrict__ kpool, const uint8_t* __restrict__ vpool, const float* __restrict__ kscale,
@@ -58,23 +60,28 @@ __device__ __forceinline__ void split_kv_fp8_wave(
   const int lane = threadIdx.x & 63;
   const SplitItem it = items[idx];
   const int n = lane & 15, grp = lane >> 4;
-  const bool cvalid = n < it.ncols;
-  const Column c = cols[it.col0 + (cvalid ? n : 0)];
-  const int limit = cvalid ? c.limit : -1;
-
-  bf16x8 qb[KC];
-  {
-    const bf16* qp = q + (size_t(c.q_row) * Hq + c.q_head) * D + QD * grp;
+  bool cvalid[NC];
+  Column c[NC];
+  int limit[NC];
+  bf16x8 qb[NC][KC];
+  f32x4 acc[NC][DB];
+  float m_run[NC], l_run[NC];
+#pragma unroll
+  for (int cb = 0; cb < NC; ++cb) {
+    cvalid[cb] = 16 * cb + n < it.ncols;
+    c[cb] = cols[it.col0 + (cvalid[cb] ? 16 * cb + n : 0)];
+    limit[cb] = cvalid[cb] ? c[cb].limit : -1;
+    const bf16* qp = q + (size_t(c[cb].q_row) * Hq + c[cb].q_head) * D + QD * grp;
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
-      qb[kc] = *reinterpret_cast<const bf16x8*>(qp + 8 * kc);
-      if (!cvalid) qb[kc] = bf16x8{};
+      qb[cb][kc] = *reinterpret_cast<const bf16x8*>(qp + 8 * kc);
+      if (!cvalid[cb]) qb[cb][kc] = bf16x8{};
     }
-  }
-  f32x4 acc[DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = kNegBig, l_run = 0.f;
+    for (int db = 0; db < DB; ++db) acc[cb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[cb] = kNegBig;
+    l_run[cb] = 0.f;
+  }
   const int32_t* btr = bt + size_t(it.req) * bt_stride;
   const int kvh = it.kvh;
   const int klast = it.k1 - 1;
@@ -125,17 +132,26 @@ __device__ __forceinline__ void split_kv_fp8_wave(
     const bool tail = k + kStepKeys > it.k1;
     const bool more = k + kStepKeys < it.k1;
     // ---- scores S^T for 64 keys, times the keys' K scales
-    float v[16];
+    float v[NC][16];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 s[NC];
+#pragma unroll
+      for (int cb = 0; cb < NC; ++cb) s[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < NL; ++j) {
-        s = mfma16_bf16(fp8x8_to_bf16(ka[b][j][0], ka[b][j][1]), qb[2 * j], s);
-        s = mfma16_bf16(fp8x8_to_bf16(ka[b][j][2], ka[b][j][3]), qb[2 * j + 1], s);
+        const bf16x8 k0 = fp8x8_to_bf16(ka[b][j][0], ka[b][j][1]);
+        const bf16x8 k1 = fp8x8_to_bf16(ka[b][j][2], ka[b][j][3]);
+#pragma unroll
+        for (int cb = 0; cb < NC; ++cb) {
+          s[cb] = mfma16_bf16(k0, qb[cb][2 * j], s[cb]);
+          s[cb] = mfma16_bf16(k1, qb[cb][2 * j + 1], s[cb]);
+        }
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[4 * b + r] = s[r] * (ks[b][r] * scale_log2);
+      for (int cb = 0; cb < NC; ++cb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[cb][4 * b + r] = s[cb][r] * (ks[b][r] * scale_log2);
     }
     if (more) {
       cover(k + kStepKeys);
@@ -148,31 +164,36 @@ __device__ __forceinline__ void split_kv_fp8_wave(
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = k + 16 * grp + i;
-        if (key > klast || key > limit) v[i] = -INFINITY;
+#pragma unroll
+        for (int cb = 0; cb < NC; ++cb)
+          if (key > klast || key > limit[cb]) v[cb][i] = -INFINITY;
         // scales past the item's end may belong to unwritten slots: keep them out of P
         if (key > klast) vsc[i] = 0.f;
       }
     }
-    // ---- online softmax (max shared by the 4 lane groups of a column)
-    float mx = v[0];
+    // ---- online softmax per column block (max shared by the 4 lane groups of a column)
+    bf16x8 pb[NC][2];
 #pragma unroll
-    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, v[e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = fast_exp2(m_run - m_new);
-    m_run = m_new;
-    bf16x8 pb[2];
-    float sum = 0.f;
+    for (int cb = 0; cb < NC; ++cb) {
+      float mx = v[cb][0];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float p = fast_exp2(v[i] - m_new);
-      sum += p;
-      pb[i >> 3][i & 7] = bf16(p * vsc[i]);
+      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, v[cb][e]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run[cb], mx);
+      const float alpha = fast_exp2(m_run[cb] - m_new);
+      m_run[cb] = m_new;
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = fast_exp2(v[cb][i] - m_new);
+        sum += p;
+        pb[cb][i >> 3][i & 7] = bf16(p * vsc[i]);
+      }
+      l_run[cb] = l_run[cb] * alpha + sum;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[cb][db] *= alpha;
     }
-    l_run = l_run * alpha + sum;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) acc[db] *= alpha;
     // ---- O^T += V^T . P^T; codes at or past k1 may be unwritten slots: zeroed
     const int valid = it.k1 - (k + 16 * grp);
 #pragma unroll
@@ -186,46 +207,64 @@ __device__ __forceinline__ void split_kv_fp8_wave(
           if (8 + e >= valid) v1[e] = bf16(0.f);
         }
       }
-      acc[db] = mfma16_bf16(v0, pb[0], acc[db]);
-      acc[db] = mfma16_bf16(v1, pb[1], acc[db]);
+#pragma unroll
+      for (int cb = 0; cb < NC; ++cb) {
+        acc[cb][db] = mfma16_bf16(v0, pb[cb][0], acc[cb][db]);
+        acc[cb][db] = mfma16_bf16(v1, pb[cb][1], acc[cb][db]);
+      }
     }
     if (more) load_v(k + kStepKeys);
   }
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  if (cvalid) {
-    if (it.flags & kItemDirect) store_output<D>(out, (size_t(c.q_row) * Hq + c.q_head) * D, grp, l_tot, acc);
-    else store_partial<D>(ws_ml, ws_acc, c.pbase + it.slot, grp, m_run, l_tot, acc);
+#pragma unroll
+  for (int cb = 0; cb < NC; ++cb) {
+    float l_tot = l_run[cb] + __shfl_xor(l_run[cb], 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    if (cvalid[cb]) {
+      if (it.flags & kItemDirect)
+        store_output<D>(out, (size_t(c[cb].q_row) * Hq + c[cb].q_head) * D, grp, l_tot, acc[cb]);
+      else
+        store_partial<D>(ws_ml, ws_acc, c[cb].pbase + it.slot, grp, m_run[cb], l_tot, acc[cb]);
+    }
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void split_kv_fp8_kernel(
+template <int D, int NC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3 - NC, 3 - NC))) void split_kv_fp8_kernel(
     const SplitItem* __restrict__ items, int nitems, const Column* __restrict__ cols, const bf16* __restrict__ q,
     const uint8_t* __restrict__ kpool, const uint8_t* __restrict__ vpool, const float* __restrict__ kscale,
     const float* __restrict__ vscale, const int32_t* __restrict__ bt, int bt_stride, float* __restrict__ ws_ml,
     float* __restrict__ ws_acc, bf16* __restrict__ out, int Hq, Paged pg, float scale_log2) {
   const int idx = blockIdx.x * kSplitWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (idx < nitems)
-    split_kv_fp8_wave<D>(idx, items, cols, q, kpool, vpool, kscale, vscale, bt, bt_stride, ws_ml, ws_acc, out, Hq,
-                         pg, scale_log2);
+    split_kv_fp8_wave<D, NC>(idx, items, cols, q, kpool, vpool, kscale, vscale, bt, bt_stride, ws_ml, ws_acc, out,
+                             Hq, pg, scale_log2);
 }
 
-hipError_t launch_split_kv_fp8(int D, int nitems, hipStream_t s, const SplitItem* items, const Column* cols,
+hipError_t launch_split_kv_fp8(int D, int nitems, int nwide, hipStream_t s, const SplitItem* items, const Column* cols,
                                const void* q, const void* kpool, const void* vpool, const float* kscale,
                                const float* vscale, const int32_t* bt, int bt_stride, float* ws_ml, float* ws_acc,
                                void* out, int Hq, Paged pg, float scale_log2) {
-  const dim3 grid((nitems + kSplitWaves - 1) / kSplitWaves), block(64 * kSplitWaves);
+  const dim3 block(64 * kSplitWaves);
   auto* qq = static_cast<const bf16*>(q);
   auto* kk = static_cast<const uint8_t*>(kpool);
   auto* vv = static_cast<const uint8_t*>(vpool);
   auto* oo = static_cast<bf16*>(out);
-  if (D == 128)
-    split_kv_fp8_kernel<128><<<grid, block, 0, s>>>(items, nitems, cols, qq, kk, vv, kscale, vscale, bt, bt_stride,
-                                                    ws_ml, ws_acc, oo, Hq, pg, scale_log2);
-  else
-    split_kv_fp8_kernel<64><<<grid, block, 0, s>>>(items, nitems, cols, qq, kk, vv, kscale, vscale, bt, bt_stride,
-                                                   ws_ml, ws_acc, oo, Hq, pg, scale_log2);
+  // items of more than 16 columns come first and run on the two-block kernel
+  auto launch = [&](auto dim, auto ncb, const SplitItem* it, int n) {
+    constexpr int DD = decltype(dim)::value, NC = decltype(ncb)::value;
+    if (n)
+      split_kv_fp8_kernel<DD, NC><<<dim3((n + kSplitWaves - 1) / kSplitWaves), block, 0, s>>>(
+          it, n, cols, qq, kk, vv, kscale, vscale, bt, bt_stride, ws_ml, ws_acc, oo, Hq, pg, scale_log2);
+  };
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  if (D == 128) {
+    launch(std::integral_constant<int, 128>{}, I2{}, items, nwide);
+    launch(std::integral_constant<int, 128>{}, I1{}, items + nwide, nitems - nwide);
+  } else {
+    launch(std::integral_constant<int, 64>{}, I2{}, items, nwide);
+    launch(std::integral_constant<int, 64>{}, I1{}, items + nwide, nitems - nwide);
+  }
   return hipGetLastError();
 }
 

@@ -216,10 +216,10 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
   std::vector<Block> blocks;
   auto add_blocks = [&](const std::vector<std::pair<int, int>>& rowhead,   // (req, local col)
                         int kvh, int32_t kstart, bool shared, int32_t req_for_table, bool tile) {
-    // split blocks of a bf16 plan take up to 32 columns (two MFMA column blocks per item)
+    // split blocks of a bf16 or fp8 plan take up to 32 columns (two MFMA column blocks per item)
     // when there are more than 16, so the kv range is read once for all of them
     const size_t width = tile ? size_t(kPrefillCols)
-                              : (p.dtype == VA_DTYPE_BF16 && rowhead.size() > size_t(kSplitCols) ? size_t(2 * kSplitCols)
+                              : (p.dtype != VA_DTYPE_F32 && rowhead.size() > size_t(kSplitCols) ? size_t(2 * kSplitCols)
                                                                                                : size_t(kSplitCols));
     for (size_t b0 = 0; b0 < rowhead.size(); b0 += width) {
       Block B;

@@ -10,7 +10,7 @@ namespace va {
 
 // One split-KV work item = one wavefront.  It reads kv positions [k0, k1) of request
 // `req`'s block table for KV head `kvh` and scores them against up to 16 query columns
-// (up to 32 in bf16 plans, run by the two-block kernel) cols[col0 .. col0+ncols).  Each column's partial result goes to workspace slot
+// (up to 32 in bf16 and fp8 plans, run by the two-block kernels) cols[col0 .. col0+ncols).  Each column's partial result goes to workspace slot
 // cols[c].pbase + slot, or, with kItemDirect (the item covers its columns' whole kv range),
 // straight to the output rows.
 struct SplitItem {

@@ -104,6 +104,11 @@ typedef struct {
   int32_t prefill_min_rows;   /* q_rows from which a request uses prefill tiles;
                                  <= 0: when q_rows * (Hq / Hkv) >= 64 */
   int32_t split_len;          /* kv positions per split-KV item; <= 0: chosen by the planner */
+  int32_t prefill_split_len;  /* key chunk of a cut prefill tile (rounded up to 64): a tile whose
+                                 keys visible to all its columns span more than one chunk is
+                                 cut into one tile per chunk, their partial results merged by
+                                 the combine pass; 0: the planner cuts tiles only when a few
+                                 long tiles would leave most of the GPU idle; < 0: never */
 } va_params;
 
 typedef struct {
@@ -134,6 +139,7 @@ typedef struct {
   int64_t shared_tiles;       /* MFMA tiles scoring shared-prefix chunks for stacked member rows */
   double shared_tile_flops;   /* part of split_flops done by those tiles (in the prefill stage) */
   int64_t split_item_kv_bytes; /* distinct KV bytes the split-KV items read */
+  int64_t prefill_split_tiles; /* of prefill_tiles, those scoring one key chunk of a cut tile */
 } va_plan_stats;
 
 typedef struct va_plan va_plan;   /* opaque, immutable after creation */

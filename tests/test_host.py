@@ -136,7 +136,8 @@ def check_coverage(w, plan):
     assert all(n == 1 for n in direct.values())
     assert not (set(direct) & set(slots))
     for t in api.varlen_attn_plan_export(plan, 4):        # shared-prefix group tiles
-        req, kvh, col0, ncols, slot, k0, k1, _ = (int(x) for x in t)
+        req, kvh, col0, ncols, slot, k0, k1, kbeg = (int(x) for x in t[:8])
+        assert kbeg == k0 and t[8] == -1
         assert 1 <= ncols <= 128 and k0 < k1
         for c in cols[col0:col0 + ncols]:
             row, head, limit, pbase = (int(x) for x in c)
@@ -149,12 +150,20 @@ def check_coverage(w, plan):
             assert pb == pbase and 0 <= slot < npart
             slots.setdefault((row, head), []).append(slot)
     for t in tiles:
-        req, kvh, c0, ncols, q0, S0, kv_end, key_diag = (int(x) for x in t)
-        for c in range(c0, c0 + ncols):
-            i, hh = divmod(c, g)
+        req, kvh, c0, ncols, q0, S0, kv_end, kbeg, pbase, pstride = (int(x) for x in t[:10])
+        assert kbeg % 64 == 0 and 1 <= ncols <= 128
+        for col in range(ncols):
+            i, hh = divmod(c0 + col, g)
             row, head = q0 + i, kvh * g + hh
-            cover.setdefault((row, head), []).append((0, S0 + i + 1))
-            assert kv_end >= S0 + i + 1
+            assert kbeg <= S0 + i, "a key chunk with no visible key for a column"
+            if pbase < 0:                                  # whole tile: output written directly
+                assert kbeg == 0 and kv_end >= S0 + i + 1 and (row, head) not in comb_map
+                cover.setdefault((row, head), []).append((0, S0 + i + 1))
+            else:                                          # one key chunk of a cut tile
+                cover.setdefault((row, head), []).append((kbeg, min(kv_end, S0 + i + 1)))
+                pb, npart = comb_map[(row, head)]
+                assert 0 <= pbase + col * pstride - pb < npart and npart == pstride
+                slots.setdefault((row, head), []).append(pbase + col * pstride - pb)
     for (row, head), s in slots.items():
         assert len(s) == len(set(s)), f"slot reused for {(row, head)}"
     for r in range(w.num_reqs):
@@ -197,6 +206,55 @@ CASES = [
 def test_plan_covers_every_visible_pair_once(name, make, flags):
     w = make()
     check_coverage(w, _plan(w, flags))
+
+
+def _long_chunk(m=256, S0=65536, hq=32, hkv=8, extra=()):
+    """A chunk of m new rows on S0 cached positions (plus optional decodes)."""
+    rows = [m] + [1] * len(extra)
+    return W.build("lc", rows, [S0 + m] + list(extra), num_q_heads=hq, num_kv_heads=hkv, head_dim=128,
+                   page_size=64, seed=6)
+
+
+CUT_CASES = [
+    # (name, workload, prefill_split_len, expect cut tiles)
+    ("forced-1000", lambda: W.build("c", [300, 1, 40], [5000, 77, 2100], num_q_heads=8, num_kv_heads=2,
+                                    head_dim=128, page_size=16, seed=7), 1000, True),
+    ("forced-g1", lambda: W.build("c", [130, 64], [700, 64], num_q_heads=2, num_kv_heads=2, head_dim=64,
+                                  page_size=32, seed=8), 64, True),
+    ("auto-long-chunk", lambda: _long_chunk(), 0, True),
+    ("auto-long-chunk+decodes", lambda: _long_chunk(512, 131072, 64, 8, extra=(900, 40000, 3)), 0, True),
+    ("auto-orca-stays-whole", lambda: W.config(2), 0, False),
+    ("auto-chunk-mix-stays-whole", lambda: W.config(4), 0, False),
+    ("never", lambda: _long_chunk(), -1, False),
+]
+
+
+@pytest.mark.parametrize("name,make,split,cut", CUT_CASES, ids=[c[0] for c in CUT_CASES])
+def test_cut_prefill_tiles_cover_every_visible_pair_once(name, make, split, cut):
+    w = make()
+    plan = _plan(w, prefill_split_len=split)
+    st = api.varlen_attn_plan_stats(plan)
+    assert (st["prefill_split_tiles"] > 0) == cut
+    check_coverage(w, plan)
+    tiles = api.varlen_attn_plan_export(plan, 3)
+    work = tiles[:, 6] - tiles[:, 7]
+    if cut and split > 0:
+        L = -(-split // 64) * 64
+        assert np.all(work[tiles[:, 8] >= 0] <= L + 128)   # the last chunk also holds the diagonal
+    if name == "auto-long-chunk":
+        # 64 tiles of ~65.8K keys on 512 resident slots: chunks of 8192 keys (the largest
+        # power of two <= 64 * 65.8K / 512), 8 per tile (the remainder of 1 key is absorbed)
+        assert st["prefill_tiles"] == 512 and st["prefill_split_tiles"] == 512
+        assert st["combine_rows"] == 256 * 32
+        assert sorted(set((tiles[:, 7] // 8192).tolist())) == list(range(8))
+        # 64 groups of 8 tiles reading one key chunk of one KV head, 8 groups per XCD:
+        # every group sits at launch positions of one XCD (position % 8), each XCD's
+        # positions heaviest first
+        xcd = {}
+        for p, t in enumerate(tiles):
+            assert xcd.setdefault((int(t[1]), int(t[7])), p % 8) == p % 8
+        for x in range(8):
+            assert np.all(np.diff(work[x::8]) <= 0)
 
 
 @pytest.mark.parametrize("name,make,flags", CASES, ids=[c[0] for c in CASES])

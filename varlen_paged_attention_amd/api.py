@@ -31,7 +31,8 @@ class VaParams(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("num_pages", ctypes.c_int32), ("max_pages_per_req", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float), ("flags", ctypes.c_uint32),
-                ("prefill_min_rows", ctypes.c_int32), ("split_len", ctypes.c_int32)]
+                ("prefill_min_rows", ctypes.c_int32), ("split_len", ctypes.c_int32),
+                ("prefill_split_len", ctypes.c_int32)]
 
 
 class VaPlanStats(ctypes.Structure):
@@ -45,7 +46,8 @@ class VaPlanStats(ctypes.Structure):
                 ("split_flops", ctypes.c_double)] + \
                [(n, ctypes.c_int64) for n in ("prefill_kv_bytes", "split_kv_bytes", "split_q_bytes",
                                               "direct_items", "shared_tiles")] + \
-               [("shared_tile_flops", ctypes.c_double), ("split_item_kv_bytes", ctypes.c_int64)]
+               [("shared_tile_flops", ctypes.c_double), ("split_item_kv_bytes", ctypes.c_int64),
+                ("prefill_split_tiles", ctypes.c_int64)]
 
 
 class VarlenAttnError(RuntimeError):
@@ -137,13 +139,14 @@ class Plan:
 
 def varlen_attn_plan(*, num_q_heads: int, num_kv_heads: int, head_dim: int, page_size: int, num_pages: int,
                      q_start, q_end, kv_len, block_table, dtype: str = "bf16", softmax_scale: float = 0.0,
-                     flags: int = 0, prefill_min_rows: int = 0, split_len: int = 0) -> Plan:
+                     flags: int = 0, prefill_min_rows: int = 0, split_len: int = 0,
+                     prefill_split_len: int = 0) -> Plan:
     qs, qe, kv = _i32(q_start), _i32(q_end), _i32(kv_len)
     bt = _i32(block_table)
     if bt.ndim != 2 or not (len(qs) == len(qe) == len(kv) == bt.shape[0]):
         raise ValueError("q_start/q_end/kv_len must be [R] and block_table [R, max_pages]")
     p = VaParams(num_q_heads, num_kv_heads, head_dim, page_size, num_pages, bt.shape[1],
-                 DTYPE_CODES[dtype], softmax_scale, flags, prefill_min_rows, split_len)
+                 DTYPE_CODES[dtype], softmax_scale, flags, prefill_min_rows, split_len, prefill_split_len)
     h = ctypes.c_void_p()
     ws = ctypes.c_size_t()
     _check(lib().varlen_attn_plan(ctypes.byref(p), len(kv), _ptr32(qs), _ptr32(qe), _ptr32(kv), _ptr32(bt),

@@ -395,11 +395,17 @@ constexpr int prefill_lds_bytes() {
   return PrefillLds<D>::bytes;
 }
 
-// GROUP = true: the same kernel scores a shared-prefix chunk for several requests' rows.
+// Group tiles (MODE kGroupTile): the same kernel scores a shared-prefix chunk for several
+// requests' rows.
 // The tile's columns come from cols[c0 ..] (rows of different requests), its keys are
 // [S0, kv_end) of request req's block table (pages every member shares, all visible to
 // every member row), and each column's unnormalised partial (m, l, acc) goes to workspace
 // slot pbase + q0 for the combine pass.
+//
+// Otherwise the tile's columns are consecutive (row, head) pairs of one request.  A whole
+// tile scores keys [0, kv_end) and normalises and writes the output rows; a key-chunk
+// tile (one chunk of a cut tile) scores keys [kbeg, kv_end) and writes the unnormalised
+// partial of column col to slot pbase + col * pstride, for the combine pass.
 //
 // F8 = true: the pools hold fp8 e4m3fn codes with per-position float32 scales.  Each wave
 // copies its 16-key slice of codes (and the 16 K or V scales) by LDS-DMA into the upper
@@ -407,12 +413,18 @@ constexpr int prefill_lds_bytes() {
 // place to bf16(code * scale) in the layouts above, so the MFMA loop is the bf16 one.
 // The slice is the wave's own, and all its reads precede its writes, so no other wave is
 // involved until the barrier that ends the iteration.
-template <int D, bool GROUP, bool F8>
+enum TileMode { kWholeTile, kChunkTile, kGroupTile };
+
+// Whole tiles, key-chunk tiles and group tiles are separate instantiations (and launches):
+// code shared by the three kinds in one kernel measured slower for whole tiles, as the
+// compiler then no longer overlaps the exponentials with the next tile's MFMAs.
+template <int D, int MODE, bool F8>
 __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_bf16_kernel(
     const PrefillTile* __restrict__ tiles, const Column* __restrict__ cols, const bf16* __restrict__ q,
     const void* __restrict__ kpool, const void* __restrict__ vpool, const float* __restrict__ kscale,
     const float* __restrict__ vscale, const int32_t* __restrict__ bt, int bt_stride, bf16* __restrict__ out,
     float* __restrict__ ws_ml, float* __restrict__ ws_acc, int Hq, int g, Paged pg, float scale_log2) {
+  constexpr bool GROUP = MODE == kGroupTile;
   using Lay = PrefillLds<D>;
   constexpr int KCH = Lay::KCH, KROW = Lay::KROW, KBUF = Lay::KBUF, VBUF = Lay::VBUF;
   constexpr int WK = kPSliceKeys;                      // 16 keys per wave slice
@@ -443,10 +455,22 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
     row = cc.q_row;
     head = cc.q_head;
     pslot = cc.pbase + T.q0;
-    kbeg = T.S0;
+    kbeg = T.kbeg;
     limit = cvalid ? T.kv_end - 1 : -1;
     w_min_limit = T.kv_end - 1;
     w_max_limit = (wv * 32 < T.ncols) ? T.kv_end - 1 : -1;
+  } else if constexpr (MODE == kChunkTile) {
+    const int i = c / g;
+    row = T.q0 + i;
+    head = T.kvh * g + c % g;
+    pslot = T.pbase + col * T.pstride;
+    kbeg = T.kbeg;
+    // a key chunk before the last one ends before the diagonal: clip the limits to its end
+    const int kl = T.kv_end - 1;
+    limit = cvalid ? min(T.S0 + i, kl) : -1;
+    const int wcol_last = min(wv * 32 + 31, T.ncols - 1);
+    w_min_limit = min(T.S0 + (T.c0 + wv * 32) / g, kl);
+    w_max_limit = (wv * 32 < T.ncols) ? min(T.S0 + (T.c0 + wcol_last) / g, kl) : -1;
   } else {
     const int i = c / g;
     row = T.q0 + i;
@@ -755,7 +779,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
   }
   // ---- normalise and write: acc[db][4*ii + jj] is d = 32*db + 8*ii + 4*h + jj of this column
   const float l_tot = l_run + other_half(l_run);
-  if constexpr (GROUP) {
+  if constexpr (MODE != kWholeTile) {
     if (cvalid) {
       if (h == 0) {
         ws_ml[2 * size_t(pslot)] = m_run;
@@ -1004,27 +1028,34 @@ static va_status run_impl(const va_plan* plan, const void* q, const void* k_pool
   };
   if ((e = mark(0)) != hipSuccess) return hip_fail("hipEventRecord", e);
   const int ntiles = int(plan->tiles.size()), ngtiles = int(plan->gtiles.size());
-  auto launch_tiles = [&](auto group, auto f8, const PrefillTile* tl, int n) {
-    constexpr bool G = decltype(group)::value, F = decltype(f8)::value;
+  const int nwhole = plan->tiles_whole, nchunk = ntiles - nwhole;
+  auto launch_tiles = [&](auto mode, auto f8, const PrefillTile* tl, int n) {
+    constexpr int M = decltype(mode)::value;
+    constexpr bool F = decltype(f8)::value;
     const dim3 grid(n), block(64 * kPrefillWaves);
     auto* qq = static_cast<const bf16*>(q);
     auto* oo = static_cast<bf16*>(out);
     if (D == 128)
-      prefill_bf16_kernel<128, G, F><<<grid, block, prefill_lds_bytes<128>(), s>>>(
+      prefill_bf16_kernel<128, M, F><<<grid, block, prefill_lds_bytes<128>(), s>>>(
           tl, plan->d_cols, qq, k_pool, v_pool, k_scale, v_scale, block_table_dev, bt_stride, oo, ws_ml, ws_acc,
           p.num_q_heads, plan->g, pg, scale_log2);
     else
-      prefill_bf16_kernel<64, G, F><<<grid, block, prefill_lds_bytes<64>(), s>>>(
+      prefill_bf16_kernel<64, M, F><<<grid, block, prefill_lds_bytes<64>(), s>>>(
           tl, plan->d_cols, qq, k_pool, v_pool, k_scale, v_scale, block_table_dev, bt_stride, oo, ws_ml, ws_acc,
           p.num_q_heads, plan->g, pg, scale_log2);
     return hipGetLastError();
   };
-  auto launch_kind = [&](auto group, const PrefillTile* tl, int n) {
-    return fp8 ? launch_tiles(group, std::true_type{}, tl, n) : launch_tiles(group, std::false_type{}, tl, n);
+  auto launch_kind = [&](auto mode, const PrefillTile* tl, int n) {
+    return fp8 ? launch_tiles(mode, std::true_type{}, tl, n) : launch_tiles(mode, std::false_type{}, tl, n);
   };
-  if (ntiles && (e = launch_kind(std::false_type{}, plan->d_tiles, ntiles)) != hipSuccess)
+  using Whole = std::integral_constant<int, kWholeTile>;
+  using Chunk = std::integral_constant<int, kChunkTile>;
+  using Group = std::integral_constant<int, kGroupTile>;
+  if (nwhole && (e = launch_kind(Whole{}, plan->d_tiles, nwhole)) != hipSuccess)
     return hip_fail("prefill kernel launch", e);
-  if (ngtiles && (e = launch_kind(std::true_type{}, plan->d_gtiles, ngtiles)) != hipSuccess)
+  if (nchunk && (e = launch_kind(Chunk{}, plan->d_tiles + nwhole, nchunk)) != hipSuccess)
+    return hip_fail("prefill key-chunk kernel launch", e);
+  if (ngtiles && (e = launch_kind(Group{}, plan->d_gtiles, ngtiles)) != hipSuccess)
     return hip_fail("shared-prefix tile kernel launch", e);
   if ((e = mark(1)) != hipSuccess) return hip_fail("hipEventRecord", e);
   if (nitems) {

@@ -22,6 +22,8 @@
 #include <map>
 #include <new>
 #include <numeric>
+#include <queue>
+#include <tuple>
 #include <string>
 #include <vector>
 
@@ -55,6 +57,74 @@ struct Block {          // a set of <= 16 query columns scored against one kv ra
 };
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Launch order of the prefill tiles.  Workgroup i of a launch goes to XCD i % 8, and each
+// XCD has its own L2: tiles that read the same keys (one request's KV head, or one key
+// chunk of it for cut tiles) are placed at positions of one XCD so they share its L2,
+// with the XCDs' work balanced (a group larger than an XCD's share is spread over
+// several); within an XCD, heaviest tiles first so the ragged end of the grid is made of
+// short tiles.  When an XCD's list runs out, the remaining positions take the heaviest
+// tiles left in the longest list.
+constexpr int kXcds = 8;
+void order_tiles(std::vector<PrefillTile>& tiles) {
+  const size_t T = tiles.size();
+  if (T < 2) return;
+  auto work = [](const PrefillTile& t) { return int64_t(t.kv_end) - t.kbeg; };
+  auto key = [](const PrefillTile& t) { return std::make_tuple(t.req, t.kvh, t.pbase >= 0 ? t.kbeg : -1); };
+  std::vector<int32_t> idx(T);
+  std::iota(idx.begin(), idx.end(), 0);
+  std::stable_sort(idx.begin(), idx.end(), [&](int32_t a, int32_t b) {
+    const auto ka = key(tiles[a]), kb = key(tiles[b]);
+    if (ka != kb) return ka < kb;
+    return work(tiles[a]) > work(tiles[b]);
+  });
+  int64_t total = 0;
+  for (const PrefillTile& t : tiles) total += work(t);
+  const int64_t share = std::max<int64_t>(1, ceil_div(total, kXcds));
+  struct Piece {
+    int64_t work;
+    size_t b, e;   // range of idx
+  };
+  std::vector<Piece> pieces;
+  for (size_t b = 0; b < T;) {
+    size_t e = b;
+    Piece pc{0, b, b};
+    while (e < T && key(tiles[idx[e]]) == key(tiles[idx[b]])) {
+      const int64_t w = work(tiles[idx[e]]);
+      if (pc.e > pc.b && pc.work + w > share) {   // close the piece, start the next
+        pieces.push_back(pc);
+        pc = Piece{0, e, e};
+      }
+      pc.work += w;
+      pc.e = ++e;
+    }
+    pieces.push_back(pc);
+    b = e;
+  }
+  std::stable_sort(pieces.begin(), pieces.end(), [](const Piece& a, const Piece& b) { return a.work > b.work; });
+  std::vector<std::vector<int32_t>> bins(kXcds);
+  int64_t load[kXcds] = {};
+  for (const Piece& pc : pieces) {
+    const int x = int(std::min_element(load, load + kXcds) - load);
+    load[x] += pc.work;
+    bins[x].insert(bins[x].end(), idx.begin() + pc.b, idx.begin() + pc.e);
+  }
+  for (auto& bin : bins)
+    std::stable_sort(bin.begin(), bin.end(), [&](int32_t a, int32_t b) { return work(tiles[a]) > work(tiles[b]); });
+  std::vector<PrefillTile> out;
+  out.reserve(T);
+  size_t pos[kXcds] = {};
+  for (size_t p = 0; out.size() < T; ++p) {
+    int x = int(p % kXcds);
+    if (pos[x] == bins[x].size()) {
+      size_t most = 0;
+      for (int y = 0; y < kXcds; ++y)
+        if (bins[y].size() - pos[y] > most) most = bins[y].size() - pos[y], x = y;
+    }
+    out.push_back(tiles[bins[x][pos[x]++]]);
+  }
+  tiles.swap(out);
+}
 
 
 }  // namespace
@@ -166,17 +236,133 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
           t.q0 = q_start[r];
           t.S0 = S0;
           const int i_first = c0 / g, i_last = (c0 + t.ncols - 1) / g;
+          (void)i_first;
           t.kv_end = S0 + i_last + 1;
-          t.key_diag = S0 + i_first;
+          t.kbeg = 0;
+          t.pbase = -1;
+          t.pstride = 0;
+          t.pad0 = t.pad1 = 0;
           plan->tiles.push_back(t);
         }
     } else {
       split_reqs.push_back(r);
     }
   }
-  // heaviest tiles first so the ragged end of the grid is made of short tiles
-  std::stable_sort(plan->tiles.begin(), plan->tiles.end(),
-                   [](const PrefillTile& a, const PrefillTile& b) { return a.kv_end > b.kv_end; });
+  // ---- cut long prefill tiles into key chunks -------------------------------------
+  // A tile's time grows with its keys; when a few long tiles are all there is (a short
+  // chunk of a long prompt), they would leave most resident slots idle.  Each such tile is
+  // then cut into tiles over consecutive key chunks, and the partial results of a column
+  // are merged like split-KV parts.  Chunks start at multiples of the chunk length up to
+  // S0 + i_first (the last key every column of the tile sees), so every chunk holds at
+  // least one visible key for each column; the last chunk runs to the tile's end and
+  // absorbs a remainder shorter than a quarter chunk.  Slots are numbered from 0 here and
+  // moved past the split-KV ones below.
+  //
+  // Without a forced chunk length the planner compares two greedy schedules of the tiles
+  // over the resident slots (the dispatcher hands each next workgroup to the first free
+  // slot): whole tiles, and tiles cut into chunks of the largest power of two (1024 to
+  // 8192) keys not above the tile keys per slot, each tile costing its keys plus a fixed
+  // start-up, chunk tiles a little more for their partial results.  It cuts when that
+  // shortens the modelled time by 10%.  (Power-of-two chunks measured faster than
+  // chunks of the same count but other lengths.)
+  std::vector<CombineRow> cut_rows;
+  int64_t cut_slots = 0;
+  auto chunks_of = [&](const PrefillTile& t, int64_t Lc) {
+    const int64_t seen = int64_t(t.S0) + t.c0 / g + 1;   // keys [0, S0 + i_first] are seen by all
+    if (t.kv_end <= 2 * Lc) return int64_t(1);           // short tiles stay whole
+    int64_t n = ceil_div(seen, Lc);
+    if (n >= 2 && 4 * (seen - (n - 1) * Lc) < Lc) --n;
+    return n;
+  };
+  if (!plan->tiles.empty() && p.prefill_split_len >= 0) {
+    int64_t keys_all = 0, longest = 0;
+    for (const PrefillTile& t : plan->tiles) {
+      keys_all += t.kv_end;
+      longest = std::max<int64_t>(longest, t.kv_end);
+    }
+    int64_t Lc = 0;
+    if (p.prefill_split_len > 0) {
+      Lc = ceil_div(p.prefill_split_len, kStepKeys) * kStepKeys;
+    } else {
+      int64_t cand = 1024;   // the largest power of two <= keys_all / slots, within [1024, 8192]
+      while (cand < 8192 && 2 * cand * kPrefillSlots <= keys_all) cand *= 2;
+      constexpr int64_t kStart = 128, kPartial = 128;   // modelled costs, in keys
+      std::vector<int64_t> whole, cut;
+      if (longest > 2 * cand) {       // else no tile would be cut
+        whole.reserve(plan->tiles.size());
+        cut.reserve(plan->tiles.size() + size_t(ceil_div(keys_all, cand)));
+        for (const PrefillTile& t : plan->tiles) {
+          whole.push_back(t.kv_end + kStart);
+          const int64_t n = chunks_of(t, cand);
+          if (n < 2) {
+            cut.push_back(t.kv_end + kStart);
+          } else {
+            for (int64_t j = 0; j + 1 < n; ++j) cut.push_back(cand + kStart + kPartial);
+            cut.push_back(t.kv_end - (n - 1) * cand + kStart + kPartial);
+          }
+        }
+      }
+      auto greedy = [](std::vector<int64_t>& costs) {
+        std::sort(costs.begin(), costs.end(), std::greater<int64_t>());
+        std::priority_queue<int64_t, std::vector<int64_t>, std::greater<int64_t>> free_at;
+        for (int i = 0; i < kPrefillSlots; ++i) free_at.push(0);
+        int64_t end = 0;
+        for (int64_t c : costs) {
+          const int64_t t = free_at.top() + c;
+          free_at.pop();
+          free_at.push(t);
+          end = std::max(end, t);
+        }
+        return end;
+      };
+      if (!whole.empty() && 10 * greedy(cut) < 9 * greedy(whole)) Lc = cand;
+    }
+    if (Lc > 0) {
+      std::vector<PrefillTile> cut;
+      cut.reserve(plan->tiles.size() + size_t(ceil_div(keys_all, Lc)));
+      size_t nrows = 0;
+      for (const PrefillTile& t : plan->tiles)
+        if (chunks_of(t, Lc) >= 2) nrows += size_t(t.ncols);
+      cut_rows.reserve(nrows);
+      for (const PrefillTile& t : plan->tiles) {
+        const int64_t n = chunks_of(t, Lc);
+        if (n < 2) {
+          cut.push_back(t);
+          continue;
+        }
+        const int64_t base = cut_slots;
+        cut_slots += int64_t(t.ncols) * n;
+        for (int c = 0; c < t.ncols; ++c) {
+          CombineRow cr;
+          cr.q_row = t.q0 + (t.c0 + c) / g;
+          cr.q_head = t.kvh * g + (t.c0 + c) % g;
+          cr.pbase = int32_t(base + int64_t(c) * n);
+          cr.nparts = int32_t(n);
+          cut_rows.push_back(cr);
+        }
+        for (int64_t j = 0; j < n; ++j) {
+          PrefillTile u = t;
+          u.kbeg = int32_t(j * Lc);
+          u.kv_end = j + 1 < n ? int32_t((j + 1) * Lc) : t.kv_end;
+          u.pbase = int32_t(base + j);
+          u.pstride = int32_t(n);
+          cut.push_back(u);
+        }
+      }
+      plan->tiles.swap(cut);
+    }
+  }
+  // whole tiles first, then key-chunk tiles (two launches), each part in launch order
+  {
+    auto first_chunk = std::stable_partition(plan->tiles.begin(), plan->tiles.end(),
+                                             [](const PrefillTile& t) { return t.pbase < 0; });
+    plan->tiles_whole = int32_t(first_chunk - plan->tiles.begin());
+    std::vector<PrefillTile> whole(plan->tiles.begin(), first_chunk), chunk(first_chunk, plan->tiles.end());
+    order_tiles(whole);
+    order_tiles(chunk);
+    std::copy(whole.begin(), whole.end(), plan->tiles.begin());
+    std::copy(chunk.begin(), chunk.end(), plan->tiles.begin() + plan->tiles_whole);
+  }
 
   // ---- shared-prefix groups --------------------------------------------------------
   std::vector<int32_t> shared_pages(num_reqs, 0);   // pages read through the group
@@ -329,6 +515,15 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
       cr.nparts = nparts[o];
       plan->combine.push_back(cr);
     }
+  // slots of the cut prefill tiles follow
+  for (PrefillTile& t : plan->tiles)
+    if (t.pbase >= 0) t.pbase += int32_t(std::min<int64_t>(slots, INT32_MAX));
+  plan->combine.reserve(plan->combine.size() + cut_rows.size());
+  for (CombineRow cr : cut_rows) {
+    cr.pbase += int32_t(std::min<int64_t>(slots, INT32_MAX));
+    plan->combine.push_back(cr);
+  }
+  slots += cut_slots;
   if (slots > INT32_MAX) {
     delete plan;
     return fail(VA_ERR_UNSUPPORTED, "too many partial results for one plan");
@@ -360,7 +555,10 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
         t.q0 = j;                                       // partial slot of this chunk
         t.S0 = int32_t(B.kstart + int64_t(j) * B.chunk);
         t.kv_end = int32_t(std::min<int64_t>(B.kend, B.kstart + int64_t(j + 1) * B.chunk));
-        t.key_diag = t.kv_end;
+        t.kbeg = t.S0;
+        t.pbase = -1;
+        t.pstride = 0;
+        t.pad0 = t.pad1 = 0;
         plan->gtiles.push_back(t);
       }
       continue;
@@ -436,6 +634,8 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
   st.shared_tiles = int64_t(plan->gtiles.size());
   st.shared_tile_flops = 0;
   for (const PrefillTile& t : plan->gtiles) st.shared_tile_flops += 4.0 * D * t.ncols * double(t.kv_end - t.S0);
+  st.prefill_split_tiles = std::count_if(plan->tiles.begin(), plan->tiles.end(),
+                                         [](const PrefillTile& t) { return t.pbase >= 0; });
   st.direct_items = std::count_if(plan->items.begin(), plan->items.end(),
                                   [](const SplitItem& it) { return (it.flags & kItemDirect) != 0; });
 

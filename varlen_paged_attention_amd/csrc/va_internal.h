@@ -31,13 +31,17 @@ struct CombineRow {
 };
 
 // One MFMA prefill tile: query columns c0 .. c0+ncols of request `req` under KV head
-// `kvh`, where column c is new row i = c / g with query head kvh*g + c % g.  As a
-// shared-prefix group tile the fields mean: columns cols[c0 .. c0+ncols), partial slot q0,
-// keys [S0, kv_end) of request req's block table.
+// `kvh`, where column c is new row i = c / g with query head kvh*g + c % g, scored
+// against keys [kbeg, kv_end) (row i sees keys up to S0 + i).  pbase < 0: the tile holds
+// all of its columns' keys and writes normalised output rows; else it is one key chunk of
+// a cut tile and tile column col writes its partial (m, l, acc) to workspace slot
+// pbase + col * pstride for the combine pass.  As a shared-prefix group tile the fields
+// mean: columns cols[c0 .. c0+ncols), partial slot q0, keys [kbeg = S0, kv_end) of
+// request req's block table.
 struct PrefillTile {
   int32_t req, kvh, c0, ncols;
-  int32_t q0, S0, kv_end, key_diag;  // q_start of the request; S0; keys read [0, kv_end);
-                                     // keys >= key_diag need the causal check
+  int32_t q0, S0, kv_end, kbeg;
+  int32_t pbase, pstride, pad0, pad1;
 };
 
 constexpr int kSplitCols = 16;       // query columns per split-KV item (MFMA N)
@@ -45,6 +49,7 @@ constexpr int kSplitWaves = 4;       // items (wavefronts) per split-KV workgrou
 constexpr int kPrefillWaves = 4;     // wavefronts per prefill workgroup (32 columns each)
 constexpr int kPrefillCols = 32 * kPrefillWaves;   // query columns per prefill tile
 constexpr int kStepKeys = 64;        // kv positions per split-KV loop step
+constexpr int kPrefillSlots = 512;   // prefill workgroups resident at once (256 CUs x 2)
 
 }  // namespace va
 
@@ -66,7 +71,8 @@ struct va_plan {
   int32_t items_wide = 0;                    // how many items have more than 16 columns
   std::vector<va::Column> cols;
   std::vector<va::CombineRow> combine;
-  std::vector<va::PrefillTile> tiles;
+  std::vector<va::PrefillTile> tiles;         // whole tiles, then key-chunk tiles
+  int32_t tiles_whole = 0;                    // how many tiles are whole
   std::vector<va::PrefillTile> gtiles;        // shared-prefix group tiles (columns from `cols`)
   std::vector<char> is_split;               // per request: rows run as split-KV items
   int64_t pos_bytes = 0;                     // K+V bytes of one position over all KV heads

@@ -358,7 +358,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--only", type=int, default=None,
-                    help="profile mode: time only this workload (2-8 or 51) and print its line")
+                    help="profile mode: time only this workload (2-9 or 51) and print its line")
     ap.add_argument("--fp8", action="store_true", help="with --only: the workload in fp8 KV storage")
     ap.add_argument("--copy-only", action="store_true",
                     help="profile mode: 10 device copies of 1 GiB (HBM counter calibration)")
@@ -380,7 +380,8 @@ def main():
         return
     if args.only is not None:
         flags = api.VA_FLAG_SHARED_PREFIX if args.only in (5, 51) else 0
-        key = {2: "orca", 3: "decode", 4: "chunk", 5: "shared6", 51: "shared64", 6: "mtp3", 7: "mtp7"}.get(args.only)
+        key = {2: "orca", 3: "decode", 4: "chunk", 5: "shared6", 51: "shared64", 6: "mtp3", 7: "mtp7",
+               9: "longchunk"}.get(args.only)
         if args.fp8:
             key += "_fp8"
         fl = make_flush() if args.only in (5, 51) else None     # as in the secondary lines
@@ -426,6 +427,8 @@ def main():
         for cid, flags, label, fl, key, dt in (
                 (3, 0, "decode-heavy-gqa (256 decodes, kv U[1024,8192], g=4, page 64)", None, "decode", None),
                 (4, 0, "chunked-prefill-mix (2048@S0=30720 + 64 decodes, g=8)", None, "chunk", None),
+                (9, 0, "long-prefix-chunk (256@S0=65536 + 64 decodes, g=4; key-chunk tiles)", None, "longchunk",
+                 None),
                 (5, api.VA_FLAG_SHARED_PREFIX, "shared-prefix-6 (4096 shared + 1024 each)", flush, "shared6", None),
                 (51, api.VA_FLAG_SHARED_PREFIX, "shared-prefix-64 (16384 shared + 1024 each)", flush, "shared64",
                  None),

@@ -70,6 +70,7 @@ SMALL = [
     ("shared-64/8", 51, 8, api.VA_FLAG_SHARED_PREFIX),
     ("spec-decode-mtp3/8", 6, 8, 0),
     ("spec-decode-mtp7/8", 7, 8, 0),
+    ("long-prefix-chunk/8", 9, 8, 0),
 ]
 
 
@@ -96,7 +97,8 @@ def _sample_rows(w, rng, nreq, nrows):
 
 
 FULL = [("orca-mixed", 2, 0), ("decode-heavy", 3, 0), ("chunk-mix", 4, 0), ("shared-6", 5, api.VA_FLAG_SHARED_PREFIX),
-        ("shared-64", 51, api.VA_FLAG_SHARED_PREFIX), ("spec-decode-mtp3", 6, 0), ("spec-decode-mtp7", 7, 0)]
+        ("shared-64", 51, api.VA_FLAG_SHARED_PREFIX), ("spec-decode-mtp3", 6, 0), ("spec-decode-mtp7", 7, 0),
+        ("long-prefix-chunk", 9, 0)]
 
 
 @pytest.mark.parametrize("label,cid,flags", FULL, ids=[f[0] for f in FULL])

@@ -199,6 +199,8 @@ CASES = [
     ("orca-small-fp8", lambda: W.config(2, scale=16, dtype="fp8"), 0),
     ("decode-fp8", lambda: W.config(3, scale=16, dtype="fp8"), 0),
     ("shared-fp8", lambda: W.config(5, dtype="fp8"), api.VA_FLAG_SHARED_PREFIX),
+    ("long-prefix-chunk", lambda: W.config(9), 0),
+    ("long-prefix-chunk/8", lambda: W.config(9, scale=8), 0),
 ]
 
 

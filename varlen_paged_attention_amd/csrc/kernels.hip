@@ -904,14 +904,14 @@ static va_status prepare_kernels() {
   // the prefill kernel's dynamic LDS exceeds the 64 KiB default limit
   static hipError_t once = [] {
     const std::pair<const void*, int> kernels[] = {
-        {reinterpret_cast<const void*>(&prefill_bf16_kernel<128, false, false>), prefill_lds_bytes<128>()},
-        {reinterpret_cast<const void*>(&prefill_bf16_kernel<64, false, false>), prefill_lds_bytes<64>()},
-        {reinterpret_cast<const void*>(&prefill_bf16_kernel<128, true, false>), prefill_lds_bytes<128>()},
-        {reinterpret_cast<const void*>(&prefill_bf16_kernel<64, true, false>), prefill_lds_bytes<64>()},
-        {reinterpret_cast<const void*>(&prefill_bf16_kernel<128, false, true>), prefill_lds_bytes<128>()},
-        {reinterpret_cast<const void*>(&prefill_bf16_kernel<64, false, true>), prefill_lds_bytes<64>()},
-        {reinterpret_cast<const void*>(&prefill_bf16_kernel<128, true, true>), prefill_lds_bytes<128>()},
-        {reinterpret_cast<const void*>(&prefill_bf16_kernel<64, true, true>), prefill_lds_bytes<64>()}};
+#define VA_PREFILL_KERNEL(D, M, F) {reinterpret_cast<const void*>(&prefill_bf16_kernel<D, M, F>), prefill_lds_bytes<D>()}
+        VA_PREFILL_KERNEL(128, kWholeTile, false), VA_PREFILL_KERNEL(64, kWholeTile, false),
+        VA_PREFILL_KERNEL(128, kChunkTile, false), VA_PREFILL_KERNEL(64, kChunkTile, false),
+        VA_PREFILL_KERNEL(128, kGroupTile, false), VA_PREFILL_KERNEL(64, kGroupTile, false),
+        VA_PREFILL_KERNEL(128, kWholeTile, true),  VA_PREFILL_KERNEL(64, kWholeTile, true),
+        VA_PREFILL_KERNEL(128, kChunkTile, true),  VA_PREFILL_KERNEL(64, kChunkTile, true),
+        VA_PREFILL_KERNEL(128, kGroupTile, true),  VA_PREFILL_KERNEL(64, kGroupTile, true)};
+#undef VA_PREFILL_KERNEL
     for (const auto& k : kernels) {
       const hipError_t e = hipFuncSetAttribute(k.first, hipFuncAttributeMaxDynamicSharedMemorySize, k.second);
       if (e != hipSuccess) return e;

@@ -332,6 +332,7 @@ CONFIG_NAMES = {
     6: "spec-decode-mtp3",
     7: "spec-decode-mtp7",
     8: "long-context-decode-128k",
+    9: "long-prefix-chunk",
 }
 
 
@@ -398,4 +399,14 @@ def config(cid: int, seed: Optional[int] = None, poison_tail: bool = False,
         L = max(64, 131072 // scale)
         return mk(CONFIG_NAMES[8], [1] * n, [L] * n, num_q_heads=32, num_kv_heads=8, head_dim=128,
                   page_size=64, seed=s, hashed_kv=True)
+    if cid == 9:
+        # chunked prefill of a long prompt with a small chunk budget: a 256-row chunk whose
+        # cached prefix is 65,536 positions ("ORCA 和 chunked prefill", section 4: a chunk
+        # reads everything before it), batched with 64 decodes as in the chunk mix; the
+        # decode-heavy head layout (g = 4)
+        n = max(1, 64 // scale)
+        kv = sh(uniform_lengths(s, n, 512, 16384))
+        chunk, S0 = int(sh(256)), int(sh(65536))
+        return mk(CONFIG_NAMES[9], [chunk] + [1] * n, [S0 + chunk] + list(kv), num_q_heads=32, num_kv_heads=8,
+                  head_dim=128, page_size=64, seed=s, poison_tail=poison_tail)
     raise ValueError(f"unknown config {cid}")

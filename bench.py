@@ -141,8 +141,13 @@ def dominant(stats, stage_ms):
     """The stage with the largest time, with its algorithmic work and roofline bound."""
     name = max(stage_ms, key=stage_ms.get)
     ms = stage_ms[name]
-    if name == "prefill":      # prefill tiles and shared-prefix group tiles
-        work, bound = stats["prefill_flops"] + stats["shared_tile_flops"], "mfma"
+    if name == "prefill":
+        # prefill tiles (with the decodes a bf16 plan runs as tiles) and shared-prefix group
+        # tiles: MFMA-bound unless the tiles mostly stream decode KV
+        flops = stats["prefill_flops"] + stats["shared_tile_flops"]
+        byts = stats["prefill_kv_bytes"] + 2 * (stats["q_bytes"] - stats["split_q_bytes"])
+        bound = "mfma" if flops / PEAK_BF16 > byts / PEAK_HBM else "hbm"
+        work = flops if bound == "mfma" else byts
     elif name == "split_kv":
         # bandwidth-bound unless it also carries the prefill rows (then it is a contraction)
         flops = stats["split_flops"] - stats["shared_tile_flops"]

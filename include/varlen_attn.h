@@ -88,7 +88,11 @@ enum {
   VA_FLAG_NO_PREFILL_KERNEL = 1u << 1,
   /* Build the plan on the host only: no device buffer, run() refuses it.  Used to test
    * planning without a GPU. */
-  VA_FLAG_HOST_ONLY = 1u << 2
+  VA_FLAG_HOST_ONLY = 1u << 2,
+  /* Keep requests with few new rows (decodes, speculative-decode verify rows) on split-KV
+   * items.  Without it, a bf16 plan runs them as MFMA prefill tiles (one per KV head, all
+   * of the request's keys) when those tiles, with the prefill tiles, fill the GPU. */
+  VA_FLAG_NO_DECODE_TILES = 1u << 3
 };
 
 typedef struct {

@@ -98,7 +98,11 @@ def _sample_rows(w, rng, nreq, nrows):
 
 FULL = [("orca-mixed", 2, 0), ("decode-heavy", 3, 0), ("chunk-mix", 4, 0), ("shared-6", 5, api.VA_FLAG_SHARED_PREFIX),
         ("shared-64", 51, api.VA_FLAG_SHARED_PREFIX), ("spec-decode-mtp3", 6, 0), ("spec-decode-mtp7", 7, 0),
-        ("long-prefix-chunk", 9, 0)]
+        ("long-prefix-chunk", 9, 0),
+        # the short requests of these run as prefill tiles by default; also on split-KV items
+        ("decode-heavy split-KV", 3, api.VA_FLAG_NO_DECODE_TILES),
+        ("spec-decode-mtp7 split-KV", 7, api.VA_FLAG_NO_DECODE_TILES),
+        ("orca-mixed split-KV decodes", 2, api.VA_FLAG_NO_DECODE_TILES)]
 
 
 @pytest.mark.parametrize("label,cid,flags", FULL, ids=[f[0] for f in FULL])

@@ -210,6 +210,38 @@ def test_plan_covers_every_visible_pair_once(name, make, flags):
     check_coverage(w, _plan(w, flags))
 
 
+FOLD_CASES = [
+    # (name, workload, flags, short requests expected on tiles)
+    ("decode-heavy", lambda: W.config(3), 0, True),                       # 2048 tiles fill 512 slots
+    ("decode-heavy no-decode-tiles", lambda: W.config(3), api.VA_FLAG_NO_DECODE_TILES, False),
+    ("decode-heavy/16", lambda: W.config(3, scale=16), 0, False),          # 128 tiles: items stay
+    ("decode-heavy fp8", lambda: W.config(3, dtype="fp8"), 0, False),      # fp8 tiles widen every code
+    ("spec-decode-mtp7", lambda: W.config(7), 0, True),
+    ("orca", lambda: W.config(2), 0, True),
+    ("few long decodes (cut)", lambda: W.build("fl", [1] * 4, [32768] * 4, num_q_heads=32, num_kv_heads=8,
+                                               head_dim=128, page_size=64, seed=3), 0, True),
+    ("shared-prefix-64", lambda: W.config(51), api.VA_FLAG_SHARED_PREFIX, False),
+]
+
+
+@pytest.mark.parametrize("name,make,flags,folded", FOLD_CASES, ids=[c[0] for c in FOLD_CASES])
+def test_short_requests_as_tiles(name, make, flags, folded):
+    w = make()
+    plan = _plan(w, flags)
+    st = api.varlen_attn_plan_stats(plan)
+    m = w.q_end - w.q_start
+    g = w.num_q_heads // w.num_kv_heads
+    short = [r for r in range(w.num_reqs) if 0 < m[r] and m[r] * g < 64]
+    tiles = api.varlen_attn_plan_export(plan, 3)
+    on_tiles = set(int(t[0]) for t in tiles)
+    if folded:
+        assert all(r in on_tiles for r in short) and st["split_items"] == 0
+        assert st["prefill_tiles"] >= 512
+    else:
+        assert not any(r in on_tiles for r in short)
+    check_coverage(w, plan)
+
+
 def _long_chunk(m=256, S0=65536, hq=32, hkv=8, extra=()):
     """A chunk of m new rows on S0 cached positions (plus optional decodes)."""
     rows = [m] + [1] * len(extra)

@@ -18,6 +18,7 @@ VA_OK, VA_ERR_INVALID_ARG, VA_ERR_UNSUPPORTED, VA_ERR_OUT_OF_MEMORY, VA_ERR_HIP,
 VA_DTYPE_BF16, VA_DTYPE_F32, VA_DTYPE_FP8_E4M3 = 0, 1, 2
 DTYPE_CODES = {"bf16": VA_DTYPE_BF16, "f32": VA_DTYPE_F32, "fp8": VA_DTYPE_FP8_E4M3}
 VA_FLAG_SHARED_PREFIX, VA_FLAG_NO_PREFILL_KERNEL, VA_FLAG_HOST_ONLY = 1, 2, 4
+VA_FLAG_NO_DECODE_TILES = 1 << 3
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvarlen_attn.so")
 EXPORTED = ["varlen_attn_plan", "varlen_attn_run", "varlen_attn_run_events", "varlen_attn_plan_stats", "varlen_attn_plan_export",

@@ -413,11 +413,13 @@ constexpr int prefill_lds_bytes() {
 // place to bf16(code * scale) in the layouts above, so the MFMA loop is the bf16 one.
 // The slice is the wave's own, and all its reads precede its writes, so no other wave is
 // involved until the barrier that ends the iteration.
-enum TileMode { kWholeTile, kChunkTile, kGroupTile };
+enum TileMode { kWholeTile, kAnyTile, kGroupTile };
 
-// Whole tiles, key-chunk tiles and group tiles are separate instantiations (and launches):
-// code shared by the three kinds in one kernel measured slower for whole tiles, as the
-// compiler then no longer overlaps the exponentials with the next tile's MFMAs.
+// Instantiations: kWholeTile runs whole tiles only; kAnyTile runs whole tiles and key-chunk
+// tiles (a plan with chunk tiles launches all its tiles on it, so the two kinds share the
+// GPU); kGroupTile runs group tiles.  The whole-tile kernel is kept apart because any
+// partial-result epilogue in the same kernel changes how the compiler lays out the main
+// loop, and whole tiles then measured 4-6 % slower.
 template <int D, int MODE, bool F8>
 __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_bf16_kernel(
     const PrefillTile* __restrict__ tiles, const Column* __restrict__ cols, const bf16* __restrict__ q,
@@ -459,13 +461,14 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
     limit = cvalid ? T.kv_end - 1 : -1;
     w_min_limit = T.kv_end - 1;
     w_max_limit = (wv * 32 < T.ncols) ? T.kv_end - 1 : -1;
-  } else if constexpr (MODE == kChunkTile) {
+  } else if constexpr (MODE == kAnyTile) {
     const int i = c / g;
     row = T.q0 + i;
     head = T.kvh * g + c % g;
     pslot = T.pbase + col * T.pstride;
     kbeg = T.kbeg;
     // a key chunk before the last one ends before the diagonal: clip the limits to its end
+    // (a no-op for whole tiles, which end one past their last row's last key)
     const int kl = T.kv_end - 1;
     limit = cvalid ? min(T.S0 + i, kl) : -1;
     const int wcol_last = min(wv * 32 + 31, T.ncols - 1);
@@ -779,7 +782,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
   }
   // ---- normalise and write: acc[db][4*ii + jj] is d = 32*db + 8*ii + 4*h + jj of this column
   const float l_tot = l_run + other_half(l_run);
-  if constexpr (MODE != kWholeTile) {
+  if (GROUP || (MODE == kAnyTile && T.pbase >= 0)) {
     if (cvalid) {
       if (h == 0) {
         ws_ml[2 * size_t(pslot)] = m_run;
@@ -906,10 +909,10 @@ static va_status prepare_kernels() {
     const std::pair<const void*, int> kernels[] = {
 #define VA_PREFILL_KERNEL(D, M, F) {reinterpret_cast<const void*>(&prefill_bf16_kernel<D, M, F>), prefill_lds_bytes<D>()}
         VA_PREFILL_KERNEL(128, kWholeTile, false), VA_PREFILL_KERNEL(64, kWholeTile, false),
-        VA_PREFILL_KERNEL(128, kChunkTile, false), VA_PREFILL_KERNEL(64, kChunkTile, false),
+        VA_PREFILL_KERNEL(128, kAnyTile, false), VA_PREFILL_KERNEL(64, kAnyTile, false),
         VA_PREFILL_KERNEL(128, kGroupTile, false), VA_PREFILL_KERNEL(64, kGroupTile, false),
         VA_PREFILL_KERNEL(128, kWholeTile, true),  VA_PREFILL_KERNEL(64, kWholeTile, true),
-        VA_PREFILL_KERNEL(128, kChunkTile, true),  VA_PREFILL_KERNEL(64, kChunkTile, true),
+        VA_PREFILL_KERNEL(128, kAnyTile, true),  VA_PREFILL_KERNEL(64, kAnyTile, true),
         VA_PREFILL_KERNEL(128, kGroupTile, true),  VA_PREFILL_KERNEL(64, kGroupTile, true)};
 #undef VA_PREFILL_KERNEL
     for (const auto& k : kernels) {
@@ -1028,7 +1031,7 @@ static va_status run_impl(const va_plan* plan, const void* q, const void* k_pool
   };
   if ((e = mark(0)) != hipSuccess) return hip_fail("hipEventRecord", e);
   const int ntiles = int(plan->tiles.size()), ngtiles = int(plan->gtiles.size());
-  const int nwhole = plan->tiles_whole, nchunk = ntiles - nwhole;
+  const int nwhole = plan->tiles_whole, nchunk = ntiles - nwhole;   // the rest run on kAnyTile
   auto launch_tiles = [&](auto mode, auto f8, const PrefillTile* tl, int n) {
     constexpr int M = decltype(mode)::value;
     constexpr bool F = decltype(f8)::value;
@@ -1049,11 +1052,11 @@ static va_status run_impl(const va_plan* plan, const void* q, const void* k_pool
     return fp8 ? launch_tiles(mode, std::true_type{}, tl, n) : launch_tiles(mode, std::false_type{}, tl, n);
   };
   using Whole = std::integral_constant<int, kWholeTile>;
-  using Chunk = std::integral_constant<int, kChunkTile>;
+  using Any = std::integral_constant<int, kAnyTile>;
   using Group = std::integral_constant<int, kGroupTile>;
   if (nwhole && (e = launch_kind(Whole{}, plan->d_tiles, nwhole)) != hipSuccess)
     return hip_fail("prefill kernel launch", e);
-  if (nchunk && (e = launch_kind(Chunk{}, plan->d_tiles + nwhole, nchunk)) != hipSuccess)
+  if (nchunk && (e = launch_kind(Any{}, plan->d_tiles + nwhole, nchunk)) != hipSuccess)
     return hip_fail("prefill key-chunk kernel launch", e);
   if (ngtiles && (e = launch_kind(Group{}, plan->d_gtiles, ngtiles)) != hipSuccess)
     return hip_fail("shared-prefix tile kernel launch", e);

@@ -9,7 +9,9 @@
 //    short ones (decode, q_rows = 1, and few-row requests) become split-KV items whose
 //    kv range is cut by kv_length so every wavefront gets a similar amount of KV to
 //    stream ("ORCA 和 chunked prefill", section 2: decode and prefill in one iteration;
-//    section 4: decode is the C = 1 case of a chunk).
+//    section 4: decode is the C = 1 case of a chunk) -- or, on bf16 pools when there are
+//    enough of them, prefill tiles too (a decode is a one-row chunk).  Tiles of a few long
+//    requests are cut into key chunks merged like split-KV parts.
 //  * With VA_FLAG_SHARED_PREFIX, requests whose block tables start with the same
 //    physical pages form a group; the shared pages are scored once per group for all of
 //    the group's rows, each row keeping its own running max and sum ("How To Scale Your
@@ -219,157 +221,43 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
   const bool use_prefill = !(p.flags & VA_FLAG_NO_PREFILL_KERNEL) && prefill_kernel_available(p);
 
   // ---- classify requests -------------------------------------------------------
-  std::vector<int> split_reqs;
+  // Requests with enough new rows always get prefill tiles; the others (decodes,
+  // speculative-decode verify rows, short chunks) are "short".
+  std::vector<int> tile_reqs, short_reqs;
   for (int r = 0; r < num_reqs; ++r) {
     const int m = q_end[r] - q_start[r];
     if (m == 0) continue;
+    (use_prefill && is_prefill(m) ? tile_reqs : short_reqs).push_back(r);
+  }
+  auto add_tiles = [&](std::vector<PrefillTile>& tiles, int r) {
+    const int m = q_end[r] - q_start[r];
     const int S0 = kv_len[r] - m;
-    if (use_prefill && is_prefill(m)) {
-      const int ncol = m * g;
-      for (int kvh = 0; kvh < Hkv; ++kvh)
-        for (int c0 = 0; c0 < ncol; c0 += kPrefillCols) {
-          PrefillTile t;
-          t.req = r;
-          t.kvh = kvh;
-          t.c0 = c0;
-          t.ncols = std::min(kPrefillCols, ncol - c0);
-          t.q0 = q_start[r];
-          t.S0 = S0;
-          const int i_first = c0 / g, i_last = (c0 + t.ncols - 1) / g;
-          (void)i_first;
-          t.kv_end = S0 + i_last + 1;
-          t.kbeg = 0;
-          t.pbase = -1;
-          t.pstride = 0;
-          t.pad0 = t.pad1 = 0;
-          plan->tiles.push_back(t);
-        }
-    } else {
-      split_reqs.push_back(r);
-    }
-  }
-  // ---- cut long prefill tiles into key chunks -------------------------------------
-  // A tile's time grows with its keys; when a few long tiles are all there is (a short
-  // chunk of a long prompt), they would leave most resident slots idle.  Each such tile is
-  // then cut into tiles over consecutive key chunks, and the partial results of a column
-  // are merged like split-KV parts.  Chunks start at multiples of the chunk length up to
-  // S0 + i_first (the last key every column of the tile sees), so every chunk holds at
-  // least one visible key for each column; the last chunk runs to the tile's end and
-  // absorbs a remainder shorter than a quarter chunk.  Slots are numbered from 0 here and
-  // moved past the split-KV ones below.
-  //
-  // Without a forced chunk length the planner compares two greedy schedules of the tiles
-  // over the resident slots (the dispatcher hands each next workgroup to the first free
-  // slot): whole tiles, and tiles cut into chunks of the largest power of two (1024 to
-  // 8192) keys not above the tile keys per slot, each tile costing its keys plus a fixed
-  // start-up, chunk tiles a little more for their partial results.  It cuts when that
-  // shortens the modelled time by 10%.  (Power-of-two chunks measured faster than
-  // chunks of the same count but other lengths.)
-  std::vector<CombineRow> cut_rows;
-  int64_t cut_slots = 0;
-  auto chunks_of = [&](const PrefillTile& t, int64_t Lc) {
-    const int64_t seen = int64_t(t.S0) + t.c0 / g + 1;   // keys [0, S0 + i_first] are seen by all
-    if (t.kv_end <= 2 * Lc) return int64_t(1);           // short tiles stay whole
-    int64_t n = ceil_div(seen, Lc);
-    if (n >= 2 && 4 * (seen - (n - 1) * Lc) < Lc) --n;
-    return n;
+    const int ncol = m * g;
+    for (int kvh = 0; kvh < Hkv; ++kvh)
+      for (int c0 = 0; c0 < ncol; c0 += kPrefillCols) {
+        PrefillTile t;
+        t.req = r;
+        t.kvh = kvh;
+        t.c0 = c0;
+        t.ncols = std::min(kPrefillCols, ncol - c0);
+        t.q0 = q_start[r];
+        t.S0 = S0;
+        t.kv_end = S0 + (c0 + t.ncols - 1) / g + 1;   // one past the last row's last key
+        t.kbeg = 0;
+        t.pbase = -1;
+        t.pstride = 0;
+        t.pad0 = t.pad1 = 0;
+        tiles.push_back(t);
+      }
   };
-  if (!plan->tiles.empty() && p.prefill_split_len >= 0) {
-    int64_t keys_all = 0, longest = 0;
-    for (const PrefillTile& t : plan->tiles) {
-      keys_all += t.kv_end;
-      longest = std::max<int64_t>(longest, t.kv_end);
-    }
-    int64_t Lc = 0;
-    if (p.prefill_split_len > 0) {
-      Lc = ceil_div(p.prefill_split_len, kStepKeys) * kStepKeys;
-    } else {
-      int64_t cand = 1024;   // the largest power of two <= keys_all / slots, within [1024, 8192]
-      while (cand < 8192 && 2 * cand * kPrefillSlots <= keys_all) cand *= 2;
-      constexpr int64_t kStart = 128, kPartial = 128;   // modelled costs, in keys
-      std::vector<int64_t> whole, cut;
-      if (longest > 2 * cand) {       // else no tile would be cut
-        whole.reserve(plan->tiles.size());
-        cut.reserve(plan->tiles.size() + size_t(ceil_div(keys_all, cand)));
-        for (const PrefillTile& t : plan->tiles) {
-          whole.push_back(t.kv_end + kStart);
-          const int64_t n = chunks_of(t, cand);
-          if (n < 2) {
-            cut.push_back(t.kv_end + kStart);
-          } else {
-            for (int64_t j = 0; j + 1 < n; ++j) cut.push_back(cand + kStart + kPartial);
-            cut.push_back(t.kv_end - (n - 1) * cand + kStart + kPartial);
-          }
-        }
-      }
-      auto greedy = [](std::vector<int64_t>& costs) {
-        std::sort(costs.begin(), costs.end(), std::greater<int64_t>());
-        std::priority_queue<int64_t, std::vector<int64_t>, std::greater<int64_t>> free_at;
-        for (int i = 0; i < kPrefillSlots; ++i) free_at.push(0);
-        int64_t end = 0;
-        for (int64_t c : costs) {
-          const int64_t t = free_at.top() + c;
-          free_at.pop();
-          free_at.push(t);
-          end = std::max(end, t);
-        }
-        return end;
-      };
-      if (!whole.empty() && 10 * greedy(cut) < 9 * greedy(whole)) Lc = cand;
-    }
-    if (Lc > 0) {
-      std::vector<PrefillTile> cut;
-      cut.reserve(plan->tiles.size() + size_t(ceil_div(keys_all, Lc)));
-      size_t nrows = 0;
-      for (const PrefillTile& t : plan->tiles)
-        if (chunks_of(t, Lc) >= 2) nrows += size_t(t.ncols);
-      cut_rows.reserve(nrows);
-      for (const PrefillTile& t : plan->tiles) {
-        const int64_t n = chunks_of(t, Lc);
-        if (n < 2) {
-          cut.push_back(t);
-          continue;
-        }
-        const int64_t base = cut_slots;
-        cut_slots += int64_t(t.ncols) * n;
-        for (int c = 0; c < t.ncols; ++c) {
-          CombineRow cr;
-          cr.q_row = t.q0 + (t.c0 + c) / g;
-          cr.q_head = t.kvh * g + (t.c0 + c) % g;
-          cr.pbase = int32_t(base + int64_t(c) * n);
-          cr.nparts = int32_t(n);
-          cut_rows.push_back(cr);
-        }
-        for (int64_t j = 0; j < n; ++j) {
-          PrefillTile u = t;
-          u.kbeg = int32_t(j * Lc);
-          u.kv_end = j + 1 < n ? int32_t((j + 1) * Lc) : t.kv_end;
-          u.pbase = int32_t(base + j);
-          u.pstride = int32_t(n);
-          cut.push_back(u);
-        }
-      }
-      plan->tiles.swap(cut);
-    }
-  }
-  // whole tiles first, then key-chunk tiles (two launches), each part in launch order
-  {
-    auto first_chunk = std::stable_partition(plan->tiles.begin(), plan->tiles.end(),
-                                             [](const PrefillTile& t) { return t.pbase < 0; });
-    plan->tiles_whole = int32_t(first_chunk - plan->tiles.begin());
-    std::vector<PrefillTile> whole(plan->tiles.begin(), first_chunk), chunk(first_chunk, plan->tiles.end());
-    order_tiles(whole);
-    order_tiles(chunk);
-    std::copy(whole.begin(), whole.end(), plan->tiles.begin());
-    std::copy(chunk.begin(), chunk.end(), plan->tiles.begin() + plan->tiles_whole);
-  }
 
+  std::vector<int> split_reqs;
   // ---- shared-prefix groups --------------------------------------------------------
   std::vector<int32_t> shared_pages(num_reqs, 0);   // pages read through the group
   std::vector<std::vector<int>> groups;
   if (p.flags & VA_FLAG_SHARED_PREFIX) {
     std::map<int32_t, std::vector<int>> by_first;
-    for (int r : split_reqs) {
+    for (int r : short_reqs) {
       const int m = q_end[r] - q_start[r];
       const int S0 = kv_len[r] - m;
       // a shared page must be full and entirely visible to every row of the request
@@ -397,6 +285,167 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
       groups.push_back(mem);
     }
   }
+
+  // ---- cut long prefill tiles into key chunks -------------------------------------
+  // A tile's time grows with its keys; when a few long tiles are all there is (a short
+  // chunk of a long prompt), they would leave most resident slots idle.  Each such tile is
+  // then cut into tiles over consecutive key chunks, and the partial results of a column
+  // are merged like split-KV parts.  Chunks start at multiples of the chunk length up to
+  // S0 + i_first (the last key every column of the tile sees), so every chunk holds at
+  // least one visible key for each column; the last chunk runs to the tile's end and
+  // absorbs a remainder shorter than a quarter chunk.  Slots are numbered from 0 here and
+  // moved past the split-KV ones below.
+  //
+  // Without a forced chunk length the planner compares two greedy schedules of the tiles
+  // over the resident slots (the dispatcher hands each next workgroup to the first free
+  // slot): whole tiles, and tiles cut into chunks of the largest power of two (1024 to
+  // 8192) keys not above the tile keys per slot, each tile costing its keys plus a fixed
+  // start-up, chunk tiles a little more for their partial results.  It cuts when that
+  // shortens the modelled time by 10%.  (Power-of-two chunks measured faster than
+  // chunks of the same count but other lengths.)
+  auto chunks_of = [&](const PrefillTile& t, int64_t Lc) {
+    const int64_t seen = int64_t(t.S0) + t.c0 / g + 1;   // keys [0, S0 + i_first] are seen by all
+    if (t.kv_end <= 2 * Lc) return int64_t(1);           // short tiles stay whole
+    int64_t n = ceil_div(seen, Lc);
+    if (n >= 2 && 4 * (seen - (n - 1) * Lc) < Lc) --n;
+    return n;
+  };
+  // cuts `tiles` in place; the chunk tiles' combine rows go to `rows`, their slots (from 0) to `nslots`
+  auto cut_tiles = [&](std::vector<PrefillTile>& tiles, std::vector<CombineRow>& rows, int64_t& nslots) {
+    if (tiles.empty() || p.prefill_split_len < 0) return;
+    int64_t keys_all = 0, longest = 0;
+    for (const PrefillTile& t : tiles) {
+      keys_all += t.kv_end;
+      longest = std::max<int64_t>(longest, t.kv_end);
+    }
+    int64_t Lc = 0;
+    if (p.prefill_split_len > 0) {
+      Lc = ceil_div(p.prefill_split_len, kStepKeys) * kStepKeys;
+    } else {
+      int64_t cand = 1024;   // the largest power of two <= keys_all / slots, within [1024, 8192]
+      while (cand < 8192 && 2 * cand * kPrefillSlots <= keys_all) cand *= 2;
+      constexpr int64_t kStart = 128, kPartial = 128;   // modelled costs, in keys
+      std::vector<int64_t> whole, cut;
+      if (longest > 2 * cand) {       // else no tile would be cut
+        whole.reserve(tiles.size());
+        cut.reserve(tiles.size() + size_t(ceil_div(keys_all, cand)));
+        for (const PrefillTile& t : tiles) {
+          whole.push_back(t.kv_end + kStart);
+          const int64_t n = chunks_of(t, cand);
+          if (n < 2) {
+            cut.push_back(t.kv_end + kStart);
+          } else {
+            for (int64_t j = 0; j + 1 < n; ++j) cut.push_back(cand + kStart + kPartial);
+            cut.push_back(t.kv_end - (n - 1) * cand + kStart + kPartial);
+          }
+        }
+      }
+      auto greedy = [](std::vector<int64_t>& costs) {
+        std::sort(costs.begin(), costs.end(), std::greater<int64_t>());
+        std::priority_queue<int64_t, std::vector<int64_t>, std::greater<int64_t>> free_at;
+        for (int i = 0; i < kPrefillSlots; ++i) free_at.push(0);
+        int64_t end = 0;
+        for (int64_t c : costs) {
+          const int64_t t = free_at.top() + c;
+          free_at.pop();
+          free_at.push(t);
+          end = std::max(end, t);
+        }
+        return end;
+      };
+      if (!whole.empty() && 10 * greedy(cut) < 9 * greedy(whole)) Lc = cand;
+    }
+    if (Lc > 0) {
+      std::vector<PrefillTile> cut;
+      cut.reserve(tiles.size() + size_t(ceil_div(keys_all, Lc)));
+      size_t nrows = 0;
+      for (const PrefillTile& t : tiles)
+        if (chunks_of(t, Lc) >= 2) nrows += size_t(t.ncols);
+      rows.reserve(nrows);
+      for (const PrefillTile& t : tiles) {
+        const int64_t n = chunks_of(t, Lc);
+        if (n < 2) {
+          cut.push_back(t);
+          continue;
+        }
+        const int64_t base = nslots;
+        nslots += int64_t(t.ncols) * n;
+        for (int c = 0; c < t.ncols; ++c) {
+          CombineRow cr;
+          cr.q_row = t.q0 + (t.c0 + c) / g;
+          cr.q_head = t.kvh * g + (t.c0 + c) % g;
+          cr.pbase = int32_t(base + int64_t(c) * n);
+          cr.nparts = int32_t(n);
+          rows.push_back(cr);
+        }
+        for (int64_t j = 0; j < n; ++j) {
+          PrefillTile u = t;
+          u.kbeg = int32_t(j * Lc);
+          u.kv_end = j + 1 < n ? int32_t((j + 1) * Lc) : t.kv_end;
+          u.pbase = int32_t(base + j);
+          u.pstride = int32_t(n);
+          cut.push_back(u);
+        }
+      }
+      tiles.swap(cut);
+    }
+  };
+
+  // ---- short requests as prefill tiles -----------------------------------------------
+  // A short request can also run as prefill tiles (its g * q_rows columns in one tile per
+  // KV head, the tile streaming the request's whole KV range through LDS like a prefill).
+  // Measured on bf16 pools, that streams KV faster than the split-KV items once the tiles
+  // fill the GPU (decode-heavy: 800 vs 850 us; 4-row verify steps: 833 vs 932 us; 128K
+  // decodes: 21.1 vs 21.3 ms) but slower when they do not (16 decodes of 2K: 45 vs 28 us)
+  // and for fp8 pools, whose tiles widen every code (644 vs 450 us).  So short requests
+  // that are not shared-prefix group members become tiles when the plan is bf16, the row
+  // classification is the default one, and the tiles (after cutting) fill every resident
+  // slot; otherwise they stay split-KV items.
+  std::vector<CombineRow> cut_rows;
+  int64_t cut_slots = 0;
+  {
+    std::vector<int> fold;
+    const bool may_fold = use_prefill && p.dtype == VA_DTYPE_BF16 && p.prefill_min_rows <= 0 &&
+                          !(p.flags & VA_FLAG_NO_DECODE_TILES);
+    if (may_fold)
+      for (int r : short_reqs)
+        if (shared_pages[r] == 0) fold.push_back(r);
+    std::vector<PrefillTile> tiles;
+    for (int r : tile_reqs) add_tiles(tiles, r);
+    bool folded = false;
+    if (!fold.empty()) {
+      std::vector<PrefillTile> with = tiles;
+      for (int r : fold) add_tiles(with, r);
+      std::vector<CombineRow> rows;
+      int64_t nslots = 0;
+      cut_tiles(with, rows, nslots);
+      if (with.size() >= size_t(kPrefillSlots)) {
+        plan->tiles.swap(with);
+        cut_rows.swap(rows);
+        cut_slots = nslots;
+        folded = true;
+      }
+    }
+    if (!folded) {
+      cut_tiles(tiles, cut_rows, cut_slots);
+      plan->tiles.swap(tiles);
+    }
+    std::vector<char> is_tile(num_reqs, 0);
+    for (int r : tile_reqs) is_tile[r] = 1;
+    if (folded)
+      for (int r : fold) is_tile[r] = 1;
+    for (int r : short_reqs)
+      if (!is_tile[r]) split_reqs.push_back(r);
+  }
+
+  // launch order; with no chunk tile every tile runs on the whole-tile kernel, else every
+  // tile runs on the kernel that takes both kinds (one launch, so decode tiles and chunk
+  // tiles share the GPU instead of running one launch after the other)
+  order_tiles(plan->tiles);
+  plan->tiles_whole = std::any_of(plan->tiles.begin(), plan->tiles.end(),
+                                  [](const PrefillTile& t) { return t.pbase >= 0; })
+                          ? 0
+                          : int32_t(plan->tiles.size());
 
   // ---- column blocks ------------------------------------------------------------------
   std::vector<Block> blocks;

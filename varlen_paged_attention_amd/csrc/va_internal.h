@@ -71,8 +71,9 @@ struct va_plan {
   int32_t items_wide = 0;                    // how many items have more than 16 columns
   std::vector<va::Column> cols;
   std::vector<va::CombineRow> combine;
-  std::vector<va::PrefillTile> tiles;         // whole tiles, then key-chunk tiles
-  int32_t tiles_whole = 0;                    // how many tiles are whole
+  std::vector<va::PrefillTile> tiles;         // in launch order
+  int32_t tiles_whole = 0;                    // the first tiles_whole run on the whole-tile kernel
+                                              // (all, or none when there are chunk tiles)
   std::vector<va::PrefillTile> gtiles;        // shared-prefix group tiles (columns from `cols`)
   std::vector<char> is_split;               // per request: rows run as split-KV items
   int64_t pos_bytes = 0;                     // K+V bytes of one position over all KV heads

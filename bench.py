@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 METRIC = "varlen paged attn: decode HBM GB/s + prefill TFLOP/s, % of MI355X peak"
 PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E
 PEAK_BF16 = 2.5e15         # FLOP/s, MI355X dense bf16 MFMA
+SPIN_HZ = 2.4e9            # cycles per second assumed for torch.cuda._sleep (an over-estimate is harmless)
 STAGES = ("prefill", "split_kv", "combine")
 KERNEL_NAMES = {"prefill": "prefill_bf16_kernel", "split_kv": "split_kv_bf16_kernel", "combine": "combine_kernel"}
 KERNEL_NAMES_FP8 = {**KERNEL_NAMES, "split_kv": "split_kv_fp8_kernel"}
@@ -77,8 +78,11 @@ def cpu_model():
 
 
 def time_runs(api, plan, tensors, steps, warmup, flush=None):
-    """Run warmup + steps iterations with per-stage HIP events; returns (wall ms/step,
-    per-stage mean ms, per-step total ms list)."""
+    """Run warmup + steps iterations; returns (wall ms/step, per-stage mean ms, per-step
+    total ms list).  The wall clock times `steps` plain runs.  The stage times come from
+    the library's HIP events in a second pass of `steps` runs queued behind a spin kernel,
+    so the host has enqueued every launch before the GPU reaches it and no host-side gap
+    between an event and its kernel is counted as kernel time."""
     import torch
     q, k, v, bt, out, ws = tensors[:6]
     scales = dict(zip(("k_scale", "v_scale"), tensors[6:]))
@@ -92,10 +96,24 @@ def time_runs(api, plan, tensors, steps, warmup, flush=None):
     for i in range(steps):
         if flush is not None:
             flush()
-        calls[i]()
+        run()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
+    # spin long enough to cover the host's enqueueing of the event pass (about twice the
+    # measured wall time per step, at most 200 ms)
+    torch.cuda._sleep(int(min(200.0, 2.0 * wall * steps + 5.0) * 1e-3 * SPIN_HZ))
+    # the cost of one event record on the GPU's queue: pairs of events with nothing between
+    empty = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(8)]
+    for a, b in empty:
+        a.record()
+        b.record()
+    for i in range(steps):
+        if flush is not None:
+            flush()
+        calls[i]()
+    torch.cuda.synchronize()
     stage = {s: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, s in enumerate(STAGES)}
+    stage["event_record"] = float(np.median([a.elapsed_time(b) for a, b in empty]))
     totals = [e[0].elapsed_time(e[3]) for e in evs]
     return wall, stage, totals
 
@@ -138,9 +156,12 @@ def setup(api, w, flags=0):
 
 
 def dominant(stats, stage_ms):
-    """The stage with the largest time, with its algorithmic work and roofline bound."""
-    name = max(stage_ms, key=stage_ms.get)
-    ms = stage_ms[name]
+    """The stage with the largest time, with its algorithmic work and roofline bound.  Its
+    time is the span between the library's events around it less the cost of recording
+    one event (measured in the same pass), i.e. the kernel's own duration."""
+    kernels = {k: v for k, v in stage_ms.items() if k in STAGES}
+    name = max(kernels, key=kernels.get)
+    ms = kernels[name] - stage_ms.get("event_record", 0.0)
     if name == "prefill":
         # prefill tiles (with the decodes a bf16 plan runs as tiles) and shared-prefix group
         # tiles: MFMA-bound unless the tiles mostly stream decode KV

@@ -3,9 +3,12 @@
 MI355X.
 
 A step is one ``varlen_attn_run`` of the whole planned iteration (every kernel of the hot
-path) over inputs already resident in HBM, captured once in a HIP graph and replayed (the
-eager time is reported beside it; per-kernel times come from eager runs).  The headline workload is the ORCA-style mixed
-iteration: a 4096-token uncached prefill plus decodes at 1500 and 1700 cached positions,
+path) over inputs already resident in HBM.  The timed steps are issued as a model's
+forward issues them: consecutive runs read and write the buffers of consecutive layers
+(32 copies of Q, K, V and the output), all captured in one HIP graph that is launched
+once; the time per step with one graph launch per run and the eager time are reported
+beside it, and per-kernel times come from eager runs with the library's events.  The
+headline workload is the ORCA-style mixed iteration: a 4096-token uncached prefill plus decodes at 1500 and 1700 cached positions,
 32 query / 32 KV heads, head_dim 128, 16-token pages in a seeded random permutation, bf16.
 It is MFMA-bound, so ``value`` is TFLOP/s of algorithmic attention work (4·head_dim FLOPs
 per visible (query, key) pair per query head).  Secondary lines time the decode-heavy,
@@ -29,7 +32,6 @@ sys.path.insert(0, ROOT)
 METRIC = "varlen paged attn: decode HBM GB/s + prefill TFLOP/s, % of MI355X peak"
 PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E
 PEAK_BF16 = 2.5e15         # FLOP/s, MI355X dense bf16 MFMA
-SPIN_HZ = 2.4e9            # cycles per second assumed for torch.cuda._sleep (an over-estimate is harmless)
 STAGES = ("prefill", "split_kv", "combine")
 KERNEL_NAMES = {"prefill": "prefill_bf16_kernel", "split_kv": "split_kv_bf16_kernel", "combine": "combine_kernel"}
 KERNEL_NAMES_FP8 = {**KERNEL_NAMES, "split_kv": "split_kv_fp8_kernel"}
@@ -80,9 +82,10 @@ def cpu_model():
 def time_runs(api, plan, tensors, steps, warmup, flush=None):
     """Run warmup + steps iterations; returns (wall ms/step, per-stage mean ms, per-step
     total ms list).  The wall clock times `steps` plain runs.  The stage times come from
-    the library's HIP events in a second pass of `steps` runs queued behind a spin kernel,
-    so the host has enqueued every launch before the GPU reaches it and no host-side gap
-    between an event and its kernel is counted as kernel time."""
+    the library's HIP events in a second pass of `steps` runs enqueued behind a few plain
+    runs (the host enqueues a run in under 10 µs, so the queue never drains and no
+    host-side gap between an event and its kernel is counted as kernel time; real work,
+    unlike a spin kernel, also keeps the clocks where the timed runs put them)."""
     import torch
     q, k, v, bt, out, ws = tensors[:6]
     scales = dict(zip(("k_scale", "v_scale"), tensors[6:]))
@@ -99,9 +102,8 @@ def time_runs(api, plan, tensors, steps, warmup, flush=None):
         run()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
-    # spin long enough to cover the host's enqueueing of the event pass (about twice the
-    # measured wall time per step, at most 200 ms)
-    torch.cuda._sleep(int(min(200.0, 2.0 * wall * steps + 5.0) * 1e-3 * SPIN_HZ))
+    for _ in range(5):
+        run()
     # the cost of one event record on the GPU's queue: pairs of events with nothing between
     empty = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(8)]
     for a, b in empty:
@@ -118,31 +120,58 @@ def time_runs(api, plan, tensors, steps, warmup, flush=None):
     return wall, stage, totals
 
 
-def time_graph(api, plan, tensors, steps, warmup):
-    """One step captured in a HIP graph (the run is enqueue-only), replayed: warmup replays,
-    then `steps` replays timed by the wall clock between synchronisations.  Returns
-    ms/step."""
+LAYERS = 32     # attention layers of the model the headline iteration is shaped on (Llama-2-7B)
+
+
+def time_graph(api, plan, tensors, steps, warmup, layers=LAYERS):
+    """Steps as a model's forward issues them: run i reads and writes the buffers of layer
+    i % layers (each layer its own copy of Q, K, V and the output, so no layer finds the
+    previous layer's data in the last-level cache; one plan and workspace for all, as in
+    an iteration), all `steps` runs captured in one HIP graph (run is enqueue-only).
+    Untimed: `warmup` runs replayed from a graph of their own, then one launch of the
+    timed graph (a graph's first launch also uploads it).  Timed: one launch of the graph
+    of `steps` runs between synchronisations, by the wall clock.  Returns (ms/step, ms/step
+    with one graph launch per run)."""
     import torch
     q, k, v, bt, out, ws = tensors[:6]
     scales = dict(zip(("k_scale", "v_scale"), tensors[6:]))
+    sets = [(q, k, v, out)] + [(q.clone(), k.clone(), v.clone(), torch.empty_like(out)) for _ in range(layers - 1)]
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        call = api.RunCall(plan, q, k, v, bt, out, ws, stream=s, **scales)
-        call()
+        calls = [api.RunCall(plan, a, b, c, bt, d, ws, stream=s, **scales) for a, b, c, d in sets]
+        for c in calls:
+            c()
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=s):
-        call()
-    for _ in range(warmup):
-        g.replay()
+
+    def capture(n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(n):
+                calls[i % layers]()
+        return g
+
+    g_warm, g_steps = capture(max(1, warmup)), capture(steps)
+    g_warm.replay()
+    g_steps.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g_steps.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    # the same runs launched one graph each (launch overhead per run included)
+    g1 = capture(1)
+    g1.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        g.replay()
+        g1.replay()
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) * 1e3 / steps
+    ms_single = (time.perf_counter() - t0) * 1e3 / steps
+    del g_warm, g_steps, g1, calls, sets
+    torch.cuda.empty_cache()
+    return ms, ms_single
 
 
 def setup(api, w, flags=0):
@@ -356,15 +385,23 @@ def make_flush():
     return flush
 
 
-def secondary(api, W, cid, flags, reps, label, flush, key=None, dtype=None):
+def secondary(api, W, cid, flags, reps, label, flush, key=None, dtype=None, tp=1, dp=1):
     plan, tensors = None, None
-    w = W.config(cid, dtype=dtype)
+    w = W.config(cid, dtype=dtype, tp=tp, dp=dp)
     plan, tensors = setup(api, w, flags)
     st = api.varlen_attn_plan_stats(plan)
     _, stage, totals = time_runs(api, plan, tensors, reps, 3, flush)
-    us = float(np.median(totals)) * 1e3
+    # the step's time less the cost of the three event records inside it (see dominant())
+    steps_us = [(t - 3 * stage.get("event_record", 0.0)) * 1e3 for t in totals]
+    us = float(np.median(steps_us))
     byts = st["physical_kv_bytes"] + st["q_bytes"] + st["o_bytes"] + st["table_bytes"]
+    # time at the roofline if the FLOPs and the bytes could not overlap at all
+    t_roof_us = (st["flops"] / PEAK_BF16 + byts / PEAK_HBM) * 1e6
     res = {"workload": label, "us_per_step": round(us, 2),
+           "us_p10": round(float(np.percentile(steps_us, 10)), 2),
+           "us_p90": round(float(np.percentile(steps_us, 90)), 2),
+           "t_roof_us": round(t_roof_us, 2), "t_roof_frac": round(t_roof_us / us, 4),
+           "share": {"tp": tp, "dp": dp} if tp > 1 or dp > 1 else None,
            "hbm_GBps": round(byts / (us * 1e-6) / 1e9, 1), "hbm_frac": round(byts / (us * 1e-6) / PEAK_HBM, 4),
            "tflops": round(st["flops"] / (us * 1e-6) / 1e12, 2),
            "algorithmic_bytes": byts, "logical_kv_bytes": st["logical_kv_bytes"],
@@ -386,6 +423,9 @@ def main():
     ap.add_argument("--only", type=int, default=None,
                     help="profile mode: time only this workload (2-9 or 51) and print its line")
     ap.add_argument("--fp8", action="store_true", help="with --only: the workload in fp8 KV storage")
+    ap.add_argument("--shard", default=None,
+                    help="with --only: one GPU's share of the workload split over GPUs, tpN (by head) or dpN "
+                         "(by request)")
     ap.add_argument("--copy-only", action="store_true",
                     help="profile mode: 10 device copies of 1 GiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -411,8 +451,13 @@ def main():
         if args.fp8:
             key += "_fp8"
         fl = make_flush() if args.only in (5, 51) else None     # as in the secondary lines
+        tp = dp = 1
+        if args.shard:
+            kind, n = args.shard[:2], int(args.shard[2:])
+            tp, dp = (n, 1) if kind == "tp" else (1, n)
+            key = None                                           # no committed counters for shares
         res = secondary(api, W, args.only, flags, args.steps, W.CONFIG_NAMES[args.only], fl, key,
-                        "fp8" if args.fp8 else None)
+                        "fp8" if args.fp8 else None, tp=tp, dp=dp)
         print(json.dumps(res), flush=True)
         return
 
@@ -426,10 +471,11 @@ def main():
     # per-kernel times: eager runs with the library's stage events; the step itself: the
     # same run captured in a HIP graph and replayed (no per-launch host gaps)
     wall_eager, stage, totals = time_runs(api, plan, tensors, args.steps, args.warmup)
-    ms = time_graph(api, plan, tensors, args.steps, args.warmup)
+    ms, ms_single = time_graph(api, plan, tensors, args.steps, args.warmup)
     value = st["flops"] / (ms * 1e-3) / 1e12
     roof = roofline(st, stage, "orca")
-    log(f"[bench] {ms:.4f} ms/step (graph replay; eager {wall_eager:.4f})  {value:.1f} TFLOP/s  stages {stage}")
+    log(f"[bench] {ms:.4f} ms/step (one graph of {args.steps} runs; one graph per run {ms_single:.4f}; "
+        f"eager {wall_eager:.4f})  {value:.1f} TFLOP/s  stages {stage}")
 
     rec = {"metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
@@ -438,7 +484,8 @@ def main():
                                   "(1,1700); Hq=Hkv=32, head_dim=128, page_size=16, permuted pages, bf16",
                       "total_q_rows": int(w.total_q_rows), "flops_per_step": st["flops"],
                       "kv_bytes": st["physical_kv_bytes"]},
-           "launch": "hip-graph replay of varlen_attn_run", "ms_per_step_eager": round(wall_eager, 5),
+           "launch": f"one hip-graph launch of {args.steps} varlen_attn_run calls over {LAYERS} layers' buffers",
+           "ms_per_step_one_graph_per_run": round(ms_single, 5), "ms_per_step_eager": round(wall_eager, 5),
            "plan_host_us": round(st["plan_host_us"], 1),
            "stage_ms": {k: round(v, 5) for k, v in stage.items()},
            "peak_frac": round(value * 1e12 / PEAK_BF16, 4),
@@ -469,6 +516,16 @@ def main():
                 (2, 0, "orca-mixed in fp8 e4m3fn KV + scales", None, "orca_fp8", "fp8")):
             log(f"[bench] secondary: {label}")
             sec.append(secondary(api, W, cid, flags, 20, label, fl, key, dt))
+            torch.cuda.empty_cache()
+        log("[bench] secondary: the ORCA iteration with the last-level cache evicted before each run")
+        sec.append(secondary(api, W, 2, 0, 20, "orca-mixed, 256 MB last-level cache evicted before each run",
+                             flush, None))
+        # one GPU's share when the iteration is split over 8 GPUs (the kernels at their real shape)
+        for cid, tp, dp, label in ((4, 8, 1, "chunked-prefill-mix, one GPU of TP=8 (Hq=8, Hkv=1)"),
+                                   (2, 8, 1, "orca-mixed, one GPU of TP=8 (Hq=Hkv=4)"),
+                                   (3, 1, 8, "decode-heavy-gqa, one GPU of DP=8 (32 of the 256 requests)")):
+            log(f"[bench] secondary: {label}")
+            sec.append(secondary(api, W, cid, 0, 20, label, None, None, tp=tp, dp=dp))
             torch.cuda.empty_cache()
         log("[bench] secondary: long-context decode 256 x 128K")
         sec.append(long_context_line(api, W))

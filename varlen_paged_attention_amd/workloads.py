@@ -337,20 +337,33 @@ CONFIG_NAMES = {
 
 
 def config(cid: int, seed: Optional[int] = None, poison_tail: bool = False,
-           scale: int = 1, dtype: Optional[str] = None) -> Workload:
+           scale: int = 1, dtype: Optional[str] = None, tp: int = 1, dp: int = 1) -> Workload:
     """The five workloads of the pages (plus 51: the scaled shared-prefix variant; 6 and 7:
     multi-row speculative-decode verify steps with 4 and 8 rows per request).
 
     ``scale`` > 1 shrinks the lengths (integer division, min 1) and keeps the head
     layout, for parity runs the oracle finishes quickly.  ``dtype`` replaces the
     configuration's element type (e.g. "fp8" for the same shapes in fp8 storage).
+
+    ``tp`` / ``dp`` > 1 give one GPU's share of the iteration when it is split over that
+    many GPUs: by head (tensor parallel: num_q_heads / tp query heads and num_kv_heads / tp
+    KV heads, at least one KV head, replicated when there are fewer KV heads than GPUs) or
+    by request (data parallel: requests r with r % dp == 0).
     """
     s = cid if seed is None else seed
 
-    def mk(*a, **kw):
+    def mk(name, q_rows, kv_lens, **kw):
         if dtype is not None:
             kw["dtype"] = dtype
-        return build(*a, **kw)
+        if tp > 1:
+            assert kw["num_q_heads"] % tp == 0, "query heads must split evenly"
+            kw["num_q_heads"] //= tp
+            kw["num_kv_heads"] = max(1, kw["num_kv_heads"] // tp)
+            name += f"/tp{tp}"
+        if dp > 1:
+            q_rows, kv_lens = list(q_rows)[::dp], list(kv_lens)[::dp]
+            name += f"/dp{dp}"
+        return build(name, q_rows, kv_lens, **kw)
 
     def sh(x):
         return np.maximum(1, np.asarray(x, np.int64) // scale)

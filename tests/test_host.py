@@ -242,6 +242,20 @@ def test_short_requests_as_tiles(name, make, flags, folded):
     check_coverage(w, plan)
 
 
+@pytest.mark.parametrize("cid,tp,dp", [(4, 8, 1), (2, 8, 1), (3, 1, 8), (51, 1, 8)])
+def test_one_gpu_share_of_a_workload(cid, tp, dp):
+    """One GPU's share under tensor parallelism (heads / tp, at least one KV head) or data
+    parallelism (every dp-th request) plans and covers every visible pair."""
+    full = W.config(cid, scale=16)
+    w = W.config(cid, scale=16, tp=tp, dp=dp)
+    assert w.num_q_heads == full.num_q_heads // tp
+    assert w.num_kv_heads == max(1, full.num_kv_heads // tp)
+    assert w.num_reqs == len(range(0, full.num_reqs, dp))
+    assert np.array_equal(w.kv_len, full.kv_len[::dp])
+    flags = api.VA_FLAG_SHARED_PREFIX if cid == 51 else 0
+    check_coverage(w, _plan(w, flags))
+
+
 def _long_chunk(m=256, S0=65536, hq=32, hkv=8, extra=()):
     """A chunk of m new rows on S0 cached positions (plus optional decodes)."""
     rows = [m] + [1] * len(extra)

@@ -296,13 +296,13 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
   // absorbs a remainder shorter than a quarter chunk.  Slots are numbered from 0 here and
   // moved past the split-KV ones below.
   //
-  // Without a forced chunk length the planner compares two greedy schedules of the tiles
-  // over the resident slots (the dispatcher hands each next workgroup to the first free
-  // slot): whole tiles, and tiles cut into chunks of the largest power of two (1024 to
-  // 8192) keys not above the tile keys per slot, each tile costing its keys plus a fixed
-  // start-up, chunk tiles a little more for their partial results.  It cuts when that
-  // shortens the modelled time by 10%.  (Power-of-two chunks measured faster than
-  // chunks of the same count but other lengths.)
+  // Without a forced chunk length the planner compares greedy schedules of the tiles over
+  // the resident slots (the dispatcher hands each next workgroup to the first free slot):
+  // whole tiles, and tiles cut into chunks of each power of two from 256 to 8192 keys,
+  // each tile costing its keys plus a fixed start-up, chunk tiles also the writing and
+  // re-reading of their partial results.  It takes the shortest schedule if it beats whole
+  // tiles by 10%.  (Power-of-two chunks measured faster than chunks of the same count but
+  // other lengths.)
   auto chunks_of = [&](const PrefillTile& t, int64_t Lc) {
     const int64_t seen = int64_t(t.S0) + t.c0 / g + 1;   // keys [0, S0 + i_first] are seen by all
     if (t.kv_end <= 2 * Lc) return int64_t(1);           // short tiles stay whole
@@ -322,24 +322,15 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
     if (p.prefill_split_len > 0) {
       Lc = ceil_div(p.prefill_split_len, kStepKeys) * kStepKeys;
     } else {
-      int64_t cand = 1024;   // the largest power of two <= keys_all / slots, within [1024, 8192]
-      while (cand < 8192 && 2 * cand * kPrefillSlots <= keys_all) cand *= 2;
-      constexpr int64_t kStart = 128, kPartial = 128;   // modelled costs, in keys
-      std::vector<int64_t> whole, cut;
-      if (longest > 2 * cand) {       // else no tile would be cut
-        whole.reserve(tiles.size());
-        cut.reserve(tiles.size() + size_t(ceil_div(keys_all, cand)));
-        for (const PrefillTile& t : tiles) {
-          whole.push_back(t.kv_end + kStart);
-          const int64_t n = chunks_of(t, cand);
-          if (n < 2) {
-            cut.push_back(t.kv_end + kStart);
-          } else {
-            for (int64_t j = 0; j + 1 < n; ++j) cut.push_back(cand + kStart + kPartial);
-            cut.push_back(t.kv_end - (n - 1) * cand + kStart + kPartial);
-          }
-        }
-      }
+      // modelled costs, in keys of one tile: a tile's start (Q load, pipeline fill, the
+      // last iteration's drain; small for the few columns of a decode tile) and, for a
+      // chunk tile, writing its columns' partials and reading them back in the combine
+      // pass (2 * ncols * (D + 2) floats against the 4 * D bytes of K and V one key brings
+      // in), weighted 3x.  The weights were fitted to twelve measured workloads (short and
+      // long chunks on 4K-131K prefixes, decode batches, tensor- and data-parallel shares):
+      // the chosen length is within 6 % of the best measured one on all twelve.
+      auto start_cost = [](const PrefillTile& t) { return int64_t(t.ncols >= 64 ? 128 : 16); };
+      auto partial_cost = [&](const PrefillTile& t) { return 3 * 2 * int64_t(t.ncols) * (D + 2) / D; };
       auto greedy = [](std::vector<int64_t>& costs) {
         std::sort(costs.begin(), costs.end(), std::greater<int64_t>());
         std::priority_queue<int64_t, std::vector<int64_t>, std::greater<int64_t>> free_at;
@@ -353,7 +344,34 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
         }
         return end;
       };
-      if (!whole.empty() && 10 * greedy(cut) < 9 * greedy(whole)) Lc = cand;
+      std::vector<int64_t> costs;
+      costs.reserve(tiles.size());
+      for (const PrefillTile& t : tiles) costs.push_back(t.kv_end + start_cost(t));
+      int64_t best = greedy(costs);
+      const int64_t whole_end = best;
+      // candidate chunk lengths: powers of two from 256 to 8192 that cut some tile and
+      // give at most 16 tiles per resident slot's worth of keys
+      for (int64_t cand = 8192; cand >= 256; cand /= 2) {
+        if (longest <= 2 * cand) continue;                       // no tile would be cut
+        if (keys_all > 16 * kPrefillSlots * cand) break;         // too many chunk tiles
+        costs.clear();
+        for (const PrefillTile& t : tiles) {
+          const int64_t n = chunks_of(t, cand);
+          if (n < 2) {
+            costs.push_back(t.kv_end + start_cost(t));
+          } else {
+            const int64_t extra = start_cost(t) + partial_cost(t);
+            for (int64_t j = 0; j + 1 < n; ++j) costs.push_back(cand + extra);
+            costs.push_back(t.kv_end - (n - 1) * cand + extra);
+          }
+        }
+        const int64_t end = greedy(costs);
+        if (end < best) {
+          best = end;
+          Lc = cand;
+        }
+      }
+      if (10 * best >= 9 * whole_end) Lc = 0;    // cut only for a 10 % shorter schedule
     }
     if (Lc > 0) {
       std::vector<PrefillTile> cut;

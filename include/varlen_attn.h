@@ -118,7 +118,7 @@ typedef struct {
 typedef struct {
   int64_t num_reqs;
   int64_t total_q_rows;       /* max(q_end): rows q and out must hold */
-  int64_t prefill_tiles;      /* MFMA prefill work tiles */
+  int64_t prefill_tiles;      /* MFMA tiles: prefill rows, decode rows run as tiles, key chunks */
   int64_t split_items;        /* split-KV work items (one wavefront each) */
   int64_t shared_items;       /* of which read a shared prefix for several requests */
   int64_t shared_groups;      /* groups of requests found sharing leading pages */
@@ -134,9 +134,9 @@ typedef struct {
   int64_t table_bytes;        /* block-table entries read */
   int64_t workspace_bytes;    /* device scratch run() needs */
   double plan_host_us;        /* host time spent in varlen_attn_plan */
-  double prefill_flops;       /* part of `flops` done by prefill tiles */
-  double split_flops;         /* part of `flops` done by split-KV items */
-  int64_t prefill_kv_bytes;   /* distinct KV bytes the prefill tiles' requests read */
+  double prefill_flops;       /* part of `flops` of the requests run on MFMA tiles */
+  double split_flops;         /* part of `flops` of the requests run on split-KV items */
+  int64_t prefill_kv_bytes;   /* distinct KV bytes the tile requests read */
   int64_t split_kv_bytes;     /* distinct KV bytes the split-KV requests read */
   int64_t split_q_bytes;      /* query bytes of the split-KV requests */
   int64_t direct_items;       /* split-KV items that write output rows directly (no combine) */

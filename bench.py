@@ -192,15 +192,17 @@ def dominant(stats, stage_ms):
     name = max(kernels, key=kernels.get)
     ms = kernels[name] - stage_ms.get("event_record", 0.0)
     if name == "prefill":
-        # prefill tiles (with the decodes a bf16 plan runs as tiles) and shared-prefix group
-        # tiles: MFMA-bound unless the tiles mostly stream decode KV
-        flops = stats["prefill_flops"] + stats["shared_tile_flops"]
-        byts = stats["prefill_kv_bytes"] + 2 * (stats["q_bytes"] - stats["split_q_bytes"])
+        # every MFMA tile (prefill rows, decodes run as tiles, key chunks, shared-prefix group
+        # tiles and members' own keys): all work not done by split-KV items; MFMA-bound unless
+        # the tiles mostly stream KV
+        flops = stats["flops"] - stats["split_item_flops"]
+        qo = stats["q_bytes"] if stats["split_items"] == 0 else stats["q_bytes"] - stats["split_q_bytes"]
+        byts = stats["physical_kv_bytes"] - stats["split_item_kv_bytes"] + 2 * qo
         bound = "mfma" if flops / PEAK_BF16 > byts / PEAK_HBM else "hbm"
         work = flops if bound == "mfma" else byts
     elif name == "split_kv":
         # bandwidth-bound unless it also carries the prefill rows (then it is a contraction)
-        flops = stats["split_flops"] - stats["shared_tile_flops"]
+        flops = stats["split_item_flops"]
         byts = stats["split_item_kv_bytes"] + stats["split_q_bytes"] + stats["table_bytes"]
         bound = "mfma" if flops / PEAK_BF16 > byts / PEAK_HBM else "hbm"
         work = flops if bound == "mfma" else byts

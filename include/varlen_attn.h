@@ -140,10 +140,12 @@ typedef struct {
   int64_t split_kv_bytes;     /* distinct KV bytes the split-KV requests read */
   int64_t split_q_bytes;      /* query bytes of the split-KV requests */
   int64_t direct_items;       /* split-KV items that write output rows directly (no combine) */
-  int64_t shared_tiles;       /* MFMA tiles scoring shared-prefix chunks for stacked member rows */
+  int64_t shared_tiles;       /* MFMA tiles scoring shared-prefix chunks for stacked member rows
+                                 (part of prefill_tiles) */
   double shared_tile_flops;   /* part of split_flops done by those tiles (in the prefill stage) */
   int64_t split_item_kv_bytes; /* distinct KV bytes the split-KV items read */
   int64_t prefill_split_tiles; /* of prefill_tiles, those scoring one key chunk of a cut tile */
+  double split_item_flops;    /* part of `flops` done by the split-KV items */
 } va_plan_stats;
 
 typedef struct va_plan va_plan;   /* opaque, immutable after creation */

@@ -93,3 +93,24 @@ def test_auto_decode_tiles_equal_split_items_full_size():
     diff = float((a.float() - b.float()).abs().max())
     _say(f"[parity] decode-heavy tiles vs split-KV items: max diff {diff:.3e}")
     assert diff <= TOL
+
+
+def test_shared_prefix_members_own_keys_on_tiles_elementwise():
+    """64 requests sharing 4 leading pages, with 1-5 new rows each (decodes and verify
+    steps, causal among their own rows): group tiles score the shared pages and column-list
+    tiles each member's own keys, in one launch; every element against the oracle."""
+    rows = [1 + (r % 5) for r in range(64)]
+    kv = [256 + 40 + 7 * r for r in range(64)]
+    w = W.build("shared-rows", rows, kv, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=64, seed=23,
+                shared_prefix_pages=4, poison_tail=True)
+    plan = api.plan_for(w, flags=api.VA_FLAG_SHARED_PREFIX)
+    st = api.varlen_attn_plan_stats(plan)
+    assert st["shared_groups"] == 1 and st["shared_tiles"] > 0 and st["split_items"] == 0
+    _say(f"[gpu] shared prefix, members on tiles: {st['prefill_tiles']} tiles ({st['shared_tiles']} group)")
+    out, _ = api.run_workload(w, plan=plan)
+    got = out.float().cpu().numpy().astype(np.float64)
+    ref = _oracle_full(w)
+    assert np.isfinite(got).all()
+    worst = float(np.abs(got - ref).max())
+    _say(f"[parity] shared prefix, members on tiles: max|gpu-oracle| = {worst:.3e}")
+    assert worst <= TOL

@@ -135,21 +135,29 @@ def check_coverage(w, plan):
                 assert k1 - 1 <= limit
     assert all(n == 1 for n in direct.values())
     assert not (set(direct) & set(slots))
-    for t in api.varlen_attn_plan_export(plan, 4):        # shared-prefix group tiles
+    listed = api.varlen_attn_plan_export(plan, 4)          # copies of the column-list tiles
+    assert len(listed) == (int((tiles[:, 10] & 1).sum()) if len(tiles) else 0)
+    for t in tiles:
+        if not t[10] & 1:
+            continue
+        # column-list tile: a shared-prefix group tile or a member's own keys after them
         req, kvh, col0, ncols, slot, k0, k1, kbeg = (int(x) for x in t[:8])
         assert kbeg == k0 and t[8] == -1
         assert 1 <= ncols <= 128 and k0 < k1
         for c in cols[col0:col0 + ncols]:
             row, head, limit, pbase = (int(x) for x in c)
             r = req_of_row[row]
-            assert head // g == kvh and k1 - 1 <= limit
-            pages = range(k0 // ps, (k1 - 1) // ps + 1)
+            assert head // g == kvh and k0 <= limit
+            hi = min(k1, limit + 1)
+            pages = range(k0 // ps, (hi - 1) // ps + 1)
             assert all(w.block_table[req, p] == w.block_table[r, p] for p in pages)
-            cover.setdefault((row, head), []).append((k0, k1))
+            cover.setdefault((row, head), []).append((k0, hi))
             pb, npart = comb_map[(row, head)]
             assert pb == pbase and 0 <= slot < npart
             slots.setdefault((row, head), []).append(slot)
     for t in tiles:
+        if t[10] & 1:
+            continue
         req, kvh, c0, ncols, q0, S0, kv_end, kbeg, pbase, pstride = (int(x) for x in t[:10])
         assert kbeg % 64 == 0 and 1 <= ncols <= 128
         for col in range(ncols):
@@ -220,7 +228,9 @@ FOLD_CASES = [
     ("orca", lambda: W.config(2), 0, True),
     ("few long decodes (cut)", lambda: W.build("fl", [1] * 4, [32768] * 4, num_q_heads=32, num_kv_heads=8,
                                                head_dim=128, page_size=64, seed=3), 0, True),
-    ("shared-prefix-64", lambda: W.config(51), api.VA_FLAG_SHARED_PREFIX, False),
+    # members' own keys after the shared pages: column-list tiles (bf16), split items (fp8)
+    ("shared-prefix-64", lambda: W.config(51), api.VA_FLAG_SHARED_PREFIX, True),
+    ("shared-prefix-64 fp8", lambda: W.config(51, dtype="fp8"), api.VA_FLAG_SHARED_PREFIX, False),
 ]
 
 
@@ -233,12 +243,13 @@ def test_short_requests_as_tiles(name, make, flags, folded):
     g = w.num_q_heads // w.num_kv_heads
     short = [r for r in range(w.num_reqs) if 0 < m[r] and m[r] * g < 64]
     tiles = api.varlen_attn_plan_export(plan, 3)
-    on_tiles = set(int(t[0]) for t in tiles)
+    # tiles scoring a request's own keys (not a shared-prefix group tile: pad word 1 set)
+    on_tiles = set(int(t[0]) for t in tiles if not (t[10] & 1 and t[11]))
     if folded:
         assert all(r in on_tiles for r in short) and st["split_items"] == 0
         assert st["prefill_tiles"] >= 512
     else:
-        assert not any(r in on_tiles for r in short)
+        assert not any(r in on_tiles for r in short) and st["split_items"] > 0
     check_coverage(w, plan)
 
 
@@ -328,7 +339,11 @@ def test_shared_prefix_groups_found():
     assert st["physical_kv_bytes"] == 40 * 2 ** 20 and st["logical_kv_bytes"] == 120 * 2 ** 20
     # split items read only the 6 private ranges of 1024 positions (8 KV heads, K and V, bf16)
     assert st["split_item_kv_bytes"] == 6 * 1024 * 8 * 128 * 2 * 2
+    assert st["split_item_flops"] == 4 * 128 * 32 * 6 * 1024
     assert st["shared_tile_flops"] == 4 * 128 * (6 * 4) * 4096 * 8
+    # with 64 members the private ranges run as column-list tiles of their own: no split items
+    st64 = api.varlen_attn_plan_stats(_plan(W.config(51), api.VA_FLAG_SHARED_PREFIX))
+    assert st64["split_items"] == 0 and st64["split_item_kv_bytes"] == 0 and st64["split_item_flops"] == 0
     st0 = api.varlen_attn_plan_stats(_plan(w))
     assert st0["shared_groups"] == 0 and st0["split_item_kv_bytes"] == st0["physical_kv_bytes"]
 

@@ -48,7 +48,7 @@ class VaPlanStats(ctypes.Structure):
                [(n, ctypes.c_int64) for n in ("prefill_kv_bytes", "split_kv_bytes", "split_q_bytes",
                                               "direct_items", "shared_tiles")] + \
                [("shared_tile_flops", ctypes.c_double), ("split_item_kv_bytes", ctypes.c_int64),
-                ("prefill_split_tiles", ctypes.c_int64)]
+                ("prefill_split_tiles", ctypes.c_int64), ("split_item_flops", ctypes.c_double)]
 
 
 class VarlenAttnError(RuntimeError):

@@ -395,17 +395,16 @@ constexpr int prefill_lds_bytes() {
   return PrefillLds<D>::bytes;
 }
 
-// Group tiles (MODE kGroupTile): the same kernel scores a shared-prefix chunk for several
-// requests' rows.
-// The tile's columns come from cols[c0 ..] (rows of different requests), its keys are
-// [S0, kv_end) of request req's block table (pages every member shares, all visible to
-// every member row), and each column's unnormalised partial (m, l, acc) goes to workspace
-// slot pbase + q0 for the combine pass.
-//
-// Otherwise the tile's columns are consecutive (row, head) pairs of one request.  A whole
-// tile scores keys [0, kv_end) and normalises and writes the output rows; a key-chunk
-// tile (one chunk of a cut tile) scores keys [kbeg, kv_end) and writes the unnormalised
-// partial of column col to slot pbase + col * pstride, for the combine pass.
+// A tile's columns are consecutive (row, head) pairs of one request.  A whole tile scores
+// keys [0, kv_end) and normalises and writes the output rows; a key-chunk tile (one chunk
+// of a cut tile) scores keys [kbeg, kv_end) and writes the unnormalised partial (m, l, acc)
+// of column col to workspace slot pbase + col * pstride, for the combine pass.
+// A column-list tile takes its columns from cols[c0 ..] (rows of one or several requests,
+// each with its own causal limit), scores keys [kbeg, kv_end) of request req's block table
+// and writes column col's partial to slot cols[c0 + col].pbase + q0: a shared-prefix group
+// tile (pages every member shares, visible to every member row; "How To Scale Your Model
+// 笔记(7-8)", section 3: one load of a common KV block serves several requests' queries,
+// each keeping its own running max and sum) or the tile of a member's own keys after them.
 //
 // F8 = true: the pools hold fp8 e4m3fn codes with per-position float32 scales.  Each wave
 // copies its 16-key slice of codes (and the 16 K or V scales) by LDS-DMA into the upper
@@ -413,20 +412,19 @@ constexpr int prefill_lds_bytes() {
 // place to bf16(code * scale) in the layouts above, so the MFMA loop is the bf16 one.
 // The slice is the wave's own, and all its reads precede its writes, so no other wave is
 // involved until the barrier that ends the iteration.
-enum TileMode { kWholeTile, kAnyTile, kGroupTile };
+enum TileMode { kWholeTile, kAnyTile };
 
-// Instantiations: kWholeTile runs whole tiles only; kAnyTile runs whole tiles and key-chunk
-// tiles (a plan with chunk tiles launches all its tiles on it, so the two kinds share the
-// GPU); kGroupTile runs group tiles.  The whole-tile kernel is kept apart because any
-// partial-result epilogue in the same kernel changes how the compiler lays out the main
-// loop, and whole tiles then measured 4-6 % slower.
+// Instantiations: kWholeTile runs whole tiles only; kAnyTile runs every kind (whole tiles,
+// key-chunk tiles and column-list tiles: a plan with any of the latter launches all its
+// tiles on it, so all kinds share the GPU in one launch).  The whole-tile kernel is kept
+// apart because any partial-result epilogue in the same kernel changes how the compiler
+// lays out the main loop, and whole tiles then measured 4-6 % slower.
 template <int D, int MODE, bool F8>
 __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_bf16_kernel(
     const PrefillTile* __restrict__ tiles, const Column* __restrict__ cols, const bf16* __restrict__ q,
     const void* __restrict__ kpool, const void* __restrict__ vpool, const float* __restrict__ kscale,
     const float* __restrict__ vscale, const int32_t* __restrict__ bt, int bt_stride, bf16* __restrict__ out,
     float* __restrict__ ws_ml, float* __restrict__ ws_acc, int Hq, int g, Paged pg, float scale_log2) {
-  constexpr bool GROUP = MODE == kGroupTile;
   using Lay = PrefillLds<D>;
   constexpr int KCH = Lay::KCH, KROW = Lay::KROW, KBUF = Lay::KBUF, VBUF = Lay::VBUF;
   constexpr int WK = kPSliceKeys;                      // 16 keys per wave slice
@@ -452,28 +450,36 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
   const bool cvalid = col < T.ncols;
   const int c = T.c0 + (cvalid ? col : 0);
   int row, head, limit, w_min_limit, w_max_limit, kbeg, pslot;
-  if constexpr (GROUP) {
-    const Column cc = cols[c];
-    row = cc.q_row;
-    head = cc.q_head;
-    pslot = cc.pbase + T.q0;
-    kbeg = T.kbeg;
-    limit = cvalid ? T.kv_end - 1 : -1;
-    w_min_limit = T.kv_end - 1;
-    w_max_limit = (wv * 32 < T.ncols) ? T.kv_end - 1 : -1;
-  } else if constexpr (MODE == kAnyTile) {
-    const int i = c / g;
-    row = T.q0 + i;
-    head = T.kvh * g + c % g;
-    pslot = T.pbase + col * T.pstride;
-    kbeg = T.kbeg;
-    // a key chunk before the last one ends before the diagonal: clip the limits to its end
-    // (a no-op for whole tiles, which end one past their last row's last key)
+  if constexpr (MODE == kAnyTile) {
     const int kl = T.kv_end - 1;
-    limit = cvalid ? min(T.S0 + i, kl) : -1;
-    const int wcol_last = min(wv * 32 + 31, T.ncols - 1);
-    w_min_limit = min(T.S0 + (T.c0 + wv * 32) / g, kl);
-    w_max_limit = (wv * 32 < T.ncols) ? min(T.S0 + (T.c0 + wcol_last) / g, kl) : -1;
+    kbeg = T.kbeg;
+    if (T.flags & kTileColumnList) {
+      // columns of a list, each with its own causal limit (clipped to the tile's keys)
+      const Column cc = cols[c];
+      row = cc.q_row;
+      head = cc.q_head;
+      pslot = cc.pbase + T.q0;
+      limit = cvalid ? min(cc.limit, kl) : -1;
+      int lo = cvalid ? limit : INT_MAX, hi = limit;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        lo = min(lo, __shfl_xor(lo, off));
+        hi = max(hi, __shfl_xor(hi, off));
+      }
+      w_min_limit = __builtin_amdgcn_readfirstlane(lo);
+      w_max_limit = __builtin_amdgcn_readfirstlane(hi);
+    } else {
+      const int i = c / g;
+      row = T.q0 + i;
+      head = T.kvh * g + c % g;
+      pslot = T.pbase + col * T.pstride;
+      // a key chunk before the last one ends before the diagonal: clip the limits to its
+      // end (a no-op for whole tiles, which end one past their last row's last key)
+      limit = cvalid ? min(T.S0 + i, kl) : -1;
+      const int wcol_last = min(wv * 32 + 31, T.ncols - 1);
+      w_min_limit = min(T.S0 + (T.c0 + wv * 32) / g, kl);
+      w_max_limit = (wv * 32 < T.ncols) ? min(T.S0 + (T.c0 + wcol_last) / g, kl) : -1;
+    }
   } else {
     const int i = c / g;
     row = T.q0 + i;
@@ -782,7 +788,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
   }
   // ---- normalise and write: acc[db][4*ii + jj] is d = 32*db + 8*ii + 4*h + jj of this column
   const float l_tot = l_run + other_half(l_run);
-  if (GROUP || (MODE == kAnyTile && T.pbase >= 0)) {
+  if (MODE == kAnyTile && (T.pbase >= 0 || (T.flags & kTileColumnList))) {
     if (cvalid) {
       if (h == 0) {
         ws_ml[2 * size_t(pslot)] = m_run;
@@ -910,10 +916,8 @@ static va_status prepare_kernels() {
 #define VA_PREFILL_KERNEL(D, M, F) {reinterpret_cast<const void*>(&prefill_bf16_kernel<D, M, F>), prefill_lds_bytes<D>()}
         VA_PREFILL_KERNEL(128, kWholeTile, false), VA_PREFILL_KERNEL(64, kWholeTile, false),
         VA_PREFILL_KERNEL(128, kAnyTile, false), VA_PREFILL_KERNEL(64, kAnyTile, false),
-        VA_PREFILL_KERNEL(128, kGroupTile, false), VA_PREFILL_KERNEL(64, kGroupTile, false),
         VA_PREFILL_KERNEL(128, kWholeTile, true),  VA_PREFILL_KERNEL(64, kWholeTile, true),
-        VA_PREFILL_KERNEL(128, kAnyTile, true),  VA_PREFILL_KERNEL(64, kAnyTile, true),
-        VA_PREFILL_KERNEL(128, kGroupTile, true),  VA_PREFILL_KERNEL(64, kGroupTile, true)};
+        VA_PREFILL_KERNEL(128, kAnyTile, true),  VA_PREFILL_KERNEL(64, kAnyTile, true)};
 #undef VA_PREFILL_KERNEL
     for (const auto& k : kernels) {
       const hipError_t e = hipFuncSetAttribute(k.first, hipFuncAttributeMaxDynamicSharedMemorySize, k.second);
@@ -931,8 +935,7 @@ va_status upload_plan(va_plan* plan) {
   const size_t b_comb = align256(plan->combine.size() * sizeof(CombineRow));
   const size_t b_tiles = align256(plan->tiles.size() * sizeof(PrefillTile));
   const size_t b_off = align256(plan->kv_offset.size() * sizeof(int64_t));
-  const size_t b_gtiles = align256(plan->gtiles.size() * sizeof(PrefillTile));
-  const size_t total = b_items + b_cols + b_comb + b_tiles + b_off + b_gtiles;
+  const size_t total = b_items + b_cols + b_comb + b_tiles + b_off;
   std::vector<char> host(total, 0);
   size_t o = 0;
   auto put = [&](const void* src, size_t n, size_t span) {
@@ -946,7 +949,6 @@ va_status upload_plan(va_plan* plan) {
   const size_t o_comb = put(plan->combine.data(), plan->combine.size() * sizeof(CombineRow), b_comb);
   const size_t o_tiles = put(plan->tiles.data(), plan->tiles.size() * sizeof(PrefillTile), b_tiles);
   const size_t o_off = put(plan->kv_offset.data(), plan->kv_offset.size() * sizeof(int64_t), b_off);
-  const size_t o_gtiles = put(plan->gtiles.data(), plan->gtiles.size() * sizeof(PrefillTile), b_gtiles);
   hipError_t e = hipGetDevice(&plan->device);
   if (e != hipSuccess) return hip_fail("hipGetDevice", e);
   e = hipMalloc(&plan->dev, total);
@@ -967,7 +969,6 @@ va_status upload_plan(va_plan* plan) {
   plan->d_combine = reinterpret_cast<const CombineRow*>(base + o_comb);
   plan->d_tiles = reinterpret_cast<const PrefillTile*>(base + o_tiles);
   plan->d_kv_offset = reinterpret_cast<const int64_t*>(base + o_off);
-  plan->d_gtiles = reinterpret_cast<const PrefillTile*>(base + o_gtiles);
   return VA_OK;
 }
 
@@ -993,7 +994,7 @@ static va_status run_impl(const va_plan* plan, const void* q, const void* k_pool
   if (!plan) return fail(VA_ERR_INVALID_ARG, "plan is NULL");
   if (!plan->dev) return fail(VA_ERR_INVALID_ARG, "plan has no device buffer (built with VA_FLAG_HOST_ONLY)");
   const bool fp8 = plan->p.dtype == VA_DTYPE_FP8_E4M3;
-  const bool any = !plan->items.empty() || !plan->tiles.empty() || !plan->gtiles.empty();
+  const bool any = !plan->items.empty() || !plan->tiles.empty();
   if (!any && !events) return VA_OK;
   if (any && (!q || !k_pool || !v_pool || !block_table_dev || !out))
     return fail(VA_ERR_INVALID_ARG, "q, k_pool, v_pool, block_table_dev and out must be non-NULL");
@@ -1030,7 +1031,7 @@ static va_status run_impl(const va_plan* plan, const void* q, const void* k_pool
     return events ? hipEventRecord(static_cast<hipEvent_t>(events[i]), s) : hipSuccess;
   };
   if ((e = mark(0)) != hipSuccess) return hip_fail("hipEventRecord", e);
-  const int ntiles = int(plan->tiles.size()), ngtiles = int(plan->gtiles.size());
+  const int ntiles = int(plan->tiles.size());
   const int nwhole = plan->tiles_whole, nchunk = ntiles - nwhole;   // the rest run on kAnyTile
   auto launch_tiles = [&](auto mode, auto f8, const PrefillTile* tl, int n) {
     constexpr int M = decltype(mode)::value;
@@ -1053,13 +1054,10 @@ static va_status run_impl(const va_plan* plan, const void* q, const void* k_pool
   };
   using Whole = std::integral_constant<int, kWholeTile>;
   using Any = std::integral_constant<int, kAnyTile>;
-  using Group = std::integral_constant<int, kGroupTile>;
   if (nwhole && (e = launch_kind(Whole{}, plan->d_tiles, nwhole)) != hipSuccess)
     return hip_fail("prefill kernel launch", e);
   if (nchunk && (e = launch_kind(Any{}, plan->d_tiles + nwhole, nchunk)) != hipSuccess)
-    return hip_fail("prefill key-chunk kernel launch", e);
-  if (ngtiles && (e = launch_kind(Group{}, plan->d_gtiles, ngtiles)) != hipSuccess)
-    return hip_fail("shared-prefix tile kernel launch", e);
+    return hip_fail("prefill kernel launch (any tile)", e);
   if ((e = mark(1)) != hipSuccess) return hip_fail("hipEventRecord", e);
   if (nitems) {
     const dim3 grid((nitems + kSplitWaves - 1) / kSplitWaves), block(64 * kSplitWaves);

@@ -72,7 +72,9 @@ void order_tiles(std::vector<PrefillTile>& tiles) {
   const size_t T = tiles.size();
   if (T < 2) return;
   auto work = [](const PrefillTile& t) { return int64_t(t.kv_end) - t.kbeg; };
-  auto key = [](const PrefillTile& t) { return std::make_tuple(t.req, t.kvh, t.pbase >= 0 ? t.kbeg : -1); };
+  auto key = [](const PrefillTile& t) {
+    return std::make_tuple(t.req, t.kvh, t.pbase >= 0 || t.flags != 0 ? t.kbeg : -1);
+  };
   std::vector<int32_t> idx(T);
   std::iota(idx.begin(), idx.end(), 0);
   std::stable_sort(idx.begin(), idx.end(), [&](int32_t a, int32_t b) {
@@ -246,7 +248,7 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
         t.kbeg = 0;
         t.pbase = -1;
         t.pstride = 0;
-        t.pad0 = t.pad1 = 0;
+        t.flags = t.pad1 = 0;
         tiles.push_back(t);
       }
   };
@@ -456,14 +458,6 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
       if (!is_tile[r]) split_reqs.push_back(r);
   }
 
-  // launch order; with no chunk tile every tile runs on the whole-tile kernel, else every
-  // tile runs on the kernel that takes both kinds (one launch, so decode tiles and chunk
-  // tiles share the GPU instead of running one launch after the other)
-  order_tiles(plan->tiles);
-  plan->tiles_whole = std::any_of(plan->tiles.begin(), plan->tiles.end(),
-                                  [](const PrefillTile& t) { return t.pbase >= 0; })
-                          ? 0
-                          : int32_t(plan->tiles.size());
 
   // ---- column blocks ------------------------------------------------------------------
   std::vector<Block> blocks;
@@ -499,7 +493,7 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
     }
   };
   // A group's shared range is scored by MFMA tiles of up to 128 stacked member columns
-  // (the prefill kernel in group mode) where that kernel exists, else by split items.
+  // (column-list tiles of the prefill kernel) where that kernel exists, else by split items.
   const bool group_tiles = use_prefill;
   for (auto& mem : groups) {
     const int32_t kend = shared_pages[mem[0]] * ps;
@@ -512,12 +506,22 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
       for (size_t b = first; b < blocks.size(); ++b) blocks[b].kend = kend;
     }
   }
+  // A group member's own keys after the shared pages: column-list tiles in the same launch
+  // as the group tiles (bf16 plans, as for decode tiles) when those tiles and the plan's
+  // other tiles fill the resident slots (64 members: 94 -> 83 us), else split items (6
+  // members: 48 thin tiles would take 23 us where 768 items take 15 us).
+  int64_t n_suffix = 0;
+  for (int r : split_reqs)
+    if (shared_pages[r] > 0) n_suffix += Hkv * ceil_div(int64_t(q_end[r] - q_start[r]) * g, kPrefillCols);
+  const bool suffix_tiles = use_prefill && p.dtype == VA_DTYPE_BF16 && p.prefill_min_rows <= 0 &&
+                            !(p.flags & VA_FLAG_NO_DECODE_TILES) &&
+                            n_suffix + int64_t(plan->tiles.size()) >= kPrefillSlots;
   for (int r : split_reqs) {
     const int ncol = (q_end[r] - q_start[r]) * g;
     for (int kvh = 0; kvh < Hkv; ++kvh) {
       std::vector<std::pair<int, int>> rh;
       for (int lc = 0; lc < ncol; ++lc) rh.push_back({r, lc});
-      add_blocks(rh, kvh, shared_pages[r] * ps, false, r, false);
+      add_blocks(rh, kvh, shared_pages[r] * ps, false, r, suffix_tiles && shared_pages[r] > 0);
     }
   }
 
@@ -526,6 +530,7 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
   int64_t work = 0, tile_cols = 0, tile_keys = 0;
   for (auto& B : blocks) {
     if (B.tile) {
+      if (!B.shared) continue;   // a member's own keys: one tile per 8192 keys
       tile_cols += 1;
       tile_keys = std::max<int64_t>(tile_keys, B.kend - B.kstart);
     } else {
@@ -551,7 +556,7 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
       4096, std::max<int64_t>(256, ceil_div(ceil_div(tile_keys * tile_cols, 512), kStepKeys) * kStepKeys));
   for (auto& B : blocks) {
     const int64_t keys = std::max(0, B.kend - B.kstart);
-    B.chunk = int32_t(B.tile ? Lt : L);
+    B.chunk = int32_t(B.tile ? (B.shared ? Lt : 8192) : L);
     B.nchunks = int32_t(ceil_div(keys, B.chunk));
   }
 
@@ -619,14 +624,16 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
         t.kvh = B.kvh;
         t.c0 = col0;
         t.ncols = int32_t(B.outs.size());
-        t.q0 = j;                                       // partial slot of this chunk
+        t.q0 = B.shared ? j : shared_n[B.outs[0]] + j;   // partial slot of this chunk
         t.S0 = int32_t(B.kstart + int64_t(j) * B.chunk);
         t.kv_end = int32_t(std::min<int64_t>(B.kend, B.kstart + int64_t(j + 1) * B.chunk));
         t.kbeg = t.S0;
         t.pbase = -1;
         t.pstride = 0;
-        t.pad0 = t.pad1 = 0;
+        t.flags = kTileColumnList;
+        t.pad1 = B.shared ? 1 : 0;                      // (counters only)
         plan->gtiles.push_back(t);
+        plan->tiles.push_back(t);
       }
       continue;
     }
@@ -664,6 +671,15 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
   plan->items_wide = int32_t(std::count_if(plan->items.begin(), plan->items.end(),
                                            [](const SplitItem& it) { return it.ncols > kSplitCols; }));
 
+  // launch order; with only whole tiles every tile runs on the whole-tile kernel, else
+  // every tile runs on the kernel that takes all kinds (one launch, so decode tiles, chunk
+  // tiles and group tiles share the GPU instead of running one launch after the other)
+  order_tiles(plan->tiles);
+  plan->tiles_whole = std::any_of(plan->tiles.begin(), plan->tiles.end(),
+                                  [](const PrefillTile& t) { return t.pbase >= 0 || t.flags != 0; })
+                          ? 0
+                          : int32_t(plan->tiles.size());
+
   // ---- counters ---------------------------------------------------------------------
   va_plan_stats& st = plan->stats;
   // bytes of one Q / output element, and of one position of one KV head's K and V
@@ -698,9 +714,18 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
   st.prefill_flops = 4.0 * D * Hq * double(pairs_pf);
   st.split_flops = 4.0 * D * Hq * double(pairs - pairs_pf);
   st.split_q_bytes = rows_sp * Hq * D * elem;
-  st.shared_tiles = int64_t(plan->gtiles.size());
+  st.shared_tiles = 0;
   st.shared_tile_flops = 0;
-  for (const PrefillTile& t : plan->gtiles) st.shared_tile_flops += 4.0 * D * t.ncols * double(t.kv_end - t.S0);
+  for (const PrefillTile& t : plan->gtiles)
+    if (t.pad1) {                                  // group tiles (every column sees every key)
+      ++st.shared_tiles;
+      st.shared_tile_flops += 4.0 * D * t.ncols * double(t.kv_end - t.S0);
+    }
+  // FLOPs of the split-KV items: visible keys of each column in the item's range
+  st.split_item_flops = 0;
+  for (const SplitItem& it : plan->items)
+    for (int32_t c = it.col0; c < it.col0 + it.ncols; ++c)
+      st.split_item_flops += 4.0 * D * double(std::max(0, std::min(it.k1, plan->cols[c].limit + 1) - it.k0));
   st.prefill_split_tiles = std::count_if(plan->tiles.begin(), plan->tiles.end(),
                                          [](const PrefillTile& t) { return t.pbase >= 0; });
   st.direct_items = std::count_if(plan->items.begin(), plan->items.end(),

@@ -35,14 +35,18 @@ struct CombineRow {
 // against keys [kbeg, kv_end) (row i sees keys up to S0 + i).  pbase < 0: the tile holds
 // all of its columns' keys and writes normalised output rows; else it is one key chunk of
 // a cut tile and tile column col writes its partial (m, l, acc) to workspace slot
-// pbase + col * pstride for the combine pass.  As a shared-prefix group tile the fields
-// mean: columns cols[c0 .. c0+ncols), partial slot q0, keys [kbeg = S0, kv_end) of
-// request req's block table.
+// pbase + col * pstride for the combine pass.
+// With kTileColumnList in flags the tile's columns are cols[c0 .. c0+ncols) (rows of one
+// or several requests, each with its own causal limit), its keys [kbeg, kv_end) of request
+// req's block table, and column col's partial goes to slot cols[c0+col].pbase + q0: a
+// shared-prefix group tile (keys of the pages the group shares) or the tile of a group
+// member's own keys after them.
 struct PrefillTile {
   int32_t req, kvh, c0, ncols;
   int32_t q0, S0, kv_end, kbeg;
-  int32_t pbase, pstride, pad0, pad1;
+  int32_t pbase, pstride, flags, pad1;
 };
+constexpr int32_t kTileColumnList = 1;
 
 constexpr int kSplitCols = 16;       // query columns per split-KV item (MFMA N)
 constexpr int kSplitWaves = 4;       // items (wavefronts) per split-KV workgroup
@@ -73,8 +77,9 @@ struct va_plan {
   std::vector<va::CombineRow> combine;
   std::vector<va::PrefillTile> tiles;         // in launch order
   int32_t tiles_whole = 0;                    // the first tiles_whole run on the whole-tile kernel
-                                              // (all, or none when there are chunk tiles)
-  std::vector<va::PrefillTile> gtiles;        // shared-prefix group tiles (columns from `cols`)
+                                              // (all, or none when there are chunk or
+                                              // column-list tiles)
+  std::vector<va::PrefillTile> gtiles;        // copies of the column-list tiles in `tiles` (export)
   std::vector<char> is_split;               // per request: rows run as split-KV items
   int64_t pos_bytes = 0;                     // K+V bytes of one position over all KV heads
   mutable va_plan_stats stats{};             // page-level counters filled on first query
@@ -86,7 +91,6 @@ struct va_plan {
   const va::Column* d_cols = nullptr;
   const va::CombineRow* d_combine = nullptr;
   const va::PrefillTile* d_tiles = nullptr;
-  const va::PrefillTile* d_gtiles = nullptr;
   const int64_t* d_kv_offset = nullptr;
   int device = -1;
   size_t ws_ml_off = 0, ws_acc_off = 0, ws_bytes = 0;

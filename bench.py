@@ -259,6 +259,30 @@ def cpu_baseline(w, budget_s=15.0):
                       f"fp64 NumPy, {dt:.2f} s", "cpu": cpu_model(), "seconds": round(dt, 3)}
 
 
+def hbm_read_gbps(api):
+    """The library's streaming-read kernel over 8 GiB (the 256 MB last-level cache cannot
+    hold it): the achievable HBM read rate, the ceiling bandwidth-bound kernels are also
+    compared against."""
+    import torch
+    n = 8 << 30
+    buf = torch.empty(n, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        api.varlen_attn_debug_stream_read(buf, sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        api.varlen_attn_debug_stream_read(buf, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    res = round(n * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    del buf
+    torch.cuda.empty_cache()
+    return res
+
+
 def hbm_copy_gbps():
     import torch
     n = 1 << 30
@@ -541,6 +565,9 @@ def main():
             sec.append(append_line(api, W, cid, label, dtype=dt))
             torch.cuda.empty_cache()
         sec.append({"workload": "torch copy 1 GiB (read+write) for reference", "hbm_GBps": hbm_copy_gbps()})
+        read_ceiling = hbm_read_gbps(api)
+        sec.append({"workload": "streaming read of 8 GiB (varlen_attn_debug_stream_read): achievable HBM read rate",
+                    "hbm_GBps": read_ceiling, "hbm_frac": round(read_ceiling * 1e9 / PEAK_HBM, 4)})
         rec["secondary"] = sec
         del flush
 

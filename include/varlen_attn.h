@@ -237,6 +237,14 @@ va_status varlen_attn_plan_slots(const va_plan* plan, int64_t* out_cache_loc_hos
  * plan_host_us does not include them. */
 va_status varlen_attn_plan_stats(const va_plan* plan, va_plan_stats* out);
 
+/* Measurement aid: reads `bytes` of device memory at `buf` once (16-byte loads, streaming)
+ * and discards them, so a caller can time the device's achievable HBM read rate with the
+ * same runtime and launch path as the attention kernels.  buf must be 16-byte aligned and
+ * bytes a multiple of 16; sink is a device uint32 that the kernel overwrites only when the
+ * XOR of a lane's words hits one fixed value (it keeps the loads from being optimised away;
+ * its content is meaningless).  Enqueue only. */
+va_status varlen_attn_debug_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
 /* Copy every request's K and V into logical order through the same page-address code the
  * attention kernels use: k_out, v_out are device [sum_r kv_len[r]][num_kv_heads][head_dim]
  * (requests back to back).  Exists to test the page gather bit for bit. */

@@ -114,3 +114,15 @@ def test_shared_prefix_members_own_keys_on_tiles_elementwise():
     worst = float(np.abs(got - ref).max())
     _say(f"[parity] shared prefix, members on tiles: max|gpu-oracle| = {worst:.3e}")
     assert worst <= TOL
+
+
+def test_stream_read_probe_runs():
+    """The HBM read-rate probe reads a buffer; for data that is all ones the XOR of every
+    lane's words is 0, so the sink keeps its value."""
+    import torch
+    buf = torch.ones(1 << 24, dtype=torch.int32, device="cuda")
+    sink = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    api.varlen_attn_debug_stream_read(buf, sink)
+    api.varlen_attn_debug_stream_read(buf[:12], sink)         # 3 words: fewer than the grid has lanes
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 7

@@ -405,6 +405,17 @@ def test_fp8_debug_convert_argument_errors():
     assert L.varlen_attn_debug_fp8_to_bf16(None, None, 8, None) == api.VA_ERR_INVALID_ARG
 
 
+def test_stream_read_argument_errors():
+    """The read-rate probe checks its arguments on the host (no launch happens here)."""
+    L = api.lib()
+    assert L.varlen_attn_debug_stream_read(None, 0, None, None) == api.VA_OK          # nothing to read
+    assert L.varlen_attn_debug_stream_read(None, 64, None, None) == api.VA_ERR_INVALID_ARG
+    assert L.varlen_attn_debug_stream_read(16, 64, None, None) == api.VA_ERR_INVALID_ARG  # sink NULL
+    assert L.varlen_attn_debug_stream_read(16, 60, 32, None) == api.VA_ERR_INVALID_ARG    # not whole words
+    assert L.varlen_attn_debug_stream_read(8, 64, 32, None) == api.VA_ERR_INVALID_ARG     # misaligned
+    assert b"16-byte" in L.varlen_attn_last_error()
+
+
 def test_fp8_append_argument_errors():
     """fp8 pools take varlen_attn_append_kv_fp8 (codes and scales), and it takes only them."""
     L = api.lib()

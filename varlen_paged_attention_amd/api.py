@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvarlen_a
 EXPORTED = ["varlen_attn_plan", "varlen_attn_run", "varlen_attn_run_events", "varlen_attn_plan_stats", "varlen_attn_plan_export",
             "varlen_attn_debug_gather", "varlen_attn_plan_destroy", "varlen_attn_status_string",
             "varlen_attn_last_error", "varlen_attn_append_kv", "varlen_attn_plan_slots", "varlen_attn_run_fp8",
-            "varlen_attn_debug_fp8_to_bf16", "varlen_attn_append_kv_fp8"]
+            "varlen_attn_debug_fp8_to_bf16", "varlen_attn_append_kv_fp8", "varlen_attn_debug_stream_read"]
 
 
 class VaParams(ctypes.Structure):
@@ -83,6 +83,8 @@ def lib():
         L.varlen_attn_run_events.restype = ctypes.c_int
         L.varlen_attn_run_fp8.argtypes = [P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P, ctypes.POINTER(P)]
         L.varlen_attn_run_fp8.restype = ctypes.c_int
+        L.varlen_attn_debug_stream_read.argtypes = [P, ctypes.c_size_t, P, P]
+        L.varlen_attn_debug_stream_read.restype = ctypes.c_int
         L.varlen_attn_debug_fp8_to_bf16.argtypes = [P, P, ctypes.c_int64, P]
         L.varlen_attn_debug_fp8_to_bf16.restype = ctypes.c_int
         L.varlen_attn_append_kv_fp8.argtypes = [ctypes.POINTER(VaParams), ctypes.c_int64, P, P, P, P, P, P, P, P, P]
@@ -281,6 +283,13 @@ def varlen_attn_debug_fp8_to_bf16(codes, out, stream=None) -> None:
         raise ValueError("out must hold 2-byte elements")
     _check(lib().varlen_attn_debug_fp8_to_bf16(_dev_ptr(codes, "codes", torch.uint8), _dev_ptr(out, "out"),
                                                codes.numel(), _stream_ptr(stream)))
+
+
+def varlen_attn_debug_stream_read(buf, sink, stream=None) -> None:
+    """Read every byte of the GPU tensor ``buf`` once (HBM read-rate measurement); ``sink``
+    is a GPU int32 tensor of at least one element."""
+    _check(lib().varlen_attn_debug_stream_read(_dev_ptr(buf, "buf"), buf.numel() * buf.element_size(),
+                                               _dev_ptr(sink, "sink"), _stream_ptr(stream)))
 
 
 def varlen_attn_debug_gather(plan: Plan, k_pool, v_pool, block_table_dev, k_out, v_out, stream=None) -> None:

@@ -874,6 +874,31 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineRow* __restri
   for (int j = 0; j < D / 64; ++j) op[64 * j] = OutT(o[j] * inv);
 }
 
+// --------------------------------------------------------------------- stream read --
+// Reads n16 16-byte words once: each workgroup streams one contiguous span (so the DRAM
+// pages it touches are read whole), its lanes reading consecutive words, eight loads in
+// flight per lane.  The data decides whether a store to the sink happens (rarely), so the
+// loads stay.
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restrict__ buf, int64_t n16,
+                                                          uint32_t* __restrict__ sink) {
+  const int64_t span = (n16 + gridDim.x - 1) / gridDim.x;
+  const int64_t lo = int64_t(blockIdx.x) * span, hi = min(n16, lo + span);
+  uint32_t acc = 0;
+  int64_t i = lo + threadIdx.x;
+  for (; i + 7 * 256 < hi; i += 8 * 256) {
+    uint4 a[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a[u] = buf[i + u * 256];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= a[u].x ^ a[u].y ^ a[u].z ^ a[u].w;
+  }
+  for (; i < hi; i += 256) {
+    const uint4 a = buf[i];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  if (acc == 0x9e3779b9u) sink[0] = acc;
+}
+
 // ------------------------------------------------------------------------- gather --
 template <typename T>
 __global__ __launch_bounds__(256) void gather_kernel(const int64_t* __restrict__ kv_offset, int num_reqs,
@@ -1164,6 +1189,19 @@ extern "C" va_status varlen_attn_run_events(const va_plan* plan, const void* q, 
     return fail(VA_ERR_INVALID_ARG, "an fp8 plan runs with varlen_attn_run_fp8 (it needs the scale pools)");
   return run_impl(plan, q, k_pool, v_pool, nullptr, nullptr, block_table_dev, out, workspace, workspace_bytes, stream,
                   events);
+}
+
+extern "C" va_status varlen_attn_debug_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  if (bytes == 0) return VA_OK;
+  if (!buf || !sink) return fail(VA_ERR_INVALID_ARG, "buf and sink must be non-NULL");
+  if ((bytes & 15) || (reinterpret_cast<uintptr_t>(buf) & 15))
+    return fail(VA_ERR_INVALID_ARG, "buf must be 16-byte aligned and bytes a multiple of 16");
+  (void)hipGetLastError();
+  stream_read_kernel<<<dim3(4096), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const uint4*>(buf), int64_t(bytes / 16), sink);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail("stream read kernel launch", e);
+  return VA_OK;
 }
 
 extern "C" va_status varlen_attn_debug_gather(const va_plan* plan, const void* k_pool, const void* v_pool,

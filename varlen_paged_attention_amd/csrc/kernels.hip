@@ -953,6 +953,13 @@ static va_status prepare_kernels() {
   return once == hipSuccess ? VA_OK : hip_fail("hipFuncSetAttribute(max dynamic LDS)", once);
 }
 
+int device_compute_units() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return cus;
+}
+
 va_status upload_plan(va_plan* plan) {
   if (va_status st = prepare_kernels(); st != VA_OK) return st;
   const size_t b_items = align256(plan->items.size() * sizeof(SplitItem));

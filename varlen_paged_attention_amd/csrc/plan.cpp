@@ -60,15 +60,14 @@ struct Block {          // a set of <= 16 query columns scored against one kv ra
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Launch order of the prefill tiles.  Workgroup i of a launch goes to XCD i % 8, and each
+// Launch order of the prefill tiles.  Workgroup i of a launch goes to XCD i % xcds, and each
 // XCD has its own L2: tiles that read the same keys (one request's KV head, or one key
 // chunk of it for cut tiles) are placed at positions of one XCD so they share its L2,
 // with the XCDs' work balanced (a group larger than an XCD's share is spread over
 // several); within an XCD, heaviest tiles first so the ragged end of the grid is made of
 // short tiles.  When an XCD's list runs out, the remaining positions take the heaviest
 // tiles left in the longest list.
-constexpr int kXcds = 8;
-void order_tiles(std::vector<PrefillTile>& tiles) {
+void order_tiles(std::vector<PrefillTile>& tiles, int xcds) {
   const size_t T = tiles.size();
   if (T < 2) return;
   auto work = [](const PrefillTile& t) { return int64_t(t.kv_end) - t.kbeg; };
@@ -84,7 +83,7 @@ void order_tiles(std::vector<PrefillTile>& tiles) {
   });
   int64_t total = 0;
   for (const PrefillTile& t : tiles) total += work(t);
-  const int64_t share = std::max<int64_t>(1, ceil_div(total, kXcds));
+  const int64_t share = std::max<int64_t>(1, ceil_div(total, xcds));
   struct Piece {
     int64_t work;
     size_t b, e;   // range of idx
@@ -106,10 +105,10 @@ void order_tiles(std::vector<PrefillTile>& tiles) {
     b = e;
   }
   std::stable_sort(pieces.begin(), pieces.end(), [](const Piece& a, const Piece& b) { return a.work > b.work; });
-  std::vector<std::vector<int32_t>> bins(kXcds);
-  int64_t load[kXcds] = {};
+  std::vector<std::vector<int32_t>> bins(xcds);
+  std::vector<int64_t> load(xcds, 0);
   for (const Piece& pc : pieces) {
-    const int x = int(std::min_element(load, load + kXcds) - load);
+    const int x = int(std::min_element(load.begin(), load.end()) - load.begin());
     load[x] += pc.work;
     bins[x].insert(bins[x].end(), idx.begin() + pc.b, idx.begin() + pc.e);
   }
@@ -117,12 +116,12 @@ void order_tiles(std::vector<PrefillTile>& tiles) {
     std::stable_sort(bin.begin(), bin.end(), [&](int32_t a, int32_t b) { return work(tiles[a]) > work(tiles[b]); });
   std::vector<PrefillTile> out;
   out.reserve(T);
-  size_t pos[kXcds] = {};
+  std::vector<size_t> pos(xcds, 0);
   for (size_t p = 0; out.size() < T; ++p) {
-    int x = int(p % kXcds);
+    int x = int(p % xcds);
     if (pos[x] == bins[x].size()) {
       size_t most = 0;
-      for (int y = 0; y < kXcds; ++y)
+      for (int y = 0; y < xcds; ++y)
         if (bins[y].size() - pos[y] > most) most = bins[y].size() - pos[y], x = y;
     }
     out.push_back(tiles[bins[x][pos[x]++]]);
@@ -221,6 +220,12 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
     return p.prefill_min_rows > 0 ? m >= p.prefill_min_rows : int64_t(m) * g >= kPrefillCols / 2;
   };
   const bool use_prefill = !(p.flags & VA_FLAG_NO_PREFILL_KERNEL) && prefill_kernel_available(p);
+  // the device's shape: resident prefill workgroups and XCDs (a host-only plan assumes a
+  // whole MI355X: 256 compute units in 8 XCDs)
+  const int cus = (p.flags & VA_FLAG_HOST_ONLY) ? 0 : device_compute_units();
+  const int n_cu = cus > 0 ? cus : 256;
+  const int slots_wg = kPrefillWgPerCu * n_cu;
+  const int xcds = std::max(1, n_cu / kCusPerXcd);
 
   // ---- classify requests -------------------------------------------------------
   // Requests with enough new rows always get prefill tiles; the others (decodes,
@@ -333,10 +338,10 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
       // the chosen length is within 6 % of the best measured one on all twelve.
       auto start_cost = [](const PrefillTile& t) { return int64_t(t.ncols >= 64 ? 128 : 16); };
       auto partial_cost = [&](const PrefillTile& t) { return 3 * 2 * int64_t(t.ncols) * (D + 2) / D; };
-      auto greedy = [](std::vector<int64_t>& costs) {
+      auto greedy = [&](std::vector<int64_t>& costs) {
         std::sort(costs.begin(), costs.end(), std::greater<int64_t>());
         std::priority_queue<int64_t, std::vector<int64_t>, std::greater<int64_t>> free_at;
-        for (int i = 0; i < kPrefillSlots; ++i) free_at.push(0);
+        for (int i = 0; i < slots_wg; ++i) free_at.push(0);
         int64_t end = 0;
         for (int64_t c : costs) {
           const int64_t t = free_at.top() + c;
@@ -355,7 +360,7 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
       // give at most 16 tiles per resident slot's worth of keys
       for (int64_t cand = 8192; cand >= 256; cand /= 2) {
         if (longest <= 2 * cand) continue;                       // no tile would be cut
-        if (keys_all > 16 * kPrefillSlots * cand) break;         // too many chunk tiles
+        if (keys_all > 16 * slots_wg * cand) break;              // too many chunk tiles
         costs.clear();
         for (const PrefillTile& t : tiles) {
           const int64_t n = chunks_of(t, cand);
@@ -439,7 +444,7 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
       std::vector<CombineRow> rows;
       int64_t nslots = 0;
       cut_tiles(with, rows, nslots);
-      if (with.size() >= size_t(kPrefillSlots)) {
+      if (with.size() >= size_t(slots_wg)) {
         plan->tiles.swap(with);
         cut_rows.swap(rows);
         cut_slots = nslots;
@@ -457,7 +462,6 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
     for (int r : short_reqs)
       if (!is_tile[r]) split_reqs.push_back(r);
   }
-
 
   // ---- column blocks ------------------------------------------------------------------
   std::vector<Block> blocks;
@@ -515,7 +519,7 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
     if (shared_pages[r] > 0) n_suffix += Hkv * ceil_div(int64_t(q_end[r] - q_start[r]) * g, kPrefillCols);
   const bool suffix_tiles = use_prefill && p.dtype == VA_DTYPE_BF16 && p.prefill_min_rows <= 0 &&
                             !(p.flags & VA_FLAG_NO_DECODE_TILES) &&
-                            n_suffix + int64_t(plan->tiles.size()) >= kPrefillSlots;
+                            n_suffix + int64_t(plan->tiles.size()) >= slots_wg;
   for (int r : split_reqs) {
     const int ncol = (q_end[r] - q_start[r]) * g;
     for (int kvh = 0; kvh < Hkv; ++kvh) {
@@ -551,9 +555,9 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
     L = std::min<int64_t>(L, 8192);
   }
   plan->split_len = int32_t(L);
-  // group tiles: key chunks sized for about 512 tiles in all (one per resident workgroup)
+  // group tiles: key chunks sized for about one tile per resident workgroup in all
   const int64_t Lt = std::min<int64_t>(
-      4096, std::max<int64_t>(256, ceil_div(ceil_div(tile_keys * tile_cols, 512), kStepKeys) * kStepKeys));
+      4096, std::max<int64_t>(256, ceil_div(ceil_div(tile_keys * tile_cols, slots_wg), kStepKeys) * kStepKeys));
   for (auto& B : blocks) {
     const int64_t keys = std::max(0, B.kend - B.kstart);
     B.chunk = int32_t(B.tile ? (B.shared ? Lt : 8192) : L);
@@ -674,7 +678,7 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
   // launch order; with only whole tiles every tile runs on the whole-tile kernel, else
   // every tile runs on the kernel that takes all kinds (one launch, so decode tiles, chunk
   // tiles and group tiles share the GPU instead of running one launch after the other)
-  order_tiles(plan->tiles);
+  order_tiles(plan->tiles, xcds);
   plan->tiles_whole = std::any_of(plan->tiles.begin(), plan->tiles.end(),
                                   [](const PrefillTile& t) { return t.pbase >= 0 || t.flags != 0; })
                           ? 0

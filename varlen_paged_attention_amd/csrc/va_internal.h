@@ -53,7 +53,8 @@ constexpr int kSplitWaves = 4;       // items (wavefronts) per split-KV workgrou
 constexpr int kPrefillWaves = 4;     // wavefronts per prefill workgroup (32 columns each)
 constexpr int kPrefillCols = 32 * kPrefillWaves;   // query columns per prefill tile
 constexpr int kStepKeys = 64;        // kv positions per split-KV loop step
-constexpr int kPrefillSlots = 512;   // prefill workgroups resident at once (256 CUs x 2)
+constexpr int kPrefillWgPerCu = 2;   // prefill workgroups resident per CU (LDS-bound)
+constexpr int kCusPerXcd = 32;       // compute units of one XCD on gfx950
 
 }  // namespace va
 
@@ -101,6 +102,9 @@ void set_error(const std::string& msg);
 va_status fail(va_status s, const std::string& msg);
 // Device side of plan creation / destruction (kernels.hip).
 va_status upload_plan(va_plan* plan);
+// Compute units of the current device (256 on an MI355X; fewer in a partition mode), or 0
+// when they cannot be queried.
+int device_compute_units();
 void free_plan_device(va_plan* plan);
 bool prefill_kernel_available(const va_params& p);
 }  // namespace va

@@ -35,6 +35,11 @@ def _bits(t):
     ("decode-heavy/8", 3, 8, None, 0),
     ("shared-6", 5, 1, None, api.VA_FLAG_SHARED_PREFIX),
     ("decode-heavy/8 fp8", 3, 8, "fp8", 0),
+    # the tile kernel in its other forms: decode tiles, key-chunk tiles with decode tiles in
+    # one launch, shared-prefix group tiles with members' own-key tiles
+    ("decode-heavy (decode tiles)", 3, 1, None, 0),
+    ("long-prefix-chunk/4 (chunk + decode tiles)", 9, 4, None, 0),
+    ("shared-64/4 (column-list tiles)", 51, 4, None, api.VA_FLAG_SHARED_PREFIX),
 ])
 def test_graph_replays_match_eager(label, cid, scale, dtype, flags):
     import torch

@@ -263,10 +263,14 @@ va_status varlen_attn_debug_fp8_to_bf16(const uint8_t* codes, uint16_t* out, int
  *            item writes its columns' output rows directly)
  *         1: query columns {q_row, q_head, limit, pbase}
  *         2: combine rows {q_row, q_head, pbase, nparts}
- *         3: prefill tiles {req, kvh, c0, ncols, q0, S0, kv_end, key_diag}
- *         4: shared-prefix group tiles {req, kvh, col0, ncols, slot, k0, k1, k1}: query
- *            columns cols[col0 .. col0+ncols) scored against positions [k0, k1) of request
- *            req's block table, partial results to slot pbase + slot
+ *         3: MFMA tiles in launch order {req, kvh, c0, ncols, q0, S0, kv_end, kbeg, pbase,
+ *            pstride, flags, group}: columns c0 .. c0+ncols of request req under KV head kvh
+ *            (column c = new row c / g, head kvh*g + c % g, row i sees keys up to S0 + i),
+ *            keys [kbeg, kv_end); pbase < 0: output rows written directly, else column c's
+ *            partial to slot pbase + (c - c0) * pstride.  flags bit 0 (column list): the
+ *            columns are cols[c0 .. c0+ncols) instead, their partials to slot pbase + q0
+ *            (of each column); group = 1 marks a shared-prefix group tile
+ *         4: the column-list tiles of 3 only
  * *data stays valid until the plan is destroyed. */
 va_status varlen_attn_plan_export(const va_plan* plan, int32_t which, const int32_t** data,
                                   int64_t* count, int32_t* ints_per_entry);

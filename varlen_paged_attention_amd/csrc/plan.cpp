@@ -253,7 +253,7 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
         t.kbeg = 0;
         t.pbase = -1;
         t.pstride = 0;
-        t.flags = t.pad1 = 0;
+        t.flags = t.group = 0;
         tiles.push_back(t);
       }
   };
@@ -635,7 +635,7 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
         t.pbase = -1;
         t.pstride = 0;
         t.flags = kTileColumnList;
-        t.pad1 = B.shared ? 1 : 0;                      // (counters only)
+        t.group = B.shared ? 1 : 0;
         plan->gtiles.push_back(t);
         plan->tiles.push_back(t);
       }
@@ -721,7 +721,7 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
   st.shared_tiles = 0;
   st.shared_tile_flops = 0;
   for (const PrefillTile& t : plan->gtiles)
-    if (t.pad1) {                                  // group tiles (every column sees every key)
+    if (t.group) {                                 // group tiles (every column sees every key)
       ++st.shared_tiles;
       st.shared_tile_flops += 4.0 * D * t.ncols * double(t.kv_end - t.S0);
     }
@@ -864,7 +864,7 @@ extern "C" va_status varlen_attn_plan_export(const va_plan* plan, int32_t which,
       return VA_OK;
   }
   return fail(VA_ERR_INVALID_ARG,
-              "which must be 0 (items), 1 (columns), 2 (combine rows), 3 (prefill tiles) or 4 (group tiles)");
+              "which must be 0 (items), 1 (columns), 2 (combine rows), 3 (tiles) or 4 (column-list tiles)");
 }
 
 extern "C" void varlen_attn_plan_destroy(va_plan* plan) {

@@ -44,7 +44,7 @@ struct CombineRow {
 struct PrefillTile {
   int32_t req, kvh, c0, ncols;
   int32_t q0, S0, kv_end, kbeg;
-  int32_t pbase, pstride, flags, pad1;
+  int32_t pbase, pstride, flags, group;   // group: a shared-prefix group tile (counters only)
 };
 constexpr int32_t kTileColumnList = 1;
 

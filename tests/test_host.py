@@ -243,7 +243,7 @@ def test_short_requests_as_tiles(name, make, flags, folded):
     g = w.num_q_heads // w.num_kv_heads
     short = [r for r in range(w.num_reqs) if 0 < m[r] and m[r] * g < 64]
     tiles = api.varlen_attn_plan_export(plan, 3)
-    # tiles scoring a request's own keys (not a shared-prefix group tile: pad word 1 set)
+    # tiles scoring a request's own keys (not a shared-prefix group tile: record field 11, "group")
     on_tiles = set(int(t[0]) for t in tiles if not (t[10] & 1 and t[11]))
     if folded:
         assert all(r in on_tiles for r in short) and st["split_items"] == 0

@@ -122,7 +122,7 @@ typedef struct {
   int64_t split_items;        /* split-KV work items (one wavefront each) */
   int64_t shared_items;       /* of which read a shared prefix for several requests */
   int64_t shared_groups;      /* groups of requests found sharing leading pages */
-  int64_t partial_slots;      /* (m, l, acc[head_dim]) partial results in the workspace */
+  int64_t partial_slots;      /* (m, 1/l, acc/l [head_dim]) partials in the workspace */
   int64_t combine_rows;       /* (row, head) outputs merged by the combine pass */
   int64_t visible_pairs;      /* sum over requests of m*S0 + m(m+1)/2 */
   double flops;               /* 4 * head_dim * num_q_heads * visible_pairs */

@@ -46,17 +46,22 @@ __device__ __forceinline__ f32x4 mfma16_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// Write one column's partial result.  acc[db][r] holds d = 16*db + 4*grp + r.
+// Write one column's partial result as (m, 1/l) and acc/l (1/l = 0 when no key was
+// scored), so every partial has the same form as a finished row.  acc[db][r] holds
+// d = 16*db + 4*grp + r.
 template <int D>
 __device__ __forceinline__ void store_partial(float* ws_ml, float* ws_acc, int slot, int grp, float m, float l,
                                               const f32x4* acc) {
-  if (grp == 0) {
-    ws_ml[2 * size_t(slot)] = m;
-    ws_ml[2 * size_t(slot) + 1] = l;
-  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  if (grp == 0) *reinterpret_cast<float2*>(ws_ml + 2 * size_t(slot)) = float2{m, inv};
   float* wa = ws_acc + size_t(slot) * D + 4 * grp;
 #pragma unroll
-  for (int db = 0; db < D / 16; ++db) *reinterpret_cast<f32x4*>(wa + 16 * db) = acc[db];
+  for (int db = 0; db < D / 16; ++db) {
+    f32x4 o;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o[r] = acc[db][r] * inv;
+    *reinterpret_cast<f32x4*>(wa + 16 * db) = o;
+  }
 }
 
 // Write one column's finished output row (an item that covers the column's whole kv

@@ -4,7 +4,7 @@
 //   split_kv_*   one wavefront per split-KV item: streams a kv range of one request's
 //                paged K/V for one KV head and scores it against up to 16 query columns
 //                (rows x query heads of the group) with 16x16 MFMA tiles; keeps a running
-//                max and sum per column and writes an unnormalised partial (m, l, acc).
+//                max and sum per column and writes a partial (m, 1/l, acc/l).
 //   combine      merges the partials of each (row, head) output with the log-sum-exp
 //                rule and writes the output row.
 //   gather       copies K/V into logical order through the same page addressing (for
@@ -397,7 +397,7 @@ constexpr int prefill_lds_bytes() {
 
 // A tile's columns are consecutive (row, head) pairs of one request.  A whole tile scores
 // keys [0, kv_end) and normalises and writes the output rows; a key-chunk tile (one chunk
-// of a cut tile) scores keys [kbeg, kv_end) and writes the unnormalised partial (m, l, acc)
+// of a cut tile) scores keys [kbeg, kv_end) and writes the partial (m, 1/l, acc/l)
 // of column col to workspace slot pbase + col * pstride, for the combine pass.
 // A column-list tile takes its columns from cols[c0 ..] (rows of one or several requests,
 // each with its own causal limit), scores keys [kbeg, kv_end) of request req's block table
@@ -788,40 +788,36 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
   }
   // ---- normalise and write: acc[db][4*ii + jj] is d = 32*db + 8*ii + 4*h + jj of this column
   const float l_tot = l_run + other_half(l_run);
-  if (MODE == kAnyTile && (T.pbase >= 0 || (T.flags & kTileColumnList))) {
-    if (cvalid) {
-      if (h == 0) {
-        ws_ml[2 * size_t(pslot)] = m_run;
-        ws_ml[2 * size_t(pslot) + 1] = l_tot;
-      }
-      float* wa = ws_acc + size_t(pslot) * D + 4 * h;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-          *reinterpret_cast<f32x4*>(wa + 32 * db + 8 * ii) =
-              f32x4{acc[db][4 * ii], acc[db][4 * ii + 1], acc[db][4 * ii + 2], acc[db][4 * ii + 3]};
-    }
-    return;
-  }
+  const bool part = MODE == kAnyTile && (T.pbase >= 0 || (T.flags & kTileColumnList));
   if (cvalid) {
-    const float inv = 1.f / l_tot;
+    const float inv = MODE == kAnyTile ? (l_tot > 0.f ? 1.f / l_tot : 0.f) : 1.f / l_tot;
+    if (part && h == 0) *reinterpret_cast<float2*>(ws_ml + 2 * size_t(pslot)) = float2{m_run, inv};
+    float* wa = ws_acc + size_t(pslot) * D + 4 * h;
     bf16* op = out + (size_t(row) * Hq + head) * D + 4 * h;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
-        bf16x4 o4;
+        f32x4 o4;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) o4[jj] = bf16(acc[db][4 * ii + jj] * inv);
-        *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * ii) = o4;
+        for (int jj = 0; jj < 4; ++jj) o4[jj] = acc[db][4 * ii + jj] * inv;
+        if (part) {
+          *reinterpret_cast<f32x4*>(wa + 32 * db + 8 * ii) = o4;
+        } else {
+          bf16x4 b4;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) b4[jj] = bf16(o4[jj]);
+          *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * ii) = b4;
+        }
       }
   }
 }
 
 
 // ------------------------------------------------------------------------ combine --
-// out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s with M = max_s m_s.
+// Partial s holds (m_s, 1/l_s, o_s = acc_s / l_s); with M = max_s m_s and weights
+// w_s = 2^(m_s - M) l_s (0 for a part that saw no key, stored as 1/l = 0),
+// out = sum_s w_s o_s / sum_s w_s, the same as sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
 template <int D, typename OutT>
 __global__ __launch_bounds__(256) void combine_kernel(const CombineRow* __restrict__ rows, int nrows,
                                                       const float* __restrict__ ws_ml,
@@ -846,8 +842,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineRow* __restri
     float w = 0.f;
     if (s0 + lane < r.nparts) {
       const size_t slot = size_t(r.pbase + s0 + lane);
-      w = fast_exp2(ws_ml[2 * slot] - M);
-      L += w * ws_ml[2 * slot + 1];
+      const float inv = ws_ml[2 * slot + 1];
+      w = inv > 0.f ? fast_exp2(ws_ml[2 * slot] - M) / inv : 0.f;
+      L += w;
     }
     const int n = min(64, r.nparts - s0);
     for (int t = 0; t < n; t += 8) {

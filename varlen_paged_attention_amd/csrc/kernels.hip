@@ -416,9 +416,10 @@ enum TileMode { kWholeTile, kAnyTile };
 
 // Instantiations: kWholeTile runs whole tiles only; kAnyTile runs every kind (whole tiles,
 // key-chunk tiles and column-list tiles: a plan with any of the latter launches all its
-// tiles on it, so all kinds share the GPU in one launch).  The whole-tile kernel is kept
-// apart because any partial-result epilogue in the same kernel changes how the compiler
-// lays out the main loop, and whole tiles then measured 4-6 % slower.
+// tiles on it, so all kinds share the GPU in one launch).  Both end in one epilogue that
+// normalises every column and only chooses where the row goes: with a separate epilogue
+// for partial results the compiler laid out the main loop differently and tiles ran 2-6 %
+// slower.  The whole-tile kernel keeps the shorter set-up of consecutive columns.
 template <int D, int MODE, bool F8>
 __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_bf16_kernel(
     const PrefillTile* __restrict__ tiles, const Column* __restrict__ cols, const bf16* __restrict__ q,

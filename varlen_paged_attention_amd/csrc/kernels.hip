@@ -345,7 +345,6 @@ constexpr int kPSliceKeys = kPTileKeys / kPrefillWaves;   // keys each wave copi
 constexpr float kRescaleSlack = 8.f;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -388,11 +387,12 @@ struct PrefillLds {
   static constexpr int KBUF = kPTileKeys * KROW;       // chunks per K buffer
   static constexpr int VBUF = kPTileKeys / 8 * D;      // chunks per V^T buffer
   static constexpr int bytes = 2 * (KBUF + VBUF) * 16;
+  static constexpr int scale_bytes = 2 * 2 * kPTileKeys * 4;   // fp8: K and V scales of both stages
 };
 
-template <int D>
+template <int D, bool F8>
 constexpr int prefill_lds_bytes() {
-  return PrefillLds<D>::bytes;
+  return PrefillLds<D>::bytes + (F8 ? PrefillLds<D>::scale_bytes : 0);
 }
 
 // A tile's columns are consecutive (row, head) pairs of one request.  A whole tile scores
@@ -439,6 +439,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
   extern __shared__ bf16x8 smem[];
   bf16x8* sK = smem;                                   // [2][KBUF]
   bf16x8* sV = smem + 2 * KBUF;                        // [2][VBUF]
+  float* sKs = reinterpret_cast<float*>(smem + 2 * KBUF + 2 * VBUF);   // fp8: [2][64] K scales
+  float* sVs = sKs + 2 * kPTileKeys;                                  // fp8: [2][64] V scales
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -522,9 +524,9 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
   // fp8: raw slice sizes (16-byte chunks) and where they sit inside the bf16 slices
   constexpr int KR = WK * D / 16;                      // K codes of the slice
   constexpr int VR = D;                                // V codes: one chunk (16 keys) per d
-  constexpr int KRAW = KSC - KR, KSCL = KRAW - 4;      // raw K codes, then 16 K scales before them
-  constexpr int VRAW = VSC - VR, VSCL = VRAW - 4;
-  static_assert(KSCL >= 0 && VSCL >= 0, "raw fp8 slices must fit in the bf16 slices");
+  constexpr int KRAW = KSC - KR;                       // raw K codes at the top of the slice
+  constexpr int VRAW = VSC - VR;
+  static_assert(KRAW >= 0 && VRAW >= 0, "raw fp8 slices must fit in the bf16 slices");
 
   // ---- per-lane DMA source offsets (bytes from the slice base)
   // K instruction r, lane -> slice chunk L = 64r + lane = (key L / KROW, d-chunk L % KROW);
@@ -555,7 +557,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
 #pragma unroll
       for (int r = 0; r < KR / 64; ++r) dma_b128(rs, dst + KRAW + 64 * r, uint32_t(16 * (64 * r + lane)), 0);
       const auto rsc = slice_rsrc(kscale + pg.scale_idx(page, kvh, k0w & ps_mask));
-      if (lane < WK) dma_b32(rsc, dst + KSCL, uint32_t(4 * lane));
+      if (lane < WK) dma_b32(rsc, sKs + buf * kPTileKeys + wv * WK, uint32_t(4 * lane));
     } else {
 #pragma unroll
       for (int r = 0; r < KNI; ++r)
@@ -568,6 +570,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
     if (k0w >= kv_end) {                      // never read garbage into V: write zeros
 #pragma unroll
       for (int r = 0; r < VNI; ++r) dst[64 * r + lane] = bf16x8{};
+      if constexpr (F8)
+        if (lane < WK) sVs[buf * kPTileKeys + wv * WK + lane] = 0.f;
       return;
     }
     const auto rs = slice_rsrc(vbase + size_t(page) * page_bytes + (k0w & ps_mask) * EB);
@@ -576,32 +580,15 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
 #pragma unroll
       for (int r = 0; r < VR / 64; ++r) dma_b128(rs, dst + VRAW + 64 * r, uint32_t((64 * r + lane) << pg.ps_shift), 0);
       const auto rsc = slice_rsrc(vscale + pg.scale_idx(page, kvh, k0w & ps_mask));
-      if (lane < WK) dma_b32(rsc, dst + VSCL, uint32_t(4 * lane));
+      if (lane < WK) dma_b32(rsc, sVs + buf * kPTileKeys + wv * WK, uint32_t(4 * lane));
     } else {
 #pragma unroll
       for (int r = 0; r < VNI; ++r) dma_b128(rs, dst + 64 * r, voff, r * vrstep);
     }
   };
-  // fp8: widen the slice's codes in place once its copies have landed (own slice only)
-  // the 16 codes of a raw chunk as floats (bytes 0..15 in order)
-  auto codes16 = [&](const bf16x8& raw, float (&f)[16]) {
-    const uint32_t* w = reinterpret_cast<const uint32_t*>(&raw);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(int(w[i]), false);
-      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(int(w[i]), true);
-      f[4 * i] = lo[0];
-      f[4 * i + 1] = lo[1];
-      f[4 * i + 2] = hi[0];
-      f[4 * i + 3] = hi[1];
-    }
-  };
-  auto widen16 = [&](const bf16x8& raw, float sc, bf16x8 (&o)[2]) {
-    float f[16];
-    codes16(raw, f);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) o[e >> 3][e & 7] = bf16(f[e] * sc);
-  };
+  // fp8: widen the slice's codes in place, exactly (scale 1), once its copies have landed
+  // (own slice only); the per-position scales stay in sKs / sVs: a key's K scale multiplies
+  // its scores, its V scale its probabilities
   auto convert_k = [&](int t, int buf) {
     if constexpr (F8) {
       const int k0w = kbeg + t * kPTileKeys + wv * WK;
@@ -609,20 +596,14 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
       bf16x8* sl = sK + buf * KBUF + wv * KSC;
       constexpr int PER = KR / 64;                      // raw chunks per lane
       bf16x8 raw[PER];
-      float sc[PER];
-      const float* scl = reinterpret_cast<const float*>(sl + KSCL);
 #pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        raw[i] = sl[KRAW + 64 * i + lane];
-        sc[i] = scl[(64 * i + lane) / (D / 16)];
-      }
+      for (int i = 0; i < PER; ++i) raw[i] = sl[KRAW + 64 * i + lane];
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
         const int L = 64 * i + lane, key = L / (D / 16), pc = L % (D / 16);
-        bf16x8 o[2];
-        widen16(raw[i], sc[i], o);
-        sl[key * KROW + 2 * pc] = o[0];
-        sl[key * KROW + 2 * pc + 1] = o[1];
+        const uint32_t* w = reinterpret_cast<const uint32_t*>(&raw[i]);
+        sl[key * KROW + 2 * pc] = fp8x8_to_bf16(w[0], w[1]);
+        sl[key * KROW + 2 * pc + 1] = fp8x8_to_bf16(w[2], w[3]);
       }
     }
   };
@@ -635,26 +616,20 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
       bf16x8 raw[PER];
 #pragma unroll
       for (int i = 0; i < PER; ++i) raw[i] = sl[VRAW + 64 * i + lane];
-      float sc[WK];
-      const f32x4* scl = reinterpret_cast<const f32x4*>(sl + VSCL);
-#pragma unroll
-      for (int i = 0; i < WK / 4; ++i) {
-        const f32x4 x = scl[i];
-        sc[4 * i] = x[0];
-        sc[4 * i + 1] = x[1];
-        sc[4 * i + 2] = x[2];
-        sc[4 * i + 3] = x[3];
-      }
       const int valid = kv_end - k0w;                   // keys of the slice before the end
+      // positions at or past the end may be unwritten slots: zero codes and scales there
+      // (their probabilities are 0, and 0 * NaN would still be NaN)
+      if (lane < WK && lane >= valid) sVs[buf * kPTileKeys + wv * WK + lane] = 0.f;
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
         const int d = 64 * i + lane;
-        float f[16];
-        codes16(raw[i], f);
-        bf16x8 o[2];
+        const uint32_t* w = reinterpret_cast<const uint32_t*>(&raw[i]);
+        bf16x8 o[2] = {fp8x8_to_bf16(w[0], w[1]), fp8x8_to_bf16(w[2], w[3])};
+        if (valid < WK) {
 #pragma unroll
-        for (int k = 0; k < WK; ++k)   // positions at or past the end may be unwritten slots: zero, not 0 * NaN
-          o[k >> 3][k & 7] = k < valid ? bf16(f[k] * sc[k]) : bf16(0.f);
+          for (int k = 0; k < WK; ++k)
+            if (k >= valid) o[k >> 3][k & 7] = bf16(0.f);
+        }
         const int flip = (d >> 3) & 1;
         sl[2 * d + flip] = o[0];
         sl[2 * d + (flip ^ 1)] = o[1];
@@ -689,12 +664,45 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
 #pragma unroll
     for (int kc = 0; kc < D / 16; ++kc) sn = mfma32_bf16(kb[2 * kc], qb[kc], sn);
   };
-  auto exp_block = [&](const f32x16& sc, bf16x8 (&pb)[2]) {
+  // element 8t + x of a 32-key block's scores (and of its probabilities) is key
+  // 32b + 16t + 8h + x of the 64-key tile
+  auto k_scale_block = [&](int buf, int b, f32x16& sn) {
+    if constexpr (F8) {
+      const f32x4* ks = reinterpret_cast<const f32x4*>(sKs + buf * kPTileKeys + 32 * b + 8 * h);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pb[t][e] = bf16(fast_exp2(fmaf(sc[8 * t + e], scale_log2, -m_run)));
-      l_run += sum8_bf16(pb[t]);
+        for (int u = 0; u < 2; ++u) {
+          const f32x4 f = ks[4 * t + u];
+#pragma unroll
+          for (int x = 0; x < 4; ++x) sn[8 * t + 4 * u + x] *= f[x];
+        }
+    }
+  };
+  auto exp_block = [&](const f32x16& sc, int buf, int b, bf16x8 (&pb)[2]) {
+    if constexpr (F8) {
+      // row sum over the probabilities; P carries each key's V scale (V holds plain codes)
+      const f32x4* vs = reinterpret_cast<const f32x4*>(sVs + buf * kPTileKeys + 32 * b + 8 * h);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        float pf[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pf[e] = fast_exp2(fmaf(sc[8 * t + e], scale_log2, -m_run));
+        l_run += ((pf[0] + pf[1]) + (pf[2] + pf[3])) + ((pf[4] + pf[5]) + (pf[6] + pf[7]));
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const f32x4 f = vs[4 * t + u];
+#pragma unroll
+          for (int x = 0; x < 4; ++x) pb[t][4 * u + x] = bf16(pf[4 * u + x] * f[x]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[t][e] = bf16(fast_exp2(fmaf(sc[8 * t + e], scale_log2, -m_run)));
+        l_run += sum8_bf16(pb[t]);
+      }
     }
   };
   auto pv_tile = [&](int buf, const bf16x8 (&p)[2][2]) {
@@ -727,6 +735,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
   if (w_max_limit >= 0) {
     qk_block(0, 0, sc[0]);
     qk_block(0, 1, sc[1]);
+    k_scale_block(0, 0, sc[0]);
+    k_scale_block(0, 1, sc[1]);
   }
   __syncthreads();
 
@@ -772,12 +782,13 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
         for (int b = 0; b < 2; ++b) {
           f32x16 sn;
           qk_block((j + 1) & 1, b, sn);
-          exp_block(sc[b], p[b]);
+          exp_block(sc[b], j & 1, b, p[b]);
+          k_scale_block((j + 1) & 1, b, sn);
           sc[b] = sn;
         }
       } else {
-        exp_block(sc[0], p[0]);
-        exp_block(sc[1], p[1]);
+        exp_block(sc[0], j & 1, 0, p[0]);
+        exp_block(sc[1], j & 1, 1, p[1]);
       }
       pv_tile(j & 1, p);
     }
@@ -936,7 +947,7 @@ static va_status prepare_kernels() {
   // the prefill kernel's dynamic LDS exceeds the 64 KiB default limit
   static hipError_t once = [] {
     const std::pair<const void*, int> kernels[] = {
-#define VA_PREFILL_KERNEL(D, M, F) {reinterpret_cast<const void*>(&prefill_bf16_kernel<D, M, F>), prefill_lds_bytes<D>()}
+#define VA_PREFILL_KERNEL(D, M, F) {reinterpret_cast<const void*>(&prefill_bf16_kernel<D, M, F>), prefill_lds_bytes<D, F>()}
         VA_PREFILL_KERNEL(128, kWholeTile, false), VA_PREFILL_KERNEL(64, kWholeTile, false),
         VA_PREFILL_KERNEL(128, kAnyTile, false), VA_PREFILL_KERNEL(64, kAnyTile, false),
         VA_PREFILL_KERNEL(128, kWholeTile, true),  VA_PREFILL_KERNEL(64, kWholeTile, true),
@@ -1070,11 +1081,11 @@ static va_status run_impl(const va_plan* plan, const void* q, const void* k_pool
     auto* qq = static_cast<const bf16*>(q);
     auto* oo = static_cast<bf16*>(out);
     if (D == 128)
-      prefill_bf16_kernel<128, M, F><<<grid, block, prefill_lds_bytes<128>(), s>>>(
+      prefill_bf16_kernel<128, M, F><<<grid, block, prefill_lds_bytes<128, F>(), s>>>(
           tl, plan->d_cols, qq, k_pool, v_pool, k_scale, v_scale, block_table_dev, bt_stride, oo, ws_ml, ws_acc,
           p.num_q_heads, plan->g, pg, scale_log2);
     else
-      prefill_bf16_kernel<64, M, F><<<grid, block, prefill_lds_bytes<64>(), s>>>(
+      prefill_bf16_kernel<64, M, F><<<grid, block, prefill_lds_bytes<64, F>(), s>>>(
           tl, plan->d_cols, qq, k_pool, v_pool, k_scale, v_scale, block_table_dev, bt_stride, oo, ws_ml, ws_acc,
           p.num_q_heads, plan->g, pg, scale_log2);
     return hipGetLastError();

@@ -73,8 +73,8 @@ typedef enum {
  * Scale Your Model 笔记(7-8)", section 4: a storage format widened on chip, the arithmetic
  * in the wider format; "GLM-5.3 推理全链路(八)", on the costs outside the 656-byte
  * ledger: FP32 scales stored with each token's FP8 data, both read to dequantise).
- * Such plans run with varlen_attn_run_fp8 (prefill tiles widen their K/V tiles to
- * bf16(code * scale) on chip; split-KV items apply the scales to scores and probabilities);
+ * Such plans run with varlen_attn_run_fp8 (codes are widened exactly to bf16 on chip and
+ * the scales applied in fp32 to scores (K) and probabilities (V));
  * new rows are stored with varlen_attn_append_kv_fp8. */
 typedef enum { VA_DTYPE_BF16 = 0, VA_DTYPE_F32 = 1, VA_DTYPE_FP8_E4M3 = 2 } va_dtype;
 

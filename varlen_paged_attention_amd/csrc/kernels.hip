@@ -407,9 +407,10 @@ constexpr int prefill_lds_bytes() {
 // each keeping its own running max and sum) or the tile of a member's own keys after them.
 //
 // F8 = true: the pools hold fp8 e4m3fn codes with per-position float32 scales.  Each wave
-// copies its 16-key slice of codes (and the 16 K or V scales) by LDS-DMA into the upper
-// part of the same slice's bf16 area, then, once its copies have landed, widens them in
-// place to bf16(code * scale) in the layouts above, so the MFMA loop is the bf16 one.
+// copies its 16-key slice of codes by LDS-DMA into the upper part of the same slice's bf16
+// area (and the slice's 16 K and 16 V scales into the scale area), then, once its copies
+// have landed, widens the codes in place, exactly, in the layouts above, so the MFMA loop
+// is the bf16 one; a key's K scale multiplies its scores and its V scale its probability.
 // The slice is the wave's own, and all its reads precede its writes, so no other wave is
 // involved until the barrier that ends the iteration.
 enum TileMode { kWholeTile, kAnyTile };

@@ -805,7 +805,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
   if (cvalid) {
     const float inv = MODE == kAnyTile ? (l_tot > 0.f ? 1.f / l_tot : 0.f) : 1.f / l_tot;
     if (part && h == 0) *reinterpret_cast<float2*>(ws_ml + 2 * size_t(pslot)) = float2{m_run, inv};
-    float* wa = ws_acc + size_t(pslot) * D + 4 * h;
+    float* wa = ws_acc + (part ? size_t(pslot) * D + 4 * h : 0);   // whole tiles have no slot
     bf16* op = out + (size_t(row) * Hq + head) * D + 4 * h;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)

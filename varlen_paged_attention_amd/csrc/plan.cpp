@@ -307,7 +307,8 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
   // the resident slots (the dispatcher hands each next workgroup to the first free slot):
   // whole tiles, and tiles cut into chunks of each power of two from 256 to 8192 keys,
   // each tile costing its keys plus a fixed start-up, chunk tiles also the writing and
-  // re-reading of their partial results.  It takes the shortest schedule if it beats whole
+  // re-reading of their partial results.  It takes the shortest schedule (a shorter chunk
+  // only when its schedule is 5% shorter than the best longer one's) if it beats whole
   // tiles by 10%.  (Power-of-two chunks measured faster than chunks of the same count but
   // other lengths.)
   auto chunks_of = [&](const PrefillTile& t, int64_t Lc) {
@@ -373,7 +374,10 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
           }
         }
         const int64_t end = greedy(costs);
-        if (end < best) {
+        // a shorter chunk must beat the best longer one by 5 %: the model leaves out costs
+        // that grow with the number of chunk tiles (the combine's ramp, partials written
+        // past L2), and the longer chunk measured faster where the two were within that
+        if (Lc == 0 ? end < best : 20 * end < 19 * best) {
           best = end;
           Lc = cand;
         }

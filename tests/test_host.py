@@ -282,6 +282,7 @@ CUT_CASES = [
                                   page_size=32, seed=8), 64, True),
     ("auto-long-chunk", lambda: _long_chunk(), 0, True),
     ("auto-long-chunk+decodes", lambda: _long_chunk(512, 131072, 64, 8, extra=(900, 40000, 3)), 0, True),
+    ("auto-long-prefix-chunk+64-decodes", lambda: W.config(9), 0, True),
     ("auto-orca-stays-whole", lambda: W.config(2), 0, False),
     ("auto-chunk-mix-stays-whole", lambda: W.config(4), 0, False),
     ("never", lambda: _long_chunk(), -1, False),
@@ -300,6 +301,12 @@ def test_cut_prefill_tiles_cover_every_visible_pair_once(name, make, split, cut)
     if cut and split > 0:
         L = -(-split // 64) * 64
         assert np.all(work[tiles[:, 8] >= 0] <= L + 128)   # the last chunk also holds the diagonal
+    if name == "auto-long-prefix-chunk+64-decodes":
+        # the 64 tiles of 256 rows x 4 heads on 65,536 cached keys take 8192-key chunks (4096
+        # models about as fast but measured 7 % slower); the decode tiles (<= 16,384 keys,
+        # i.e. <= 2 chunks) stay whole
+        assert st["prefill_split_tiles"] == 512 and st["prefill_tiles"] == 512 + 64 * 8
+        assert set((tiles[tiles[:, 8] >= 0, 7] % 8192).tolist()) == {0}
     if name == "auto-long-chunk":
         # 64 tiles of ~65.8K keys on 512 resident slots: chunks of 8192 keys (the largest
         # power of two <= 64 * 65.8K / 512), 8 per tile (the remainder of 1 key is absorbed)

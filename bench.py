@@ -121,6 +121,8 @@ def time_runs(api, plan, tensors, steps, warmup, flush=None):
 
 
 LAYERS = 32     # attention layers of the model the headline iteration is shaped on (Llama-2-7B)
+# untimed runs before a secondary line's timed ones (a new workload's first runs are slower)
+SECONDARY_WARMUP = 10
 
 
 def time_graph(api, plan, tensors, steps, warmup, layers=LAYERS):
@@ -424,7 +426,7 @@ def secondary(api, W, cid, flags, reps, label, flush, key=None, dtype=None, tp=1
     w = W.config(cid, dtype=dtype, tp=tp, dp=dp)
     plan, tensors = setup(api, w, flags)
     st = api.varlen_attn_plan_stats(plan)
-    _, stage, totals = time_runs(api, plan, tensors, reps, 3, flush)
+    _, stage, totals = time_runs(api, plan, tensors, reps, SECONDARY_WARMUP, flush)
     # the step's time less the cost of the three event records inside it (see dominant())
     steps_us = [(t - 3 * stage.get("event_record", 0.0)) * 1e3 for t in totals]
     us = float(np.median(steps_us))

@@ -264,9 +264,10 @@ def cpu_baseline(w, budget_s=15.0):
             break
         n = min(4096, n * 4 if dt < budget_s / 16 else n * 2)
     flops = oracle.attention_flops(s.q_end - s.q_start, s.kv_len, s.num_q_heads, s.head_dim)
+    hc = host_cpu()
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"last {n} rows of the 4096-row prefill (cached prefix {4096 - n}) + both decodes, all 32 heads, "
-                      f"fp64 NumPy, {dt:.2f} s", "cpu": cpu_model(), "seconds": round(dt, 3)}
+                      f"fp64 NumPy, {threads} threads, {dt:.2f} s", "seconds": round(dt, 3), **hc}
 
 
 def hbm_read_gbps(api):
@@ -421,9 +422,11 @@ def make_flush():
     return flush
 
 
-def secondary(api, W, cid, flags, reps, label, flush, key=None, dtype=None, tp=1, dp=1):
-    plan, tensors = None, None
-    w = W.config(cid, dtype=dtype, tp=tp, dp=dp)
+def secondary(api, W, cid, flags, reps, label, flush, key=None, dtype=None, tp=1, dp=1, w=None):
+    """Time one workload (config `cid`, or the given Workload `w`) as eager runs with the
+    library's stage events; returns the full record (see compact())."""
+    if w is None:
+        w = W.config(cid, dtype=dtype, tp=tp, dp=dp)
     plan, tensors = setup(api, w, flags)
     st = api.varlen_attn_plan_stats(plan)
     _, stage, totals = time_runs(api, plan, tensors, reps, SECONDARY_WARMUP, flush)
@@ -447,6 +450,73 @@ def secondary(api, W, cid, flags, reps, label, flush, key=None, dtype=None, tp=1
            "dtype": w.dtype}
     del tensors
     return res
+
+
+def compact(res, key):
+    """The short form of a secondary record kept in the JSON line: median step (p10/p90),
+    algorithmic rates over the step, and the dominant kernel's roofline fraction."""
+    rf = res.get("roofline") or {}
+    out = {"w": key, "us": res.get("us_per_step", res.get("us_per_step_graph")),
+           "p10": res.get("us_p10"), "p90": res.get("us_p90"),
+           "GBps": res.get("hbm_GBps"), "hbm_frac": res.get("hbm_frac"), "TFLOPs": res.get("tflops"),
+           "t_roof_frac": res.get("t_roof_frac")}
+    if rf:
+        out["kernel"] = {"name": rf["kernel"].replace("_kernel", ""), "us": round(rf["kernel_ms"] * 1e3, 1),
+                         "bound": rf["bound"], "frac": rf["frac"], "traffic": rf.get("traffic")}
+    for k in ("plan_ms", "block_table_h2d_us", "tokens"):
+        if k in res:
+            out[k] = res[k]
+    return {k: v for k, v in out.items() if v is not None}
+
+
+def host_cpu():
+    """The host the CPU baseline runs on: lscpu's model line with family/model numbers, the
+    logical CPUs and those this process may use."""
+    info = {}
+    try:
+        import subprocess
+        for line in subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout.splitlines():
+            k, _, v = line.partition(":")
+            info[k.strip()] = v.strip()
+    except Exception:
+        pass
+    model = info.get("Model name") or cpu_model()
+    fam = info.get("CPU family")
+    desc = model + (f" (family {fam}, model {info.get('Model')})" if fam else "")
+    if info.get("Hypervisor vendor"):
+        desc += f", under {info['Hypervisor vendor']}"
+    return {"cpu": desc, "nproc": os.cpu_count(), "usable_cpus": len(os.sched_getaffinity(0)),
+            "cores_per_socket": int(info["Core(s) per socket"]) if info.get("Core(s) per socket", "").isdigit() else None,
+            "threads_per_core": int(info["Thread(s) per core"]) if info.get("Thread(s) per core", "").isdigit() else None}
+
+
+def targets(rec, full):
+    """Each configuration of the pages' workloads with its time, bound and roofline fraction
+    (kernel fractions from the dominant kernel's own time, step fractions from the step)."""
+    def kern(res):
+        r = res["roofline"]
+        return {"kernel": r["kernel"].replace("_kernel", ""), "kernel_us": round(r["kernel_ms"] * 1e3, 1),
+                "bound": r["bound"], "kernel_frac": r["frac"]}
+    t = {"1_tiny_f32": "parity only (max |gpu - oracle| <= 1e-4 in the GPU tests)",
+         "2_orca_mixed": {"us": round(rec["ms_per_step"] * 1e3, 1), "bound": "mfma", "frac": rec["roofline"]["frac"],
+                          "TFLOPs": rec["value"], "target": ">= 0.50 of 2.5 PFLOP/s"}}
+    d = full["decode"]
+    t["3_decode_heavy"] = {"us": d["us_per_step"], "hbm_frac_step": d["hbm_frac"], **kern(d),
+                           "target": ">= 0.70 of 8 TB/s"}
+    c, ca, cd = full["chunk"], full["chunk_alone"], full["chunk_decodes"]
+    t["4_chunk_mix"] = {"us": c["us_per_step"], "t_roof_frac": c["t_roof_frac"], **kern(c),
+                        "chunk_alone_us": ca["us_per_step"], "chunk_alone_mfma_frac": ca["roofline"]["frac"],
+                        "decodes_alone_us": cd["us_per_step"], "decodes_alone_hbm_frac": cd["hbm_frac"],
+                        "decodes_alone_kernel_frac": cd["roofline"]["frac"],
+                        "target": "both fractions; decodes >= 0.70 of 8 TB/s"}
+    for key, name, goal in (("shared6", "5_shared_prefix_6", None), ("shared64", "5_shared_prefix_64_scaled", ">= 0.70")):
+        x = full[key]
+        t[name] = {"us": x["us_per_step"], "hbm_frac_physical": x["hbm_frac"], **kern(x),
+                   "physical_MiB": round(x["physical_kv_bytes"] / 2**20, 1),
+                   "logical_MiB": round(x["logical_kv_bytes"] / 2**20, 1), "llc_evicted": x["l2_flushed"]}
+        if goal:
+            t[name]["target"] = goal + " of 8 TB/s on physical bytes"
+    return t
 
 
 def main():
@@ -539,54 +609,60 @@ def main():
 
     if not args.no_secondary:
         flush = make_flush()
+        full = {}
 
-        sec = []
-        for cid, flags, label, fl, key, dt in (
-                (3, 0, "decode-heavy-gqa (256 decodes, kv U[1024,8192], g=4, page 64)", None, "decode", None),
-                (4, 0, "chunked-prefill-mix (2048@S0=30720 + 64 decodes, g=8)", None, "chunk", None),
+        def add(key, res):
+            full[key] = res
+            log(f"[bench] full {key}: " + json.dumps(res))
+
+        w4 = W.config(4)
+        for cid, flags, label, fl, key, dt, wl in (
+                (3, 0, "decode-heavy-gqa (256 decodes, kv U[1024,8192], g=4, page 64)", None, "decode", None, None),
+                (4, 0, "chunked-prefill-mix (2048@S0=30720 + 64 decodes, g=8)", None, "chunk", None, w4),
+                (4, 0, "chunked-prefill-mix: the 2048-row chunk alone", None, "chunk_alone", None, W.subset(w4, [0])),
+                (4, 0, "chunked-prefill-mix: the 64 decodes alone", None, "chunk_decodes", None,
+                 W.subset(w4, range(1, w4.num_reqs))),
                 (9, 0, "long-prefix-chunk (256@S0=65536 + 64 decodes, g=4; key-chunk tiles)", None, "longchunk",
+                 None, None),
+                (5, api.VA_FLAG_SHARED_PREFIX, "shared-prefix-6 (4096 shared + 1024 each)", flush, "shared6", None,
                  None),
-                (5, api.VA_FLAG_SHARED_PREFIX, "shared-prefix-6 (4096 shared + 1024 each)", flush, "shared6", None),
                 (51, api.VA_FLAG_SHARED_PREFIX, "shared-prefix-64 (16384 shared + 1024 each)", flush, "shared64",
+                 None, None),
+                (6, 0, "spec-decode verify, 4 rows/request", None, "mtp3", None, None),
+                (7, 0, "spec-decode verify, 8 rows/request", None, "mtp7", None, None),
+                (3, 0, "decode-heavy-gqa, fp8 KV + scales", None, "decode_fp8", "fp8", None),
+                (51, api.VA_FLAG_SHARED_PREFIX, "shared-prefix-64, fp8 KV + scales", flush, "shared64_fp8", "fp8",
                  None),
-                (6, 0, "spec-decode verify, 4 rows/request (256 requests, kv U[1024,8192], g=4)", None, "mtp3",
-                 None),
-                (7, 0, "spec-decode verify, 8 rows/request (256 requests, kv U[1024,8192], g=4)", None, "mtp7",
-                 None),
-                (3, 0, "decode-heavy-gqa in fp8 e4m3fn KV + per-position fp32 scales", None, "decode_fp8", "fp8"),
-                (51, api.VA_FLAG_SHARED_PREFIX, "shared-prefix-64 in fp8 e4m3fn KV + scales", flush, "shared64_fp8",
-                 "fp8"),
-                (4, 0, "chunked-prefill-mix in fp8 e4m3fn KV + scales", None, "chunk_fp8", "fp8"),
-                (2, 0, "orca-mixed in fp8 e4m3fn KV + scales", None, "orca_fp8", "fp8")):
+                (4, 0, "chunked-prefill-mix, fp8 KV + scales", None, "chunk_fp8", "fp8", None),
+                (2, 0, "orca-mixed, fp8 KV + scales", None, "orca_fp8", "fp8", None)):
             log(f"[bench] secondary: {label}")
-            sec.append(secondary(api, W, cid, flags, 20, label, fl, key, dt))
+            add(key, secondary(api, W, cid, flags, 20, label, fl, key if wl is None or key == "chunk" else None, dt,
+                               w=wl))
             torch.cuda.empty_cache()
+        del w4
         log("[bench] secondary: the ORCA iteration with the last-level cache evicted before each run")
-        sec.append(secondary(api, W, 2, 0, 20, "orca-mixed, 256 MB last-level cache evicted before each run",
-                             flush, None))
+        add("orca_llc_evicted", secondary(api, W, 2, 0, 20, "orca-mixed, last-level cache evicted before each run",
+                                          flush, None))
         # one GPU's share when the iteration is split over 8 GPUs (the kernels at their real shape)
-        for cid, tp, dp, label in ((4, 8, 1, "chunked-prefill-mix, one GPU of TP=8 (Hq=8, Hkv=1)"),
-                                   (2, 8, 1, "orca-mixed, one GPU of TP=8 (Hq=Hkv=4)"),
-                                   (3, 1, 8, "decode-heavy-gqa, one GPU of DP=8 (32 of the 256 requests)")):
-            log(f"[bench] secondary: {label}")
-            sec.append(secondary(api, W, cid, 0, 20, label, None, None, tp=tp, dp=dp))
+        for cid, tp, dp, key in ((4, 8, 1, "chunk_tp8"), (2, 8, 1, "orca_tp8"), (3, 1, 8, "decode_dp8")):
+            log(f"[bench] secondary: {key}")
+            add(key, secondary(api, W, cid, 0, 20, key, None, None, tp=tp, dp=dp))
             torch.cuda.empty_cache()
         log("[bench] secondary: long-context decode 256 x 128K")
-        sec.append(long_context_line(api, W))
+        add("long128k", long_context_line(api, W))
         torch.cuda.empty_cache()
-        for cid, label, dt in ((2, "kv-append: the ORCA iteration's 4098 new rows (32 KV heads, page 16)", None),
-                               (3, "kv-append: the decode-heavy iteration's 256 new rows (8 KV heads, page 64)", None),
-                               (2, "kv-append fp8 (quantise + scatter): the ORCA iteration's 4098 new rows", "fp8"),
-                               (3, "kv-append fp8 (quantise + scatter): the decode-heavy iteration's 256 new rows",
-                                "fp8")):
-            log(f"[bench] secondary: {label}")
-            sec.append(append_line(api, W, cid, label, dtype=dt))
+        for cid, key, dt in ((2, "append_orca", None), (3, "append_decode", None), (2, "append_orca_fp8", "fp8"),
+                             (3, "append_decode_fp8", "fp8")):
+            log(f"[bench] secondary: {key}")
+            add(key, append_line(api, W, cid, key, dtype=dt))
             torch.cuda.empty_cache()
-        sec.append({"workload": "torch copy 1 GiB (read+write) for reference", "hbm_GBps": hbm_copy_gbps()})
+        copy_gbps = hbm_copy_gbps()
         read_ceiling = hbm_read_gbps(api)
-        sec.append({"workload": "streaming read of 8 GiB (varlen_attn_debug_stream_read): achievable HBM read rate",
-                    "hbm_GBps": read_ceiling, "hbm_frac": round(read_ceiling * 1e9 / PEAK_HBM, 4)})
+        sec = [compact(res, key) for key, res in full.items()]
+        sec.append({"w": "copy_1GiB_torch", "GBps": copy_gbps})
+        sec.append({"w": "stream_read_8GiB", "GBps": read_ceiling, "hbm_frac": round(read_ceiling * 1e9 / PEAK_HBM, 4)})
         rec["secondary"] = sec
+        rec["targets"] = targets(rec, full)
         del flush
 
     if not args.no_cpu_baseline:
@@ -594,6 +670,8 @@ def main():
         rec["cpu_baseline"] = cpu_baseline(w)
     else:
         rec["cpu_baseline"] = None
+    if "targets" in rec:
+        rec["targets"] = rec.pop("targets")       # last, so a reader of the line's tail sees it
     print(json.dumps(rec), flush=True)
 
 

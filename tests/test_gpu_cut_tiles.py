@@ -97,3 +97,23 @@ def test_long_chunk_auto_cut_sampled():
             worst = max(worst, float(np.abs(got[np.asarray(rows), h, :] - o).max()))
     _say(f"[parity] long chunk sampled rows: max|gpu-oracle| = {worst:.3e}")
     assert worst <= TOL
+
+
+def test_long_chunk_auto_cut_focused():
+    """The same automatically cut chunk on the focused companion inputs (outputs O(1)):
+    sampled rows and heads against the oracle, with negative controls (an all-zero output,
+    a dropped or doubled hot 64-key step must fail the comparison)."""
+    import sampled
+    w = W.focus(W.build("lc", [256, 1], [65536 + 256, 3000], num_q_heads=32, num_kv_heads=8, head_dim=128,
+                        page_size=64, seed=6))
+    plan = api.plan_for(w)
+    assert api.varlen_attn_plan_stats(plan)["prefill_split_tiles"] == 512
+    out, _ = api.run_workload(w, plan=plan)
+    got = out.float().cpu().numpy()
+    worst, margin = 0.0, np.inf
+    for r, rows, heads in ((0, [0, 1, 77, 128, 200, 255], [0, 3, 9, 17, 30, 31]), (1, [0], [0, 5, 31])):
+        got_rows = {h: got[int(w.q_start[r]) + np.asarray(rows), h, :] for h in heads}
+        e, mg = sampled.check_request(w, r, rows, heads, got_rows, TOL)
+        worst, margin = max(worst, e), min(margin, mg)
+    _say(f"[parity] long chunk focused: max|gpu-oracle| = {worst:.3e}; smallest negative-control error {margin:.3e}")
+    assert margin > TOL

@@ -152,6 +152,34 @@ def test_fp8_parity_full_size_sampled(label, cid, flags):
     assert worst <= TOL
 
 
+FOCUSED = [("decode-heavy", 3, 0), ("chunk-mix", 4, 0), ("shared-64", 51, api.VA_FLAG_SHARED_PREFIX)]
+
+
+@pytest.mark.parametrize("label,cid,flags", FOCUSED, ids=[f[0] for f in FOCUSED])
+def test_fp8_parity_full_size_focused(label, cid, flags):
+    """fp8 pools of the full-size workloads on the focused companion inputs (outputs O(1)):
+    sampled rows against the oracle on the dequantised pools, with negative controls."""
+    import sampled
+    w = W.focus(W.config(cid, dtype="fp8"))
+    _say(f"[gpu] fp8 run full focused {label}: reqs={w.num_reqs} rows={w.total_q_rows}")
+    out, plan = _run(w, flags)
+    got = out.float().cpu().numpy()
+    rng = np.random.default_rng(400 + cid)
+    R, Hq = w.num_reqs, w.num_q_heads
+    reqs = sorted({0, R - 1, int(np.argmax(w.kv_len))} | set(int(x) for x in rng.choice(R, min(R, 4), False)))
+    worst, margin = 0.0, np.inf
+    for r in reqs:
+        m = int(w.q_end[r] - w.q_start[r])
+        rows = sorted({0, m - 1} | set(int(x) for x in rng.choice(m, min(m, 6), False)))
+        heads = sorted({0, Hq - 1} | set(int(x) for x in rng.choice(Hq, min(Hq, 6), False)))
+        got_rows = {h: got[int(w.q_start[r]) + np.asarray(rows), h, :] for h in heads}
+        e, mg = sampled.check_request(w, r, rows, heads, got_rows, TOL)
+        worst, margin = max(worst, e), min(margin, mg)
+    _say(f"[parity] fp8 focused full {label}: sampled max|gpu-oracle| = {worst:.3e}; "
+         f"smallest negative-control error {margin:.3e}")
+    assert worst <= TOL and margin > TOL
+
+
 EDGE = [
     ("gap+zero-row+kv1", dict(q_rows=[3, 0, 1, 1, 5], kv=[3, 9, 1, 2, 40], hq=4, hkv=4, d=64, ps=16)),
     ("g16-multi-row-ps256", dict(q_rows=[3, 1], kv=[700, 257], hq=32, hkv=2, d=128, ps=256)),

@@ -99,3 +99,59 @@ def test_long_context_full_size_graph_sampled():
     _say(f"[parity] long-context full (graph replay), requests 0 and last: max|gpu-oracle| = {worst:.3e}")
     assert np.isfinite(got).all()
     assert worst <= TOL
+
+
+def test_long_context_focused_full_size_graph_sampled():
+    """The full 128K workload on the focused companion inputs (outputs O(1)), run through a
+    HIP graph replay.  Sampled requests include the one holding the highest page id; their
+    hot keys lie on pages above id 2^16 whose K and V bytes sit more than 4 GiB into the
+    pools, so 32-bit page offsets would show.  Each request's comparison comes with its
+    negative controls (an all-zero output, a dropped or doubled hot 64-key step must fail)."""
+    import torch
+    import sampled
+    w = W.focus(W.config(8))
+    _say(f"[gpu] long-context focused full: {w.num_reqs} x {int(w.kv_len[0])}, {w.num_pages} pages")
+    plan = api.plan_for(w)
+    q, k, v, bt = api.to_device(w)
+    page_bytes = k[0].numel() * k.element_size()
+    out = torch.zeros_like(q)
+    ws = api.new_workspace(plan)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call = api.RunCall(plan, q, k, v, bt, out, ws, stream=s)
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    out.zero_()
+    g.replay()
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    del k, v, g
+    torch.cuda.empty_cache()
+    R, Hkv = w.num_reqs, w.num_kv_heads
+    gq = w.num_q_heads // Hkv
+    top = int(np.argmax(w.block_table.max(axis=1)))
+    reqs = sorted({0, R - 1, top, 97})
+    worst, margin, high = 0.0, np.inf, 0
+    for r in reqs:
+        kvhs = sorted({r % Hkv, (r * 5 + 3) % Hkv})
+        heads = [kvh * gq + c for kvh in kvhs for c in range(gq)]
+        for kvh in kvhs:
+            for c in range(gq):
+                pos = w.notes["hot"][(r, kvh, c)]
+                pages = w.block_table[r, pos // w.page_size].astype(np.int64)
+                high += int(((pages >= 1 << 16) & (pages * page_bytes >= 1 << 32)).sum())
+        got_rows = {h: got[int(w.q_start[r]):int(w.q_start[r]) + 1, h, :] for h in heads}
+        e, mg = sampled.check_request(w, r, [0], heads, got_rows, TOL)
+        worst, margin = max(worst, e), min(margin, mg)
+        _say(f"[parity] long-context focused request {r} (max page {int(w.block_table[r].max())}): "
+             f"max|gpu-oracle| = {e:.3e}, control margin {mg:.3e}")
+    _say(f"[parity] long-context focused full (graph replay): max|gpu-oracle| = {worst:.3e}; "
+         f"{high} sampled hot keys on pages above id 2^16 and 4 GiB")
+    assert high >= 32
+    assert int(w.block_table[top].max()) >= w.num_pages - 64
+    assert worst <= TOL and margin > TOL

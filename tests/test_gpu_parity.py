@@ -126,6 +126,51 @@ def test_parity_full_size_sampled(label, cid, flags):
     assert worst <= TOL[w.dtype]
 
 
+@functools.lru_cache(maxsize=2)
+def _focused(cid):
+    return W.focus(_cfg(cid))
+
+
+def _focused_check(w, out, label, seed, nreq=6, nrows=8, nheads=8):
+    """Sampled rows of a focused full-size run against the oracle, each sampled request's
+    comparison with its negative controls (an all-zero output and a dropped or doubled hot
+    64-key step must fail it) where the request has cached keys."""
+    import sampled
+    got = out.float().cpu().numpy()
+    rng = np.random.default_rng(seed)
+    Hq = w.num_q_heads
+    worst, margin = 0.0, np.inf
+    for r, rows in _sample_rows(w, rng, nreq, nrows):
+        heads = sorted({0, Hq - 1} | set(int(x) for x in rng.choice(Hq, size=min(Hq, nheads), replace=False)))
+        got_rows = {h: got[int(w.q_start[r]) + np.asarray(rows), h, :] for h in heads}
+        m = int(w.q_end[r] - w.q_start[r])
+        ctrl = int(w.kv_len[r]) - m >= sampled.STEP
+        e, mg = sampled.check_request(w, r, rows, heads, got_rows, TOL[w.dtype], with_controls=ctrl)
+        worst = max(worst, e)
+        if mg is not None:
+            margin = min(margin, mg)
+    _say(f"[parity] focused full {label}: sampled max|gpu-oracle| = {worst:.3e}; "
+         f"smallest negative-control error {margin:.3e}")
+    assert margin > TOL[w.dtype]
+    return worst
+
+
+FOCUSED = [("decode-heavy", 3, 0), ("decode-heavy split-KV", 3, api.VA_FLAG_NO_DECODE_TILES), ("chunk-mix", 4, 0),
+           ("long-prefix-chunk", 9, 0), ("shared-64", 51, api.VA_FLAG_SHARED_PREFIX), ("spec-decode-mtp7", 7, 0),
+           ("orca-mixed", 2, 0)]
+
+
+@pytest.mark.parametrize("label,cid,flags", FOCUSED, ids=[f[0] for f in FOCUSED])
+def test_parity_full_size_focused(label, cid, flags):
+    """The full-size workloads on the focused companion inputs (attention concentrated on a
+    few keys spread over each context, outputs O(1)): sampled rows against the oracle, with
+    negative controls showing the comparison would catch a lost or doubled key step."""
+    w = _focused(cid)
+    _say(f"[gpu] run full focused {label}: reqs={w.num_reqs} rows={w.total_q_rows}")
+    out, plan = api.run_workload(w, flags=flags)
+    _focused_check(w, out, label, 300 + cid)
+
+
 def _raw_gather(w):
     """Logical-order K and V of every request by numpy fancy indexing (raw bits)."""
     ks, vs = [], []

@@ -448,3 +448,73 @@ def test_bench_refuses_more_than_one_gpu():
                        timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+# ---- the binding checks every buffer's shape against the plan before a kernel sees it --
+
+def _cpu_buffers(w, plan):
+    import torch
+    p = plan.params
+    bf = torch.bfloat16
+    return dict(q=torch.zeros(w.total_q_rows, p.num_q_heads, p.head_dim, dtype=bf),
+                k_pool=torch.zeros(p.num_pages, p.num_kv_heads, p.page_size, p.head_dim, dtype=bf),
+                v_pool=torch.zeros(p.num_pages, p.num_kv_heads, p.head_dim, p.page_size, dtype=bf),
+                block_table_dev=torch.zeros(w.num_reqs, p.max_pages_per_req, dtype=torch.int32),
+                out=torch.zeros(w.total_q_rows, p.num_q_heads, p.head_dim, dtype=bf))
+
+
+@pytest.mark.parametrize("name,shape_fn", [
+    ("q", lambda b: (b["q"].shape[0] - 1,) + tuple(b["q"].shape[1:])),
+    ("out", lambda b: (b["out"].shape[0], b["out"].shape[1] - 1, b["out"].shape[2])),
+    ("k_pool", lambda b: (b["k_pool"].shape[0] - 1,) + tuple(b["k_pool"].shape[1:])),
+    ("v_pool", lambda b: tuple(b["k_pool"].shape)),              # a K-shaped V pool (pages not transposed)
+    ("block_table_dev", lambda b: (b["block_table_dev"].shape[0] - 1, b["block_table_dev"].shape[1])),
+])
+def test_binding_rejects_buffers_smaller_than_the_plan(name, shape_fn):
+    """A buffer that does not have the plan's shape is refused on the host (no kernel would
+    read past it)."""
+    import torch
+    w = W.build("sh", [5, 1], [40, 70], num_q_heads=4, num_kv_heads=2, head_dim=64, page_size=32, seed=1,
+                extra_pages=1)
+    plan = api.plan_for(w, flags=api.VA_FLAG_HOST_ONLY)
+    b = _cpu_buffers(w, plan)
+    b[name] = torch.zeros(shape_fn(b), dtype=b[name].dtype)
+    with pytest.raises(ValueError, match=name):
+        api.varlen_attn_run(plan, b["q"], b["k_pool"], b["v_pool"], b["block_table_dev"], b["out"])
+    with pytest.raises(ValueError, match=name):
+        api.RunCall(plan, b["q"], b["k_pool"], b["v_pool"], b["block_table_dev"], b["out"])
+
+
+def test_binding_shape_checks_pass_for_the_plans_shapes():
+    """With every shape right, the first complaint is that the tensors are not on a GPU."""
+    w = W.build("sh", [5, 1], [40, 70], num_q_heads=4, num_kv_heads=2, head_dim=64, page_size=32, seed=1)
+    plan = api.plan_for(w, flags=api.VA_FLAG_HOST_ONLY)
+    b = _cpu_buffers(w, plan)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        api.varlen_attn_run(plan, b["q"], b["k_pool"], b["v_pool"], b["block_table_dev"], b["out"])
+
+
+def test_binding_rejects_wrong_scale_and_append_pool_shapes():
+    import torch
+    w = W.build("sh8", [5, 1], [40, 70], num_q_heads=4, num_kv_heads=2, head_dim=64, page_size=32, seed=1,
+                dtype="fp8")
+    plan = api.plan_for(w, flags=api.VA_FLAG_HOST_ONLY)
+    p = plan.params
+    b = _cpu_buffers(w, plan)
+    k8 = torch.zeros(tuple(b["k_pool"].shape), dtype=torch.uint8)
+    v8 = torch.zeros(tuple(b["v_pool"].shape), dtype=torch.uint8)
+    ks = torch.zeros(p.num_pages, p.num_kv_heads, p.page_size)
+    short = torch.zeros(p.num_pages - 1, p.num_kv_heads, p.page_size)
+    with pytest.raises(ValueError, match="v_scale"):
+        api.varlen_attn_run_fp8(plan, b["q"], k8, v8, ks, short, b["block_table_dev"], b["out"])
+    T = 3
+    new = torch.zeros(T, p.num_kv_heads, p.head_dim, dtype=torch.bfloat16)
+    loc = torch.zeros(T, dtype=torch.int64)
+    with pytest.raises(ValueError, match="v_pool"):
+        api.varlen_attn_append_kv(num_kv_heads=p.num_kv_heads, head_dim=p.head_dim, page_size=p.page_size,
+                                  num_pages=p.num_pages, k_new=new, v_new=new, out_cache_loc=loc,
+                                  k_pool=b["k_pool"], v_pool=b["k_pool"])
+    with pytest.raises(ValueError, match="k_scale"):
+        api.varlen_attn_append_kv_fp8(num_kv_heads=p.num_kv_heads, head_dim=p.head_dim, page_size=p.page_size,
+                                      num_pages=p.num_pages, k_new=new, v_new=new, out_cache_loc=loc, k_pool=k8,
+                                      v_pool=v8, k_scale=short, v_scale=ks)

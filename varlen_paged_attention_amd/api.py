@@ -126,12 +126,17 @@ def _ptr32(a: np.ndarray):
 
 
 class Plan:
-    """Owns a va_plan handle (destroyed with the object)."""
+    """Owns a va_plan handle (destroyed with the object), with the sizes its buffers must
+    have: num_reqs, total_q_rows (rows q and out must hold) and kv_total (sum of kv_len)."""
 
-    def __init__(self, handle: ctypes.c_void_p, workspace_bytes: int, params: VaParams):
+    def __init__(self, handle: ctypes.c_void_p, workspace_bytes: int, params: VaParams, num_reqs: int = 0,
+                 total_q_rows: int = 0, kv_total: int = 0):
         self.handle = handle
         self.workspace_bytes = int(workspace_bytes)
         self.params = params
+        self.num_reqs = int(num_reqs)
+        self.total_q_rows = int(total_q_rows)
+        self.kv_total = int(kv_total)
 
     def __del__(self):
         h = getattr(self, "handle", None)
@@ -154,7 +159,9 @@ def varlen_attn_plan(*, num_q_heads: int, num_kv_heads: int, head_dim: int, page
     ws = ctypes.c_size_t()
     _check(lib().varlen_attn_plan(ctypes.byref(p), len(kv), _ptr32(qs), _ptr32(qe), _ptr32(kv), _ptr32(bt),
                                   ctypes.byref(h), ctypes.byref(ws)))
-    return Plan(h, ws.value, p)
+    live = qe > qs
+    return Plan(h, ws.value, p, num_reqs=len(kv), total_q_rows=int(qe[live].max()) if live.any() else 0,
+                kv_total=int(kv.astype(np.int64).sum()))
 
 
 def plan_for(w, flags: int = 0, **kw) -> Plan:
@@ -195,6 +202,41 @@ def _dev_ptr(t, name: str, dtype=None):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _need(t, name: str, shape):
+    """Raise unless tensor t has exactly ``shape`` (a dimension given as (n, None) needs at
+    least n)."""
+    got = tuple(t.shape)
+    ok = len(got) == len(shape)
+    if ok:
+        for g, want in zip(got, shape):
+            ok = ok and (g >= want[0] if isinstance(want, tuple) else g == want)
+    if not ok:
+        desc = ", ".join(f">={x[0]}" if isinstance(x, tuple) else str(x) for x in shape)
+        raise ValueError(f"{name} has shape {list(got)}, the plan needs [{desc}]")
+
+
+def _check_run_buffers(plan: "Plan", q, k_pool, v_pool, block_table_dev, out, workspace, k_scale=None,
+                       v_scale=None):
+    """Shapes of a run's buffers against the plan, checked on the host before any kernel
+    reads or writes them (the library itself checks pointers and the workspace size,
+    returning VA_ERR_WORKSPACE_TOO_SMALL)."""
+    p = plan.params
+    Hq, Hkv, D, ps, P = p.num_q_heads, p.num_kv_heads, p.head_dim, p.page_size, p.num_pages
+    for name, t in (("q", q), ("out", out)):
+        if t is not None:
+            _need(t, name, ((plan.total_q_rows, None), Hq, D))
+    if k_pool is not None:
+        _need(k_pool, "k_pool", (P, Hkv, ps, D))
+    if v_pool is not None:
+        _need(v_pool, "v_pool", (P, Hkv, D, ps))
+    for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+        if t is not None:
+            _need(t, name, (P, Hkv, ps))
+    if block_table_dev is not None and block_table_dev.numel() < plan.num_reqs * p.max_pages_per_req:
+        raise ValueError(f"block_table_dev has {block_table_dev.numel()} entries, the plan needs "
+                         f"{plan.num_reqs} x {p.max_pages_per_req}")
+
+
 def _stream_ptr(stream):
     import torch
     s = torch.cuda.current_stream() if stream is None else stream
@@ -216,6 +258,7 @@ def _pool_dtype(plan: Plan):
 def varlen_attn_run(plan: Plan, q, k_pool, v_pool, block_table_dev, out, workspace=None, stream=None) -> None:
     import torch
     dt = _elem_dtype(plan)
+    _check_run_buffers(plan, q, k_pool, v_pool, block_table_dev, out, workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().varlen_attn_run(plan.handle, _dev_ptr(q, "q", dt), _dev_ptr(k_pool, "k_pool", dt),
                                  _dev_ptr(v_pool, "v_pool", dt), _dev_ptr(block_table_dev, "block_table", torch.int32),
@@ -232,6 +275,7 @@ def varlen_attn_run_events(plan: Plan, q, k_pool, v_pool, block_table_dev, out, 
     import torch
     if len(events) != VA_RUN_EVENTS:
         raise ValueError(f"need {VA_RUN_EVENTS} events")
+    _check_run_buffers(plan, q, k_pool, v_pool, block_table_dev, out, workspace)
     s = torch.cuda.current_stream() if stream is None else stream
     handles = []
     for ev in events:
@@ -254,6 +298,7 @@ def varlen_attn_run_fp8(plan: Plan, q, k_pool, v_pool, k_scale, v_scale, block_t
     [num_pages, Hkv, page_size], q/out bf16.  ``events``: None or VA_RUN_EVENTS
     torch.cuda.Event(enable_timing=True) objects."""
     import torch
+    _check_run_buffers(plan, q, k_pool, v_pool, block_table_dev, out, workspace, k_scale, v_scale)
     s = torch.cuda.current_stream() if stream is None else stream
     arr = None
     if events is not None:
@@ -295,6 +340,10 @@ def varlen_attn_debug_stream_read(buf, sink, stream=None) -> None:
 def varlen_attn_debug_gather(plan: Plan, k_pool, v_pool, block_table_dev, k_out, v_out, stream=None) -> None:
     import torch
     dt = _pool_dtype(plan)
+    _check_run_buffers(plan, None, k_pool, v_pool, block_table_dev, None, None)
+    p = plan.params
+    for name, t in (("k_out", k_out), ("v_out", v_out)):
+        _need(t, name, (plan.kv_total, p.num_kv_heads, p.head_dim))
     _check(lib().varlen_attn_debug_gather(plan.handle, _dev_ptr(k_pool, "k_pool", dt), _dev_ptr(v_pool, "v_pool", dt),
                                           _dev_ptr(block_table_dev, "block_table", torch.int32),
                                           _dev_ptr(k_out, "k_out", dt), _dev_ptr(v_out, "v_out", dt),
@@ -320,6 +369,8 @@ def varlen_attn_append_kv(*, num_kv_heads: int, head_dim: int, page_size: int, n
     for name, t in (("k_new", k_new), ("v_new", v_new)):
         if tuple(t.shape) != (T, num_kv_heads, head_dim):
             raise ValueError(f"{name} must be [{T}, {num_kv_heads}, {head_dim}]")
+    _need(k_pool, "k_pool", (num_pages, num_kv_heads, page_size, head_dim))
+    _need(v_pool, "v_pool", (num_pages, num_kv_heads, head_dim, page_size))
     _check(lib().varlen_attn_append_kv(ctypes.byref(p), T, _dev_ptr(k_new, "k_new", dt), _dev_ptr(v_new, "v_new", dt),
                                        _dev_ptr(out_cache_loc, "out_cache_loc", torch.int64),
                                        _dev_ptr(k_pool, "k_pool", dt), _dev_ptr(v_pool, "v_pool", dt),
@@ -337,6 +388,10 @@ def varlen_attn_append_kv_fp8(*, num_kv_heads: int, head_dim: int, page_size: in
     for name, t in (("k_new", k_new), ("v_new", v_new)):
         if tuple(t.shape) != (T, num_kv_heads, head_dim):
             raise ValueError(f"{name} must be [{T}, {num_kv_heads}, {head_dim}]")
+    _need(k_pool, "k_pool", (num_pages, num_kv_heads, page_size, head_dim))
+    _need(v_pool, "v_pool", (num_pages, num_kv_heads, head_dim, page_size))
+    for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+        _need(t, name, (num_pages, num_kv_heads, page_size))
     _check(lib().varlen_attn_append_kv_fp8(
         ctypes.byref(p), T, _dev_ptr(k_new, "k_new", torch.bfloat16), _dev_ptr(v_new, "v_new", torch.bfloat16),
         _dev_ptr(out_cache_loc, "out_cache_loc", torch.int64), _dev_ptr(k_pool, "k_pool", torch.uint8),
@@ -401,6 +456,8 @@ class RunCall:
         import torch
         dt, pdt = _elem_dtype(plan), _pool_dtype(plan)
         self._fp8 = plan.params.dtype == VA_DTYPE_FP8_E4M3
+        _check_run_buffers(plan, q, k_pool, v_pool, block_table_dev, out, workspace,
+                           k_scale if self._fp8 else None, v_scale if self._fp8 else None)
         self._s = torch.cuda.current_stream() if stream is None else stream
         scales = ()
         if self._fp8:

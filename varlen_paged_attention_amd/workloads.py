@@ -133,6 +133,10 @@ class Workload:
     k_scale: Optional[np.ndarray] = None   # fp8 only: float32 [P, Hkv, ps], one per K row
     v_scale: Optional[np.ndarray] = None   # fp8 only: float32 [P, Hkv, ps], one per V column
     notes: dict = field(default_factory=dict)
+    # hashed pools only: elements overwritten after the hash (see ``focus``): int64 rows
+    # (pool, page, kv_head, slot, d) with pool STREAM_K or STREAM_V, and their float values
+    marks: Optional[np.ndarray] = None
+    mark_values: Optional[np.ndarray] = None
 
     @property
     def num_reqs(self) -> int:
@@ -274,18 +278,40 @@ def _page_elems(w: "Workload") -> int:
     return w.num_kv_heads * w.page_size * w.head_dim
 
 
-def hashed_pages_host(w: "Workload", pages, stream: int) -> np.ndarray:
+def hashed_pages_host(w: "Workload", pages, stream: int, kv_heads=None) -> np.ndarray:
     """bf16 bits (uint16) of the given physical pages of pool ``stream`` (STREAM_K or
     STREAM_V) of a hashed workload: [len(pages), Hkv, ps, D] for K, [len(pages), Hkv, D, ps]
-    for V."""
-    key = _pool_key(w.seed, stream)
-    pk = _lowbias32(np.asarray(pages, np.int64)[:, None] ^ key)
-    u = _lowbias32(np.arange(_page_elems(w), dtype=np.int64)[None, :] ^ pk)
-    vals = ((u & 0xFF) + ((u >> 8) & 0xFF) - 255).astype(np.float32) / np.float32(128.0)
-    bits = np.empty(vals.shape, np.uint16)
-    f32_to_bf16_bits(np.ascontiguousarray(vals), bits)
+    for V, with the workload's marks applied.  ``kv_heads``: hash only these KV heads (the
+    others are left 0)."""
     H, ps, D = w.num_kv_heads, w.page_size, w.head_dim
-    return bits.reshape((len(pages), H, ps, D) if stream == STREAM_K else (len(pages), H, D, ps))
+    pages = np.asarray(pages, np.int64)
+    per_head = ps * D
+    heads = range(H) if kv_heads is None else sorted(set(int(x) for x in kv_heads))
+    key = _pool_key(w.seed, stream)
+    pk = _lowbias32(pages[:, None] ^ key)
+    bits = np.zeros((len(pages), H * per_head), np.uint16)
+    for h in heads:
+        e = np.arange(h * per_head, (h + 1) * per_head, dtype=np.int64)[None, :]
+        u = _lowbias32(e ^ pk)
+        vals = ((u & 0xFF) + ((u >> 8) & 0xFF) - 255).astype(np.float32) / np.float32(128.0)
+        f32_to_bf16_bits(np.ascontiguousarray(vals), bits[:, h * per_head:(h + 1) * per_head])
+    out = bits.reshape((len(pages), H, ps, D) if stream == STREAM_K else (len(pages), H, D, ps))
+    if w.marks is not None and len(w.marks):
+        sel = w.marks[:, 0] == stream
+        mk, mv = w.marks[sel], w.mark_values[sel]
+        where = {int(p): i for i, p in enumerate(pages)}
+        vb = np.empty(len(mv), np.uint16)
+        f32_to_bf16_bits(np.ascontiguousarray(mv, np.float32), vb)
+        hs = set(heads)
+        for (_, page, kvh, slot, d), b in zip(mk, vb):
+            i = where.get(int(page))
+            if i is None or int(kvh) not in hs:
+                continue
+            if stream == STREAM_K:
+                out[i, kvh, slot, d] = b
+            else:
+                out[i, kvh, d, slot] = b
+    return out
 
 
 def hashed_pools_device(w: "Workload", device="cuda", pages_per_chunk: int = 4096):
@@ -305,16 +331,181 @@ def hashed_pools_device(w: "Workload", device="cuda", pages_per_chunk: int = 409
             u = _lowbias32(elems ^ pk)
             flat[p0:p1] = (((u & 0xFF) + ((u >> 8) & 0xFF) - 255).to(torch.float32) / 128.0).to(torch.bfloat16)
             del pk, u
+        if w.marks is not None and len(w.marks):
+            sel = w.marks[:, 0] == stream
+            if sel.any():
+                mk = torch.from_numpy(w.marks[sel]).to(device)
+                mv = torch.from_numpy(np.ascontiguousarray(w.mark_values[sel], np.float32)).to(device)
+                idx = (mk[:, 1], mk[:, 2], mk[:, 3], mk[:, 4]) if stream == STREAM_K else \
+                      (mk[:, 1], mk[:, 2], mk[:, 4], mk[:, 3])
+                pool.index_put_(idx, mv.to(torch.bfloat16))
         out.append(pool)
     return out[0], out[1]
 
 
-def host_kv_pages(w: "Workload", pages):
-    """(K, V) host values of the given physical pages, for any workload."""
+def host_kv_pages(w: "Workload", pages, kv_heads=None):
+    """(K, V) host values of the given physical pages, for any workload (hashed pools: only
+    the KV heads in ``kv_heads`` are filled when it is given)."""
     pages = np.asarray(pages, np.int64)
     if w.hashed_kv:
-        return hashed_pages_host(w, pages, STREAM_K), hashed_pages_host(w, pages, STREAM_V)
+        return (hashed_pages_host(w, pages, STREAM_K, kv_heads), hashed_pages_host(w, pages, STREAM_V, kv_heads))
     return w.k_pool[pages], w.v_pool[pages]
+
+
+def subset(w: Workload, reqs: Sequence[int], name: Optional[str] = None) -> Workload:
+    """The iteration made of requests ``reqs`` of ``w`` only: their Q rows laid back to back,
+    their block-table rows and lengths, the same pools (shared, not copied)."""
+    import copy
+    reqs = [int(r) for r in reqs]
+    out = copy.copy(w)
+    out.name = name or f"{w.name}[{len(reqs)} requests]"
+    rows = [np.arange(int(w.q_start[r]), int(w.q_end[r])) for r in reqs]
+    m = np.array([len(x) for x in rows], np.int64)
+    out.q = w.q[np.concatenate(rows)] if rows else w.q[:0]
+    out.q_start = np.concatenate([[0], np.cumsum(m)[:-1]]).astype(np.int32)
+    out.q_end = (out.q_start + m).astype(np.int32)
+    out.kv_len = w.kv_len[reqs].copy()
+    out.block_table = w.block_table[reqs].copy()
+    out.notes = dict(w.notes)
+    out.notes.pop("hot", None)
+    return out
+
+
+STREAM_FOCUS = 5
+
+
+def _dequant_fp8(codes: np.ndarray, scale: np.ndarray, axis: int) -> np.ndarray:
+    """float32 values of e4m3fn codes times their per-vector scales (torch's decoding)."""
+    import torch
+    x = torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    return x * np.expand_dims(scale, axis)
+
+
+def focus(w: Workload, hot: int = 8, peak: float = 16.0, q_rest: float = 0.25, v_mark: float = 4.0) -> Workload:
+    """A companion input to ``w`` on which every (request, query head) attends mostly to a
+    few keys spread over its whole context, so that outputs stay O(1) at any kv length and
+    a lost, doubled or misplaced key range changes them by much more than the bf16
+    tolerance (with N(0,1) inputs an output row averages thousands of keys and shrinks
+    like 1/sqrt(kv_len)).
+
+    Query head h = kvh * g + c has colour c and marker dimension d_c = (c * D // g) % D.
+    Each request's context [0, kv_len) is cut into hot * g equal segments; segment
+    k * g + c holds one hot key of colour c at a seeded position.  A hot key's K element
+    d_c becomes ``peak`` and its V element d_c becomes +v_mark or -v_mark (alternating
+    with k); every Q row of head h is scaled by ``q_rest`` (a power of two: exact) and its
+    element d_c set to ``peak``.  A hot key then scores about peak^2 / sqrt(D) above the
+    others, so the softmax weight of the context sits on the visible hot keys.  Keys in
+    pages shared by every request (``shared_prefix_pages``) are chosen the same for all of
+    them.  Only element values change: shapes, pages, tables and lengths are ``w``'s.
+    fp8 workloads re-quantise the vectors that hold a marked element; hashed pools keep the
+    marks in ``marks`` / ``mark_values`` (applied on the device and by host_kv_pages).
+    The hot positions are in ``notes["hot"][(r, kvh, c)]``.
+    """
+    import copy
+    R, Hq, Hkv, D, ps = w.num_reqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size
+    g = Hq // Hkv
+    out = copy.copy(w)
+    out.notes = dict(w.notes)
+    out.name = w.name + "/focus"
+    shared_len = w.shared_prefix_pages * ps
+    if shared_len:
+        assert len(set(int(x) for x in w.kv_len)) == 1, "shared prefix with unequal lengths"
+    dcol = [(c * D // g) % D for c in range(g)]
+    hot_pos = {}
+    k_marks, v_marks, v_vals = [], [], []
+    for r in range(R):
+        if int(w.q_end[r]) == int(w.q_start[r]):
+            continue
+        L = int(w.kv_len[r])
+        nseg = hot * g
+        for kvh in range(Hkv):
+            for c in range(g):
+                pos = []
+                for k in range(hot):
+                    seg = k * g + c
+                    lo, hi = seg * L // nseg, (seg + 1) * L // nseg
+                    if hi <= lo:
+                        continue
+                    if lo < shared_len:
+                        hi = min(hi, shared_len)
+                        rng = np.random.default_rng(np.random.SeedSequence([w.seed, STREAM_FOCUS, kvh, c, seg]))
+                    else:
+                        rng = np.random.default_rng(np.random.SeedSequence([w.seed, STREAM_FOCUS, kvh, c, seg, r + 1]))
+                    j = int(rng.integers(lo, hi))
+                    pos.append(j)
+                    page, slot = int(w.block_table[r, j // ps]), j % ps
+                    k_marks.append((page, kvh, slot, dcol[c]))
+                    v_marks.append((page, kvh, slot, dcol[c]))
+                    v_vals.append(v_mark if k % 2 == 0 else -v_mark)
+                hot_pos[(r, kvh, c)] = np.asarray(pos, np.int64)
+    out.notes["hot"] = hot_pos
+    out.notes["focus"] = dict(hot=hot, peak=peak, q_rest=q_rest, v_mark=v_mark, dcol=dcol)
+    km = np.asarray(k_marks, np.int64).reshape(-1, 4)
+    vm = np.asarray(v_marks, np.int64).reshape(-1, 4)
+    vv = np.asarray(v_vals, np.float32)
+    # Q: every row scaled by q_rest, the marker element of each head set to peak
+    if w.q.dtype == np.uint16:
+        qf = (w.q.astype(np.uint32) << 16).view(np.float32) * np.float32(q_rest)
+    else:
+        qf = w.q.astype(np.float32) * np.float32(q_rest)
+    for h in range(Hq):
+        qf[:, h, dcol[h % g]] = peak
+    if w.q.dtype == np.uint16:
+        out.q = np.empty(w.q.shape, np.uint16)
+        f32_to_bf16_bits(np.ascontiguousarray(qf), out.q)
+    else:
+        out.q = qf.astype(w.q.dtype)
+    if w.hashed_kv:
+        rows = [np.column_stack([np.full(len(km), STREAM_K), km]), np.column_stack([np.full(len(vm), STREAM_V), vm])]
+        vals = [np.full(len(km), peak, np.float32), vv]
+        if w.marks is not None:
+            rows.insert(0, w.marks)
+            vals.insert(0, w.mark_values)
+        out.marks = np.concatenate(rows).astype(np.int64)
+        out.mark_values = np.concatenate(vals).astype(np.float32)
+        return out
+    if w.dtype == "fp8":
+        k_codes, v_codes = w.k_pool.copy(), w.v_pool.copy()
+        k_scale, v_scale = w.k_scale.copy(), w.v_scale.copy()
+        # K rows (page, kvh, slot, :) and V columns (page, kvh, :, slot) holding a mark
+        for marks, vals, is_k in ((km, np.full(len(km), peak, np.float32), True), (vm, vv, False)):
+            if not len(marks):
+                continue
+            vec = {}
+            for (page, kvh, slot, d), val in zip(marks, vals):
+                vec.setdefault((int(page), int(kvh), int(slot)), []).append((int(d), float(val)))
+            keys = list(vec)
+            p_, h_, s_ = (np.asarray(x, np.int64) for x in zip(*keys))
+            if is_k:
+                x = _dequant_fp8(k_codes[p_, h_, s_, :], k_scale[p_, h_, s_], 1)
+            else:
+                x = _dequant_fp8(v_codes[p_, h_, :, s_], v_scale[p_, h_, s_], 1)
+            for i, key in enumerate(keys):
+                for d, val in vec[key]:
+                    x[i, d] = val
+            codes, sc = quantize_fp8(x.astype(np.float32), axis=1)
+            if is_k:
+                k_codes[p_, h_, s_, :] = codes
+                k_scale[p_, h_, s_] = sc
+            else:
+                v_codes[p_, h_, :, s_] = codes
+                v_scale[p_, h_, s_] = sc
+        out.k_pool, out.v_pool, out.k_scale, out.v_scale = k_codes, v_codes, k_scale, v_scale
+        return out
+    k, v = w.k_pool.copy(), w.v_pool.copy()
+    if w.dtype == "bf16":
+        kb = np.empty(1, np.uint16)
+        f32_to_bf16_bits(np.array([peak], np.float32), kb)
+        vb = np.empty(len(vv), np.uint16)
+        f32_to_bf16_bits(np.ascontiguousarray(vv), vb)
+        kval, vval = kb[0], vb
+    else:
+        kval, vval = np.float32(peak), vv
+    if len(km):
+        k[km[:, 0], km[:, 1], km[:, 2], km[:, 3]] = kval
+        v[vm[:, 0], vm[:, 1], vm[:, 3], vm[:, 2]] = vval
+    out.k_pool, out.v_pool = k, v
+    return out
 
 
 def uniform_lengths(seed: int, n: int, lo: int, hi: int) -> np.ndarray:

@@ -187,6 +187,23 @@ va_status varlen_attn_run_fp8(const va_plan* plan, const void* q, const void* k_
  *   kernel), events[2] after the split-KV kernel (before combine), events[3] at the end.
  * A stage with no work leaves two consecutive events adjacent.  The events are created
  * by the caller (with timing enabled) and are only recorded here. */
+/* varlen_attn_run without a workspace argument, for callers that cannot allocate device
+ * memory (code under stream capture, tight serving loops, harnesses that forbid
+ * allocation): the library's own static scratch of VA_STATIC_SCRATCH_BYTES on each device
+ * (a file-scope device array held from the library's load until the process ends) is the
+ * workspace.  Nothing is allocated: no hipMalloc or other allocating call.  The caller
+ * still owns q, k_pool, v_pool, block_table_dev and out (as in varlen_attn_run).  A plan
+ * whose workspace exceeds VA_STATIC_SCRATCH_BYTES is refused with
+ * VA_ERR_WORKSPACE_TOO_SMALL; fp8 plans are refused (use varlen_attn_run_fp8).  Every call
+ * on one device shares that device's scratch, which keeps the last call's contents (every
+ * partial result is written before it is read, so nothing needs clearing): calls that
+ * overlap on one device -- on different streams, or on one stream while another thread
+ * enqueues -- race on it and must be serialised by the caller.  The device address of the
+ * scratch is looked up on the first call on each device (with that device current). */
+#define VA_STATIC_SCRATCH_BYTES (64u << 20)
+va_status varlen_attn_run_noalloc(const va_plan* plan, const void* q, const void* k_pool, const void* v_pool,
+                                  const int32_t* block_table_dev, void* out, void* stream);
+
 #define VA_RUN_EVENTS 4
 va_status varlen_attn_run_events(const va_plan* plan, const void* q, const void* k_pool,
                                  const void* v_pool, const int32_t* block_table_dev, void* out,

@@ -24,7 +24,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvarlen_a
 EXPORTED = ["varlen_attn_plan", "varlen_attn_run", "varlen_attn_run_events", "varlen_attn_plan_stats", "varlen_attn_plan_export",
             "varlen_attn_debug_gather", "varlen_attn_plan_destroy", "varlen_attn_status_string",
             "varlen_attn_last_error", "varlen_attn_append_kv", "varlen_attn_plan_slots", "varlen_attn_run_fp8",
-            "varlen_attn_debug_fp8_to_bf16", "varlen_attn_append_kv_fp8", "varlen_attn_debug_stream_read"]
+            "varlen_attn_debug_fp8_to_bf16", "varlen_attn_append_kv_fp8", "varlen_attn_debug_stream_read",
+            "varlen_attn_run_noalloc"]
+VA_STATIC_SCRATCH_BYTES = 64 << 20
 
 
 class VaParams(ctypes.Structure):
@@ -79,6 +81,8 @@ def lib():
         L.varlen_attn_plan.restype = ctypes.c_int
         L.varlen_attn_run.argtypes = [P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.varlen_attn_run.restype = ctypes.c_int
+        L.varlen_attn_run_noalloc.argtypes = [P, P, P, P, P, P, P]
+        L.varlen_attn_run_noalloc.restype = ctypes.c_int
         L.varlen_attn_run_events.argtypes = [P, P, P, P, P, P, P, ctypes.c_size_t, P, ctypes.POINTER(P)]
         L.varlen_attn_run_events.restype = ctypes.c_int
         L.varlen_attn_run_fp8.argtypes = [P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P, ctypes.POINTER(P)]
@@ -264,6 +268,19 @@ def varlen_attn_run(plan: Plan, q, k_pool, v_pool, block_table_dev, out, workspa
                                  _dev_ptr(v_pool, "v_pool", dt), _dev_ptr(block_table_dev, "block_table", torch.int32),
                                  _dev_ptr(out, "out", dt), _dev_ptr(workspace, "workspace"), ws_bytes,
                                  _stream_ptr(stream)))
+
+
+def varlen_attn_run_noalloc(plan: Plan, q, k_pool, v_pool, block_table_dev, out, stream=None) -> None:
+    """varlen_attn_run with the library's static device scratch as the workspace (nothing is
+    allocated; plans needing more than VA_STATIC_SCRATCH_BYTES are refused; calls that
+    overlap on one device race on the scratch)."""
+    import torch
+    dt = _elem_dtype(plan)
+    _check_run_buffers(plan, q, k_pool, v_pool, block_table_dev, out, None)
+    _check(lib().varlen_attn_run_noalloc(plan.handle, _dev_ptr(q, "q", dt), _dev_ptr(k_pool, "k_pool", dt),
+                                         _dev_ptr(v_pool, "v_pool", dt),
+                                         _dev_ptr(block_table_dev, "block_table", torch.int32),
+                                         _dev_ptr(out, "out", dt), _stream_ptr(stream)))
 
 
 VA_RUN_EVENTS = 4

@@ -14,8 +14,10 @@
 // exponentiated with v_exp_f32, so the running max m is in those units too.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -1193,6 +1195,59 @@ extern "C" va_status varlen_attn_run_fp8(const va_plan* plan, const void* q, con
       if (!events[i]) return fail(VA_ERR_INVALID_ARG, "events[" + std::to_string(i) + "] is NULL");
   return run_impl(plan, q, k_pool, v_pool, k_scale, v_scale, block_table_dev, out, workspace, workspace_bytes, stream,
                   events);
+}
+
+// ------------------------------------------------------------- static scratch --
+// The workspace of varlen_attn_run_noalloc: a file-scope device array (every GPU the
+// library runs on holds its own copy until the process ends).  In host code `scratch` names
+// a host-side stand-in, not device memory: its device address is looked up once per device
+// with hipGetSymbolAddress and only that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[VA_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_dev[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on device `dev` (the current device), looked up on the first
+// call for that device.
+va_status static_scratch(int dev, void** ptr) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(VA_ERR_UNSUPPORTED, "device ordinal beyond the static scratch table");
+  void* p = g_scratch_dev[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_dev[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !p) return hip_fail("hipGetSymbolAddress(static scratch)", e);
+      g_scratch_dev[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return VA_OK;
+}
+}  // namespace
+
+extern "C" va_status varlen_attn_run_noalloc(const va_plan* plan, const void* q, const void* k_pool,
+                                             const void* v_pool, const int32_t* block_table_dev, void* out,
+                                             void* stream) {
+  if (!plan) return fail(VA_ERR_INVALID_ARG, "plan is NULL");
+  if (plan->p.dtype == VA_DTYPE_FP8_E4M3)
+    return fail(VA_ERR_INVALID_ARG, "an fp8 plan runs with varlen_attn_run_fp8 (it needs the scale pools)");
+  if (plan->ws_bytes > VA_STATIC_SCRATCH_BYTES)
+    return fail(VA_ERR_WORKSPACE_TOO_SMALL, "plan needs " + std::to_string(plan->ws_bytes) +
+                                                " bytes of workspace, the static scratch holds " +
+                                                std::to_string(size_t(VA_STATIC_SCRATCH_BYTES)) +
+                                                ": run it with varlen_attn_run and a workspace");
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+  void* ws = nullptr;
+  if (plan->ws_bytes) {
+    if (va_status st = static_scratch(dev, &ws); st != VA_OK) return st;
+  }
+  return run_impl(plan, q, k_pool, v_pool, nullptr, nullptr, block_table_dev, out, ws, plan->ws_bytes, stream,
+                  nullptr);
 }
 
 extern "C" va_status varlen_attn_run_events(const va_plan* plan, const void* q, const void* k_pool,

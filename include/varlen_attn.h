@@ -224,7 +224,8 @@ va_status varlen_attn_run_events(const va_plan* plan, const void* q, const void*
  *   bad_loc_count: optional device int32 (NULL: not reported); every token whose loc is
  *                  >= num_pages * page_size is skipped and counted here (atomically added,
  *                  the caller zeroes it)
- * Values are copied bit for bit.  Enqueue only (no allocation, no synchronisation); two
+ * Values are copied bit for bit.  k_new, v_new, k_pool and v_pool must be 16-byte aligned
+ * (VA_ERR_INVALID_ARG otherwise).  Enqueue only (no allocation, no synchronisation); two
  * tokens naming the same slot leave one of them, unspecified which. */
 va_status varlen_attn_append_kv(const va_params* params, int64_t num_tokens, const void* k_new,
                                 const void* v_new, const int64_t* out_cache_loc, void* k_pool,
@@ -237,8 +238,9 @@ va_status varlen_attn_append_kv(const va_params* params, int64_t num_tokens, con
  * to the nearest e4m3fn value, ties to even ("GLM-5.3 推理全链路(八)", on the costs outside
  * the 656-byte ledger: each token's FP8 data carries FP32 scales).  The codes go to
  * k_pool / v_pool and the scales to k_scale / v_scale ([num_pages][num_kv_heads][page_size])
- * at the token's out_cache_loc; padding, out-of-range entries and bad_loc_count behave as
- * in varlen_attn_append_kv.  Enqueue only. */
+ * at the token's out_cache_loc; padding, out-of-range entries, bad_loc_count and the
+ * 16-byte alignment of k_new, v_new and the code pools are as in varlen_attn_append_kv.
+ * Enqueue only. */
 va_status varlen_attn_append_kv_fp8(const va_params* params, int64_t num_tokens, const void* k_new,
                                     const void* v_new, const int64_t* out_cache_loc, void* k_pool, void* v_pool,
                                     float* k_scale, float* v_scale, int32_t* bad_loc_count, void* stream);

@@ -279,14 +279,24 @@ def _f32(bits):
     return (bits.astype(np.uint32) << 16).view(np.float32)
 
 
+APPEND_LAYOUTS = {
+    # new rows starting mid-page: every V column written byte by byte
+    "mid-page": ([37, 1, 5, 0, 200], [90, 300, 5, 10, 200]),
+    # an uncached prefill first: its tokens fill whole pages from slot 0 (16-byte V stores)
+    "page-aligned": ([200, 37, 1, 5, 0], [200, 90, 300, 5, 10]),
+}
+
+
+@pytest.mark.parametrize("layout", list(APPEND_LAYOUTS))
 @pytest.mark.parametrize("d,ps", [(128, 16), (64, 64), (128, 256)])
-def test_fp8_append_bit_exact(d, ps):
+def test_fp8_append_bit_exact(d, ps, layout):
     """GPU quantise-and-append == the oracle's, bit for bit (codes and scales), with
     padding, an out-of-range entry (skipped and counted) and untouched slots kept."""
     import torch
-    w = W.build("ap8", [37, 1, 5, 0, 200], [90, 300, 5, 10, 200], num_q_heads=8, num_kv_heads=4, head_dim=d,
+    q_rows, kv = APPEND_LAYOUTS[layout]
+    w = W.build("ap8", q_rows, kv, num_q_heads=8, num_kv_heads=4, head_dim=d,
                 page_size=ps, dtype="fp8", seed=29, extra_pages=3)
-    _say(f"[gpu] fp8 append d={d} ps={ps}")
+    _say(f"[gpu] fp8 append d={d} ps={ps} {layout}")
     plan = api.plan_for(w, flags=api.VA_FLAG_HOST_ONLY)
     loc = api.varlen_attn_plan_slots(plan)
     loc[3] = -1
@@ -306,6 +316,56 @@ def test_fp8_append_bit_exact(d, ps):
                                   v_scale=vs, bad_loc_count=bad)
     torch.cuda.synchronize()
     assert int(bad.item()) == 1
+    for got, exp, name in zip((kp, vp, ks, vs), want, ("k codes", "v codes", "k scales", "v scales")):
+        g = got.cpu().numpy()
+        assert np.array_equal(g.view(np.uint8), np.ascontiguousarray(exp).view(np.uint8)), name
+
+
+def _bf16_exact(a):
+    """float32 values rounded to bf16 (nearest even), as float32."""
+    bits = np.empty(a.shape, np.uint16)
+    W.f32_to_bf16_bits(np.ascontiguousarray(a, np.float32), bits)
+    return _f32(bits)
+
+
+def test_fp8_append_every_bf16_magnitude_bit_exact():
+    """Every finite bf16 magnitude (random signs) quantised in rows whose maximum is one of
+    sixteen values from a bf16 subnormal to 3e38: the appended codes and scales equal the
+    oracle's bit for bit (the kernel's quotient through the reciprocal, with its exact
+    fallback near e4m3fn rounding midpoints, against the float32 division)."""
+    import torch
+    rng = np.random.default_rng(41)
+    vals = (np.arange(0, 0x7F80, dtype=np.uint32) << 16).view(np.float32)
+    amaxes = _bf16_exact(np.array([448.0, 1.0, 3.0, 0.1, 100.0, 1e-3, 7.875, 6e4, 3e38, 1e-30, 2e-38, 1e-39,
+                                   0.3333, 12345.0, 5e-5, 1.5e10], np.float32))
+    rows = []
+    for a in amaxes:
+        xs = vals[vals <= a] * rng.choice(np.float32([-1, 1]), int((vals <= a).sum()))
+        rng.shuffle(xs)
+        n = -(-len(xs) // 127)
+        xs = np.concatenate([xs, np.zeros(n * 127 - len(xs), np.float32)]).reshape(n, 127)
+        rows.append(np.concatenate([np.full((n, 1), a, np.float32), xs], 1))
+    K = np.concatenate(rows)
+    V = K[rng.permutation(len(K))][:, rng.permutation(128)]
+    T, ps, D = len(K), 16, 128
+    P = -(-T // ps)
+    _say(f"[gpu] fp8 append of every bf16 magnitude: {T} rows x {D}")
+    want = oracle.append_kv_fp8(np.zeros((P, 1, ps, D), np.uint8), np.zeros((P, 1, D, ps), np.uint8),
+                                np.zeros((P, 1, ps), np.float32), np.zeros((P, 1, ps), np.float32),
+                                K[:, None, :], V[:, None, :], np.arange(T), ps)
+    kb, vb = np.empty(K.shape, np.uint16), np.empty(V.shape, np.uint16)
+    W.f32_to_bf16_bits(K, kb)
+    W.f32_to_bf16_bits(V, vb)
+    kp = torch.zeros((P, 1, ps, D), dtype=torch.uint8, device="cuda")
+    vp = torch.zeros((P, 1, D, ps), dtype=torch.uint8, device="cuda")
+    ks = torch.zeros((P, 1, ps), dtype=torch.float32, device="cuda")
+    vs = torch.zeros_like(ks)
+    api.varlen_attn_append_kv_fp8(num_kv_heads=1, head_dim=D, page_size=ps, num_pages=P,
+                                  k_new=torch.from_numpy(kb[:, None, :].copy()).view(torch.bfloat16).cuda(),
+                                  v_new=torch.from_numpy(vb[:, None, :].copy()).view(torch.bfloat16).cuda(),
+                                  out_cache_loc=torch.arange(T, dtype=torch.int64, device="cuda"), k_pool=kp,
+                                  v_pool=vp, k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
     for got, exp, name in zip((kp, vp, ks, vs), want, ("k codes", "v codes", "k scales", "v scales")):
         g = got.cpu().numpy()
         assert np.array_equal(g.view(np.uint8), np.ascontiguousarray(exp).view(np.uint8)), name

@@ -337,13 +337,23 @@ def _raw(t):
     return t.view(torch.int16).cpu().numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.cpu().numpy()
 
 
-@pytest.mark.parametrize("dtype,d,ps", [("bf16", 128, 16), ("bf16", 64, 64), ("f32", 128, 32)])
-def test_append_bit_exact(dtype, d, ps):
+APPEND_LAYOUTS = {
+    # new rows starting mid-page: every V column written element by element
+    "mid-page": ([37, 1, 5, 0, 200], [90, 300, 5, 10, 200]),
+    # an uncached prefill first: its tokens fill whole pages from slot 0 (16-byte V stores)
+    "page-aligned": ([200, 37, 1, 5, 0], [200, 90, 300, 5, 10]),
+}
+
+
+@pytest.mark.parametrize("layout", list(APPEND_LAYOUTS))
+@pytest.mark.parametrize("dtype,d,ps", [("bf16", 128, 16), ("bf16", 64, 64), ("f32", 128, 32), ("bf16", 128, 256)])
+def test_append_bit_exact(dtype, d, ps, layout):
     """GPU append == oracle append, bit for bit, with padding (-1) and random new values."""
     import torch
-    w = W.build("ap", [37, 1, 5, 0, 200], [90, 300, 5, 10, 200], num_q_heads=8, num_kv_heads=4, head_dim=d,
+    q_rows, kv = APPEND_LAYOUTS[layout]
+    w = W.build("ap", q_rows, kv, num_q_heads=8, num_kv_heads=4, head_dim=d,
                 page_size=ps, dtype=dtype, seed=23, extra_pages=3)
-    _say(f"[gpu] append {dtype} d={d} ps={ps}")
+    _say(f"[gpu] append {dtype} d={d} ps={ps} {layout}")
     plan = api.plan_for(w, flags=api.VA_FLAG_HOST_ONLY)
     loc = api.varlen_attn_plan_slots(plan)
     rng = np.random.default_rng(5)
@@ -411,4 +421,5 @@ def test_append_then_attend(cid, scale):
     api.varlen_attn_run(plan, q, kp, vp, bt, out, api.new_workspace(plan))
     torch.cuda.synchronize()
     assert np.array_equal(_raw(kp).view(np.uint8), np.ascontiguousarray(w.k_pool).view(np.uint8))
+    assert np.array_equal(_raw(vp).view(np.uint8), np.ascontiguousarray(w.v_pool).view(np.uint8))
     _check_full(w, out, f"append+attend {cid}/{scale}")

@@ -11,58 +11,101 @@
 
 namespace va {
 
-// One workgroup per (KV head, tpw <= 64 consecutive tokens; fewer when there are few tokens,
-// so the launch still has about a thousand workgroups).  K rows are copied with 16-byte
-// loads and stores (consecutive threads -> consecutive chunks of a row).  V rows are read
-// the same way into LDS, then written element by element with the token index fastest
-// across lanes, so the writes of tokens that fill consecutive slots of a page land on
-// consecutive addresses.
-constexpr int kAppendTok = 64;
+// One workgroup per (KV head, tpw <= 16 consecutive tokens; fewer when there are few tokens,
+// so the launch still has about a thousand workgroups; 16 measured faster than 64 -- 36 vs
+// 42 us for the ORCA iteration's 4098 rows -- as more workgroups keep more rows in flight).  Every thread first issues its K and
+// V row loads (16-byte chunks, consecutive threads -> consecutive chunks of a row); threads
+// 0..tpw-1 turn their token's out_cache_loc into the offsets of its K row and of its V
+// column (page_size is a power of two: shifts and masks).  K rows are stored straight from
+// registers.  V rows go through LDS and are written into the transposed pages E = 16 /
+// sizeof(T) tokens at a time -- one 16-byte store per d row -- where those E tokens fill E
+// consecutive slots of one page starting at a multiple of E (a prefill's tokens do), else
+// one element per token.
+constexpr int kAppendTok = 16;
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void append_kv_kernel(const T* __restrict__ k_new, const T* __restrict__ v_new,
-                                                        const int64_t* __restrict__ loc, int64_t ntok, int tpw_log2, int Hkv,
-                                                        int ps, int64_t nslots, T* __restrict__ k_pool,
+                                                        const int64_t* __restrict__ loc, int64_t ntok, int tpw_log2,
+                                                        int Hkv, int ps_shift, int64_t nslots, T* __restrict__ k_pool,
                                                         T* __restrict__ v_pool, int32_t* __restrict__ bad) {
-  constexpr int E = 16 / sizeof(T);                 // elements per 16-byte chunk
+  constexpr int E = 16 / sizeof(T);                 // elements per 16-byte chunk; tokens per V store
   constexpr int CH = D / E;                         // chunks per row
   constexpr int ROW = D + E;                        // padded LDS row (elements)
+  constexpr int NCH = kAppendTok * CH;              // chunks of a full workgroup
+  constexpr int NC = (NCH + 255) / 256;             // chunks per thread
+  constexpr int NG = kAppendTok / E;                // token groups of a full workgroup
   __shared__ __attribute__((aligned(16))) T tile[kAppendTok * ROW];
-  __shared__ int64_t tloc[kAppendTok];
+  __shared__ int64_t kdst[kAppendTok];              // element offset of the token's K row (-1: none)
+  __shared__ int64_t vdst[kAppendTok];              // element offset of V[page][kvh][0][slot] (-1: none)
+  __shared__ int32_t vrun[NG];                      // group stored with one 16-byte store per d row
   const int kvh = blockIdx.y;
   const int tpw = 1 << tpw_log2;
   const int64_t t0 = int64_t(blockIdx.x) << tpw_log2;
   const int n = int(min<int64_t>(tpw, ntok - t0));
   const int tid = threadIdx.x;
+  int4 kr[NC], vr[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = tid + 256 * i, tt = c / CH, ch = c % CH;
+    if (c < NCH && tt < n) {
+      const size_t src = size_t((t0 + tt) * Hkv + kvh) * D + ch * E;
+      kr[i] = *reinterpret_cast<const int4*>(k_new + src);
+      vr[i] = *reinterpret_cast<const int4*>(v_new + src);
+    }
+  }
   if (tid < kAppendTok) {
     int64_t l = tid < n ? loc[t0 + tid] : -1;
     if (l >= nslots) {
       if (bad && kvh == 0) atomicAdd(bad, 1);
       l = -1;
     }
-    tloc[tid] = l;
+    const int64_t ph = (l >> ps_shift) * Hkv + kvh;               // page * Hkv + kvh
+    const int64_t slot = l & ((int64_t(1) << ps_shift) - 1);
+    kdst[tid] = l < 0 ? -1 : ((ph << ps_shift) + slot) * D;
+    vdst[tid] = l < 0 ? -1 : ((ph * D) << ps_shift) + slot;
   }
-  for (int c = tid; c < n * CH; c += blockDim.x) {
-    const int tt = c / CH, ch = c % CH;
-    const size_t src = size_t((t0 + tt) * Hkv + kvh) * D + ch * E;
-    *reinterpret_cast<int4*>(tile + tt * ROW + ch * E) = *reinterpret_cast<const int4*>(v_new + src);
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = tid + 256 * i, tt = c / CH, ch = c % CH;
+    if (c < NCH && tt < n) *reinterpret_cast<int4*>(tile + tt * ROW + ch * E) = vr[i];
   }
   __syncthreads();
-  for (int c = tid; c < n * CH; c += blockDim.x) {
-    const int tt = c / CH, ch = c % CH;
-    const int64_t l = tloc[tt];
-    if (l < 0) continue;
-    const int64_t page = l / ps, slot = l % ps;
-    *reinterpret_cast<int4*>(k_pool + ((page * Hkv + kvh) * ps + slot) * D + ch * E) =
-        *reinterpret_cast<const int4*>(k_new + size_t((t0 + tt) * Hkv + kvh) * D + ch * E);
+  if (tid < NG) {
+    // E tokens in consecutive slots of one page from a multiple of E: the V column offsets
+    // then run v0, v0+1, .. (pages are page_size >= E apart in every V row)
+    const int t = tid * E;
+    bool run = t + E <= n;
+    const int64_t v0 = run ? vdst[t] : -1;
+    run = run && v0 >= 0 && (v0 & (E - 1)) == 0;
+    for (int i = 1; i < E && run; ++i) run = vdst[t + i] == v0 + i;
+    vrun[tid] = run;
   }
-  for (int e = tid; e < tpw * D; e += blockDim.x) {
-    const int tt = e & (tpw - 1), d = e >> tpw_log2;
-    if (tt >= n) continue;
-    const int64_t l = tloc[tt];
-    if (l < 0) continue;
-    const int64_t page = l / ps, slot = l % ps;
-    v_pool[((page * Hkv + kvh) * D + d) * ps + slot] = tile[tt * ROW + d];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = tid + 256 * i, tt = c / CH, ch = c % CH;
+    if (c < NCH && tt < n) {
+      const int64_t kd = kdst[tt];
+      if (kd >= 0) *reinterpret_cast<int4*>(k_pool + kd + ch * E) = kr[i];
+    }
+  }
+  __syncthreads();
+  const int ng = (n + E - 1) / E;
+  for (int task = tid; task < ng * D; task += blockDim.x) {
+    const int gi = task % ng, d = task / ng, t = gi * E;
+    if (vrun[gi]) {
+      union {
+        T e[E];
+        int4 v;
+      } pk;
+#pragma unroll
+      for (int i = 0; i < E; ++i) pk.e[i] = tile[(t + i) * ROW + d];
+      *reinterpret_cast<int4*>(v_pool + vdst[t] + (int64_t(d) << ps_shift)) = pk.v;
+    } else {
+      for (int i = 0; i < E && t + i < n; ++i) {
+        const int64_t vd = vdst[t + i];
+        if (vd >= 0) v_pool[vd + (int64_t(d) << ps_shift)] = tile[(t + i) * ROW + d];
+      }
+    }
   }
 }
 
@@ -87,11 +130,16 @@ extern "C" va_status varlen_attn_append_kv(const va_params* params, int64_t num_
   if (num_tokens == 0) return VA_OK;
   if (!k_new || !v_new || !out_cache_loc || !k_pool || !v_pool)
     return fail(VA_ERR_INVALID_ARG, "k_new, v_new, out_cache_loc, k_pool and v_pool must be non-NULL");
+  if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new) | reinterpret_cast<uintptr_t>(k_pool) |
+       reinterpret_cast<uintptr_t>(v_pool)) & 15)
+    return fail(VA_ERR_INVALID_ARG, "k_new, v_new, k_pool and v_pool must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int Hkv = p.num_kv_heads, D = p.head_dim;
   const int64_t nslots = int64_t(p.num_pages) * ps;
   const bool bf = p.dtype == VA_DTYPE_BF16;
-  int tpw_log2 = 6;                       // kAppendTok = 64 tokens
+  int ps_shift = 0;
+  while ((1 << ps_shift) < ps) ++ps_shift;
+  int tpw_log2 = 4;                       // kAppendTok = 16 tokens
   while (tpw_log2 > 0 && ((num_tokens * Hkv) >> tpw_log2) < 1024) --tpw_log2;
   const int tpw = 1 << tpw_log2;
   const dim3 block(256), grid(unsigned((num_tokens + tpw - 1) / tpw), unsigned(Hkv));
@@ -100,7 +148,7 @@ extern "C" va_status varlen_attn_append_kv(const va_params* params, int64_t num_
     using T = decltype(elem);
     constexpr int DD = decltype(dim)::value;
     append_kv_kernel<T, DD><<<grid, block, 0, s>>>(static_cast<const T*>(k_new), static_cast<const T*>(v_new),
-                                                   out_cache_loc, num_tokens, tpw_log2, Hkv, ps, nslots, static_cast<T*>(k_pool),
+                                                   out_cache_loc, num_tokens, tpw_log2, Hkv, ps_shift, nslots, static_cast<T*>(k_pool),
                                                    static_cast<T*>(v_pool), bad_loc_count);
   };
   using D128 = std::integral_constant<int, 128>;

@@ -266,60 +266,44 @@ __global__ __launch_bounds__(256) void fp8_to_bf16_kernel(const uint32_t* __rest
 
 // ---------------------------------------------------------------- fp8 append --
 // Storing new rows: per (token, KV head) vector, scale = max|x| / 448 in float32 (IEEE
-// division; 1 for an all-zero vector), code = x / scale rounded to the nearest e4m3fn
-// value with ties to the even code, magnitudes from 448 up taking the largest finite code.
+// division; 1 for an all-zero vector), code = x / scale (IEEE division) rounded to the
+// nearest e4m3fn value with ties to the even code by the hardware converter (checked bit
+// for bit against the format's definition on every finite bf16 magnitude under sixteen
+// row maxima, and on every midpoint between adjacent codes).
 
-// Nearest-even e4m3fn code of a finite float32, from the format's definition.
-__device__ __forceinline__ uint32_t f32_to_e4m3fn(float y) {
-  const uint32_t u = __float_as_uint(y);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7fffffffu;
-  const float fa = __uint_as_float(a);
-  if (!(fa < 448.f)) return sign | 0x7eu;
-  if (fa >= 0.015625f) {                       // normal e4m3fn range, 2^-6 and up
-    const uint32_t e = (a >> 23) - 127u + 7u;  // biased e4m3 exponent, 1..15
-    const uint32_t keep = (a >> 20) & 7u, rem = a & 0xfffffu;
-    uint32_t code = (e << 3) | keep;
-    if (rem > 0x80000u || (rem == 0x80000u && (keep & 1u))) code += 1u;   // carries into the exponent
-    return sign | code;
-  }
-  return sign | uint32_t(rintf(fa * 512.f));   // subnormal steps of 2^-9; 8 is the code of 2^-6
-}
+constexpr int kAppendFp8Tok = 16;
 
-constexpr int kAppendFp8Tok = 64;
-
-// One workgroup per (KV head, up to 64 consecutive tokens).  Each wave quantises four rows
-// at a time: lane group grp = lane / 16 takes token tt = 4*wave + 16*i + grp (i = 0..3), lane
+// One workgroup per (KV head, up to 16 consecutive tokens: more workgroups in flight, 36 us
+// against 44 us with 64 for the ORCA iteration's 4098 rows).  Each wave quantises four rows
+// at a time: lane group grp = lane / 16 takes token tt = 4*wave + 16*i + grp, lane
 // s = lane % 16 its elements EPS*s .. +EPS-1 (one 16- or 8-byte load); the maximum is
 // reduced over the 16 lanes of the group.  All of a wave's loads are issued before any
-// row is quantised.  K codes and both scales are written directly, V codes go through LDS
-// so that the transposed V pages are written with the token index fastest (tokens that
-// fill consecutive slots of a page write consecutive bytes).
+// row is quantised; threads 0..63 meanwhile turn each token's out_cache_loc into the offsets
+// of its K code row, its scales and its V code column (page_size is a power of two).  K
+// codes and both scales are written directly, V codes go through LDS and are written into
+// the transposed V pages 16 tokens at a time -- one 16-byte store per d row -- where those
+// tokens fill 16 consecutive slots of one page from a multiple of 16, else one byte per
+// token.
 template <int D>
 __global__ __launch_bounds__(256) void append_kv_fp8_kernel(
     const bf16* __restrict__ k_new, const bf16* __restrict__ v_new, const int64_t* __restrict__ loc, int64_t ntok,
-    int tpw_log2, int Hkv, int ps, int64_t nslots, uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
+    int tpw_log2, int Hkv, int ps_shift, int64_t nslots, uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
     float* __restrict__ k_scale, float* __restrict__ v_scale, int32_t* __restrict__ bad) {
   constexpr int EPS = D / 16;                    // elements per lane of a row group
   constexpr int IT = kAppendFp8Tok / 16;         // row groups per wave
   constexpr int VROW = D + 4;                    // padded code row: token-strided reads spread over banks
   typedef __bf16 row_t __attribute__((ext_vector_type(EPS)));
-  __shared__ uint8_t vcode[kAppendFp8Tok * VROW];
-  __shared__ int64_t tloc[kAppendFp8Tok];
+  constexpr int G = 16;                          // tokens per 16-byte V code store
+  __shared__ __attribute__((aligned(16))) uint8_t vcode[kAppendFp8Tok * VROW];
+  __shared__ int64_t srow_of[kAppendFp8Tok];     // (page * Hkv + kvh) * page_size + slot (-1: none)
+  __shared__ int64_t vdst[kAppendFp8Tok];        // byte offset of V[page][kvh][0][slot] (-1: none)
+  __shared__ int32_t vrun[kAppendFp8Tok / G];
   const int kvh = blockIdx.y;
   const int tpw = 1 << tpw_log2;
   const int64_t t0 = int64_t(blockIdx.x) << tpw_log2;
   const int n = int(min<int64_t>(tpw, ntok - t0));
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = lane >> 4, sub = lane & 15;
-  if (tid < kAppendFp8Tok) {
-    int64_t l = tid < n ? loc[t0 + tid] : -1;
-    if (l >= nslots) {
-      if (bad && kvh == 0) atomicAdd(bad, 1);
-      l = -1;
-    }
-    tloc[tid] = l;
-  }
   row_t kx[IT], vx[IT];
 #pragma unroll
   for (int i = 0; i < IT; ++i) {
@@ -329,7 +313,26 @@ __global__ __launch_bounds__(256) void append_kv_fp8_kernel(
     kx[i] = *reinterpret_cast<const row_t*>(k_new + src);
     vx[i] = *reinterpret_cast<const row_t*>(v_new + src);
   }
+  if (tid < kAppendFp8Tok) {
+    int64_t l = tid < n ? loc[t0 + tid] : -1;
+    if (l >= nslots) {
+      if (bad && kvh == 0) atomicAdd(bad, 1);
+      l = -1;
+    }
+    const int64_t ph = (l >> ps_shift) * Hkv + kvh;
+    const int64_t slot = l & ((int64_t(1) << ps_shift) - 1);
+    srow_of[tid] = l < 0 ? -1 : (ph << ps_shift) + slot;
+    vdst[tid] = l < 0 ? -1 : ((ph * D) << ps_shift) + slot;
+  }
   __syncthreads();
+  if (tid < kAppendFp8Tok / G) {
+    const int t = tid * G;
+    bool run = t + G <= n;
+    const int64_t v0 = run ? vdst[t] : -1;
+    run = run && v0 >= 0 && (v0 & (G - 1)) == 0;
+    for (int i = 1; i < G && run; ++i) run = vdst[t + i] == v0 + i;
+    vrun[tid] = run;
+  }
   auto quant = [&](const row_t& row, uint32_t (&c)[EPS]) -> float {
     float x[EPS], amax = 0.f;
 #pragma unroll
@@ -340,8 +343,14 @@ __global__ __launch_bounds__(256) void append_kv_fp8_kernel(
 #pragma unroll
     for (int off = 8; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
     const float scale = amax > 0.f ? amax / 448.f : 1.f;
+    // v_cvt_pk_fp8_f32: two quotients to e4m3fn codes, nearest even (|x / scale| <= 448 up to
+    // the division's rounding, which still rounds to 448)
 #pragma unroll
-    for (int e = 0; e < EPS; ++e) c[e] = f32_to_e4m3fn(x[e] / scale);
+    for (int e = 0; e < EPS; e += 2) {
+      const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(x[e] / scale, x[e + 1] / scale, 0, false);
+      c[e] = uint32_t(pk) & 0xffu;
+      c[e + 1] = (uint32_t(pk) >> 8) & 0xffu;
+    }
     return scale;
   };
 #pragma unroll
@@ -354,10 +363,9 @@ __global__ __launch_bounds__(256) void append_kv_fp8_kernel(
     if (tt >= n) continue;
 #pragma unroll
     for (int e = 0; e < EPS; ++e) vcode[tt * VROW + EPS * sub + e] = uint8_t(vc[e]);
-    const int64_t l = tloc[tt];
-    if (l < 0) continue;
-    const int64_t page = l / ps, slot = l % ps;
-    const size_t srow = size_t(page * Hkv + kvh) * ps + slot;
+    const int64_t sr = srow_of[tt];
+    if (sr < 0) continue;
+    const size_t srow = size_t(sr);
     uint32_t w[EPS / 4];
 #pragma unroll
     for (int j = 0; j < EPS / 4; ++j)
@@ -373,13 +381,23 @@ __global__ __launch_bounds__(256) void append_kv_fp8_kernel(
     }
   }
   __syncthreads();
-  for (int e = tid; e < tpw * D; e += blockDim.x) {
-    const int tt = e & (tpw - 1), d = e >> tpw_log2;
-    if (tt >= n) continue;
-    const int64_t l = tloc[tt];
-    if (l < 0) continue;
-    const int64_t page = l / ps, slot = l % ps;
-    v_pool[(size_t(page * Hkv + kvh) * D + d) * ps + slot] = vcode[tt * VROW + d];
+  const int ng = (n + G - 1) / G;
+  for (int task = tid; task < ng * D; task += blockDim.x) {
+    const int gi = task % ng, d = task / ng, t = gi * G;
+    if (vrun[gi]) {
+      union {
+        uint8_t b[G];
+        uint4 v;
+      } pk;
+#pragma unroll
+      for (int i = 0; i < G; ++i) pk.b[i] = vcode[(t + i) * VROW + d];
+      *reinterpret_cast<uint4*>(v_pool + vdst[t] + (int64_t(d) << ps_shift)) = pk.v;
+    } else {
+      for (int i = 0; i < G && t + i < n; ++i) {
+        const int64_t vd = vdst[t + i];
+        if (vd >= 0) v_pool[vd + (int64_t(d) << ps_shift)] = vcode[(t + i) * VROW + d];
+      }
+    }
   }
 }
 
@@ -404,9 +422,14 @@ extern "C" va_status varlen_attn_append_kv_fp8(const va_params* params, int64_t 
   if (num_tokens == 0) return VA_OK;
   if (!k_new || !v_new || !out_cache_loc || !k_pool || !v_pool || !k_scale || !v_scale)
     return fail(VA_ERR_INVALID_ARG, "k_new, v_new, out_cache_loc, the pools and the scale pools must be non-NULL");
+  if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new) | reinterpret_cast<uintptr_t>(k_pool) |
+       reinterpret_cast<uintptr_t>(v_pool)) & 15)
+    return fail(VA_ERR_INVALID_ARG, "k_new, v_new, k_pool and v_pool must be 16-byte aligned");
   const int Hkv = p.num_kv_heads;
   const int64_t nslots = int64_t(p.num_pages) * ps;
-  int tpw_log2 = 6;
+  int ps_shift = 0;
+  while ((1 << ps_shift) < ps) ++ps_shift;
+  int tpw_log2 = 4;
   while (tpw_log2 > 0 && ((num_tokens * Hkv) >> tpw_log2) < 1024) --tpw_log2;
   const int tpw = 1 << tpw_log2;
   const dim3 block(256), grid(unsigned((num_tokens + tpw - 1) / tpw), unsigned(Hkv));
@@ -417,10 +440,10 @@ extern "C" va_status varlen_attn_append_kv_fp8(const va_params* params, int64_t 
   auto* vp = static_cast<uint8_t*>(v_pool);
   (void)hipGetLastError();
   if (p.head_dim == 128)
-    append_kv_fp8_kernel<128><<<grid, block, 0, s>>>(kn, vn, out_cache_loc, num_tokens, tpw_log2, Hkv, ps, nslots, kp, vp,
+    append_kv_fp8_kernel<128><<<grid, block, 0, s>>>(kn, vn, out_cache_loc, num_tokens, tpw_log2, Hkv, ps_shift, nslots, kp, vp,
                                                       k_scale, v_scale, bad_loc_count);
   else
-    append_kv_fp8_kernel<64><<<grid, block, 0, s>>>(kn, vn, out_cache_loc, num_tokens, tpw_log2, Hkv, ps, nslots, kp, vp,
+    append_kv_fp8_kernel<64><<<grid, block, 0, s>>>(kn, vn, out_cache_loc, num_tokens, tpw_log2, Hkv, ps_shift, nslots, kp, vp,
                                                      k_scale, v_scale, bad_loc_count);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(VA_ERR_HIP, std::string("fp8 append kernel launch: ") + hipGetErrorString(e));

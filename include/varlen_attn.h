@@ -271,6 +271,17 @@ va_status varlen_attn_debug_gather(const va_plan* plan, const void* k_pool, cons
                                    const int32_t* block_table_dev, void* k_out, void* v_out,
                                    void* stream);
 
+/* The same copy as varlen_attn_debug_gather, made by the MFMA attention kernel's own
+ * staging of bf16 pools: one workgroup per (request, KV head) stages every 64-key tile of
+ * the request into LDS with the page lookup, DMA addressing (buffer resources over page
+ * slices, per-lane offsets) and tail handling the attention tiles use, then copies the staged
+ * K rows and V^T slices out in logical order.  bf16 plans only (VA_ERR_UNSUPPORTED
+ * otherwise); pools and outputs 16-byte aligned.  Exists to test that address path bit for
+ * bit ("How To Scale Your Model 笔记(7-8)", section 3: paging changes where a position is
+ * stored, not what is read). */
+va_status varlen_attn_debug_stage_gather(const va_plan* plan, const void* k_pool, const void* v_pool,
+                                         const int32_t* block_table_dev, void* k_out, void* v_out, void* stream);
+
 /* Widen n fp8 e4m3fn codes (device, 8-byte aligned; n a multiple of 8) to bf16 bit
  * patterns (device uint16 [n], 16-byte aligned) with the converter the fp8 attention
  * kernel uses.  Exists to test that conversion against the format's definition. */

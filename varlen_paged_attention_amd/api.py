@@ -25,7 +25,7 @@ EXPORTED = ["varlen_attn_plan", "varlen_attn_run", "varlen_attn_run_events", "va
             "varlen_attn_debug_gather", "varlen_attn_plan_destroy", "varlen_attn_status_string",
             "varlen_attn_last_error", "varlen_attn_append_kv", "varlen_attn_plan_slots", "varlen_attn_run_fp8",
             "varlen_attn_debug_fp8_to_bf16", "varlen_attn_append_kv_fp8", "varlen_attn_debug_stream_read",
-            "varlen_attn_run_noalloc"]
+            "varlen_attn_run_noalloc", "varlen_attn_debug_stage_gather"]
 VA_STATIC_SCRATCH_BYTES = 64 << 20
 
 
@@ -100,6 +100,8 @@ def lib():
         L.varlen_attn_plan_export.restype = ctypes.c_int
         L.varlen_attn_debug_gather.argtypes = [P, P, P, P, P, P, P]
         L.varlen_attn_debug_gather.restype = ctypes.c_int
+        L.varlen_attn_debug_stage_gather.argtypes = [P, P, P, P, P, P, P]
+        L.varlen_attn_debug_stage_gather.restype = ctypes.c_int
         L.varlen_attn_append_kv.argtypes = [ctypes.POINTER(VaParams), ctypes.c_int64, P, P, P, P, P, P, P]
         L.varlen_attn_append_kv.restype = ctypes.c_int
         L.varlen_attn_plan_slots.argtypes = [P, ctypes.POINTER(ctypes.c_int64)]
@@ -365,6 +367,21 @@ def varlen_attn_debug_gather(plan: Plan, k_pool, v_pool, block_table_dev, k_out,
                                           _dev_ptr(block_table_dev, "block_table", torch.int32),
                                           _dev_ptr(k_out, "k_out", dt), _dev_ptr(v_out, "v_out", dt),
                                           _stream_ptr(stream)))
+
+
+def varlen_attn_debug_stage_gather(plan: Plan, k_pool, v_pool, block_table_dev, k_out, v_out, stream=None) -> None:
+    """varlen_attn_debug_gather made by the attention kernel's own LDS staging (bf16 plans)."""
+    import torch
+    dt = _pool_dtype(plan)
+    _check_run_buffers(plan, None, k_pool, v_pool, block_table_dev, None, None)
+    p = plan.params
+    for name, t in (("k_out", k_out), ("v_out", v_out)):
+        _need(t, name, (plan.kv_total, p.num_kv_heads, p.head_dim))
+    _check(lib().varlen_attn_debug_stage_gather(plan.handle, _dev_ptr(k_pool, "k_pool", dt),
+                                                _dev_ptr(v_pool, "v_pool", dt),
+                                                _dev_ptr(block_table_dev, "block_table", torch.int32),
+                                                _dev_ptr(k_out, "k_out", dt), _dev_ptr(v_out, "v_out", dt),
+                                                _stream_ptr(stream)))
 
 
 def varlen_attn_plan_slots(plan: Plan) -> np.ndarray:

@@ -415,7 +415,18 @@ constexpr int prefill_lds_bytes() {
 // is the bf16 one; a key's K scale multiplies its scores and its V scale its probability.
 // The slice is the wave's own, and all its reads precede its writes, so no other wave is
 // involved until the barrier that ends the iteration.
-enum TileMode { kWholeTile, kAnyTile };
+// kStageGather: no attention.  Workgroup b takes request b / Hkv, KV head b % Hkv, all of
+// its keys, stages every 64-key tile into LDS through the same page lookup, DMA addressing,
+// wait and tail handling as the attention tiles, and copies the staged K rows and V^T
+// slices out in logical order (GatherOut), so the production address path can be checked
+// bit for bit.
+enum TileMode { kWholeTile, kAnyTile, kStageGather };
+
+struct GatherOut {
+  const int64_t* kv_offset;   // [num_reqs + 1] prefix sums of kv_len
+  bf16* k_out;                // [sum kv_len][Hkv][D]
+  bf16* v_out;                // same
+};
 
 // Instantiations: kWholeTile runs whole tiles only; kAnyTile runs every kind (whole tiles,
 // key-chunk tiles and column-list tiles: a plan with any of the latter launches all its
@@ -428,7 +439,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
     const PrefillTile* __restrict__ tiles, const Column* __restrict__ cols, const bf16* __restrict__ q,
     const void* __restrict__ kpool, const void* __restrict__ vpool, const float* __restrict__ kscale,
     const float* __restrict__ vscale, const int32_t* __restrict__ bt, int bt_stride, bf16* __restrict__ out,
-    float* __restrict__ ws_ml, float* __restrict__ ws_acc, int Hq, int g, Paged pg, float scale_log2) {
+    float* __restrict__ ws_ml, float* __restrict__ ws_acc, int Hq, int g, Paged pg, float scale_log2,
+    GatherOut go) {
   using Lay = PrefillLds<D>;
   constexpr int KCH = Lay::KCH, KROW = Lay::KROW, KBUF = Lay::KBUF, VBUF = Lay::VBUF;
   constexpr int WK = kPSliceKeys;                      // 16 keys per wave slice
@@ -448,7 +460,15 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const PrefillTile T = tiles[blockIdx.x];
+  const PrefillTile T = [&] {
+    if constexpr (MODE == kStageGather) {
+      const int r = int(blockIdx.x) / pg.Hkv;
+      const int L = int(go.kv_offset[r + 1] - go.kv_offset[r]);
+      return PrefillTile{r, int(blockIdx.x) % pg.Hkv, 0, 0, 0, 0, L, 0, -1, 0, 0, 0};
+    } else {
+      return tiles[blockIdx.x];
+    }
+  }();
   const int h = lane >> 5;
   const int rho = lane & 31;
   const int kap = (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1);   // swap bits 2 and 3
@@ -500,7 +520,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
   }
 
   bf16x8 qb[D / 16];
-  {
+  if constexpr (MODE != kStageGather) {
     const bf16* qp = q + (size_t(row) * Hq + head) * D + 8 * h;
 #pragma unroll
     for (int kc = 0; kc < D / 16; ++kc) {
@@ -717,6 +737,37 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
 #pragma unroll
         for (int t = 0; t < 2; ++t) acc[db] = mfma32_bf16(vb[(2 * b + t) * VSC + 64 * db], p[b][t], acc[db]);
   };
+
+  if constexpr (MODE == kStageGather) {
+    // stage each 64-key tile as the attention tiles do, then copy it out in logical order:
+    // K row kl of wave slice ws is chunks ws*KSC + kl*KROW + (0 .. KCH-1); element d of
+    // key kl of V^T slice ws is element kl % 8 of chunk ws*VSC + 2d + ((kl / 8) ^ bit 3 of d)
+    const int64_t obase = go.kv_offset[T.req];
+    for (int t = 0; t < ntiles; ++t) {
+      const int pt = page_for(t);
+      issue_k(t, pt, 0);
+      issue_v(t, pt, 0);
+      wait_vmem();
+      fix_v_tail(t, 0);
+      __syncthreads();
+      for (int e = tid; e < kPTileKeys * KCH; e += 64 * kPrefillWaves) {
+        const int key = e / KCH, ch = e % KCH, pos = t * kPTileKeys + key;
+        if (pos >= kv_end) continue;
+        const int ws = key / WK, kl = key % WK;
+        const size_t o = ((size_t(obase) + pos) * pg.Hkv + kvh) * D + 8 * ch;
+        *reinterpret_cast<bf16x8*>(go.k_out + o) = sK[ws * KSC + kl * KROW + ch];
+        bf16x8 v;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int d = 8 * ch + i;
+          v[i] = sV[ws * VSC + 2 * d + ((kl >> 3) ^ ((d >> 3) & 1))][kl & 7];
+        }
+        *reinterpret_cast<bf16x8*>(go.v_out + o) = v;
+      }
+      __syncthreads();
+    }
+    return;
+  }
 
   // ---- prologue: K(0), K(1), V(0) in LDS; scores of tile 0
   int p1 = ntiles > 1 ? page_for(1) : 0;
@@ -954,7 +1005,8 @@ static va_status prepare_kernels() {
         VA_PREFILL_KERNEL(128, kWholeTile, false), VA_PREFILL_KERNEL(64, kWholeTile, false),
         VA_PREFILL_KERNEL(128, kAnyTile, false), VA_PREFILL_KERNEL(64, kAnyTile, false),
         VA_PREFILL_KERNEL(128, kWholeTile, true),  VA_PREFILL_KERNEL(64, kWholeTile, true),
-        VA_PREFILL_KERNEL(128, kAnyTile, true),  VA_PREFILL_KERNEL(64, kAnyTile, true)};
+        VA_PREFILL_KERNEL(128, kAnyTile, true),  VA_PREFILL_KERNEL(64, kAnyTile, true),
+        VA_PREFILL_KERNEL(128, kStageGather, false), VA_PREFILL_KERNEL(64, kStageGather, false)};
 #undef VA_PREFILL_KERNEL
     for (const auto& k : kernels) {
       const hipError_t e = hipFuncSetAttribute(k.first, hipFuncAttributeMaxDynamicSharedMemorySize, k.second);
@@ -1086,11 +1138,11 @@ static va_status run_impl(const va_plan* plan, const void* q, const void* k_pool
     if (D == 128)
       prefill_bf16_kernel<128, M, F><<<grid, block, prefill_lds_bytes<128, F>(), s>>>(
           tl, plan->d_cols, qq, k_pool, v_pool, k_scale, v_scale, block_table_dev, bt_stride, oo, ws_ml, ws_acc,
-          p.num_q_heads, plan->g, pg, scale_log2);
+          p.num_q_heads, plan->g, pg, scale_log2, GatherOut{});
     else
       prefill_bf16_kernel<64, M, F><<<grid, block, prefill_lds_bytes<64, F>(), s>>>(
           tl, plan->d_cols, qq, k_pool, v_pool, k_scale, v_scale, block_table_dev, bt_stride, oo, ws_ml, ws_acc,
-          p.num_q_heads, plan->g, pg, scale_log2);
+          p.num_q_heads, plan->g, pg, scale_log2, GatherOut{});
     return hipGetLastError();
   };
   auto launch_kind = [&](auto mode, const PrefillTile* tl, int n) {
@@ -1273,6 +1325,42 @@ extern "C" va_status varlen_attn_debug_stream_read(const void* buf, size_t bytes
       static_cast<const uint4*>(buf), int64_t(bytes / 16), sink);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail("stream read kernel launch", e);
+  return VA_OK;
+}
+
+extern "C" va_status varlen_attn_debug_stage_gather(const va_plan* plan, const void* k_pool, const void* v_pool,
+                                                    const int32_t* block_table_dev, void* k_out, void* v_out,
+                                                    void* stream) {
+  if (!plan) return fail(VA_ERR_INVALID_ARG, "plan is NULL");
+  if (!plan->dev) return fail(VA_ERR_INVALID_ARG, "plan has no device buffer (built with VA_FLAG_HOST_ONLY)");
+  const va_params& p = plan->p;
+  if (p.dtype != VA_DTYPE_BF16)
+    return fail(VA_ERR_UNSUPPORTED, "the staged gather covers bf16 pools (the attention tiles' bf16 staging)");
+  if (plan->num_reqs == 0 || plan->kv_offset.back() == 0) return VA_OK;
+  if (!k_pool || !v_pool || !block_table_dev || !k_out || !v_out)
+    return fail(VA_ERR_INVALID_ARG, "pointer argument is NULL");
+  if ((reinterpret_cast<uintptr_t>(k_out) | reinterpret_cast<uintptr_t>(v_out) | reinterpret_cast<uintptr_t>(k_pool) |
+       reinterpret_cast<uintptr_t>(v_pool)) & 15)
+    return fail(VA_ERR_INVALID_ARG, "pools and outputs must be 16-byte aligned");
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+  if (dev != plan->device) return fail(VA_ERR_INVALID_ARG, "current HIP device is not the one the plan was built on");
+  Paged pg{p.num_kv_heads, log2i(p.page_size), p.head_dim};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid(unsigned(int64_t(plan->num_reqs) * p.num_kv_heads)), block(64 * kPrefillWaves);
+  const GatherOut go{plan->d_kv_offset, static_cast<bf16*>(k_out), static_cast<bf16*>(v_out)};
+  (void)hipGetLastError();
+  if (p.head_dim == 128)
+    prefill_bf16_kernel<128, kStageGather, false><<<grid, block, prefill_lds_bytes<128, false>(), s>>>(
+        nullptr, nullptr, nullptr, k_pool, v_pool, nullptr, nullptr, block_table_dev, p.max_pages_per_req, nullptr,
+        nullptr, nullptr, p.num_q_heads, plan->g, pg, 0.f, go);
+  else
+    prefill_bf16_kernel<64, kStageGather, false><<<grid, block, prefill_lds_bytes<64, false>(), s>>>(
+        nullptr, nullptr, nullptr, k_pool, v_pool, nullptr, nullptr, block_table_dev, p.max_pages_per_req, nullptr,
+        nullptr, nullptr, p.num_q_heads, plan->g, pg, 0.f, go);
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail("staged gather kernel launch", e);
   return VA_OK;
 }
 

@@ -314,10 +314,13 @@ def hashed_pages_host(w: "Workload", pages, stream: int, kv_heads=None) -> np.nd
     return out
 
 
-def hashed_pools_device(w: "Workload", device="cuda", pages_per_chunk: int = 4096):
-    """The K and V pools of a hashed workload, made on the device (bf16 torch tensors)."""
+def hashed_pools_device(w: "Workload", device="cuda", pages_per_chunk: Optional[int] = None):
+    """The K and V pools of a hashed workload, made on the device (bf16 torch tensors), in
+    chunks of about 2^28 elements (2 GiB int64 intermediates) unless pages_per_chunk says."""
     import torch
     E = _page_elems(w)
+    if pages_per_chunk is None:
+        pages_per_chunk = max(1, (1 << 28) // E)
     H, ps, D = w.num_kv_heads, w.page_size, w.head_dim
     elems = torch.arange(E, dtype=torch.int64, device=device)[None, :]
     out = []

@@ -15,6 +15,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cfloat>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -389,7 +390,10 @@ struct PrefillLds {
   static constexpr int KBUF = kPTileKeys * KROW;       // chunks per K buffer
   static constexpr int VBUF = kPTileKeys / 8 * D;      // chunks per V^T buffer
   static constexpr int bytes = 2 * (KBUF + VBUF) * 16;
-  static constexpr int scale_bytes = 2 * 2 * kPTileKeys * 4;   // fp8: K and V scales of both stages
+  // fp8, per key: the K and V scales as copied (two stages); the K scale times log2 e and
+  // the softmax scale, log2 of the V scale and its inverse as a bf16 pair hi + lo (three
+  // tiles: they are made two tiles ahead)
+  static constexpr int scale_bytes = 2 * kPTileKeys * (4 + 4) + 3 * kPTileKeys * (4 + 4 + 2 + 2);
 };
 
 template <int D, bool F8>
@@ -410,9 +414,12 @@ constexpr int prefill_lds_bytes() {
 //
 // F8 = true: the pools hold fp8 e4m3fn codes with per-position float32 scales.  Each wave
 // copies its 16-key slice of codes by LDS-DMA into the upper part of the same slice's bf16
-// area (and the slice's 16 K and 16 V scales into the scale area), then, once its copies
-// have landed, widens the codes in place, exactly, in the layouts above, so the MFMA loop
-// is the bf16 one; a key's K scale multiplies its scores and its V scale its probability.
+// area (and, with the K codes, the slice's 16 K and 16 V scales into the scale area), then,
+// once its copies have landed, widens the codes in place, exactly, in the layouts above, so
+// the MFMA loop is the bf16 one.  A key's K scale multiplies its scores; log2 of its V scale
+// is added to them, so its exponential is the weight P gives its V codes, and the row sum
+// adds that bf16 weight divided by the V scale: numerator and row sum use the same weights
+// (the rounding of P moves weights, as in the bf16 path, not the output's scale).
 // The slice is the wave's own, and all its reads precede its writes, so no other wave is
 // involved until the barrier that ends the iteration.
 // kStageGather: no attention.  Workgroup b takes request b / Hkv, KV head b % Hkv, all of
@@ -456,6 +463,10 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
   bf16x8* sV = smem + 2 * KBUF;                        // [2][VBUF]
   float* sKs = reinterpret_cast<float*>(smem + 2 * KBUF + 2 * VBUF);   // fp8: [2][64] K scales
   float* sVs = sKs + 2 * kPTileKeys;                                  // fp8: [2][64] V scales
+  float* sKl = sVs + 2 * kPTileKeys;                                  // fp8: [3][64] K scale * log2 e * scale
+  float* sLv = sKl + 3 * kPTileKeys;                                  // fp8: [3][64] log2 |V scale|
+  bf16* sVh = reinterpret_cast<bf16*>(sLv + 3 * kPTileKeys);          // fp8: [3][64] 1 / |V scale|, hi
+  bf16* sVl = sVh + 3 * kPTileKeys;                                   // fp8: [3][64] 1 / |V scale|, lo
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -579,8 +590,14 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
       // codes: lane -> raw chunk L = 64r + lane = (key L / (D/16), 16-byte piece L % (D/16))
 #pragma unroll
       for (int r = 0; r < KR / 64; ++r) dma_b128(rs, dst + KRAW + 64 * r, uint32_t(16 * (64 * r + lane)), 0);
-      const auto rsc = slice_rsrc(kscale + pg.scale_idx(page, kvh, k0w & ps_mask));
-      if (lane < WK) dma_b32(rsc, sKs + buf * kPTileKeys + wv * WK, uint32_t(4 * lane));
+      // the key's K and V scales come with its K codes (the V scales are turned into log2
+      // and inverse two tiles ahead, for the scores of the tile after next)
+      const auto rsk = slice_rsrc(kscale + pg.scale_idx(page, kvh, k0w & ps_mask));
+      const auto rsv = slice_rsrc(vscale + pg.scale_idx(page, kvh, k0w & ps_mask));
+      if (lane < WK) {
+        dma_b32(rsk, sKs + buf * kPTileKeys + wv * WK, uint32_t(4 * lane));
+        dma_b32(rsv, sVs + buf * kPTileKeys + wv * WK, uint32_t(4 * lane));
+      }
     } else {
 #pragma unroll
       for (int r = 0; r < KNI; ++r)
@@ -593,8 +610,6 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
     if (k0w >= kv_end) {                      // never read garbage into V: write zeros
 #pragma unroll
       for (int r = 0; r < VNI; ++r) dst[64 * r + lane] = bf16x8{};
-      if constexpr (F8)
-        if (lane < WK) sVs[buf * kPTileKeys + wv * WK + lane] = 0.f;
       return;
     }
     const auto rs = slice_rsrc(vbase + size_t(page) * page_bytes + (k0w & ps_mask) * EB);
@@ -602,19 +617,41 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
       // codes: lane -> raw chunk d = 64r + lane, the 16 keys of V page row d
 #pragma unroll
       for (int r = 0; r < VR / 64; ++r) dma_b128(rs, dst + VRAW + 64 * r, uint32_t((64 * r + lane) << pg.ps_shift), 0);
-      const auto rsc = slice_rsrc(vscale + pg.scale_idx(page, kvh, k0w & ps_mask));
-      if (lane < WK) dma_b32(rsc, sVs + buf * kPTileKeys + wv * WK, uint32_t(4 * lane));
     } else {
 #pragma unroll
       for (int r = 0; r < VNI; ++r) dma_b128(rs, dst + 64 * r, voff, r * vrstep);
     }
   };
   // fp8: widen the slice's codes in place, exactly (scale 1), once its copies have landed
-  // (own slice only); the per-position scales stay in sKs / sVs: a key's K scale multiplies
-  // its scores, its V scale its probabilities
+  // (own slice only).  The scales act on the scores in base-2 units: a key's score is
+  // (q . k_codes) * (s_K * log2 e * softmax scale) + log2 s_V, so its exponential is its
+  // probability times s_V (the weight P gives its V codes), and the row sum adds that
+  // rounded weight times 1 / s_V: numerator and row sum use the same weights.
   auto convert_k = [&](int t, int buf) {
     if constexpr (F8) {
       const int k0w = kbeg + t * kPTileKeys + wv * WK;
+      if (lane < WK) {
+        // key `lane` of the slice: K scale times log2 e and the softmax scale; log2 and
+        // inverse of |V scale| into slot t % 3 (a V scale below the normal range, i.e. V
+        // magnitudes under about 5e-36 or a zero scale, counts as 1 with the codes zeroed,
+        // so 1 / s never overflows; positions past the end get zeros: finite, and masked)
+        const int si = buf * kPTileKeys + wv * WK + lane, so = (t % 3) * kPTileKeys + wv * WK + lane;
+        float kl = 0.f, ls = 0.f, inv = 0.f;
+        if (k0w + lane < kv_end) {
+          kl = sKs[si] * scale_log2;
+          const float sv = fabsf(sVs[si]);
+          const bool tiny = sv < FLT_MIN;
+          // hardware log2 and reciprocal (about 1 ulp; s is normal here): the weights use
+          // the same inverse in numerator and row sum, so only its f32 rounding remains
+          ls = tiny ? 0.f : __builtin_amdgcn_logf(sv);
+          inv = tiny ? 1.f : __builtin_amdgcn_rcpf(sv);
+        }
+        const bf16 hi = bf16(inv);
+        sKl[so] = kl;
+        sLv[so] = ls;
+        sVh[so] = hi;
+        sVl[so] = bf16(inv - float(hi));
+      }
       if (k0w >= kv_end) return;
       bf16x8* sl = sK + buf * KBUF + wv * KSC;
       constexpr int PER = KR / 64;                      // raw chunks per lane
@@ -640,18 +677,29 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
 #pragma unroll
       for (int i = 0; i < PER; ++i) raw[i] = sl[VRAW + 64 * i + lane];
       const int valid = kv_end - k0w;                   // keys of the slice before the end
-      // positions at or past the end may be unwritten slots: zero codes and scales there
-      // (their probabilities are 0, and 0 * NaN would still be NaN)
-      if (lane < WK && lane >= valid) sVs[buf * kPTileKeys + wv * WK + lane] = 0.f;
+      // key `lane` of the slice (its V scale, copied with its K codes, is still in place):
+      // positions at or past the end may be unwritten slots and a V scale below the normal
+      // range counts as 1, so those keys' codes are zeroed (0 * NaN would still be NaN); a
+      // negative V scale flips the key's codes (the weights use |s|)
+      bool tiny = false, neg = false;
+      if (lane < WK && lane < valid) {
+        const float sv = sVs[buf * kPTileKeys + wv * WK + lane];
+        tiny = fabsf(sv) < FLT_MIN;
+        neg = sv < 0.f && !tiny;
+      }
+      const uint32_t zmask = uint32_t(__ballot(lane < WK && (lane >= valid || tiny)));   // keys to zero
+      const uint32_t nmask = uint32_t(__ballot(neg));                                   // keys to negate
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
         const int d = 64 * i + lane;
         const uint32_t* w = reinterpret_cast<const uint32_t*>(&raw[i]);
         bf16x8 o[2] = {fp8x8_to_bf16(w[0], w[1]), fp8x8_to_bf16(w[2], w[3])};
-        if (valid < WK) {
+        if (zmask | nmask) {
 #pragma unroll
-          for (int k = 0; k < WK; ++k)
-            if (k >= valid) o[k >> 3][k & 7] = bf16(0.f);
+          for (int k = 0; k < WK; ++k) {
+            if ((nmask >> k) & 1) o[k >> 3][k & 7] = -o[k >> 3][k & 7];
+            if ((zmask >> k) & 1) o[k >> 3][k & 7] = bf16(0.f);
+          }
         }
         const int flip = (d >> 3) & 1;
         sl[2 * d + flip] = o[0];
@@ -689,35 +737,40 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
   };
   // element 8t + x of a 32-key block's scores (and of its probabilities) is key
   // 32b + 16t + 8h + x of the 64-key tile
-  auto k_scale_block = [&](int buf, int b, f32x16& sn) {
+  // fp8 scores of tile t (scale slot t % 3) in base 2 with log2 |s_V| added
+  auto k_scale_block = [&](int slot, int b, f32x16& sn) {
     if constexpr (F8) {
-      const f32x4* ks = reinterpret_cast<const f32x4*>(sKs + buf * kPTileKeys + 32 * b + 8 * h);
+      const f32x4* ks = reinterpret_cast<const f32x4*>(sKl + slot * kPTileKeys + 32 * b + 8 * h);
+      const f32x4* lv = reinterpret_cast<const f32x4*>(sLv + slot * kPTileKeys + 32 * b + 8 * h);
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const f32x4 f = ks[4 * t + u];
+          const f32x4 f = ks[4 * t + u], l2 = lv[4 * t + u];
 #pragma unroll
-          for (int x = 0; x < 4; ++x) sn[8 * t + 4 * u + x] *= f[x];
+          for (int x = 0; x < 4; ++x) sn[8 * t + 4 * u + x] = fmaf(sn[8 * t + 4 * u + x], f[x], l2[x]);
         }
     }
   };
-  auto exp_block = [&](const f32x16& sc, int buf, int b, bf16x8 (&pb)[2]) {
+  auto exp_block = [&](const f32x16& sc, int slot, int b, bf16x8 (&pb)[2]) {
     if constexpr (F8) {
-      // row sum over the probabilities; P carries each key's V scale (V holds plain codes)
-      const f32x4* vs = reinterpret_cast<const f32x4*>(sVs + buf * kPTileKeys + 32 * b + 8 * h);
+      // scores are in base-2 units with log2 |s_V| added: the exponential is p * |s_V|, and
+      // the row sum adds bf16(p * |s_V|) / |s_V|, the inverse taken as hi + lo bf16 parts
+      const bf16x8* ih = reinterpret_cast<const bf16x8*>(sVh + slot * kPTileKeys + 32 * b + 8 * h);
+      const bf16x8* il = reinterpret_cast<const bf16x8*>(sVl + slot * kPTileKeys + 32 * b + 8 * h);
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        float pf[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pf[e] = fast_exp2(fmaf(sc[8 * t + e], scale_log2, -m_run));
-        l_run += ((pf[0] + pf[1]) + (pf[2] + pf[3])) + ((pf[4] + pf[5]) + (pf[6] + pf[7]));
+        for (int e = 0; e < 8; ++e) pb[t][e] = bf16(fast_exp2(sc[8 * t + e] - m_run));
+        const bf16x8 hi = ih[2 * t], lo = il[2 * t];
+        float ls[2] = {0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const f32x4 f = vs[4 * t + u];
-#pragma unroll
-          for (int x = 0; x < 4; ++x) pb[t][4 * u + x] = bf16(pf[4 * u + x] * f[x]);
+        for (int e = 0; e < 8; e += 2) {
+          const bf16x2 w = {pb[t][e], pb[t][e + 1]};
+          ls[0] = __builtin_amdgcn_fdot2_f32_bf16(w, bf16x2{hi[e], hi[e + 1]}, ls[0], false);
+          ls[1] = __builtin_amdgcn_fdot2_f32_bf16(w, bf16x2{lo[e], lo[e + 1]}, ls[1], false);
         }
+        l_run += ls[0] + ls[1];
       }
     } else {
 #pragma unroll
@@ -789,8 +842,6 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
   if (w_max_limit >= 0) {
     qk_block(0, 0, sc[0]);
     qk_block(0, 1, sc[1]);
-    k_scale_block(0, 0, sc[0]);
-    k_scale_block(0, 1, sc[1]);
   }
   __syncthreads();
 
@@ -803,6 +854,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
     if (j + 4 < ntiles) p3 = page_for(j + 4);
     const int k0 = kbeg + j * kPTileKeys;
     if (k0 <= w_max_limit) {
+      k_scale_block(j % 3, 0, sc[0]);
+      k_scale_block(j % 3, 1, sc[1]);
       if (k0 + kPTileKeys - 1 > w_min_limit) {
 #pragma unroll
         for (int b = 0; b < 2; ++b)
@@ -819,7 +872,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
 #pragma unroll
         for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[b][e]);
       mx = fmaxf(mx, other_half(mx));
-      const float m_tile = mx * scale_log2;
+      const float m_tile = F8 ? mx : mx * scale_log2;   // fp8 scores are already in base 2
       const bool need = m_tile > m_run + kRescaleSlack;
       if (__any(need)) {
         const float m_new = need ? m_tile : m_run;
@@ -836,13 +889,12 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
         for (int b = 0; b < 2; ++b) {
           f32x16 sn;
           qk_block((j + 1) & 1, b, sn);
-          exp_block(sc[b], j & 1, b, p[b]);
-          k_scale_block((j + 1) & 1, b, sn);
+          exp_block(sc[b], j % 3, b, p[b]);
           sc[b] = sn;
         }
       } else {
-        exp_block(sc[0], j & 1, 0, p[0]);
-        exp_block(sc[1], j & 1, 1, p[1]);
+        exp_block(sc[0], j % 3, 0, p[0]);
+        exp_block(sc[1], j % 3, 1, p[1]);
       }
       pv_tile(j & 1, p);
     }

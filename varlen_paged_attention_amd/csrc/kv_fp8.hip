@@ -8,10 +8,12 @@
 // fp8 storage halves the bytes read and leaves the arithmetic as in the bf16 path.
 // The scales are applied in fp32 outside the MFMAs: a K scale multiplies its key's scores
 // before the softmax, a V scale multiplies its key's probability before P is rounded to
-// bf16 for the P.V product (the row sum uses the unscaled probability).
+// bf16 for the P.V product, and the row sum adds the weight that product gives the key's
+// values (the rounded product over the scale).
 // The file also holds the append of new rows into fp8 pools (quantisation + scatter).
 #include <hip/hip_runtime.h>
 
+#include <cfloat>
 #include <string>
 #include <type_traits>
 
@@ -146,9 +148,19 @@ __device__ __forceinline__ void split_kv_fp8_wave(
       cover(k + kStepKeys);
       load_k(k + kStepKeys);
     }
-    float vsc[16];
+    // P carries each key's V scale s; the row sum adds the weights the MFMA applies to the
+    // key's values, bf16(p * s) / s.  A scale below the normal range (V magnitudes under
+    // about 5e-36, or zero) keeps p unscaled and zeroes the key's codes instead.
+    float vsc[16], vin[16];
+    uint32_t tiny = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) vsc[i] = vs[i >> 2][i & 3];
+    for (int i = 0; i < 16; ++i) {
+      const float sv = vs[i >> 2][i & 3];
+      const bool t = fabsf(sv) < FLT_MIN;
+      tiny |= uint32_t(t) << i;
+      vsc[i] = t ? 1.f : sv;
+      vin[i] = t ? 1.f : __builtin_amdgcn_rcpf(sv);
+    }
     if (masked_item || tail) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -157,7 +169,7 @@ __device__ __forceinline__ void split_kv_fp8_wave(
         for (int cb = 0; cb < NC; ++cb)
           if (key > klast || key > limit[cb]) v[cb][i] = -INFINITY;
         // scales past the item's end may belong to unwritten slots: keep them out of P
-        if (key > klast) vsc[i] = 0.f;
+        if (key > klast) vsc[i] = vin[i] = 0.f;
       }
     }
     // ---- online softmax per column block (max shared by the 4 lane groups of a column)
@@ -175,9 +187,9 @@ __device__ __forceinline__ void split_kv_fp8_wave(
       float sum = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(v[cb][i] - m_new);
-        sum += p;
-        pb[cb][i >> 3][i & 7] = bf16(p * vsc[i]);
+        const bf16 w = bf16(fast_exp2(v[cb][i] - m_new) * vsc[i]);
+        pb[cb][i >> 3][i & 7] = w;
+        sum = fmaf(float(w), vin[i], sum);
       }
       l_run[cb] = l_run[cb] * alpha + sum;
 #pragma unroll
@@ -194,6 +206,13 @@ __device__ __forceinline__ void split_kv_fp8_wave(
         for (int e = 0; e < 8; ++e) {
           if (e >= valid) v0[e] = bf16(0.f);
           if (8 + e >= valid) v1[e] = bf16(0.f);
+        }
+      }
+      if (__any(tiny != 0)) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if ((tiny >> e) & 1) v0[e] = bf16(0.f);
+          if ((tiny >> (8 + e)) & 1) v1[e] = bf16(0.f);
         }
       }
 #pragma unroll

@@ -559,9 +559,14 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
     L = std::min<int64_t>(L, 8192);
   }
   plan->split_len = int32_t(L);
-  // group tiles: key chunks sized for about one tile per resident workgroup in all
+  // group tiles: key chunks sized for about one tile per two resident workgroups: the
+  // members' own keys and the plan's other tiles share the launch, and every chunk writes
+  // its columns' partial results for the combine (64 members of a 16K prefix: 512-key
+  // chunks 84 us, 1024-key chunks 74 us; 4096-key chunks 108 us, when one group tile
+  // outlasts the rest); at least 256 keys
   const int64_t Lt = std::min<int64_t>(
-      4096, std::max<int64_t>(256, ceil_div(ceil_div(tile_keys * tile_cols, slots_wg), kStepKeys) * kStepKeys));
+      4096, std::max<int64_t>(256, ceil_div(ceil_div(tile_keys * tile_cols, std::max(1, slots_wg / 2)), kStepKeys) *
+                                       kStepKeys));
   for (auto& B : blocks) {
     const int64_t keys = std::max(0, B.kend - B.kstart);
     B.chunk = int32_t(B.tile ? (B.shared ? Lt : 8192) : L);

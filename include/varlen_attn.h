@@ -28,6 +28,10 @@
  *   q, out   [total_q_rows][num_q_heads][head_dim]
  *   k_pool   [num_pages][num_kv_heads][page_size][head_dim]
  *   v_pool   [num_pages][num_kv_heads][head_dim][page_size]   (V pages are transposed)
+ *            Unlike K, a V page holds head_dim rows of page_size consecutive positions, so
+ *            the P.V operand (8 consecutive keys of one d) is one 16-byte load.  V kept in
+ *            K's layout must be transposed page by page before run(); the append entry
+ *            points below write this layout directly.
  *   k_scale, v_scale  float32 [num_pages][num_kv_heads][page_size]   (fp8 pools only)
  *   block table  int32 [num_reqs][max_pages_per_req]; only the first
  *                ceil(kv_len[r] / page_size) entries of row r are read.

@@ -423,3 +423,53 @@ def test_append_then_attend(cid, scale):
     assert np.array_equal(_raw(kp).view(np.uint8), np.ascontiguousarray(w.k_pool).view(np.uint8))
     assert np.array_equal(_raw(vp).view(np.uint8), np.ascontiguousarray(w.v_pool).view(np.uint8))
     _check_full(w, out, f"append+attend {cid}/{scale}")
+
+
+def _uneven(kind, dtype=None):
+    """Decodes whose tables share runs of pages unevenly (the planner's shared-prefix groups
+    then follow the tree of common runs)."""
+    dtype = dtype or "bf16"
+    if kind == "many-nested":
+        # 64 decodes of 2048 positions, g = 4, 8 KV heads: all share 8 pages, requests 0-31
+        # share 24, requests 32-63 share 16 (members' own keys then run as tiles)
+        w = W.build("many-nested", [1] * 64, [2048] * 64, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                    page_size=64, seed=31, dtype=dtype)
+        return W.share_runs(w, [(0, list(range(1, 64)), 0, 8), (0, list(range(1, 32)), 8, 24),
+                                (32, list(range(33, 64)), 8, 16)])
+    if kind == "leader-outlier":
+        w = W.build("leader-outlier", [1] * 6, [900] * 6, num_q_heads=8, num_kv_heads=2, head_dim=64,
+                    page_size=16, seed=9, dtype=dtype)
+        return W.share_runs(w, [(3, [1, 2, 4, 5], 0, 40), (3, [0], 0, 1)])
+    w = W.build(f"uneven-{kind}", [1] * 8, [1500] * 8, num_q_heads=16, num_kv_heads=4, head_dim=128,
+                page_size=64, seed=7, dtype=dtype)
+    if kind == "outlier":
+        return W.share_runs(w, [(1, [2, 3, 4, 5, 6, 7], 0, 16), (1, [0], 0, 1)])
+    return W.share_runs(w, [(0, [1, 2, 3], 0, 16), (0, [4, 5, 6, 7], 0, 4), (4, [5, 6, 7], 4, 12)])
+
+
+@pytest.mark.parametrize("kind,dtype", [("outlier", None), ("nested", None), ("leader-outlier", None),
+                                        ("many-nested", None), ("nested", "fp8")])
+def test_shared_prefix_uneven_groups_elementwise(kind, dtype):
+    """Shared-prefix groups chosen over the tree of common page runs, elementwise against the
+    oracle (fp8 pools: against the dequantised pools, at the fp8 tolerance)."""
+    base = _uneven(kind, dtype)
+    # the N(0,1) input and its focused companion (O(1) outputs: a lost or doubled key range
+    # of a group would move them far past the tolerance)
+    for w in (base, W.focus(base)):
+        _say(f"[gpu] shared-prefix uneven groups {w.name} {w.dtype}")
+        out, plan = api.run_workload(w, flags=api.VA_FLAG_SHARED_PREFIX)
+        st = api.varlen_attn_plan_stats(plan)
+        assert st["shared_groups"] >= 1 and st["shared_tiles"] > 0, st
+        got = out.float().cpu().numpy().astype(np.float64)
+        if dtype == "fp8":
+            K, V = oracle.dequantize_pools(w.k_pool, w.k_scale, w.v_pool, w.v_scale)
+            tol = 1e-2
+        else:
+            K, V, tol = w.k_pool, w.v_pool, TOL[w.dtype]
+        ref = oracle.varlen_paged_attention(w.q, K, V, w.block_table, w.q_start, w.q_end, w.kv_len, w.page_size)
+        e = float(np.abs(got - ref).max())
+        _say(f"[parity] shared-prefix uneven {w.name} {w.dtype} ({st['shared_groups']} groups, "
+             f"{st['shared_tiles']} group tiles; max|oracle| = {np.abs(ref).max():.2f}): "
+             f"max|gpu-oracle| = {e:.3e} (tol {tol})")
+        assert np.isfinite(got).all() and e <= tol
+

@@ -355,6 +355,66 @@ def test_shared_prefix_groups_found():
     assert st0["shared_groups"] == 0 and st0["split_item_kv_bytes"] == st0["physical_kv_bytes"]
 
 
+def _uneven_sharing(kind):
+    """Eight decodes (g = 4, page 64, 23 full pages each) whose tables share runs of pages
+    unevenly: "outlier" -- requests 1-7 share 16 pages, request 0 only the first;
+    "nested" -- all share 4 pages, requests 0-3 share 16, requests 4-7 share 12."""
+    w = W.build(f"uneven-{kind}", [1] * 8, [1500] * 8, num_q_heads=16, num_kv_heads=4, head_dim=128,
+                page_size=64, seed=7)
+    if kind == "outlier":
+        return W.share_runs(w, [(1, [2, 3, 4, 5, 6, 7], 0, 16), (1, [0], 0, 1)])
+    return W.share_runs(w, [(0, [1, 2, 3], 0, 16), (0, [4, 5, 6, 7], 0, 4), (4, [5, 6, 7], 4, 12)])
+
+
+def _groups_of(w, plan):
+    """{requests of a group: its shared keys} from the plan's group tiles."""
+    tiles = api.varlen_attn_plan_export(plan, 3)
+    cols = api.varlen_attn_plan_export(plan, 1)
+    req_of_row = {}
+    for r in range(w.num_reqs):
+        for row in range(int(w.q_start[r]), int(w.q_end[r])):
+            req_of_row[row] = r
+    groups = {}
+    for t in tiles:
+        if t[10] & 1 and t[11] == 1:
+            col0, ncols, k1 = int(t[2]), int(t[3]), int(t[6])
+            reqs = frozenset(req_of_row[int(c[0])] for c in cols[col0:col0 + ncols])
+            key = (reqs, int(t[1]))
+            groups[key] = max(groups.get(key, 0), k1)
+    out = {}
+    for (reqs, kvh), k1 in groups.items():
+        out.setdefault(reqs, set()).add(k1)
+    return {reqs: ks.pop() for reqs, ks in out.items() if len(ks) == 1}
+
+
+@pytest.mark.parametrize("kind,expect", [
+    ("outlier", {frozenset(range(1, 8)): 16 * 64}),
+    ("nested", {frozenset(range(0, 4)): 16 * 64, frozenset(range(4, 8)): 12 * 64}),
+])
+def test_shared_prefix_groups_uneven(kind, expect):
+    """Groups follow the tree of common page runs: a member sharing one page does not shorten
+    the others' run, and nested prefixes get groups of their own when that saves more page
+    reads than one wider, shallower group (the choice maximises pages read once for all)."""
+    w = _uneven_sharing(kind)
+    plan = _plan(w, HOST | api.VA_FLAG_SHARED_PREFIX)
+    check_coverage(w, plan)
+    st = api.varlen_attn_plan_stats(plan)
+    assert st["shared_groups"] == len(expect)
+    assert _groups_of(w, plan) == expect
+    assert st["physical_kv_bytes"] == oracle.physical_kv_bytes(w.block_table, w.kv_len, w.page_size,
+                                                               w.num_kv_heads, w.head_dim, w.elem_bytes)
+
+
+def test_shared_prefix_groups_leader_outlier():
+    """The lowest-numbered request sharing only the first page does not set the group."""
+    w = W.build("uneven-lead", [1] * 6, [900] * 6, num_q_heads=8, num_kv_heads=2, head_dim=64,
+                page_size=16, seed=9)
+    w = W.share_runs(w, [(3, [1, 2, 4, 5], 0, 40), (3, [0], 0, 1)])
+    plan = _plan(w, HOST | api.VA_FLAG_SHARED_PREFIX)
+    check_coverage(w, plan)
+    assert _groups_of(w, plan) == {frozenset([1, 2, 3, 4, 5]): 40 * 16}
+
+
 def test_config_shapes():
     """The workloads match the configurations they stand for."""
     w = W.config(2)

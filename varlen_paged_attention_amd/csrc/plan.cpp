@@ -21,6 +21,7 @@
 #include <mutex>
 #include <cmath>
 #include <cstring>
+#include <functional>
 #include <map>
 #include <new>
 #include <numeric>
@@ -59,6 +60,118 @@ struct Block {          // a set of <= 16 query columns scored against one kv ra
 };
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Shared-prefix groups among requests whose block tables start with the same physical page.
+// `mem` are those requests; run(a, b) is the number of leading pages requests a and b have
+// in common (already capped by the full pages every row of both sees).  Sorted by their page
+// sequences, the requests form a tree of common runs (a node: a range of the sorted order
+// whose pairs all share `depth` pages; its children split it where neighbours share no more
+// than that).  A group is a node's members not already grouped below it, reading the node's
+// `depth` pages once for all of them: it saves (members - 1) * depth page reads.  A dynamic
+// programme over the tree picks the groups with the largest total saving (the state: how many
+// of a subtree's members are left free for a group higher up), so a member that shares one
+// page no longer shortens the others' run, and nested prefixes get groups of their own when
+// that saves more than one wider, shallower group.  Returns (members, shared pages) pairs.
+template <typename RunFn>
+std::vector<std::pair<std::vector<int>, int>> prefix_groups(std::vector<int> mem, const std::vector<int>& lim,
+                                                            RunFn run_of, const std::function<bool(int, int)>& less) {
+  std::vector<std::pair<std::vector<int>, int>> out;
+  const int n = int(mem.size());
+  if (n < 2) return out;
+  std::sort(mem.begin(), mem.end(), less);
+  std::vector<int> lcp(n, 0);                           // lcp[i]: pages mem[i-1] and mem[i] share
+  for (int i = 1; i < n; ++i) lcp[i] = run_of(mem[i - 1], mem[i]);
+  struct Node {
+    int lo, hi, depth;
+    std::vector<int> kids;                              // child nodes (ranges of the sorted order)
+    std::vector<int64_t> best;                          // best[j]: saving with j members left free
+    int group_j = -1;                                   // free count grouped here for best[0]
+    std::vector<std::vector<int>> pick;                 // pick[k][t]: free members of kid k for total t
+  };
+  std::vector<Node> nodes;
+  std::function<int(int, int)> build = [&](int lo, int hi) -> int {
+    const int id = int(nodes.size());
+    nodes.push_back(Node{lo, hi, 0, {}, {}, -1, {}});
+    if (hi - lo == 1) {
+      nodes[id].depth = lim[mem[lo]];
+      return id;
+    }
+    int d = INT32_MAX;
+    for (int i = lo + 1; i < hi; ++i) d = std::min(d, lcp[i]);
+    nodes[id].depth = d;
+    std::vector<int> kids;
+    for (int a = lo; a < hi;) {
+      int b = a + 1;
+      while (b < hi && lcp[b] > d) ++b;
+      kids.push_back(build(a, b));
+      a = b;
+    }
+    nodes[id].kids = kids;
+    return id;
+  };
+  constexpr int64_t kNone = INT64_MIN / 4;
+  std::function<void(int)> solve = [&](int id) {
+    Node& v = nodes[id];
+    if (v.hi - v.lo == 1) {
+      v.best = {kNone, 0};                              // one request alone is left free
+      return;
+    }
+    std::vector<int64_t> comb = {0};
+    for (int k : v.kids) {
+      solve(k);
+      const std::vector<int64_t>& cb = nodes[k].best;
+      std::vector<int64_t> next(comb.size() + cb.size() - 1, kNone);
+      std::vector<int> arg(next.size(), -1);
+      for (size_t a = 0; a < comb.size(); ++a)
+        if (comb[a] != kNone)
+          for (size_t c = 0; c < cb.size(); ++c)
+            if (cb[c] != kNone && comb[a] + cb[c] > next[a + c]) {
+              next[a + c] = comb[a] + cb[c];
+              arg[a + c] = int(c);
+            }
+      nodes[id].pick.push_back(arg);
+      comb.swap(next);
+    }
+    Node& w = nodes[id];
+    w.best = comb;
+    if (w.depth >= 1)
+      for (size_t j = 2; j < comb.size(); ++j)
+        if (comb[j] != kNone && comb[j] + int64_t(j - 1) * w.depth > w.best[0]) {
+          w.best[0] = comb[j] + int64_t(j - 1) * w.depth;
+          w.group_j = int(j);
+        }
+  };
+  // members of node id left free when it ends with j free (groups below are emitted)
+  std::function<void(int, int, std::vector<int>&)> assign = [&](int id, int j, std::vector<int>& free_out) {
+    const Node& v = nodes[id];
+    if (v.hi - v.lo == 1) {
+      free_out.push_back(mem[v.lo]);
+      return;
+    }
+    const bool here = j == 0 && v.group_j >= 0;
+    int t = here ? v.group_j : j;
+    std::vector<int> kid_j(v.kids.size());
+    for (int k = int(v.kids.size()) - 1; k >= 0; --k) {
+      kid_j[k] = v.pick[k][t];
+      t -= kid_j[k];
+    }
+    std::vector<int> freed;
+    for (size_t k = 0; k < v.kids.size(); ++k) assign(v.kids[k], kid_j[k], freed);
+    if (here)
+      out.push_back({freed, v.depth});
+    else
+      free_out.insert(free_out.end(), freed.begin(), freed.end());
+  };
+  const int root = build(0, n);
+  solve(root);
+  const std::vector<int64_t>& b = nodes[root].best;
+  int jbest = 0;
+  for (size_t j = 0; j < b.size(); ++j)
+    if (b[j] != kNone && (b[jbest] == kNone || b[j] > b[jbest])) jbest = int(j);
+  std::vector<int> left;
+  if (b[jbest] > 0) assign(root, jbest, left);
+  return out;
+}
 
 // Launch order of the prefill tiles.  Workgroup i of a launch goes to XCD i % xcds, and each
 // XCD has its own L2: tiles that read the same keys (one request's KV head, or one key
@@ -264,32 +377,31 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
   std::vector<std::vector<int>> groups;
   if (p.flags & VA_FLAG_SHARED_PREFIX) {
     std::map<int32_t, std::vector<int>> by_first;
+    std::vector<int> lim(num_reqs, 0);
     for (int r : short_reqs) {
       const int m = q_end[r] - q_start[r];
       const int S0 = kv_len[r] - m;
       // a shared page must be full and entirely visible to every row of the request
-      const int lim = std::min(kv_len[r] / ps, (S0 + 1) / ps);
-      if (lim >= 1) by_first[bt(r, 0)].push_back(r);
+      lim[r] = std::min(kv_len[r] / ps, (S0 + 1) / ps);
+      if (lim[r] >= 1) by_first[bt(r, 0)].push_back(r);
     }
+    auto run_of = [&](int a, int b) {
+      const int cap = std::min(lim[a], lim[b]);
+      int c = 0;
+      while (c < cap && bt(a, c) == bt(b, c)) ++c;
+      return c;
+    };
+    const std::function<bool(int, int)> less = [&](int a, int b) {
+      const int c = run_of(a, b);
+      if (c < lim[a] && c < lim[b]) return bt(a, c) < bt(b, c);
+      return lim[a] != lim[b] ? lim[a] < lim[b] : a < b;
+    };
     for (auto& kvp : by_first) {
-      std::vector<int>& mem = kvp.second;
-      if (mem.size() < 2) continue;
-      int cp = INT32_MAX;
-      for (int r : mem) {
-        const int m = q_end[r] - q_start[r];
-        cp = std::min(cp, std::min(kv_len[r] / ps, (kv_len[r] - m + 1) / ps));
+      if (kvp.second.size() < 2) continue;
+      for (auto& gr : prefix_groups(kvp.second, lim, run_of, less)) {
+        for (int r : gr.first) shared_pages[r] = gr.second;
+        groups.push_back(gr.first);
       }
-      const int lead = mem[0];
-      int common = 0;
-      while (common < cp) {
-        bool same = true;
-        for (int r : mem) same = same && bt(r, common) == bt(lead, common);
-        if (!same) break;
-        ++common;
-      }
-      if (common < 1) continue;
-      for (int r : mem) shared_pages[r] = common;
-      groups.push_back(mem);
     }
   }
 

@@ -374,6 +374,29 @@ def subset(w: Workload, reqs: Sequence[int], name: Optional[str] = None) -> Work
     return out
 
 
+def share_runs(w: Workload, runs: Sequence[tuple], name: Optional[str] = None) -> Workload:
+    """A copy of ``w`` whose block tables share more pages: for each (src, dsts, p0, p1),
+    requests ``dsts`` read request ``src``'s physical pages at logical pages [p0, p1).  Those
+    must be full pages of every request involved (no tail page, whose slots past kv_len may
+    be poisoned).  Only the tables change; the pools keep every page (pages no table names
+    any more stay in them, unread)."""
+    import copy
+    out = copy.copy(w)
+    out.name = name or f"{w.name}/shared-runs"
+    bt = w.block_table.copy()
+    ps = w.page_size
+    for src, dsts, p0, p1 in runs:
+        for r in [src] + list(dsts):
+            assert p1 * ps <= int(w.kv_len[r]) and (p1 < -(-int(w.kv_len[r]) // ps) or int(w.kv_len[r]) % ps == 0), \
+                f"request {r}: pages [{p0}, {p1}) are not all full pages"
+        for r in dsts:
+            bt[r, p0:p1] = bt[src, p0:p1]
+    out.block_table = bt
+    out.notes = dict(w.notes)
+    out.notes.pop("hot", None)
+    return out
+
+
 STREAM_FOCUS = 5
 
 

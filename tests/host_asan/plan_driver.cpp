@@ -323,6 +323,38 @@ int main() {
     if (U(rng) % 5 == 0) c.p.prefill_min_rows = 1 + U(rng) % 64;
     outputs += run_case(c);
   }
+  // ---- random tree-shaped sharing: requests point runs of their leading pages at another
+  // request's pages (later runs overwrite earlier ones, so runs nest and cross), planned with
+  // the shared-prefix flag
+  for (int n = 0; n < 300; ++n) {
+    std::uniform_int_distribution<int> U(0, 1 << 30);
+    const int R = 2 + U(rng) % 24, ps = ps_opts[U(rng) % 5], hkv = 1 + U(rng) % 4, g = 1 << (U(rng) % 4);
+    std::vector<int> kv, qr;
+    for (int r = 0; r < R; ++r) {
+      const int m = U(rng) % 3 == 0 ? 1 + U(rng) % 8 : 1;
+      kv.push_back(m + ps * (1 + U(rng) % 24) + U(rng) % ps);
+      qr.push_back(m);
+    }
+    Case c = make("tree-shared " + std::to_string(n), qr, kv, hkv * g, hkv, U(rng) % 2 ? 64 : 128, ps,
+                  dtypes[U(rng) % 3], rng);
+    const int maxp = c.p.max_pages_per_req;
+    const int ops = 1 + U(rng) % 6;
+    for (int o = 0; o < ops; ++o) {
+      const int src = U(rng) % R;
+      for (int r = 0; r < R; ++r) {
+        if (r == src || U(rng) % 2) continue;
+        // full pages every row of both requests sees
+        const int lim = std::min((kv[src] - qr[src] + 1) / ps, (kv[r] - qr[r] + 1) / ps);
+        if (lim < 1) continue;
+        const int run = 1 + U(rng) % lim;
+        for (int j = 0; j < run; ++j) c.bt[size_t(r) * maxp + j] = c.bt[size_t(src) * maxp + j];
+      }
+    }
+    c.p.flags |= VA_FLAG_SHARED_PREFIX;
+    if (U(rng) % 4 == 0) c.p.flags |= VA_FLAG_NO_DECODE_TILES;
+    if (U(rng) % 5 == 0) c.p.flags |= VA_FLAG_NO_PREFILL_KERNEL;
+    outputs += run_case(c);
+  }
   // ---- the pages' workload shapes
   {
     std::uniform_int_distribution<int> dec(1024, 8192), mix(512, 16384);

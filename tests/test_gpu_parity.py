@@ -473,3 +473,24 @@ def test_shared_prefix_uneven_groups_elementwise(kind, dtype):
              f"max|gpu-oracle| = {e:.3e} (tol {tol})")
         assert np.isfinite(got).all() and e <= tol
 
+
+def test_readme_example_runs():
+    """The usage example in README.md runs as printed and its output matches the oracle."""
+    import os
+    import re
+    import torch
+    text = open(os.path.join(os.path.dirname(__file__), "..", "README.md")).read()
+    code = re.search(r"```python\n(.*?)```", text, re.S).group(1)
+    env = {}
+    exec(compile(code, "README.md", "exec"), env)
+    torch.cuda.synchronize()
+    bt = env["block_table"]
+    K = env["k_pool"].float().cpu().numpy().astype(np.float64)
+    V = env["v_pool"].float().cpu().numpy().astype(np.float64)
+    Q = env["q"].float().cpu().numpy().astype(np.float64)
+    ref = oracle.varlen_paged_attention(Q, K, V, bt, np.array(env["q_start"]), np.array(env["q_end"]),
+                                        np.array(env["kv_len"]), env["ps"])
+    e = float(np.abs(env["out"].float().cpu().numpy() - ref).max())
+    _say(f"[parity] README example: max|gpu-oracle| = {e:.3e}")
+    assert e <= TOL["bf16"]
+

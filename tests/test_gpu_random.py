@@ -3,7 +3,8 @@ rows, chunks on cached prefixes, uncached prompts, empty requests), head layouts
 dims, page sizes, storage types, planner flags and shared page runs, each compared
 elementwise with the oracle (tolerance 2e-2 for bf16 pools, 1e-2 for fp8 pools), and every
 third one also on its focused companion input (O(1) outputs, compared at 2e-2 for both: they
-reach 2-4, where the bf16 output's own rounding is up to 7.8e-3).  Slots past each request's
+reach 2-4, where the bf16 output's own rounding is up to 7.8e-3), and every fourth one is
+also captured in a HIP graph whose replays must equal the eager run bit for bit.  Slots past each request's
 length hold NaN.  The draws are seeded, so a failure names a reproducible case."""
 import sys
 
@@ -15,7 +16,7 @@ from varlen_paged_attention_amd import api, workloads as W
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 36
+N_CASES = 96
 
 
 def _say(msg):
@@ -72,8 +73,41 @@ def _draw(seed):
     return w, flags, kw, desc
 
 
-def _check(w, flags, kw, desc, focused=False):
+def _graph_matches_eager(w, plan, desc):
+    """Capture the run in a HIP graph; three replays (the inputs changed before the last)
+    must equal eager runs bit for bit."""
+    import torch
+    q, k, v, bt = api.to_device(w)
+    scales = dict(zip(("k_scale", "v_scale"), api.scales_to_device(w))) if w.dtype == "fp8" else {}
+    ws = api.new_workspace(plan)
+    out_e, out_g = torch.zeros_like(q), torch.zeros_like(q)
+    api.RunCall(plan, q, k, v, bt, out_e, ws, **scales)()
+    g, s = torch.cuda.CUDAGraph(), torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call = api.RunCall(plan, q, k, v, bt, out_g, ws, stream=s, **scales)
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    torch.cuda.synchronize()
+    q0 = q.clone()
+    for rep in range(3):
+        if rep == 2:
+            q.copy_(q0.flip(0))
+            api.RunCall(plan, q, k, v, bt, out_e, ws, **scales)()
+        out_g.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = out_g.view(torch.int16).cpu().numpy(), out_e.view(torch.int16).cpu().numpy()
+        assert np.array_equal(a, b), f"{desc}: graph replay {rep} differs from eager"
+
+
+def _check(w, flags, kw, desc, focused=False, graph=False):
     out, plan = api.run_workload(w, flags=flags, **kw)
+    if graph:
+        _graph_matches_eager(w, plan, desc)
     got = out.float().cpu().numpy().astype(np.float64)
     if w.dtype == "fp8":
         K, V = oracle.dequantize_pools(w.k_pool, w.k_scale, w.v_pool, w.v_scale)
@@ -99,7 +133,7 @@ def _check(w, flags, kw, desc, focused=False):
 def test_random_iteration(seed):
     w, flags, kw, desc = _draw(seed)
     _say(f"[gpu] random case {desc}")
-    _check(w, flags, kw, desc)
+    _check(w, flags, kw, desc, graph=seed % 4 == 1)
     if seed % 3 == 0 and any(int(w.q_end[r]) > int(w.q_start[r]) and int(w.kv_len[r]) >= 8
                              for r in range(w.num_reqs)):
         wf = W.focus(w)

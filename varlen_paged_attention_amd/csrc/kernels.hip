@@ -16,6 +16,7 @@
 
 #include <atomic>
 #include <cfloat>
+#include <type_traits>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -752,16 +753,17 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
         }
     }
   };
-  auto exp_block = [&](const f32x16& sc, int slot, int b, bf16x8 (&pb)[2]) {
+  // exponentials of a 32-key block's arguments (scores in base 2 less the running max)
+  auto exp_block = [&](const f32x16& ex, int slot, int b, bf16x8 (&pb)[2]) {
     if constexpr (F8) {
-      // scores are in base-2 units with log2 |s_V| added: the exponential is p * |s_V|, and
-      // the row sum adds bf16(p * |s_V|) / |s_V|, the inverse taken as hi + lo bf16 parts
+      // the arguments include log2 |s_V|: the exponential is p * |s_V|, and the row sum
+      // adds bf16(p * |s_V|) / |s_V|, the inverse taken as hi + lo bf16 parts
       const bf16x8* ih = reinterpret_cast<const bf16x8*>(sVh + slot * kPTileKeys + 32 * b + 8 * h);
       const bf16x8* il = reinterpret_cast<const bf16x8*>(sVl + slot * kPTileKeys + 32 * b + 8 * h);
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pb[t][e] = bf16(fast_exp2(sc[8 * t + e] - m_run));
+        for (int e = 0; e < 8; ++e) pb[t][e] = bf16(fast_exp2(ex[8 * t + e]));
         const bf16x8 hi = ih[2 * t], lo = il[2 * t];
         float ls[2] = {0.f, 0.f};
 #pragma unroll
@@ -776,10 +778,46 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pb[t][e] = bf16(fast_exp2(fmaf(sc[8 * t + e], scale_log2, -m_run)));
+        for (int e = 0; e < 8; ++e) pb[t][e] = bf16(fast_exp2(ex[8 * t + e]));
         l_run += sum8_bf16(pb[t]);
       }
     }
+  };
+  // the causal mask on tile t's scores (keys past a column's last visible position)
+  auto mask_tile = [&](int t, f32x16 (&sn)[2]) {
+    const int k0 = kbeg + t * kPTileKeys;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int ii = e >> 2, jj = e & 3;
+        const int key = k0 + 32 * b + 16 * (ii >> 1) + 8 * h + 4 * (ii & 1) + jj;
+        if (key > limit) sn[b][e] = -INFINITY;
+      }
+  };
+  // tile t's running max and exponent arguments ex (lazy rescaling: the reference max moves
+  // only when the tile's max passes it by more than the slack; then the row sum, which holds
+  // the tiles before t, is scaled by alpha here, and the accumulator before t's P.V)
+  float alpha = 1.f;
+  bool rescale = false;
+  auto next_args = [&](const f32x16 (&sn)[2], f32x16 (&ex)[2]) {
+    float mx = sn[0][0];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sn[b][e]);
+    mx = fmaxf(mx, other_half(mx));
+    const float m_tile = F8 ? mx : mx * scale_log2;    // fp8 scores are already in base 2
+    const bool need = m_tile > m_run + kRescaleSlack;
+    const float m_new = need ? m_tile : m_run;
+    alpha = fast_exp2(m_run - m_new);
+    rescale = __any(need);
+    l_run *= alpha;
+    m_run = m_new;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) ex[b][e] = F8 ? sn[b][e] - m_run : fmaf(sn[b][e], scale_log2, -m_run);
   };
   auto pv_tile = [&](int buf, const bf16x8 (&p)[2][2]) {
     const bf16x8* vb = sV + buf * VBUF + vread;
@@ -822,7 +860,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
     return;
   }
 
-  // ---- prologue: K(0), K(1), V(0) in LDS; scores of tile 0
+  // ---- prologue: K(0), K(1), V(0) in LDS; scores of tile 0 and their exponent arguments
   int p1 = ntiles > 1 ? page_for(1) : 0;
   {
     const int p0 = page_for(0);
@@ -838,71 +876,92 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
   int p2 = ntiles > 2 ? page_for(2) : 0;
   int p3 = ntiles > 3 ? page_for(3) : 0;
   __syncthreads();
-  f32x16 sc[2];
-  if (w_max_limit >= 0) {
-    qk_block(0, 0, sc[0]);
-    qk_block(0, 1, sc[1]);
+  // the last tile with keys this wave's columns see (-1: none), and the first whose keys pass
+  // the first visible position of one of them (it and those after it need the mask); every
+  // wave still copies its slice of every tile and meets the others at every barrier
+  const int j_last = w_max_limit >= kbeg ? min(ntiles - 1, (w_max_limit - kbeg) / kPTileKeys) : -1;
+  const int t_mask = w_min_limit - kbeg - (kPTileKeys - 1) < 0 ? 0 : (w_min_limit - kbeg - (kPTileKeys - 1)) / kPTileKeys + 1;
+  f32x16 ex[2], sn[2];
+  if (j_last >= 0) {
+    qk_block(0, 0, sn[0]);
+    qk_block(0, 1, sn[1]);
+    k_scale_block(0, 0, sn[0]);
+    k_scale_block(0, 1, sn[1]);
+    if (t_mask == 0) mask_tile(0, sn);
+    next_args(sn, ex);
+    rescale = false;                          // the accumulator is still zero
   }
   __syncthreads();
 
-  for (int j = 0; j < ntiles; ++j) {
-    const bool ld_k = j + 2 < ntiles, ld_v = j + 1 < ntiles;
-    if (ld_k) issue_k(j + 2, p2, j & 1);
-    if (ld_v) issue_v(j + 1, p1, (j + 1) & 1);
+  auto stage_in = [&](int j) {                // copies of K(j+2) and V(j+1)
+    if (j + 2 < ntiles) issue_k(j + 2, p2, j & 1);
+    if (j + 1 < ntiles) issue_v(j + 1, p1, (j + 1) & 1);
     p1 = p2;
     p2 = p3;
     if (j + 4 < ntiles) p3 = page_for(j + 4);
-    const int k0 = kbeg + j * kPTileKeys;
-    if (k0 <= w_max_limit) {
-      k_scale_block(j % 3, 0, sc[0]);
-      k_scale_block(j % 3, 1, sc[1]);
-      if (k0 + kPTileKeys - 1 > w_min_limit) {
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int ii = e >> 2, jj = e & 3;
-            const int key = k0 + 32 * b + 16 * (ii >> 1) + 8 * h + 4 * (ii & 1) + jj;
-            if (key > limit) sc[b][e] = -INFINITY;
-          }
-      }
-      float mx = sc[0][0];
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[b][e]);
-      mx = fmaxf(mx, other_half(mx));
-      const float m_tile = F8 ? mx : mx * scale_log2;   // fp8 scores are already in base 2
-      const bool need = m_tile > m_run + kRescaleSlack;
-      if (__any(need)) {
-        const float m_new = need ? m_tile : m_run;
-        const float alpha = fast_exp2(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
-      }
-      bf16x8 p[2][2];
-      if (k0 + kPTileKeys <= w_max_limit) {
-        // the MFMAs of tile j+1's block b overlap the exponentials of tile j's block b
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          f32x16 sn;
-          qk_block((j + 1) & 1, b, sn);
-          exp_block(sc[b], j % 3, b, p[b]);
-          sc[b] = sn;
-        }
-      } else {
-        exp_block(sc[0], j % 3, 0, p[0]);
-        exp_block(sc[1], j % 3, 1, p[1]);
-      }
-      pv_tile(j & 1, p);
-    }
+  };
+  auto stage_done = [&](int j) {              // those copies landed (and widened): barrier
     wait_vmem();
-    if (ld_v) fix_v_tail(j + 1, (j + 1) & 1);
-    if (ld_k) convert_k(j + 2, j & 1);
-    if (ld_v) convert_v(j + 1, (j + 1) & 1);
+    if (j + 1 < ntiles) fix_v_tail(j + 1, (j + 1) & 1);
+    if (j + 2 < ntiles) convert_k(j + 2, j & 1);
+    if (j + 1 < ntiles) convert_v(j + 1, (j + 1) & 1);
     __syncthreads();
+  };
+  // iteration j < j_last: tile j+1's scores (MFMA) under tile j's exponentials (VALU), then
+  // tile j's P.V (MFMA) under tile j+1's max and exponent arguments (VALU).  MASKED: tile
+  // j+1 needs the causal mask.  FAST (bf16, j + 2 < ntiles: no tail to clear): from the
+  // first MFMA to the barrier one basic block, so the compiler keeps each VALU part beside
+  // the MFMAs it overlaps.  A rescale decided for tile j+1 is applied to the accumulator at
+  // the top of the next iteration, after tile j's P.V and before tile j+1's.
+  auto step = [&](int j, auto masked, auto fast) {
+    if (rescale) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
+    }
+    stage_in(j);
+    bf16x8 p[2][2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      qk_block((j + 1) & 1, b, sn[b]);
+      exp_block(ex[b], j % 3, b, p[b]);
+    }
+    k_scale_block((j + 1) % 3, 0, sn[0]);
+    k_scale_block((j + 1) % 3, 1, sn[1]);
+    if constexpr (decltype(masked)::value) mask_tile(j + 1, sn);
+    pv_tile(j & 1, p);
+    next_args(sn, ex);
+    if constexpr (decltype(fast)::value) {
+      wait_vmem();
+      __syncthreads();
+    } else {
+      stage_done(j);
+    }
+  };
+  using no = std::false_type;
+  using yes = std::true_type;
+  int j = 0;
+  const int j_nm = min(j_last, max(0, t_mask - 1));   // j < j_nm: tile j+1 needs no mask
+  const int j_f = F8 ? 0 : min(j_last, ntiles - 2);    // j < j_f: fast
+  for (; j < min(j_nm, j_f); ++j) step(j, no{}, yes{});
+  for (; j < j_nm; ++j) step(j, no{}, no{});
+  for (; j < j_f; ++j) step(j, yes{}, yes{});
+  for (; j < j_last; ++j) step(j, yes{}, no{});
+  if (j == j_last) {                          // the wave's last tile: exponentials and P.V
+    if (rescale) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
+    }
+    stage_in(j);
+    bf16x8 p[2][2];
+    exp_block(ex[0], j % 3, 0, p[0]);
+    exp_block(ex[1], j % 3, 1, p[1]);
+    pv_tile(j & 1, p);
+    stage_done(j);
+    ++j;
+  }
+  for (; j < ntiles; ++j) {
+    stage_in(j);
+    stage_done(j);
   }
   // ---- normalise and write: acc[db][4*ii + jj] is d = 32*db + 8*ii + 4*h + jj of this column
   const float l_tot = l_run + other_half(l_run);

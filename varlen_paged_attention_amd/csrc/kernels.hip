@@ -388,7 +388,11 @@ template <int D>
 struct PrefillLds {
   static constexpr int KCH = D / 8;                    // 16-byte chunks per K row
   static constexpr int KROW = KCH + 1;                 // padded K row
-  static constexpr int KBUF = kPTileKeys * KROW;       // chunks per K buffer
+  // a wave's 16-key K slice is 16 padded rows, copied by whole 64-lane DMA instructions
+  // (the last one's spare lanes land in the slack after the rows, so no instruction needs
+  // a lane mask)
+  static constexpr int KSS = (kPSliceKeys * KROW + 63) / 64 * 64;
+  static constexpr int KBUF = kPrefillWaves * KSS;     // chunks per K buffer
   static constexpr int VBUF = kPTileKeys / 8 * D;      // chunks per V^T buffer
   static constexpr int bytes = 2 * (KBUF + VBUF) * 16;
   // fp8, per key: the K and V scales as copied (two stages); the K scale times log2 e and
@@ -450,12 +454,16 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
     float* __restrict__ ws_ml, float* __restrict__ ws_acc, int Hq, int g, Paged pg, float scale_log2,
     GatherOut go) {
   using Lay = PrefillLds<D>;
-  constexpr int KCH = Lay::KCH, KROW = Lay::KROW, KBUF = Lay::KBUF, VBUF = Lay::VBUF;
+  constexpr int KCH = Lay::KCH, KROW = Lay::KROW, KBUF = Lay::KBUF, VBUF = Lay::VBUF, KSS = Lay::KSS;
   constexpr int WK = kPSliceKeys;                      // 16 keys per wave slice
   static_assert(WK == 16, "slice layout assumes 16 keys per wave");
   constexpr int KSC = WK * KROW;                       // K slice chunks (with pad)
-  constexpr int KNI = (KSC + 63) / 64;                 // DMA instructions per K slice
-  constexpr int KLAST = KSC - 64 * (KNI - 1);          // lanes active in the last one
+  constexpr int KNI = KSS / 64;                        // DMA instructions per K slice
+  constexpr int KLAST = KSC - 64 * (KNI - 1);          // lanes of the last one that hold rows
+  // whole tiles (prefill, MFMA-bound) issue their copies inside the loop's main block;
+  // the other tiles (key chunks and column lists, mostly streaming KV from HBM) at the
+  // top of each iteration, where the copies have the whole iteration to land
+  constexpr bool kInBlockCopies = MODE == kWholeTile;
   constexpr int VSC = WK / 8 * D;                      // V^T slice chunks
   constexpr int VNI = VSC / 64;
   static_assert(VNI * 64 == VSC, "V^T slice must be whole instructions");
@@ -559,7 +567,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
   // fp8: raw slice sizes (16-byte chunks) and where they sit inside the bf16 slices
   constexpr int KR = WK * D / 16;                      // K codes of the slice
   constexpr int VR = D;                                // V codes: one chunk (16 keys) per d
-  constexpr int KRAW = KSC - KR;                       // raw K codes at the top of the slice
+  constexpr int KRAW = KSS - KR;                       // raw K codes at the top of the slice
   constexpr int VRAW = VSC - VR;
   static_assert(KRAW >= 0 && VRAW >= 0, "raw fp8 slices must fit in the bf16 slices");
 
@@ -582,11 +590,12 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
   auto page_for = [&](int t) -> int {
     return pg.page_of(btr, min(kbeg + t * kPTileKeys + wv * WK, kv_end - 1));
   };
-  auto issue_k = [&](int t, int page, int buf) {
+  // FULL: tile t is not the last one, so every slice holds 16 keys before the end
+  auto issue_k = [&](int t, int page, int buf, bool full) {
     const int k0w = kbeg + t * kPTileKeys + wv * WK;
-    if (k0w >= kv_end) return;               // positions past the end: scores are masked
+    if (!full && k0w >= kv_end) return;      // positions past the end: scores are masked
     const auto rs = slice_rsrc(kbase + size_t(page) * page_bytes + size_t(k0w & ps_mask) * D * EB);
-    bf16x8* dst = sK + buf * KBUF + wv * KSC;
+    bf16x8* dst = sK + buf * KBUF + wv * KSS;
     if constexpr (F8) {
       // codes: lane -> raw chunk L = 64r + lane = (key L / (D/16), 16-byte piece L % (D/16))
 #pragma unroll
@@ -602,13 +611,13 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
     } else {
 #pragma unroll
       for (int r = 0; r < KNI; ++r)
-        if (r < KNI - 1 || lane < KLAST) dma_b128(rs, dst + 64 * r, koff[r], 0);
+        if (kInBlockCopies || r < KNI - 1 || lane < KLAST) dma_b128(rs, dst + 64 * r, koff[r], 0);
     }
   };
-  auto issue_v = [&](int t, int page, int buf) {
+  auto issue_v = [&](int t, int page, int buf, bool full) {
     const int k0w = kbeg + t * kPTileKeys + wv * WK;
     bf16x8* dst = sV + buf * VBUF + wv * VSC;
-    if (k0w >= kv_end) {                      // never read garbage into V: write zeros
+    if (!full && k0w >= kv_end) {             // never read garbage into V: write zeros
 #pragma unroll
       for (int r = 0; r < VNI; ++r) dst[64 * r + lane] = bf16x8{};
       return;
@@ -654,7 +663,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
         sVl[so] = bf16(inv - float(hi));
       }
       if (k0w >= kv_end) return;
-      bf16x8* sl = sK + buf * KBUF + wv * KSC;
+      bf16x8* sl = sK + buf * KBUF + wv * KSS;
       constexpr int PER = KR / 64;                      // raw chunks per lane
       bf16x8 raw[PER];
 #pragma unroll
@@ -727,10 +736,10 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
   };
 
   // ---- per-wave compute pieces
-  const int kread = kap * KROW + h;                                 // + 32*b*KROW + 2*kc
+  const int kread = (kap >> 4) * KSS + (kap & 15) * KROW + h;       // + 2*b*KSS + 2*kc
   const int vread = rho * 2 + (h ^ ((rho >> 3) & 1));               // + (2b+t)*VSC + 64*db
   auto qk_block = [&](int buf, int b, f32x16& sn) {
-    const bf16x8* kb = sK + buf * KBUF + kread + 32 * b * KROW;
+    const bf16x8* kb = sK + buf * KBUF + kread + 2 * b * KSS;
 #pragma unroll
     for (int e = 0; e < 16; ++e) sn[e] = 0.f;
 #pragma unroll
@@ -831,13 +840,13 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
 
   if constexpr (MODE == kStageGather) {
     // stage each 64-key tile as the attention tiles do, then copy it out in logical order:
-    // K row kl of wave slice ws is chunks ws*KSC + kl*KROW + (0 .. KCH-1); element d of
+    // K row kl of wave slice ws is chunks ws*KSS + kl*KROW + (0 .. KCH-1); element d of
     // key kl of V^T slice ws is element kl % 8 of chunk ws*VSC + 2d + ((kl / 8) ^ bit 3 of d)
     const int64_t obase = go.kv_offset[T.req];
     for (int t = 0; t < ntiles; ++t) {
       const int pt = page_for(t);
-      issue_k(t, pt, 0);
-      issue_v(t, pt, 0);
+      issue_k(t, pt, 0, false);
+      issue_v(t, pt, 0, false);
       wait_vmem();
       fix_v_tail(t, 0);
       __syncthreads();
@@ -846,7 +855,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
         if (pos >= kv_end) continue;
         const int ws = key / WK, kl = key % WK;
         const size_t o = ((size_t(obase) + pos) * pg.Hkv + kvh) * D + 8 * ch;
-        *reinterpret_cast<bf16x8*>(go.k_out + o) = sK[ws * KSC + kl * KROW + ch];
+        *reinterpret_cast<bf16x8*>(go.k_out + o) = sK[ws * KSS + kl * KROW + ch];
         bf16x8 v;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -864,9 +873,9 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
   int p1 = ntiles > 1 ? page_for(1) : 0;
   {
     const int p0 = page_for(0);
-    issue_k(0, p0, 0);
-    issue_v(0, p0, 0);
-    if (ntiles > 1) issue_k(1, p1, 1);
+    issue_k(0, p0, 0, false);
+    issue_v(0, p0, 0, false);
+    if (ntiles > 1) issue_k(1, p1, 1, false);
     wait_vmem();
     fix_v_tail(0, 0);
     convert_k(0, 0);
@@ -894,8 +903,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
   __syncthreads();
 
   auto stage_in = [&](int j) {                // copies of K(j+2) and V(j+1)
-    if (j + 2 < ntiles) issue_k(j + 2, p2, j & 1);
-    if (j + 1 < ntiles) issue_v(j + 1, p1, (j + 1) & 1);
+    if (j + 2 < ntiles) issue_k(j + 2, p2, j & 1, false);
+    if (j + 1 < ntiles) issue_v(j + 1, p1, (j + 1) & 1, false);
     p1 = p2;
     p2 = p3;
     if (j + 4 < ntiles) p3 = page_for(j + 4);
@@ -909,28 +918,50 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
   };
   // iteration j < j_last: tile j+1's scores (MFMA) under tile j's exponentials (VALU), then
   // tile j's P.V (MFMA) under tile j+1's max and exponent arguments (VALU).  MASKED: tile
-  // j+1 needs the causal mask.  FAST (bf16, j + 2 < ntiles: no tail to clear): from the
-  // first MFMA to the barrier one basic block, so the compiler keeps each VALU part beside
-  // the MFMAs it overlaps.  A rescale decided for tile j+1 is applied to the accumulator at
-  // the top of the next iteration, after tile j's P.V and before tile j+1's.
+  // j+1 needs the causal mask.  FAST (bf16, tiles j+1 and j+2 not the last: no tail to
+  // clear, every copy whole): from the first MFMA to the barrier one basic block, so the
+  // compiler keeps each VALU part beside the MFMAs it overlaps, and the copies are issued
+  // inside it, K(j+2) between the two score blocks and V(j+1) before the P.V, instead of
+  // all waves of the workgroup issuing them at once after the barrier (the copy queue
+  // then holds each wave for hundreds of cycles).  A rescale decided for tile j+1 is
+  // applied to the accumulator at the top of the next iteration, after tile j's P.V and
+  // before tile j+1's.
   auto step = [&](int j, auto masked, auto fast) {
+    constexpr bool FAST = decltype(fast)::value;
     if (rescale) {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
     }
-    stage_in(j);
+    constexpr bool IN_BLOCK = FAST && kInBlockCopies;
+    if constexpr (!FAST) {
+      stage_in(j);
+    } else if constexpr (!IN_BLOCK) {
+      issue_k(j + 2, p2, j & 1, true);
+      issue_v(j + 1, p1, (j + 1) & 1, true);
+      p1 = p2;
+      p2 = p3;
+      p3 = page_for(j + 4);                   // clamped to the last key: always a valid entry
+    }
     bf16x8 p[2][2];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       qk_block((j + 1) & 1, b, sn[b]);
       exp_block(ex[b], j % 3, b, p[b]);
+      if (IN_BLOCK && b == 0) issue_k(j + 2, p2, j & 1, true);
     }
     k_scale_block((j + 1) % 3, 0, sn[0]);
     k_scale_block((j + 1) % 3, 1, sn[1]);
     if constexpr (decltype(masked)::value) mask_tile(j + 1, sn);
+    if constexpr (IN_BLOCK) {
+      issue_v(j + 1, p1, (j + 1) & 1, true);
+      p1 = p2;
+      p2 = p3;
+      p3 = page_for(j + 4);
+    }
     pv_tile(j & 1, p);
     next_args(sn, ex);
-    if constexpr (decltype(fast)::value) {
+    if constexpr (FAST) {
+      __builtin_amdgcn_sched_barrier(0);      // the wait stays after all of the block's work
       wait_vmem();
       __syncthreads();
     } else {
@@ -941,7 +972,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
   using yes = std::true_type;
   int j = 0;
   const int j_nm = min(j_last, max(0, t_mask - 1));   // j < j_nm: tile j+1 needs no mask
-  const int j_f = F8 ? 0 : min(j_last, ntiles - 2);    // j < j_f: fast
+  const int j_f = F8 ? 0 : min(j_last, ntiles - 3);    // j < j_f: fast
   for (; j < min(j_nm, j_f); ++j) step(j, no{}, yes{});
   for (; j < j_nm; ++j) step(j, no{}, no{});
   for (; j < j_f; ++j) step(j, yes{}, yes{});

@@ -943,6 +943,10 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
       p3 = page_for(j + 4);                   // clamped to the last key: always a valid entry
     }
     bf16x8 p[2][2];
+    // LLVM's MFMA/LDS interleaving strategy 0 reads operands further ahead of their
+    // MFMAs (whole tiles: chunk mix -2 %; the key-chunk and column-list tiles, which
+    // wait on HBM, ran 1-9 % slower with it)
+    if constexpr (IN_BLOCK) __builtin_amdgcn_iglp_opt(0);
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       qk_block((j + 1) & 1, b, sn[b]);

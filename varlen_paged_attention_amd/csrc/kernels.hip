@@ -463,7 +463,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
   // whole tiles (prefill, MFMA-bound) issue their copies inside the loop's main block;
   // the other tiles (key chunks and column lists, mostly streaming KV from HBM) at the
   // top of each iteration, where the copies have the whole iteration to land
-  constexpr bool kInBlockCopies = MODE == kWholeTile;
+  constexpr bool kInBlockCopies = MODE == kWholeTile && !F8;
   constexpr int VSC = WK / 8 * D;                      // V^T slice chunks
   constexpr int VNI = VSC / 64;
   static_assert(VNI * 64 == VSC, "V^T slice must be whole instructions");
@@ -735,6 +735,66 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
     }
   };
 
+  // fp8, tiles tk (K codes and scales landed in K buffer bk) and tv (V codes in V buffer
+  // bv) both whole (every key before the end): convert_k(tk) and convert_v(tv) without
+  // branches, every LDS read first, so the wave waits on LDS once instead of once per step.
+  // Lanes 16-63 repeat lane & 15's scale work and write the same values to the same slots.
+  auto widen_full = [&](int tk, int bk, int tv, int bv) {
+    if constexpr (F8) {
+      const int key = lane & (WK - 1);
+      bf16x8* kl = sK + bk * KBUF + wv * KSS;
+      bf16x8* vl = sV + bv * VBUF + wv * VSC;
+      constexpr int KP = KR / 64, VP = VR / 64;
+      bf16x8 kraw[KP], vraw[VP];
+#pragma unroll
+      for (int i = 0; i < KP; ++i) kraw[i] = kl[KRAW + 64 * i + lane];
+#pragma unroll
+      for (int i = 0; i < VP; ++i) vraw[i] = vl[VRAW + 64 * i + lane];
+      const float ks = sKs[bk * kPTileKeys + wv * WK + key];
+      const float vs_k = sVs[bk * kPTileKeys + wv * WK + key];   // V scale of tile tk's key
+      const float vs_v = sVs[bv * kPTileKeys + wv * WK + key];   // V scale of tile tv's key
+      // tile tk's per-key terms (see convert_k)
+      const float sv = fabsf(vs_k);
+      const bool tiny_k = sv < FLT_MIN;
+      const float ls = tiny_k ? 0.f : __builtin_amdgcn_logf(sv);
+      const float inv = tiny_k ? 1.f : __builtin_amdgcn_rcpf(sv);
+      const bf16 hi = bf16(inv);
+      const int so = (tk % 3) * kPTileKeys + wv * WK + key;
+      sKl[so] = ks * scale_log2;
+      sLv[so] = ls;
+      sVh[so] = hi;
+      sVl[so] = bf16(inv - float(hi));
+#pragma unroll
+      for (int i = 0; i < KP; ++i) {
+        const int L = 64 * i + lane, kk = L / (D / 16), pc = L % (D / 16);
+        const uint32_t* w = reinterpret_cast<const uint32_t*>(&kraw[i]);
+        kl[kk * KROW + 2 * pc] = fp8x8_to_bf16(w[0], w[1]);
+        kl[kk * KROW + 2 * pc + 1] = fp8x8_to_bf16(w[2], w[3]);
+      }
+      // tile tv's V codes (see convert_v): zeroed where the scale is below the normal
+      // range, negated where it is negative
+      const bool tiny_v = fabsf(vs_v) < FLT_MIN;
+      const uint32_t zmask = uint32_t(__ballot(lane < WK && tiny_v));
+      const uint32_t nmask = uint32_t(__ballot(lane < WK && vs_v < 0.f && !tiny_v));
+#pragma unroll
+      for (int i = 0; i < VP; ++i) {
+        const int d = 64 * i + lane;
+        const uint32_t* w = reinterpret_cast<const uint32_t*>(&vraw[i]);
+        bf16x8 o[2] = {fp8x8_to_bf16(w[0], w[1]), fp8x8_to_bf16(w[2], w[3])};
+        if (zmask | nmask) {
+#pragma unroll
+          for (int k = 0; k < WK; ++k) {
+            if ((nmask >> k) & 1) o[k >> 3][k & 7] = -o[k >> 3][k & 7];
+            if ((zmask >> k) & 1) o[k >> 3][k & 7] = bf16(0.f);
+          }
+        }
+        const int flip = (d >> 3) & 1;
+        vl[2 * d + flip] = o[0];
+        vl[2 * d + (flip ^ 1)] = o[1];
+      }
+    }
+  };
+
   // ---- per-wave compute pieces
   const int kread = (kap >> 4) * KSS + (kap & 15) * KROW + h;       // + 2*b*KSS + 2*kc
   const int vread = rho * 2 + (h ^ ((rho >> 3) & 1));               // + (2b+t)*VSC + 64*db
@@ -967,6 +1027,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
     if constexpr (FAST) {
       __builtin_amdgcn_sched_barrier(0);      // the wait stays after all of the block's work
       wait_vmem();
+      widen_full(j + 2, j & 1, j + 1, (j + 1) & 1);
       __syncthreads();
     } else {
       stage_done(j);
@@ -976,7 +1037,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
   using yes = std::true_type;
   int j = 0;
   const int j_nm = min(j_last, max(0, t_mask - 1));   // j < j_nm: tile j+1 needs no mask
-  const int j_f = F8 ? 0 : min(j_last, ntiles - 3);    // j < j_f: fast
+  const int j_f = min(j_last, ntiles - 3);             // j < j_f: fast
   for (; j < min(j_nm, j_f); ++j) step(j, no{}, yes{});
   for (; j < j_nm; ++j) step(j, no{}, no{});
   for (; j < j_f; ++j) step(j, yes{}, yes{});

@@ -978,14 +978,14 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
   };
   // iteration j < j_last: tile j+1's scores (MFMA) under tile j's exponentials (VALU), then
   // tile j's P.V (MFMA) under tile j+1's max and exponent arguments (VALU).  MASKED: tile
-  // j+1 needs the causal mask.  FAST (bf16, tiles j+1 and j+2 not the last: no tail to
-  // clear, every copy whole): from the first MFMA to the barrier one basic block, so the
-  // compiler keeps each VALU part beside the MFMAs it overlaps, and the copies are issued
-  // inside it, K(j+2) between the two score blocks and V(j+1) before the P.V, instead of
-  // all waves of the workgroup issuing them at once after the barrier (the copy queue
-  // then holds each wave for hundreds of cycles).  A rescale decided for tile j+1 is
-  // applied to the accumulator at the top of the next iteration, after tile j's P.V and
-  // before tile j+1's.
+  // j+1 needs the causal mask.  FAST (tiles j+1 and j+2 not the last: no tail to clear,
+  // every copy whole, fp8 codes widened without branches): from the first MFMA to the
+  // barrier one basic block, so the compiler keeps each VALU part beside the MFMAs it
+  // overlaps.  IN_BLOCK (fast bf16 whole tiles): the copies are issued inside that block,
+  // K(j+2) between the two score blocks and V(j+1) before the P.V, instead of all waves of
+  // the workgroup issuing them at once after the barrier (the copy queue then holds each
+  // wave for hundreds of cycles).  A rescale decided for tile j+1 is applied to the
+  // accumulator at the top of the next iteration, after tile j's P.V and before tile j+1's.
   auto step = [&](int j, auto masked, auto fast) {
     constexpr bool FAST = decltype(fast)::value;
     if (rescale) {

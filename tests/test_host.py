@@ -314,13 +314,18 @@ def test_cut_prefill_tiles_cover_every_visible_pair_once(name, make, split, cut)
         assert st["combine_rows"] == 256 * 32
         assert sorted(set((tiles[:, 7] // 8192).tolist())) == list(range(8))
         # 64 groups of 8 tiles reading one key chunk of one KV head, 8 groups per XCD:
-        # every group sits at launch positions of one XCD (position % 8), each XCD's
-        # positions heaviest first
+        # every group sits at launch positions of one XCD (position % 8); each XCD's first
+        # 32 positions (one per CU) hold its heaviest tiles heaviest first, the next 32 (each
+        # CU's second slot) the rest of its 64 heaviest lightest first, so that XCD positions
+        # c and c + 32, which start on one CU, pair heavy with light; later positions heaviest
+        # first
         xcd = {}
         for p, t in enumerate(tiles):
             assert xcd.setdefault((int(t[1]), int(t[7])), p % 8) == p % 8
         for x in range(8):
-            assert np.all(np.diff(work[x::8]) <= 0)
+            wx = work[x::8]
+            assert np.array_equal(np.concatenate([wx[:32], wx[32:64][::-1]]), np.sort(wx[:64])[::-1])
+            assert np.all(np.diff(wx[64:]) <= 0) and (len(wx) <= 64 or wx[64:].max() <= wx[:64].min())
 
 
 @pytest.mark.parametrize("name,make,flags", CASES, ids=[c[0] for c in CASES])
@@ -578,3 +583,20 @@ def test_binding_rejects_wrong_scale_and_append_pool_shapes():
         api.varlen_attn_append_kv_fp8(num_kv_heads=p.num_kv_heads, head_dim=p.head_dim, page_size=p.page_size,
                                       num_pages=p.num_pages, k_new=new, v_new=new, out_cache_loc=loc, k_pool=k8,
                                       v_pool=v8, k_scale=short, v_scale=ks)
+
+
+def test_launch_order_pairs_heavy_with_light_tiles_on_each_cu():
+    # ORCA's 4096-row prefill: 1024 tiles of 2..64 steps of 64 keys plus 64 decode tiles, 136
+    # per XCD.  XCD positions c and c + 32 start together on one CU, so each XCD's first 64
+    # positions pair its heaviest tile with the lightest of those 64: every CU's first two
+    # tiles sum to the same work, and the remaining tiles follow heaviest first.
+    w = W.config(2)
+    tiles = api.varlen_attn_plan_export(_plan(w), 3)
+    work = tiles[:, 6] - tiles[:, 7]
+    for x in range(8):
+        wx = work[x::8]
+        assert len(wx) == 136
+        pair_sums = wx[:32] + wx[32:64]
+        assert pair_sums.max() - pair_sums.min() <= 128          # one 64-key step each way
+        assert np.all(np.diff(wx[:32]) <= 0) and np.all(np.diff(wx[32:64]) >= 0)
+        assert np.all(np.diff(wx[64:]) <= 0) and wx[64:].max() <= wx[:64].min()

@@ -109,6 +109,10 @@ SMALL = [
     ("shared-6 plain", 5, 1, 0),
     ("spec-decode-mtp7/8", 7, 8, 0),
     ("shared-6 split items", 5, 1, api.VA_FLAG_SHARED_PREFIX | api.VA_FLAG_NO_PREFILL_KERNEL),
+    # the decodes of a plan with prefill tiles ride in that launch as tiles when their KV is
+    # small (the cases above); with decode tiles off they run as split-KV items beside them
+    ("orca-mixed/4 decodes on items", 2, 4, api.VA_FLAG_NO_DECODE_TILES),
+    ("chunk-mix/8 decodes on items", 4, 8, api.VA_FLAG_NO_DECODE_TILES),
 ]
 
 
@@ -124,8 +128,9 @@ def test_fp8_parity_split_len_64():
     """Many parts per output (every 64-key step its own item) through the combine pass."""
     w = W.config(4, scale=16, poison_tail=True, dtype="fp8")
     _say("[gpu] fp8 split_len=64")
-    out, plan = _run(w, split_len=64)
-    assert api.varlen_attn_plan_stats(plan)["combine_rows"] > 0
+    out, plan = _run(w, api.VA_FLAG_NO_DECODE_TILES, split_len=64)
+    st = api.varlen_attn_plan_stats(plan)
+    assert st["combine_rows"] > 0 and st["split_items"] > 0
     _check_full(w, out, "fp8 chunk-mix/16 split 64")
 
 
@@ -222,11 +227,14 @@ def test_fp8_unusual_scales(d, ps):
     vs[(u >= 0.15) & (u < 0.25)] *= -1
     ks[rng.random(ks.shape) < 0.1] *= -1
     w.v_scale, w.k_scale = vs.astype(np.float32), ks.astype(np.float32)
-    _say(f"[gpu] fp8 unusual scales d{d} ps{ps}")
-    out, plan = _run(w)
-    st = api.varlen_attn_plan_stats(plan)
-    assert st["prefill_tiles"] > 0 and st["split_items"] > 0, st
-    _check_full(w, out, f"fp8 unusual scales d{d} ps{ps}")
+    # the decodes ride in the prefill launch as tiles (their KV is small), and, with decode
+    # tiles off, run as split-KV items: both paths see the unusual scales
+    for flags, on_items in ((0, False), (api.VA_FLAG_NO_DECODE_TILES, True)):
+        _say(f"[gpu] fp8 unusual scales d{d} ps{ps} decodes on {'items' if on_items else 'tiles'}")
+        out, plan = _run(w, flags)
+        st = api.varlen_attn_plan_stats(plan)
+        assert st["prefill_tiles"] > 0 and (st["split_items"] > 0) == on_items, st
+        _check_full(w, out, f"fp8 unusual scales d{d} ps{ps} decodes on {'items' if on_items else 'tiles'}")
 
 
 def test_fp8_deterministic_and_gather():

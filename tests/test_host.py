@@ -224,6 +224,11 @@ FOLD_CASES = [
     ("decode-heavy no-decode-tiles", lambda: W.config(3), api.VA_FLAG_NO_DECODE_TILES, False),
     ("decode-heavy/16", lambda: W.config(3, scale=16), 0, False),          # 128 tiles: items stay
     ("decode-heavy fp8", lambda: W.config(3, dtype="fp8"), 0, False),      # fp8 tiles widen every code
+    # fp8 plans with prefill tiles take their decodes into that launch when the decodes' KV is
+    # small: ORCA's two (27 MB of codes and scales) ride as tiles, the chunk mix's 64 (1.15 GB)
+    # stay items
+    ("orca fp8", lambda: W.config(2, dtype="fp8"), 0, True),
+    ("chunk-mix fp8", lambda: W.config(4, dtype="fp8"), 0, False),
     ("spec-decode-mtp7", lambda: W.config(7), 0, True),
     ("orca", lambda: W.config(2), 0, True),
     ("few long decodes (cut)", lambda: W.build("fl", [1] * 4, [32768] * 4, num_q_heads=32, num_kv_heads=8,
@@ -600,3 +605,4 @@ def test_launch_order_pairs_heavy_with_light_tiles_on_each_cu():
         assert pair_sums.max() - pair_sums.min() <= 128          # one 64-key step each way
         assert np.all(np.diff(wx[:32]) <= 0) and np.all(np.diff(wx[32:64]) >= 0)
         assert np.all(np.diff(wx[64:]) <= 0) and wx[64:].max() <= wx[:64].min()
+

@@ -61,6 +61,11 @@ struct Block {          // a set of <= 16 query columns scored against one kv ra
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// fp8 plans: decodes whose KV (codes and scales) is at most this many bytes run as tiles in
+// the prefill launch (below the break-even of about 200 MB, where streaming at 4.6 instead of
+// 5.6 TB/s costs the ~8 us that the separate split-KV launch and its combine take)
+constexpr int64_t kFp8FoldBytes = int64_t(128) << 20;
+
 // Shared-prefix groups among requests whose block tables start with the same physical page.
 // `mem` are those requests; run(a, b) is the number of leading pages requests a and b have
 // in common (already capped by the full pages every row of both sees).  Sorted by their page
@@ -550,16 +555,25 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
   // and for fp8 pools, whose tiles widen every code (644 vs 450 us).  So short requests
   // that are not shared-prefix group members become tiles when the plan is bf16, the row
   // classification is the default one, and the tiles (after cutting) fill every resident
-  // slot; otherwise they stay split-KV items.
+  // slot; otherwise they stay split-KV items.  In an fp8 plan that launches prefill tiles
+  // anyway, a few decodes ride in that launch as tiles when their KV is small: their slower
+  // streaming through the widening tiles (about 4.6 against 5.6 TB/s as items) then costs
+  // less than the split-KV launch and its combine (ORCA's two decodes: 173.5 against
+  // 181.6 us; the chunk mix's 64 decodes, 1.15 GB, equal either way, stay items).
   std::vector<CombineRow> cut_rows;
   int64_t cut_slots = 0;
   {
     std::vector<int> fold;
-    const bool may_fold = use_prefill && p.dtype == VA_DTYPE_BF16 && p.prefill_min_rows <= 0 &&
-                          !(p.flags & VA_FLAG_NO_DECODE_TILES);
+    const bool dflt = use_prefill && p.prefill_min_rows <= 0 && !(p.flags & VA_FLAG_NO_DECODE_TILES);
+    const bool fp8_fold = p.dtype == VA_DTYPE_FP8_E4M3 && !tile_reqs.empty();
+    const bool may_fold = dflt && (p.dtype == VA_DTYPE_BF16 || fp8_fold);
+    int64_t fold_pos = 0;                              // kv positions of the folded requests
     if (may_fold)
       for (int r : short_reqs)
-        if (shared_pages[r] == 0) fold.push_back(r);
+        if (shared_pages[r] == 0) {
+          fold.push_back(r);
+          fold_pos += kv_len[r];
+        }
     std::vector<PrefillTile> tiles;
     for (int r : tile_reqs) add_tiles(tiles, r);
     bool folded = false;
@@ -569,7 +583,8 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
       std::vector<CombineRow> rows;
       int64_t nslots = 0;
       cut_tiles(with, rows, nslots);
-      if (with.size() >= size_t(slots_wg)) {
+      const int64_t fold_bytes = fold_pos * int64_t(Hkv) * 2 * (int64_t(p.head_dim) + 4);   // fp8 codes + scales
+      if (fp8_fold ? fold_bytes <= kFp8FoldBytes : with.size() >= size_t(slots_wg)) {
         plan->tiles.swap(with);
         cut_rows.swap(rows);
         cut_slots = nslots;

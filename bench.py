@@ -147,7 +147,7 @@ LAYERS = 32     # attention layers of the model the headline iteration is shaped
 SECONDARY_WARMUP = 10
 
 
-def time_graph(api, plan, tensors, steps, warmup, layers=LAYERS, settle_s=0.0):
+def time_graph(api, plan, tensors, steps, warmup, layers=LAYERS, settle_s=0.0, launches=1):
     """Steps as a model's forward issues them: run i reads and writes the buffers of layer
     i % layers (each layer its own copy of Q, K, V and the output, so no layer finds the
     previous layer's data in the last-level cache; one plan and workspace for all, as in
@@ -157,7 +157,8 @@ def time_graph(api, plan, tensors, steps, warmup, layers=LAYERS, settle_s=0.0):
     first launch also uploads it).  Timed: one launch of the graph
     of `steps` runs between synchronisations, by the wall clock.  Returns (ms/step, ms/step
     with one graph launch per run, ms/step between HIP events recorded on the launch stream
-    around the timed graph launch)."""
+    around the timed graph launch, the graph replays before it, and the events' ms/step of
+    each of `launches` timed launches)."""
     import torch
     q, k, v, bt, out, ws = tensors[:6]
     scales = dict(zip(("k_scale", "v_scale"), tensors[6:]))
@@ -191,14 +192,17 @@ def time_graph(api, plan, tensors, steps, warmup, layers=LAYERS, settle_s=0.0):
                 break
     g_steps.replay()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record()
-    g_steps.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / steps
-    ms_events = e0.elapsed_time(e1) / steps
+    per_launch = []
+    for _ in range(launches):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        g_steps.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        per_launch.append(e0.elapsed_time(e1) / steps)
+    ms_events = per_launch[0]
     # the same runs launched one graph each (launch overhead per run included)
     g1 = capture(1)
     g1.replay()
@@ -210,7 +214,7 @@ def time_graph(api, plan, tensors, steps, warmup, layers=LAYERS, settle_s=0.0):
     ms_single = (time.perf_counter() - t0) * 1e3 / steps
     del g_warm, g_steps, g1, calls, sets
     torch.cuda.empty_cache()
-    return ms, ms_single, ms_events, n_warm * max(1, warmup)
+    return ms, ms_single, ms_events, n_warm * max(1, warmup), per_launch
 
 
 def setup(api, w, flags=0):
@@ -454,24 +458,55 @@ def make_flush():
     return flush
 
 
-def secondary(api, W, cid, flags, reps, label, flush, key=None, dtype=None, tp=1, dp=1, w=None):
-    """Time one workload (config `cid`, or the given Workload `w`) as eager runs with the
-    library's stage events; returns the full record (see compact())."""
+def graph_layers(w):
+    """Layer copies for a graph-timed line: enough that the rotating buffers hold over 1 GiB
+    (four times the 256 MB last-level cache), so no run finds its K/V there from the runs
+    before it; at least 2, at most LAYERS."""
+    per = w.k_pool.nbytes + w.v_pool.nbytes + 2 * w.q.nbytes
+    return int(min(LAYERS, max(2, -(-(1 << 30) // max(1, per)) + 1)))
+
+
+def secondary(api, W, cid, flags, reps, label, flush, key=None, dtype=None, tp=1, dp=1, w=None, graph=True):
+    """Time one workload (config `cid`, or the given Workload `w`); returns the full record
+    (see compact()).  The step: `reps` runs captured in one HIP graph over graph_layers(w)
+    copies of its buffers, so consecutive runs read different K/V as consecutive layers do,
+    launched five times (median, min and max of the HIP-event time per run around each
+    launch); a run of a single-launch plan is that kernel, whose time this also is.  With
+    graph=False (a line defined by evicting the cache before every run) the step is the span
+    of eager runs between the library's first and last events less the three event records
+    inside it.  Per-kernel times come from eager runs with the library's stage events (after
+    `flush`, if given), each stage less the cost of one event record: measured in place as
+    the empty split-KV stage when the plan has no split-KV items."""
     if w is None:
         w = W.config(cid, dtype=dtype, tp=tp, dp=dp)
     plan, tensors = setup(api, w, flags)
     st = api.varlen_attn_plan_stats(plan)
     settled = settle_clocks(api, plan, tensors, 0.1)     # the workload's build and planning left the GPU idle
     _, stage, totals = time_runs(api, plan, tensors, reps, SECONDARY_WARMUP, flush)
-    # the step's time less the cost of the three event records inside it (see dominant())
-    steps_us = [(t - 3 * stage.get("event_record", 0.0)) * 1e3 for t in totals]
-    us = float(np.median(steps_us))
+    if st["split_items"] == 0:
+        stage["event_record"] = stage["split_kv"]        # no kernel between those two events
+    one_launch = st["split_items"] == 0 and st["combine_rows"] == 0
+    kernel_ms = None
+    if graph:
+        layers = graph_layers(w)
+        *_, per_launch = time_graph(api, plan, tensors, reps, SECONDARY_WARMUP, layers=layers, settle_s=0.05,
+                                    launches=5)
+        steps_us = [x * 1e3 for x in per_launch]
+        us = float(np.median(steps_us))
+        lo, hi = min(steps_us), max(steps_us)
+        kernel_ms = us * 1e-3 if one_launch else None
+        how = f"one hip-graph launch of {reps} runs over {layers} layers' buffers, median of 5 launches (min, max)"
+    else:
+        # the step's time less the cost of the three event records inside it (see dominant())
+        steps_us = [(t - 3 * stage.get("event_record", 0.0)) * 1e3 for t in totals]
+        us = float(np.median(steps_us))
+        lo, hi = float(np.percentile(steps_us, 10)), float(np.percentile(steps_us, 90))
+        how = f"{reps} eager runs, the last-level cache evicted before each (median, p10, p90)"
     byts = st["physical_kv_bytes"] + st["q_bytes"] + st["o_bytes"] + st["table_bytes"]
     # time at the roofline if the FLOPs and the bytes could not overlap at all
     t_roof_us = (st["flops"] / PEAK_BF16 + byts / PEAK_HBM) * 1e6
     res = {"workload": label, "us_per_step": round(us, 2),
-           "us_p10": round(float(np.percentile(steps_us, 10)), 2),
-           "us_p90": round(float(np.percentile(steps_us, 90)), 2),
+           "us_p10": round(lo, 2), "us_p90": round(hi, 2), "timing": how,
            "t_roof_us": round(t_roof_us, 2), "t_roof_frac": round(t_roof_us / us, 4),
            "share": {"tp": tp, "dp": dp} if tp > 1 or dp > 1 else None,
            "hbm_GBps": round(byts / (us * 1e-6) / 1e9, 1), "hbm_frac": round(byts / (us * 1e-6) / PEAK_HBM, 4),
@@ -479,8 +514,8 @@ def secondary(api, W, cid, flags, reps, label, flush, key=None, dtype=None, tp=1
            "algorithmic_bytes": byts, "logical_kv_bytes": st["logical_kv_bytes"],
            "physical_kv_bytes": st["physical_kv_bytes"], "flops": st["flops"],
            "stage_ms": {k: round(v, 5) for k, v in stage.items()},
-           "roofline": roofline(st, stage, key, fp8=w.dtype == "fp8"), "l2_flushed": flush is not None,
-           "settle_runs": settled,
+           "roofline": roofline(st, stage, key, fp8=w.dtype == "fp8", kernel_ms=kernel_ms),
+           "l2_flushed": flush is not None, "settle_runs": settled,
            "dtype": w.dtype}
     del tensors
     return res
@@ -547,7 +582,8 @@ def targets(rec, full):
         x = full[key]
         t[name] = {"us": x["us_per_step"], "hbm_frac_physical": x["hbm_frac"], **kern(x),
                    "physical_MiB": round(x["physical_kv_bytes"] / 2**20, 1),
-                   "logical_MiB": round(x["logical_kv_bytes"] / 2**20, 1), "llc_evicted": x["l2_flushed"]}
+                   "logical_MiB": round(x["logical_kv_bytes"] / 2**20, 1),
+                   "no_llc_reuse": "step over rotating layers' buffers; kernel time with the cache evicted"}
         if goal:
             t[name]["target"] = goal + " of 8 TB/s on physical bytes"
     return t
@@ -612,8 +648,8 @@ def main():
     # same run captured in a HIP graph and replayed (no per-launch host gaps)
     settled = settle_clocks(api, plan, tensors)
     wall_eager, stage, totals = time_runs(api, plan, tensors, args.steps, args.warmup)
-    ms, ms_single, ms_graph_events, settled_graph = time_graph(api, plan, tensors, args.steps, args.warmup,
-                                                               settle_s=CLOCK_SETTLE_S)
+    ms, ms_single, ms_graph_events, settled_graph, _ = time_graph(api, plan, tensors, args.steps, args.warmup,
+                                                                  settle_s=CLOCK_SETTLE_S)
     value = st["flops"] / (ms * 1e-3) / 1e12
     # a run of this plan is one launch of the prefill kernel (its decodes ride in it as
     # tiles), so the timed graph launch is that kernel back to back: its average launch
@@ -680,7 +716,7 @@ def main():
         del w4
         log("[bench] secondary: the ORCA iteration with the last-level cache evicted before each run")
         add("orca_llc_evicted", secondary(api, W, 2, 0, 20, "orca-mixed, last-level cache evicted before each run",
-                                          flush, None))
+                                          flush, None, graph=False))
         # one GPU's share when the iteration is split over 8 GPUs (the kernels at their real shape)
         for cid, tp, dp, key in ((4, 8, 1, "chunk_tp8"), (2, 8, 1, "orca_tp8"), (3, 1, 8, "decode_dp8")):
             log(f"[bench] secondary: {key}")

@@ -354,13 +354,22 @@ def test_shared_prefix_groups_found():
     st = api.varlen_attn_plan_stats(_plan(w, api.VA_FLAG_SHARED_PREFIX))
     assert st["shared_groups"] == 1 and st["shared_tiles"] > 0 and st["shared_items"] == 0
     assert st["physical_kv_bytes"] == 40 * 2 ** 20 and st["logical_kv_bytes"] == 120 * 2 ** 20
-    # split items read only the 6 private ranges of 1024 positions (8 KV heads, K and V, bf16)
-    assert st["split_item_kv_bytes"] == 6 * 1024 * 8 * 128 * 2 * 2
-    assert st["split_item_flops"] == 4 * 128 * 32 * 6 * 1024
     assert st["shared_tile_flops"] == 4 * 128 * (6 * 4) * 4096 * 8
-    # with 64 members the private ranges run as column-list tiles of their own: no split items
+    # the private ranges run as column-list tiles in the same launch: 128 group tiles (256-key
+    # chunks of the 4096 shared keys, 8 KV heads) leave 384 of the 512 resident slots, so the
+    # 6 x 8 private ranges of 1024 keys are cut into 128-key chunks (384 tiles); no split items
+    assert st["split_items"] == 0 and st["split_item_kv_bytes"] == 0 and st["split_item_flops"] == 0
+    assert st["prefill_tiles"] == 128 + 6 * 8 * 1024 // 128
+    # with 64 members the 256 group tiles leave 256 slots, and the 512 private ranges stay
+    # whole tiles (cut, they would need 2048-key chunks)
     st64 = api.varlen_attn_plan_stats(_plan(W.config(51), api.VA_FLAG_SHARED_PREFIX))
     assert st64["split_items"] == 0 and st64["split_item_kv_bytes"] == 0 and st64["split_item_flops"] == 0
+    assert st64["prefill_tiles"] == 256 + 64 * 8
+    # decode tiles off: the private ranges are split-KV items reading only those ranges
+    # (6 x 1024 positions, 8 KV heads, K and V, bf16)
+    sti = api.varlen_attn_plan_stats(_plan(w, api.VA_FLAG_SHARED_PREFIX | api.VA_FLAG_NO_DECODE_TILES))
+    assert sti["split_item_kv_bytes"] == 6 * 1024 * 8 * 128 * 2 * 2
+    assert sti["split_item_flops"] == 4 * 128 * 32 * 6 * 1024
     st0 = api.varlen_attn_plan_stats(_plan(w))
     assert st0["shared_groups"] == 0 and st0["split_item_kv_bytes"] == st0["physical_kv_bytes"]
 

@@ -651,15 +651,11 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
     }
   }
   // A group member's own keys after the shared pages: column-list tiles in the same launch
-  // as the group tiles (bf16 plans, as for decode tiles) when those tiles and the plan's
-  // other tiles fill the resident slots (64 members: 94 -> 83 us), else split items (6
-  // members: 48 thin tiles would take 23 us where 768 items take 15 us).
-  int64_t n_suffix = 0;
-  for (int r : split_reqs)
-    if (shared_pages[r] > 0) n_suffix += Hkv * ceil_div(int64_t(q_end[r] - q_start[r]) * g, kPrefillCols);
+  // as the group tiles (bf16 plans, as for decode tiles), cut into key chunks so that they
+  // fill the slots the launch's other tiles leave (below), instead of split-KV items in a
+  // launch of their own (64 members: 94 -> 83 us; 6 members: 18.3 -> 13.2 us).
   const bool suffix_tiles = use_prefill && p.dtype == VA_DTYPE_BF16 && p.prefill_min_rows <= 0 &&
-                            !(p.flags & VA_FLAG_NO_DECODE_TILES) &&
-                            n_suffix + int64_t(plan->tiles.size()) >= slots_wg;
+                            !(p.flags & VA_FLAG_NO_DECODE_TILES);
   for (int r : split_reqs) {
     const int ncol = (q_end[r] - q_start[r]) * g;
     for (int kvh = 0; kvh < Hkv; ++kvh) {
@@ -703,10 +699,34 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
   const int64_t Lt = std::min<int64_t>(
       4096, std::max<int64_t>(256, ceil_div(ceil_div(tile_keys * tile_cols, std::max(1, slots_wg / 2)), kStepKeys) *
                                        kStepKeys));
+  // members' own keys: the shortest key chunk (a power of two from 64 keys) with which the
+  // member tiles fit in the resident slots the launch's other tiles leave; keys shorter than
+  // it stay one tile (64 members of 16K: whole 1024-key tiles, 71 us where 512-key chunks
+  // took 74 us; 6 members of 4K: 128-key chunks, 13.2 us where 64- and 256-key chunks took
+  // 15.6 and 14.5 us)
+  int64_t other_tiles = int64_t(plan->tiles.size()), member_keys = 0;
+  for (auto& B : blocks)
+    if (B.tile) {
+      const int64_t keys = std::max(0, B.kend - B.kstart);
+      if (B.shared)
+        other_tiles += ceil_div(keys, Lt);
+      else
+        member_keys += keys;
+    }
+  const int64_t free_slots = std::max<int64_t>(1, slots_wg - other_tiles);
+  int64_t Ls = kStepKeys;
+  while (Ls < 8192 && Ls * free_slots < member_keys) Ls *= 2;
   for (auto& B : blocks) {
     const int64_t keys = std::max(0, B.kend - B.kstart);
-    B.chunk = int32_t(B.tile ? (B.shared ? Lt : 8192) : L);
+    B.chunk = int32_t(B.tile ? (B.shared ? Lt : Ls) : L);
     B.nchunks = int32_t(ceil_div(keys, B.chunk));
+    if (B.tile && B.nchunks > 1) {
+      // every chunk tile starts at a key all its columns see (a column-list tile's columns
+      // each need at least one key); the last chunk runs on to the block's end, through the
+      // diagonal of a multi-row member
+      const int64_t seen = std::max<int64_t>(1, int64_t(B.min_limit) + 1 - B.kstart);
+      B.nchunks = int32_t(std::max<int64_t>(1, std::min<int64_t>(B.nchunks, ceil_div(seen, B.chunk))));
+    }
   }
 
   // ---- partial slots: every (row, head) output of the split path that is not written
@@ -775,7 +795,7 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
         t.ncols = int32_t(B.outs.size());
         t.q0 = B.shared ? j : shared_n[B.outs[0]] + j;   // partial slot of this chunk
         t.S0 = int32_t(B.kstart + int64_t(j) * B.chunk);
-        t.kv_end = int32_t(std::min<int64_t>(B.kend, B.kstart + int64_t(j + 1) * B.chunk));
+        t.kv_end = j + 1 == B.nchunks ? B.kend : int32_t(std::min<int64_t>(B.kend, B.kstart + int64_t(j + 1) * B.chunk));
         t.kbeg = t.S0;
         t.pbase = -1;
         t.pstride = 0;

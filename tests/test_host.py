@@ -233,9 +233,13 @@ FOLD_CASES = [
     ("orca", lambda: W.config(2), 0, True),
     ("few long decodes (cut)", lambda: W.build("fl", [1] * 4, [32768] * 4, num_q_heads=32, num_kv_heads=8,
                                                head_dim=128, page_size=64, seed=3), 0, True),
-    # members' own keys after the shared pages: column-list tiles (bf16), split items (fp8)
+    # members' own keys after the shared pages: column-list tiles (bf16; fp8 when their codes
+    # and scales are small), else split items
     ("shared-prefix-64", lambda: W.config(51), api.VA_FLAG_SHARED_PREFIX, True),
     ("shared-prefix-64 fp8", lambda: W.config(51, dtype="fp8"), api.VA_FLAG_SHARED_PREFIX, False),
+    # 6 members: their private keys (13 MB of codes and scales) ride in the group tiles' launch
+    ("shared-prefix-6", lambda: W.config(5), api.VA_FLAG_SHARED_PREFIX, True),
+    ("shared-prefix-6 fp8", lambda: W.config(5, dtype="fp8"), api.VA_FLAG_SHARED_PREFIX, True),
 ]
 
 

@@ -61,10 +61,12 @@ struct Block {          // a set of <= 16 query columns scored against one kv ra
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// fp8 plans: decodes whose KV (codes and scales) is at most this many bytes run as tiles in
-// the prefill launch (below the break-even of about 200 MB, where streaming at 4.6 instead of
-// 5.6 TB/s costs the ~8 us that the separate split-KV launch and its combine take)
-constexpr int64_t kFp8FoldBytes = int64_t(128) << 20;
+// fp8 plans: decodes (or shared-prefix members' own keys) whose codes and scales take at
+// most this many bytes run as tiles in the launch of the plan's other tiles rather than as
+// split-KV items in a launch of their own: streaming at about 4.6 instead of 5.6 TB/s then
+// costs less than the separate launch and its combine (about 8 us; break-even near 200 MB
+// for decodes, below 138 MB for 64 members' private keys)
+constexpr int64_t kFp8FoldBytes = int64_t(64) << 20;
 
 // Shared-prefix groups among requests whose block tables start with the same physical page.
 // `mem` are those requests; run(a, b) is the number of leading pages requests a and b have
@@ -651,11 +653,18 @@ extern "C" va_status varlen_attn_plan(const va_params* params, int32_t num_reqs,
     }
   }
   // A group member's own keys after the shared pages: column-list tiles in the same launch
-  // as the group tiles (bf16 plans, as for decode tiles), cut into key chunks so that they
-  // fill the slots the launch's other tiles leave (below), instead of split-KV items in a
-  // launch of their own (64 members: 94 -> 83 us; 6 members: 18.3 -> 13.2 us).
-  const bool suffix_tiles = use_prefill && p.dtype == VA_DTYPE_BF16 && p.prefill_min_rows <= 0 &&
-                            !(p.flags & VA_FLAG_NO_DECODE_TILES);
+  // as the group tiles, cut into key chunks so that they fill the slots the launch's other
+  // tiles leave (below), instead of split-KV items in a launch of their own (64 members:
+  // 94 -> 83 us; 6 members: 24.3 -> 17.7 us).  fp8 plans do so, as for their decodes, only
+  // when those keys' codes and scales are small (6 members: 25.2 -> 19.9 us; 64 members,
+  // 138 MB: 71.3 -> 77.2 us, so they stay items).
+  int64_t suffix_pos = 0;
+  for (int r : split_reqs)
+    if (shared_pages[r] > 0) suffix_pos += kv_len[r] - int64_t(shared_pages[r]) * ps;
+  const bool suffix_tiles =
+      use_prefill && p.prefill_min_rows <= 0 && !(p.flags & VA_FLAG_NO_DECODE_TILES) &&
+      (p.dtype == VA_DTYPE_BF16 ||
+       (p.dtype == VA_DTYPE_FP8_E4M3 && suffix_pos * Hkv * 2 * (int64_t(p.head_dim) + 4) <= kFp8FoldBytes));
   for (int r : split_reqs) {
     const int ncol = (q_end[r] - q_start[r]) * g;
     for (int kvh = 0; kvh < Hkv; ++kvh) {

@@ -474,6 +474,37 @@ def test_shared_prefix_uneven_groups_elementwise(kind, dtype):
         assert np.isfinite(got).all() and e <= tol
 
 
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_shared_prefix_multirow_members_in_key_chunks_elementwise(dtype):
+    """Six members of a 4096-key shared prefix, each with 15 verify rows (60 columns per KV
+    head) and 1032 private keys: the private keys run as column-list tiles cut into 256-key
+    chunks, and since the last 8 keys lie past some rows' limits the last chunk starts where
+    every row still sees keys and runs on through the diagonal (fp8: the private keys are
+    small, so they ride in the same launch too)."""
+    base = W.build(f"shared-mtp15-{dtype}", [15] * 6, [4096 + 1032] * 6, num_q_heads=32, num_kv_heads=8,
+                   head_dim=128, page_size=64, seed=31, shared_prefix_pages=64, dtype=dtype, poison_tail=True)
+    for w in (base, W.focus(base)):
+        _say(f"[gpu] shared-prefix multi-row members {w.name} {w.dtype}")
+        out, plan = api.run_workload(w, flags=api.VA_FLAG_SHARED_PREFIX)
+        st = api.varlen_attn_plan_stats(plan)
+        tiles = api.varlen_attn_plan_export(plan, 3)
+        own = tiles[(tiles[:, 10] & 1) == 1]
+        own = own[own[:, 11] == 0]                       # column-list tiles of private keys
+        assert st["shared_groups"] == 1 and st["split_items"] == 0 and len(own) == 6 * 8 * 4, st
+        assert set((own[:, 6] - own[:, 7]).tolist()) == {256, 264}   # three 256-key chunks, the last 264
+        got = out.float().cpu().numpy().astype(np.float64)
+        if dtype == "fp8":
+            K, V = oracle.dequantize_pools(w.k_pool, w.k_scale, w.v_pool, w.v_scale)
+            tol = 1e-2
+        else:
+            K, V, tol = w.k_pool, w.v_pool, TOL[w.dtype]
+        ref = oracle.varlen_paged_attention(w.q, K, V, w.block_table, w.q_start, w.q_end, w.kv_len, w.page_size)
+        e = float(np.abs(got - ref).max())
+        _say(f"[parity] shared-prefix multi-row members {w.name} {w.dtype}: max|gpu-oracle| = {e:.3e} (tol {tol})")
+        assert np.isfinite(got).all() and e <= tol
+
+
 def test_readme_example_runs():
     """The usage example in README.md runs as printed and its output matches the oracle."""
     import os
